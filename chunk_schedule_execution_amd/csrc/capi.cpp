@@ -1,0 +1,378 @@
+// C ABI entry points and the device runtime of a plan: upload of the lowered
+// tables, plan-owned staging / scratch / flag memory, epochs, launch, status, trace.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "ccl_internal.h"
+
+using namespace ccl;
+
+namespace {
+
+thread_local std::string g_detail;
+
+int set_error(int code, const std::string& msg) {
+  g_detail = msg;
+  return code;
+}
+
+#define HIP_TRY(expr)                                                                        \
+  do {                                                                                       \
+    hipError_t e_ = (expr);                                                                  \
+    if (e_ != hipSuccess) fail(CCL_ERR_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+template <typename F>
+int guarded(F&& f) {
+  try {
+    return f();
+  } catch (const Error& e) {
+    return set_error(e.code, e.what());
+  } catch (const std::bad_alloc&) {
+    return set_error(CCL_ERR_OUT_OF_RESOURCES, "host allocation failed");
+  } catch (const std::exception& e) {
+    return set_error(CCL_ERR_INTERNAL, e.what());
+  } catch (...) {
+    return set_error(CCL_ERR_INTERNAL, "unknown exception");
+  }
+}
+
+}  // namespace
+
+struct ccl_plan {
+  HostPlan hp;
+  bool device = false;
+  int device_id = -1;
+  std::vector<void*> allocs;
+  DevWG* d_wgs = nullptr;
+  DevInstr* d_ins = nullptr;
+  DevXfer* d_xf = nullptr;
+  int32_t* d_waits = nullptr;
+  unsigned long long* d_xflags = nullptr;
+  unsigned long long* d_dflags = nullptr;
+  unsigned char* d_staging = nullptr;
+  unsigned char* d_scratch = nullptr;
+  unsigned int* d_err = nullptr;
+  unsigned long long* d_abort = nullptr;
+  unsigned long long* d_trace = nullptr;
+  hipEvent_t last = nullptr;
+  bool launched = false;
+  unsigned long long epoch = 0;
+  long long timeout_ticks = 0;
+  int64_t scratch_stride = 0;  // bytes between ranks' scratch
+  std::mutex mu;
+
+  void* dev_alloc(size_t bytes) {
+    void* p = nullptr;
+    if (bytes == 0) bytes = 256;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) fail(CCL_ERR_OUT_OF_RESOURCES, "hipMalloc(" + std::to_string(bytes) + "): " + hipGetErrorString(e));
+    allocs.push_back(p);
+    return p;
+  }
+  void release() {
+    if (last) {
+      hipEventSynchronize(last);
+      hipEventDestroy(last);
+      last = nullptr;
+    }
+    for (void* p : allocs) hipFree(p);
+    allocs.clear();
+  }
+  ~ccl_plan() { release(); }
+};
+
+namespace {
+
+template <typename T>
+T* upload(ccl_plan* p, const std::vector<T>& v) {
+  T* d = static_cast<T*>(p->dev_alloc(std::max<size_t>(1, v.size()) * sizeof(T)));
+  if (!v.empty()) HIP_TRY(hipMemcpy(d, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice));
+  return d;
+}
+
+void setup_device(ccl_plan* p) {
+  HostPlan& hp = p->hp;
+  HIP_TRY(hipGetDevice(&p->device_id));
+  int cus = 0, rate_khz = 0;
+  HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device_id));
+  HIP_TRY(hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, p->device_id));
+  int blocks = 0;
+  std::string err;
+  int rc = executor_max_blocks_per_cu(hp.cfg.dtype, hp.cfg.nthreads, &blocks, &err);
+  if (rc) fail(rc, err);
+  hp.max_resident_wgs = blocks * cus;
+  if (int(hp.dwg.size()) > hp.max_resident_wgs)
+    fail(CCL_ERR_OUT_OF_RESOURCES, "plan needs " + std::to_string(hp.dwg.size()) + " co-resident workgroups, the device holds " +
+                                       std::to_string(hp.max_resident_wgs) + " at " + std::to_string(hp.cfg.nthreads) +
+                                       " threads");
+  if (rate_khz <= 0) rate_khz = 100000;
+  p->timeout_ticks = (long long)(hp.cfg.timeout_us * (rate_khz / 1000.0));
+  p->d_wgs = upload(p, hp.dwg);
+  p->d_ins = upload(p, hp.dins);
+  p->d_xf = upload(p, hp.dxf);
+  p->d_waits = upload(p, hp.dwaits);
+  size_t nx = std::max<size_t>(1, hp.dxf.size());
+  int nd = 0;
+  for (const auto& D : hp.dins) nd = std::max(nd, D.done_flag + 1);
+  p->d_xflags = static_cast<unsigned long long*>(p->dev_alloc(nx * 8));
+  HIP_TRY(hipMemset(p->d_xflags, 0, nx * 8));
+  p->d_dflags = static_cast<unsigned long long*>(p->dev_alloc(std::max(1, nd) * 8));
+  HIP_TRY(hipMemset(p->d_dflags, 0, std::max(1, nd) * 8));
+  p->d_staging = static_cast<unsigned char*>(p->dev_alloc(size_t(hp.staging_bytes)));
+  p->scratch_stride = ((hp.scratch_elems_per_rank * hp.esz) + 255) / 256 * 256;
+  if (p->scratch_stride) p->d_scratch = static_cast<unsigned char*>(p->dev_alloc(size_t(p->scratch_stride) * hp.P));
+  p->d_err = static_cast<unsigned int*>(p->dev_alloc(16));
+  HIP_TRY(hipMemset(p->d_err, 0, 16));
+  p->d_abort = static_cast<unsigned long long*>(p->dev_alloc(8));
+  HIP_TRY(hipMemset(p->d_abort, 0, 8));
+  if (hp.cfg.flags & CCL_FLAG_TRACE) {
+    p->d_trace = static_cast<unsigned long long*>(p->dev_alloc(hp.dwg.size() * 32));
+    HIP_TRY(hipMemset(p->d_trace, 0, hp.dwg.size() * 32));
+  }
+  HIP_TRY(hipEventCreateWithFlags(&p->last, hipEventDisableTiming));
+  HIP_TRY(hipDeviceSynchronize());
+  p->device = true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ccl_version(void) { return 1; }
+
+const char* ccl_error_string(int status) {
+  switch (status) {
+    case CCL_OK: return "success";
+    case CCL_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case CCL_ERR_INVALID_PROGRAM: return "invalid program";
+    case CCL_ERR_UNSUPPORTED: return "unsupported";
+    case CCL_ERR_OUT_OF_RESOURCES: return "out of resources";
+    case CCL_ERR_HIP: return "HIP runtime error";
+    case CCL_ERR_TIMEOUT: return "device wait timed out";
+    case CCL_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+const char* ccl_last_error_detail(void) { return g_detail.c_str(); }
+
+int ccl_plan_create(const ccl_program_desc* prog, int nranks, int nchunks, int parallel_factor,
+                    const ccl_plan_config* cfg, ccl_plan** out) {
+  if (!out) return set_error(CCL_ERR_INVALID_ARGUMENT, "null output pointer");
+  *out = nullptr;
+  return guarded([&] {
+    ccl_plan* p = new ccl_plan();
+    try {
+      compile_plan(p->hp, prog, nranks, nchunks, parallel_factor, cfg);
+      if (!(p->hp.cfg.flags & CCL_FLAG_HOST_ONLY)) {
+        setup_device(p);
+      } else {
+        int blocks = std::max(1, 2048 / p->hp.cfg.nthreads);
+        p->hp.max_resident_wgs = blocks * p->hp.cfg.num_cus;
+        if (int(p->hp.dwg.size()) > p->hp.max_resident_wgs)
+          fail(CCL_ERR_OUT_OF_RESOURCES, "plan needs more co-resident workgroups than the assumed device holds");
+      }
+    } catch (...) {
+      delete p;
+      throw;
+    }
+    *out = p;
+    return CCL_OK;
+  });
+}
+
+int ccl_plan_destroy(ccl_plan* plan) {
+  if (!plan) return CCL_OK;
+  return guarded([&] {
+    delete plan;
+    return CCL_OK;
+  });
+}
+
+int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbufs, int64_t count, void* stream) {
+  if (!plan) return set_error(CCL_ERR_INVALID_ARGUMENT, "null plan");
+  return guarded([&] {
+    std::lock_guard<std::mutex> lk(plan->mu);
+    HostPlan& hp = plan->hp;
+    if (!plan->device) fail(CCL_ERR_INVALID_ARGUMENT, "plan was created host-only");
+    if (!sendbufs || !recvbufs) fail(CCL_ERR_INVALID_ARGUMENT, "null buffer table");
+    if (count < 0 || count > hp.cfg.max_count) fail(CCL_ERR_INVALID_ARGUMENT, "count out of range [0, max_count]");
+    if (count % hp.granule)
+      fail(CCL_ERR_INVALID_ARGUMENT, "count must be a multiple of " + std::to_string(hp.granule) + " for this program");
+    for (int r = 0; r < hp.P; ++r) {
+      if (!sendbufs[r] || !recvbufs[r]) fail(CCL_ERR_INVALID_ARGUMENT, "null buffer for rank " + std::to_string(r));
+      if (sendbufs[r] == recvbufs[r]) fail(CCL_ERR_INVALID_ARGUMENT, "in-place execution is not supported");
+    }
+    if (count == 0) return CCL_OK;
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev != plan->device_id) fail(CCL_ERR_INVALID_ARGUMENT, "plan belongs to another device");
+    ExecArgs A{};
+    A.wgs = plan->d_wgs;
+    A.ins = plan->d_ins;
+    A.xf = plan->d_xf;
+    A.waits = plan->d_waits;
+    A.xflags = plan->d_xflags;
+    A.dflags = plan->d_dflags;
+    A.staging = plan->d_staging;
+    A.err = plan->d_err;
+    A.abort_word = plan->d_abort;
+    A.trace = plan->d_trace;
+    A.count = count;
+    A.slice_elems = hp.slice_elems;
+    A.epoch = plan->epoch + 1;
+    A.timeout_ticks = plan->timeout_ticks;
+    A.nchunks = hp.C;
+    A.k = hp.k;
+    for (int r = 0; r < hp.P; ++r) {
+      A.base[CCL_BUF_INPUT][r] = const_cast<unsigned char*>(static_cast<const unsigned char*>(sendbufs[r]));
+      A.base[CCL_BUF_OUTPUT][r] = static_cast<unsigned char*>(recvbufs[r]);
+      A.base[CCL_BUF_SCRATCH][r] = plan->d_scratch ? plan->d_scratch + size_t(plan->scratch_stride) * r : nullptr;
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (plan->launched) HIP_TRY(hipStreamWaitEvent(s, plan->last, 0));
+    std::string err;
+    int rc = launch_executor(A, hp.cfg.dtype, int(hp.dwg.size()), hp.cfg.nthreads, stream, &err);
+    if (rc) fail(rc, err);
+    plan->epoch += 1;
+    HIP_TRY(hipEventRecord(plan->last, s));
+    plan->launched = true;
+    return CCL_OK;
+  });
+}
+
+int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info) {
+  if (!plan || !info) return set_error(CCL_ERR_INVALID_ARGUMENT, "null argument");
+  return guarded([&] {
+    const HostPlan& hp = plan->hp;
+    std::memset(info, 0, sizeof *info);
+    info->nranks = hp.P;
+    info->nchunks = hp.C;
+    info->parallel_factor = hp.k;
+    info->dtype = hp.cfg.dtype;
+    info->num_workgroups = int(hp.dwg.size());
+    info->max_wg_per_rank = hp.max_wg_per_rank;
+    info->num_instructions = int(hp.dins.size());
+    info->num_subpipelines = hp.num_subpipes;
+    info->num_connections = hp.num_connections;
+    info->num_transfers = int(hp.dxf.size());
+    info->num_waits = int(hp.dwaits.size());
+    info->count_granule = hp.granule;
+    info->nthreads = hp.cfg.nthreads;
+    info->slice_bytes = int(hp.slice_elems * hp.esz);
+    info->max_resident_wgs = hp.max_resident_wgs;
+    info->staging_bytes = hp.staging_bytes;
+    info->scratch_bytes = hp.scratch_elems_per_rank * hp.esz * hp.P;
+    int nd = 0;
+    for (const auto& D : hp.dins) nd = std::max(nd, D.done_flag + 1);
+    info->flag_bytes = int64_t(hp.dxf.size() + nd) * 8;
+    info->table_bytes = int64_t(hp.dwg.size() * sizeof(DevWG) + hp.dins.size() * sizeof(DevInstr) +
+                                hp.dxf.size() * sizeof(DevXfer) + hp.dwaits.size() * 4);
+    for (int i = 0; i < 6; ++i) info->compile_ms[i] = hp.ms[i];
+    for (const auto& D : hp.dins) info->opcode_hist[D.op & 15]++;
+    return CCL_OK;
+  });
+}
+
+int64_t ccl_plan_bytes(const ccl_plan* plan, int64_t count) {
+  if (!plan) return set_error(CCL_ERR_INVALID_ARGUMENT, "null plan");
+  if (count < 0 || count > plan->hp.cfg.max_count) return set_error(CCL_ERR_INVALID_ARGUMENT, "count out of range");
+  int64_t v = 0;
+  int rc = guarded([&] {
+    v = plan_bytes(plan->hp, count);
+    return CCL_OK;
+  });
+  return rc ? rc : v;
+}
+
+int ccl_plan_export(const ccl_plan* plan, ccl_instr_info* out, size_t cap, size_t* n) {
+  if (!plan || !n || (cap && !out)) return set_error(CCL_ERR_INVALID_ARGUMENT, "null argument");
+  return guarded([&] {
+    const HostPlan& hp = plan->hp;
+    *n = hp.dins.size();
+    size_t j = 0;
+    for (size_t w = 0; w < hp.dwg.size(); ++w) {
+      const DevWG& G = hp.dwg[w];
+      for (int t = 0; t < G.n && j < cap; ++t, ++j) {
+        const DevInstr& D = hp.dins[G.first + t];
+        const Instr& I = hp.ins[hp.dins_base[G.first + t]];
+        ccl_instr_info& o = out[j];
+        o.rank = G.rank;
+        o.wg = int(w);
+        o.subpipe = I.sp;
+        o.channel = I.channel;
+        o.instance = D.instance;
+        o.opcode = int(D.op);
+        o.a_buf = D.a_buf;
+        o.a_idx = D.a_idx;
+        o.b_buf = D.b_buf;
+        o.b_idx = D.b_idx;
+        o.d_buf = D.d_buf;
+        o.d_idx = D.d_idx;
+        o.count = D.cnt;
+        o.recv_peer = I.xin >= 0 ? hp.xf[I.xin].src_rank : -1;
+        o.send_peer = I.xout >= 0 ? hp.xf[I.xout].dst_rank : -1;
+        o.xin = D.xin;
+        o.xout = D.xout;
+        o.nwaits = D.nwaits;
+        o.chunk_id = I.chunk_id;
+        o.done_flag = D.done_flag;
+      }
+    }
+    return CCL_OK;
+  });
+}
+
+int ccl_plan_check(const ccl_plan* plan, uint64_t seed, int nsims) {
+  if (!plan || nsims < 0) return set_error(CCL_ERR_INVALID_ARGUMENT, "bad argument");
+  return guarded([&] {
+    check_lowered(plan->hp, seed, nsims);
+    return CCL_OK;
+  });
+}
+
+int ccl_plan_status(ccl_plan* plan) {
+  if (!plan) return set_error(CCL_ERR_INVALID_ARGUMENT, "null plan");
+  return guarded([&] {
+    std::lock_guard<std::mutex> lk(plan->mu);
+    if (!plan->device) return CCL_OK;
+    if (plan->launched) HIP_TRY(hipEventSynchronize(plan->last));
+    unsigned int e[4] = {0, 0, 0, 0};
+    HIP_TRY(hipMemcpy(e, plan->d_err, sizeof e, hipMemcpyDeviceToHost));
+    if (e[0] == 0) return CCL_OK;
+    HIP_TRY(hipMemset(plan->d_err, 0, sizeof e));
+    fail(-int(e[0]), "launch " + std::to_string(e[3]) + ": workgroup " + std::to_string(e[1]) + " timed out at instruction " +
+                         std::to_string(e[2]));
+  });
+}
+
+int ccl_plan_read_trace(ccl_plan* plan, void* host, size_t bytes) {
+  if (!plan || !host) return set_error(CCL_ERR_INVALID_ARGUMENT, "null argument");
+  return guarded([&] {
+    std::lock_guard<std::mutex> lk(plan->mu);
+    if (!plan->d_trace) fail(CCL_ERR_INVALID_ARGUMENT, "plan was not created with CCL_FLAG_TRACE");
+    size_t need = plan->hp.dwg.size() * 32;
+    if (bytes < need) fail(CCL_ERR_INVALID_ARGUMENT, "trace buffer too small");
+    if (plan->launched) HIP_TRY(hipEventSynchronize(plan->last));
+    HIP_TRY(hipMemcpy(host, plan->d_trace, need, hipMemcpyDeviceToHost));
+    return CCL_OK;
+  });
+}
+
+int ccl_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int nthreads, void* stream) {
+  if (!dst || !src || bytes % 16 || nblocks < 1 || nthreads < 64 || nthreads > 1024 || nthreads % 64)
+    return set_error(CCL_ERR_INVALID_ARGUMENT, "copy probe: bad arguments");
+  return guarded([&] {
+    std::string err;
+    int rc = launch_copy_probe(dst, src, bytes, nblocks, nthreads, stream, &err);
+    if (rc) fail(rc, err);
+    return CCL_OK;
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Internal host-side structures of the plan compiler and runtime.
+#pragma once
+
+#include <cstdint>
+#include <stdexcept>
+#include <string>
+#include <vector>
+
+#include "../../include/ccl.h"
+#include "device_abi.h"
+
+namespace ccl {
+
+struct Error : std::runtime_error {
+  int code;
+  Error(int c, const std::string& m) : std::runtime_error(m), code(c) {}
+};
+[[noreturn]] void fail(int code, const std::string& msg);
+
+// Chunk geometry shared by the lowering, byte accounting and the plan checker:
+// chunk j covers [floor(j*N/C), floor((j+1)*N/C)); instance i of k takes
+// [lo + floor(i*len/k), lo + floor((i+1)*len/k)) of a one-chunk range.
+inline int64_t chunk_bound(int64_t j, int64_t N, int64_t C) { return (j * N) / C; }
+
+struct Range {
+  int64_t lo = 0, len = 0;
+};
+inline Range op_range(int idx, int cnt, int instance, int k, int64_t N, int64_t C) {
+  int64_t lo = chunk_bound(idx, N, C), hi = chunk_bound(idx + cnt, N, C);
+  if (k > 1) {
+    int64_t len = hi - lo;
+    int64_t a = lo + (instance * len) / k, b = lo + ((instance + 1) * len) / k;
+    return {a, b - a};
+  }
+  return {lo, hi - lo};
+}
+
+struct Loc {
+  int buf = -1;
+  int idx = 0;
+  bool valid() const { return buf >= 0; }
+  bool operator==(const Loc& o) const { return buf == o.buf && idx == o.idx; }
+};
+
+// An instruction of the base program (instance 0), primitive or fused.
+struct Instr {
+  int rank = 0, channel = 0, cnt = 1;
+  bool recv = false;  // first operand is the staging slot of transfer xin
+  Loc a, b, d;        // local first operand (if !recv), added operand, local destination
+  int xin = -1, xout = -1;
+  int chunk_id = 0;
+  int pos = 0;        // program position of its first primitive
+  // results of scheduling and allocation
+  int sp = -1;        // sub-pipeline
+  int wg = -1;        // base workgroup
+  int done_flag = -1; // base completion-flag id
+  std::vector<int> waits;  // base instruction ids whose completion it awaits
+  uint32_t opbits() const {
+    return (recv ? OPB_RECV : 0u) | (b.valid() ? OPB_SRCB : 0u) | (d.valid() ? OPB_DSTA : 0u) |
+           (xout >= 0 ? OPB_SEND : 0u);
+  }
+};
+
+struct Xfer {
+  int src_rank = 0, dst_rank = 0, channel = 0, cnt = 1;
+  int sender = -1, receiver = -1;  // base instruction ids
+  int phase_idx = -1;
+};
+
+struct BaseWG {
+  int rank = 0, channel = 0;
+  int in_peer = -1, out_peer = -1;
+  std::vector<int> instrs;  // execution order
+};
+
+struct HostPlan {
+  // input
+  ccl_program_desc desc{};
+  std::vector<ccl_chunk_op> ops;
+  int P = 0, C = 0, k = 1;
+  int out_chunks = 0, scr_chunks = 0;
+  ccl_plan_config cfg{};
+  int esz = 4;
+  int granule = 1;
+  // base program after compilation
+  std::vector<Instr> ins;
+  std::vector<Xfer> xf;
+  std::vector<BaseWG> wgs;
+  int num_subpipes = 0;
+  int num_done_flags = 0;
+  int num_base_waits = 0;
+  // lowered tables (all instances)
+  std::vector<DevWG> dwg;
+  std::vector<DevInstr> dins;
+  std::vector<DevXfer> dxf;
+  std::vector<int32_t> dwaits;
+  std::vector<int> dins_base;  // base instruction id of each lowered instruction
+  int64_t staging_bytes = 0;
+  int64_t scratch_elems_per_rank = 0;
+  int64_t slice_elems = 0;
+  int num_connections = 0;
+  int max_wg_per_rank = 0;
+  int max_resident_wgs = 0;
+  double ms[6] = {0, 0, 0, 0, 0, 0};
+};
+
+// compiler.cpp
+void compile_plan(HostPlan& hp, const ccl_program_desc* prog, int nranks, int nchunks, int k,
+                  const ccl_plan_config* cfg);
+int64_t output_chunks(const ccl_program_desc& d);
+int64_t plan_bytes(const HostPlan& hp, int64_t count);
+int64_t output_elems(const HostPlan& hp, int64_t count);
+void group_members(const ccl_program_desc& d, int r, std::vector<int>& members, int& pos);
+int group_count(const ccl_program_desc& d);
+
+// simulate.cpp
+void check_lowered(const HostPlan& hp, uint64_t seed, int nsims);
+
+// executor.hip
+int launch_executor(const ExecArgs& args, int dtype, int nwg, int nthreads, void* stream,
+                    std::string* err);
+int executor_max_blocks_per_cu(int dtype, int nthreads, int* blocks, std::string* err);
+int launch_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int nthreads,
+                      void* stream, std::string* err);
+
+}  // namespace ccl

@@ -1,0 +1,67 @@
+// Records the host compiler lowers a plan into and the executor kernel reads.
+// Layout: a rank x workgroup x pipeline-order table (ReSCCL report, section 2.2,
+// "lightweight kernel generation": rank, thread-block and pipeline dimensions),
+// kept as data that one generic kernel interprets.
+#pragma once
+#include <stdint.h>
+
+namespace ccl {
+
+constexpr int kMaxRanks = 64;
+constexpr int kNumBufs = 3;  // input, output, scratch
+
+// Opcode bits of a lowered instruction (same values as CCL_I_* in ccl.h).
+enum : uint32_t { OPB_RECV = 1u, OPB_SRCB = 2u, OPB_DSTA = 4u, OPB_SEND = 8u };
+
+struct DevWG {  // one workgroup of the launch
+  int32_t rank;
+  int32_t first;  // first instruction in DevInstr[]
+  int32_t n;      // number of instructions, run in order
+  int32_t trace_slot;
+};
+
+struct DevInstr {  // 64 bytes, read wave-uniformly
+  uint32_t op;     // OPB_* bits
+  int32_t cnt;     // chunks covered
+  int32_t a_buf, a_idx;  // local first operand (unless OPB_RECV)
+  int32_t b_buf, b_idx;  // local second operand (OPB_SRCB)
+  int32_t d_buf, d_idx;  // local destination (OPB_DSTA)
+  int32_t xin, xout;     // transfer ids (OPB_RECV / OPB_SEND)
+  int32_t wait_begin, nwaits;  // completion flags to await, in DevExec::waits
+  int32_t done_flag;           // completion flag to set (-1 = none)
+  int32_t instance;            // instance sub-chunk index (0..k-1)
+  int32_t pad0, pad1;
+};
+
+struct DevXfer {  // 32 bytes: one send -> recv transfer
+  uint64_t slot_off;  // byte offset of its staging slot in the staging pool (256-aligned)
+  int32_t phase_idx;  // chunk whose range start fixes the data's offset inside the slot (-1: none)
+  int32_t instance;
+  int32_t cnt;
+  int32_t pad0, pad1, pad2;
+};
+
+// Kernel arguments, passed by value.
+struct ExecArgs {
+  const DevWG* wgs;
+  const DevInstr* ins;
+  const DevXfer* xf;
+  const int32_t* waits;
+  unsigned long long* xflags;  // per transfer: epoch << 24 | slices completed
+  unsigned long long* dflags;  // per completion flag: epoch when done
+  unsigned char* staging;
+  unsigned int* err;           // [code, wg, instr, epoch_lo]
+  unsigned long long* abort_word;  // epoch of an aborted launch
+  unsigned long long* trace;   // 4 words per workgroup, or null
+  int64_t count;               // elements per rank input for this launch
+  int64_t slice_elems;         // slice length in elements (multiple of 64)
+  unsigned long long epoch;    // launch number, >= 1
+  long long timeout_ticks;     // watchdog budget per wait, device wall-clock ticks
+  int32_t nchunks;             // chunk unit of the input
+  int32_t k;                   // parallel factor (instances)
+  unsigned char* base[kNumBufs][kMaxRanks];  // per-rank buffer base pointers
+};
+
+constexpr unsigned long long kEpochShift = 24;  // slices per transfer < 2^24
+
+}  // namespace ccl

@@ -1,0 +1,172 @@
+// AutoCCL-style tuner (AutoCCL report, "Methods" 1 and 2): the implementation choice
+// (here: which program, i.e. algorithm) splits the space into subspaces; inside each,
+// the resource parameters -- channels/instances (nc), threads per workgroup (nt),
+// pipelining chunk (c) -- are tuned one coordinate at a time, each increased while the
+// bandwidth keeps improving, relying on its unimodal shape.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <string>
+#include <vector>
+
+#include "ccl_internal.h"
+
+using namespace ccl;
+
+namespace {
+
+thread_local std::string g_tune_detail;
+
+int index_of(const int32_t* v, int n, int32_t x) {
+  for (int i = 0; i < n; ++i)
+    if (v[i] == x) return i;
+  return 0;
+}
+
+struct Coord {
+  const int32_t* vals;
+  int n;
+  int32_t ccl_tune_point::*field;
+};
+
+}  // namespace
+
+extern "C" {
+
+int ccl_tune_coordinate_descent(const ccl_tune_space* space, const ccl_tune_point* start, ccl_tune_objective objective,
+                                void* user, ccl_tune_point* best, ccl_tune_report* report) {
+  if (!space || !objective || !best || !report) return CCL_ERR_INVALID_ARGUMENT;
+  if (space->nfactors < 1 || space->nnthreads < 1 || space->nslices < 1 || space->nvariants < 1 || !space->factors ||
+      !space->nthreads || !space->slices)
+    return CCL_ERR_INVALID_ARGUMENT;
+  const Coord coords[3] = {{space->factors, space->nfactors, &ccl_tune_point::parallel_factor},
+                           {space->nthreads, space->nnthreads, &ccl_tune_point::nthreads},
+                           {space->slices, space->nslices, &ccl_tune_point::slice_bytes}};
+  int evals = 0;
+  bool have_best = false;
+  double best_score = -1.0, start_score = -1.0;
+  for (int v = 0; v < space->nvariants; ++v) {
+    ccl_tune_point pt;
+    pt.variant = v;
+    int idx[3];
+    for (int c = 0; c < 3; ++c) {
+      idx[c] = start ? index_of(coords[c].vals, coords[c].n, start->*(coords[c].field)) : 0;
+      pt.*(coords[c].field) = coords[c].vals[idx[c]];
+    }
+    double score = objective(&pt, user);
+    ++evals;
+    if (v == 0) start_score = score;
+    for (int c = 0; c < 3; ++c) {
+      // step this coordinate up while the objective improves
+      while (idx[c] + 1 < coords[c].n) {
+        ccl_tune_point cand = pt;
+        cand.*(coords[c].field) = coords[c].vals[idx[c] + 1];
+        double s = objective(&cand, user);
+        ++evals;
+        if (!(s > score)) break;
+        pt = cand;
+        score = s;
+        idx[c] += 1;
+      }
+    }
+    if (score >= 0 && (!have_best || score > best_score)) {
+      have_best = true;
+      best_score = score;
+      *best = pt;
+    }
+  }
+  report->evaluations = evals;
+  report->best_score = best_score;
+  report->start_score = start_score;
+  return have_best ? CCL_OK : CCL_ERR_OUT_OF_RESOURCES;
+}
+
+struct DeviceTuneCtx {
+  const ccl_program_desc* const* variants;
+  int64_t count;
+  ccl_plan_config base;
+  hipStream_t stream;
+  int warmup, iters;
+  std::vector<void*> in, out;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int last_error;
+};
+
+static double device_objective(const ccl_tune_point* pt, void* user) {
+  auto* c = static_cast<DeviceTuneCtx*>(user);
+  const ccl_program_desc* prog = c->variants[pt->variant];
+  ccl_plan_config cfg = c->base;
+  cfg.nthreads = pt->nthreads;
+  cfg.slice_bytes = pt->slice_bytes;
+  cfg.flags &= ~(CCL_FLAG_HOST_ONLY | CCL_FLAG_TRACE);
+  ccl_plan* plan = nullptr;
+  int rc = ccl_plan_create(prog, prog->nranks, prog->in_chunks, pt->parallel_factor, &cfg, &plan);
+  if (rc) return -1.0;  // infeasible (e.g. not enough co-resident workgroups)
+  for (int i = 0; i < c->warmup && rc == 0; ++i)
+    rc = ccl_execute(plan, (const void* const*)c->in.data(), c->out.data(), c->count, c->stream);
+  hipEventRecord(c->e0, c->stream);
+  for (int i = 0; i < c->iters && rc == 0; ++i)
+    rc = ccl_execute(plan, (const void* const*)c->in.data(), c->out.data(), c->count, c->stream);
+  hipEventRecord(c->e1, c->stream);
+  hipEventSynchronize(c->e1);
+  if (rc == 0) rc = ccl_plan_status(plan);
+  float ms = 0.f;
+  hipEventElapsedTime(&ms, c->e0, c->e1);
+  ccl_plan_destroy(plan);
+  if (rc) {
+    c->last_error = rc;
+    return -1.0;
+  }
+  double t = ms * 1e-3 / std::max(1, c->iters);
+  int esz = c->base.dtype == CCL_BF16 ? 2 : 4;
+  return t > 0 ? double(c->count) * esz / t / 1e9 : -1.0;  // algorithm bandwidth, GB/s
+}
+
+int ccl_tune(const ccl_program_desc* const* variants, int nvariants, int64_t count, const ccl_plan_config* base,
+             const ccl_tune_space* space, void* stream, ccl_tune_point* best, ccl_tune_report* report) {
+  if (!variants || nvariants < 1 || !base || !space || !best || !report || count < 1) return CCL_ERR_INVALID_ARGUMENT;
+  int P = variants[0]->nranks;
+  for (int v = 0; v < nvariants; ++v)
+    if (!variants[v] || variants[v]->nranks != P || variants[v]->collective != variants[0]->collective)
+      return CCL_ERR_INVALID_ARGUMENT;
+  DeviceTuneCtx c;
+  c.variants = variants;
+  c.count = count;
+  c.base = *base;
+  c.base.max_count = std::max<int64_t>(base->max_count, count);
+  c.stream = reinterpret_cast<hipStream_t>(stream);
+  c.warmup = std::max(0, space->warmup);
+  c.iters = std::max(1, space->iters);
+  c.last_error = 0;
+  int esz = base->dtype == CCL_BF16 ? 2 : 4;
+  // buffer sizes: the largest output any supported collective needs for count
+  ccl_program_desc probe = *variants[0];
+  int64_t oc = output_chunks(probe);
+  int64_t out_elems = oc >= 0 ? (oc * count) / probe.in_chunks + 1 : count * P;
+  int rc = CCL_OK;
+  for (int r = 0; r < P && rc == 0; ++r) {
+    void* a = nullptr;
+    void* b = nullptr;
+    if (hipMalloc(&a, size_t(count) * esz) != hipSuccess || hipMalloc(&b, size_t(out_elems) * esz) != hipSuccess) {
+      if (a) hipFree(a);
+      rc = CCL_ERR_OUT_OF_RESOURCES;
+      break;
+    }
+    hipMemset(a, 0, size_t(count) * esz);
+    c.in.push_back(a);
+    c.out.push_back(b);
+  }
+  if (rc == 0 && (hipEventCreate(&c.e0) != hipSuccess || hipEventCreate(&c.e1) != hipSuccess)) rc = CCL_ERR_HIP;
+  ccl_tune_space sp = *space;
+  sp.nvariants = nvariants;
+  if (rc == 0) rc = ccl_tune_coordinate_descent(&sp, nullptr, device_objective, &c, best, report);
+  hipDeviceSynchronize();
+  for (void* p : c.in) hipFree(p);
+  for (void* p : c.out) hipFree(p);
+  if (c.e0) hipEventDestroy(c.e0);
+  if (c.e1) hipEventDestroy(c.e1);
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+"""Convenience wrapper over the C ABI: a ``Plan`` object owning one ``ccl_plan``.
+
+torch supplies device memory (``data_ptr``) and the stream (``cuda_stream``);
+everything else -- compilation, the launch, the kernel -- is in ``libccl.so``.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+from . import capi
+from .dsl import Program
+
+DTYPES = {"f32": capi.CCL_F32, "bf16": capi.CCL_BF16, "i32": capi.CCL_I32}
+ELEM_SIZE = {"f32": 4, "bf16": 2, "i32": 4}
+SCHEDULERS = {"program": capi.CCL_SCHED_PROGRAM_ORDER, "hpds": capi.CCL_SCHED_HPDS, "rr": capi.CCL_SCHED_RR}
+WG_ALLOC = {"connection": capi.CCL_WG_CONNECTION, "state": capi.CCL_WG_STATE}
+
+
+@dataclass
+class PlanConfig:
+    dtype: str = "f32"
+    max_count: int = 1 << 20
+    nthreads: int = 512
+    slice_bytes: int = 256 * 1024
+    scheduler: str = "hpds"
+    wg_alloc: str = "state"
+    trace: bool = False
+    host_only: bool = False
+    no_fusion: bool = False
+    num_cus: int = 0
+    timeout_us: int = 0
+
+    def to_c(self) -> capi.ccl_plan_config:
+        flags = 0
+        if self.trace:
+            flags |= capi.CCL_FLAG_TRACE
+        if self.host_only:
+            flags |= capi.CCL_FLAG_HOST_ONLY
+        if self.no_fusion:
+            flags |= capi.CCL_FLAG_NO_FUSION
+        return capi.ccl_plan_config(DTYPES[self.dtype], capi.CCL_REDOP_SUM, int(self.max_count), int(self.nthreads),
+                                    int(self.slice_bytes), SCHEDULERS[self.scheduler], WG_ALLOC[self.wg_alloc],
+                                    flags, int(self.num_cus), int(self.timeout_us))
+
+
+class Plan:
+    def __init__(self, prog: Program, parallel_factor: int = 1, config: PlanConfig | None = None, **kw):
+        self.program = prog
+        self.config = config if config is not None else PlanConfig(**kw)
+        self.parallel_factor = parallel_factor
+        self._desc = prog.to_desc()
+        self.handle = capi.ccl_plan_create(self._desc, prog.nranks, prog.in_chunks, parallel_factor,
+                                           self.config.to_c())
+
+    # ---- queries -------------------------------------------------------------
+    def info(self) -> dict:
+        i = capi.ccl_plan_info(self.handle)
+        d = {name: getattr(i, name) for name, _ in capi.ccl_plan_info_t._fields_
+             if name not in ("compile_ms", "opcode_hist", "reserved")}
+        d["compile_ms"] = list(i.compile_ms)
+        d["opcode_hist"] = list(i.opcode_hist)
+        return d
+
+    def bytes(self, count: int) -> int:
+        return capi.ccl_plan_bytes(self.handle, count)
+
+    def export(self):
+        return capi.ccl_plan_export(self.handle)
+
+    def check(self, seed: int = 1, nsims: int = 4) -> None:
+        capi.ccl_plan_check(self.handle, seed, nsims)
+
+    def status(self) -> None:
+        capi.ccl_plan_status(self.handle)
+
+    def trace(self):
+        return capi.ccl_plan_read_trace(self.handle, self.info()["num_workgroups"])
+
+    def output_len(self, count: int) -> int:
+        return (self.program.out_chunks * count) // self.program.in_chunks
+
+    # ---- execution -----------------------------------------------------------
+    def execute(self, inputs, outputs, count: int | None = None, stream=None) -> None:
+        """inputs / outputs: per-rank torch tensors (or objects with data_ptr())."""
+        if count is None:
+            count = inputs[0].numel()
+        s = 0
+        if stream is not None:
+            s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        else:
+            import torch
+            s = torch.cuda.current_stream().cuda_stream
+        capi.ccl_execute(self.handle, [t.data_ptr() for t in inputs], [t.data_ptr() for t in outputs], count, s)
+
+    def destroy(self) -> None:
+        if self.handle:
+            capi.ccl_plan_destroy(self.handle)
+            self.handle = 0
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *a):
+        self.destroy()

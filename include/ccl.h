@@ -1,0 +1,304 @@
+/*
+ * ccl.h -- C ABI of the chunk-schedule collective executor for MI355X (gfx950).
+ *
+ * A collective is written as a chunk program: copy and reduce operations on
+ * chunks of per-rank input, output and scratch buffers, in program order
+ * (MSCCLang report, section 3.1 "System design": the chunk-oriented DSL, its
+ * input/output/scratch buffers and copy/reduce operations). ccl_plan_create
+ * compiles it once: dependency DAG, send/recv instruction generation, fusion into
+ * recv-reduce-copy-send style instructions, replication into parallel instances
+ * on separate channels (MSCCLang report, section 3.1, compiler steps), scheduling
+ * into sub-pipelines with hierarchical-priority dynamic scheduling and merging of
+ * never co-active connections onto one workgroup (ReSCCL report, section 2.2
+ * "System design"). ccl_execute then runs the whole collective as one HIP kernel
+ * launch on a stream.
+ *
+ * The P ranks are virtual ranks that live on one GPU: every rank's buffers sit
+ * in the same HBM, a "send" writes the receiving rank's staging slot and then
+ * release-stores a flag, a "recv" acquire-polls that flag and reads the slot.
+ *
+ * Conventions for every entry point:
+ *   - Status codes: CCL_OK (0) on success, a negative CCL_ERR_* otherwise. No C++
+ *     exception crosses this boundary. ccl_last_error_detail() gives a
+ *     thread-local text for the last failure of the calling thread.
+ *   - Pointers named "device" are HIP device pointers owned by the caller. All
+ *     other pointers are host pointers owned by the caller and only read during
+ *     the call unless stated otherwise.
+ *   - A stream argument is a hipStream_t passed as void* (NULL = null stream).
+ *   - Element counts are in elements of the plan's dtype; chunk indices and chunk
+ *     counts are in chunks.
+ */
+#ifndef CCL_H
+#define CCL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define CCL_OK 0
+#define CCL_ERR_INVALID_ARGUMENT (-1) /* bad sizes, pointers, counts, or mismatched parameters */
+#define CCL_ERR_INVALID_PROGRAM (-2)  /* program fails verification (bounds, input writes, postcondition, ...) */
+#define CCL_ERR_UNSUPPORTED (-3)      /* dtype / reduction / collective not supported */
+#define CCL_ERR_OUT_OF_RESOURCES (-4) /* more workgroups than can be co-resident, or allocation failure */
+#define CCL_ERR_HIP (-5)              /* a HIP runtime call failed */
+#define CCL_ERR_TIMEOUT (-6)          /* a device spin-wait exceeded its watchdog budget */
+#define CCL_ERR_INTERNAL (-7)
+
+/* ---- program description (MSCCLang report, section 3.1: chunks, buffers, copy/reduce) ---- */
+#define CCL_OP_COPY 0   /* dst <- src */
+#define CCL_OP_REDUCE 1 /* dst <- dst + src (one storage-dtype rounding) */
+
+#define CCL_BUF_INPUT 0   /* read-only per-rank input (the caller's send buffer) */
+#define CCL_BUF_OUTPUT 1  /* per-rank output (the caller's receive buffer) */
+#define CCL_BUF_SCRATCH 2 /* per-rank scratch owned by the plan */
+
+#define CCL_REDOP_SUM 0
+
+#define CCL_F32 0
+#define CCL_BF16 1 /* stored as bf16, added in fp32, rounded to nearest-even at every store */
+#define CCL_I32 2  /* two's-complement wrap */
+
+/* Collective: picks the postcondition the verifier checks and the buffer sizes. */
+#define CCL_COLL_ALLREDUCE 0     /* out = N elements */
+#define CCL_COLL_ALLGATHER 1     /* out = P*N (or L*N with CCL_SCOPE_INTRA) */
+#define CCL_COLL_REDUCESCATTER 2 /* out = N/P (or N/L with CCL_SCOPE_INTRA); N must divide */
+#define CCL_COLL_ALLTOALL 3      /* out = N */
+#define CCL_COLL_ALLTONEXT 4     /* out = N; rank 0's output is left untouched */
+#define CCL_COLL_CUSTOM 5        /* no postcondition check; out_chunks taken from the program */
+
+/* Group scope for P = G*L ranks numbered r = g*L + l. */
+#define CCL_SCOPE_ALL 0   /* the collective spans all P ranks */
+#define CCL_SCOPE_INTRA 1 /* an independent collective inside each group of L consecutive ranks */
+#define CCL_SCOPE_INTER 2 /* an independent collective among the G ranks of each lane l */
+
+typedef struct {
+  uint8_t kind;     /* CCL_OP_COPY or CCL_OP_REDUCE */
+  uint8_t redop;    /* CCL_REDOP_SUM */
+  uint16_t channel; /* channel label; instructions of different channels never share a workgroup
+                       under connection-based allocation */
+  int32_t src_rank, src_buf, src_idx;
+  int32_t dst_rank, dst_buf, dst_idx;
+  int32_t count; /* chunks covered, >= 1 */
+} ccl_chunk_op;  /* 32 bytes */
+
+typedef struct {
+  int32_t collective;     /* CCL_COLL_* */
+  int32_t nranks;         /* P */
+  int32_t in_chunks;      /* chunks the input of N elements is cut into (the plan's chunk unit) */
+  int32_t out_chunks;     /* chunks of the output buffer */
+  int32_t scratch_chunks; /* chunks of per-rank scratch (0 if unused) */
+  int32_t group_size;     /* L for CCL_SCOPE_INTRA / CCL_SCOPE_INTER, else ignored */
+  int32_t group_scope;    /* CCL_SCOPE_* */
+  int32_t reserved;
+  const ccl_chunk_op* ops; /* host array of nops operations, in program order; copied by create */
+  size_t nops;
+} ccl_program_desc;
+
+/*
+ * Chunk geometry. With N = count elements per rank input and C = in_chunks, chunk
+ * j of every buffer covers elements [floor(j*N/C), floor((j+1)*N/C)); buffers longer
+ * than the input simply have more chunks. With parallel factor k > 1 each chunk
+ * is split the same way into k instance sub-chunks and instance i runs on its own
+ * channel (MSCCLang report, section 3.1: parallelization factor and channels).
+ */
+
+/* ---- plan configuration -------------------------------------------------- */
+#define CCL_SCHED_PROGRAM_ORDER 0 /* every workgroup runs its tasks in program order */
+#define CCL_SCHED_HPDS 1          /* hierarchical-priority dynamic scheduling (ReSCCL report, section 2.2) */
+#define CCL_SCHED_RR 2            /* round-robin over chunks, no link-conflict check */
+
+#define CCL_WG_CONNECTION 0 /* one workgroup per (channel, recv peer, send peer) signature of a rank */
+#define CCL_WG_STATE 1      /* additionally merge workgroups of one rank that are never co-active */
+
+#define CCL_FLAG_TRACE 0x1u      /* record per-workgroup busy/wait timestamps (ccl_plan_read_trace) */
+#define CCL_FLAG_HOST_ONLY 0x2u  /* compile and lower on the host only; no HIP call, no execute */
+#define CCL_FLAG_NO_FUSION 0x4u  /* keep primitive send/recv/copy/reduce instructions */
+#define CCL_FLAG_NO_VERIFY 0x8u  /* skip the symbolic postcondition check at create */
+
+typedef struct {
+  int32_t dtype;       /* CCL_F32, CCL_BF16 or CCL_I32 */
+  int32_t redop;       /* CCL_REDOP_SUM */
+  int64_t max_count;   /* largest per-rank input element count ccl_execute will be given (>= 1) */
+  int32_t nthreads;    /* threads per workgroup: 64..1024, multiple of 64 (0 = 512) */
+  int32_t slice_bytes; /* pipelining slice per transfer step, bytes (0 = 256 KiB) */
+  int32_t scheduler;   /* CCL_SCHED_* */
+  int32_t wg_alloc;    /* CCL_WG_* */
+  uint32_t flags;      /* CCL_FLAG_* */
+  int32_t num_cus;     /* CUs assumed by the co-residency check for HOST_ONLY plans (0 = 256) */
+  int64_t timeout_us;  /* watchdog budget of one device spin-wait, microseconds (0 = 2,000,000) */
+} ccl_plan_config;
+
+typedef struct ccl_plan ccl_plan;
+
+/*
+ * Compile `prog` into a plan. `nranks` must equal prog->nranks and `nchunks`
+ * prog->in_chunks (both are restated so that a caller cannot pair a program with
+ * the wrong shape silently). `parallel_factor` k >= 1 replicates the program into
+ * k instances. Unless CCL_FLAG_HOST_ONLY is set the plan allocates its device
+ * memory (instruction tables, staging slots sized for max_count, flags, scratch)
+ * on the current HIP device and checks that every workgroup can be resident at
+ * once. The plan is immutable afterwards.
+ * Errors: INVALID_ARGUMENT (sizes, mismatched nranks/nchunks, null pointers),
+ * INVALID_PROGRAM (chunk out of range, write to an input, length mismatch, failed
+ * postcondition), UNSUPPORTED, OUT_OF_RESOURCES (too many workgroups,
+ * hipMalloc failure), HIP. On error *out is NULL and nothing is leaked.
+ */
+int ccl_plan_create(const ccl_program_desc* prog, int nranks, int nchunks, int parallel_factor,
+                    const ccl_plan_config* cfg, ccl_plan** out);
+
+/*
+ * Run the collective once on `stream`: sendbufs[r] / recvbufs[r] (r < P) are
+ * device pointers to rank r's input (count elements) and output (the
+ * collective's output length for count). Out of place: outputs must not overlap
+ * inputs. Enqueues exactly one kernel (none when count == 0) and returns at once;
+ * the buffers must stay valid until the stream passes the kernel. Launches of one
+ * plan are serialized: a launch on another stream first waits for the previous one.
+ * Errors: INVALID_ARGUMENT (count > max_count, count not a multiple of the plan's
+ * count granule or of P where the collective needs it, null pointers, HOST_ONLY
+ * plan), HIP, TIMEOUT if an earlier launch of this plan reported a watchdog expiry
+ * that was not yet collected with ccl_plan_status.
+ */
+int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbufs, int64_t count,
+                void* stream);
+
+/* Wait for the plan's last launch and free everything it owns. NULL is a no-op. */
+int ccl_plan_destroy(ccl_plan* plan);
+
+typedef struct {
+  int32_t nranks, nchunks, parallel_factor, dtype;
+  int32_t num_workgroups;     /* total, all ranks and instances */
+  int32_t max_wg_per_rank;
+  int32_t num_instructions;   /* lowered, all instances */
+  int32_t num_subpipelines;   /* of the base schedule */
+  int32_t num_connections;    /* distinct (src rank, dst rank, channel), all instances */
+  int32_t num_transfers;      /* send->recv pairs, all instances */
+  int32_t num_waits;          /* cross-workgroup completion waits, all instances */
+  int32_t count_granule;      /* ccl_execute's count must be a multiple of this */
+  int32_t nthreads, slice_bytes;
+  int32_t max_resident_wgs;   /* co-residency bound the plan was checked against */
+  int32_t reserved;
+  int64_t staging_bytes, scratch_bytes, flag_bytes, table_bytes;
+  double compile_ms[6];       /* verify, DAG, fusion, schedule, workgroup allocation, lowering */
+  int32_t opcode_hist[16];    /* lowered instructions by opcode bits (see ccl_instr_info.opcode) */
+} ccl_plan_info_t;
+
+int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info);
+
+/*
+ * Algorithmic HBM bytes one ccl_execute moves for `count`: for every instruction,
+ * (operands read + destinations written) x elements x element size, summed over
+ * all instances and ranks. Returns a negative status on error.
+ */
+int64_t ccl_plan_bytes(const ccl_plan* plan, int64_t count);
+
+/* One lowered instruction, for inspection and tests. opcode bits: */
+#define CCL_I_RECV 0x1 /* first operand is the incoming transfer's staging slot */
+#define CCL_I_SRCB 0x2 /* a second, local operand is added (reduce) */
+#define CCL_I_DSTA 0x4 /* the result is stored to a local buffer */
+#define CCL_I_SEND 0x8 /* the result is stored to the outgoing transfer's staging slot */
+
+typedef struct {
+  int32_t rank, wg, subpipe, channel, instance;
+  int32_t opcode;
+  int32_t a_buf, a_idx; /* local first operand (when not CCL_I_RECV) */
+  int32_t b_buf, b_idx;
+  int32_t d_buf, d_idx;
+  int32_t count;        /* chunks */
+  int32_t recv_peer, send_peer; /* -1 if none */
+  int32_t xin, xout;    /* transfer ids, -1 if none */
+  int32_t nwaits;       /* completion waits on other workgroups before the first slice */
+  int32_t chunk_id;     /* chunk the scheduler attributes the task to */
+  int32_t done_flag;    /* >= 0 if other workgroups wait for this instruction */
+} ccl_instr_info;
+
+/* Copy up to `cap` lowered instructions (ordered by workgroup, then execution
+ * order) into `out`; *n receives the total number. */
+int ccl_plan_export(const ccl_plan* plan, ccl_instr_info* out, size_t cap, size_t* n);
+
+/*
+ * Host-side check of the lowered plan: run every workgroup's instruction list
+ * on symbolic values (multisets of contributing input elements) under the flag
+ * protocol, in `nsims` seeded random interleavings at slice granularity, with
+ * a small element count. Reports INVALID_PROGRAM if some interleaving deadlocks
+ * or ends with an output that violates the collective's postcondition.
+ */
+int ccl_plan_check(const ccl_plan* plan, uint64_t seed, int nsims);
+
+/* After the plan's last launch: CCL_OK, or CCL_ERR_TIMEOUT if a watchdog fired
+ * (the error is then cleared). Synchronizes with the plan's last launch. */
+int ccl_plan_status(ccl_plan* plan);
+
+/* Per-workgroup trace of the last launch of a CCL_FLAG_TRACE plan: for each
+ * workgroup four uint64 values {first instruction start, last instruction end,
+ * ticks spent waiting on flags, instructions run}, ticks of the 100 MHz device
+ * wall clock. `bytes` must hold num_workgroups * 32. */
+int ccl_plan_read_trace(ccl_plan* plan, void* host, size_t bytes);
+
+/* ---- tuner (AutoCCL report, "Methods" 1-2: resource parameters tuned by
+ * coordinate descent inside each implementation subspace) ---------------- */
+typedef struct {
+  int32_t variant;         /* algorithm subspace (index into the program list) */
+  int32_t parallel_factor; /* channels / instances (nc) */
+  int32_t nthreads;        /* threads per workgroup (nt) */
+  int32_t slice_bytes;     /* chunk size of one pipelined step (c) */
+} ccl_tune_point;
+
+typedef struct {
+  const int32_t* factors;  int32_t nfactors;  /* ascending candidate values */
+  const int32_t* nthreads; int32_t nnthreads;
+  const int32_t* slices;   int32_t nslices;
+  int32_t nvariants;       /* subspaces 0..nvariants-1 */
+  int32_t warmup, iters;   /* per device evaluation */
+} ccl_tune_space;
+
+typedef struct {
+  int32_t evaluations;     /* objective evaluations made */
+  int32_t reserved;
+  double best_score;       /* objective at the returned point (higher is better) */
+  double start_score;      /* objective at the starting point */
+} ccl_tune_report;
+
+/* Objective: higher is better; a negative value marks an infeasible point. */
+typedef double (*ccl_tune_objective)(const ccl_tune_point* point, void* user);
+
+/*
+ * Subspace coordinate descent: for every variant, starting from the smallest
+ * candidate of each coordinate (or from `start` where it lies in the space),
+ * optimize parallel_factor, then nthreads, then slice_bytes; each coordinate is
+ * stepped up through its ascending candidates while the objective improves. The
+ * best point over all variants is returned. Pure host logic.
+ */
+int ccl_tune_coordinate_descent(const ccl_tune_space* space, const ccl_tune_point* start,
+                                ccl_tune_objective objective, void* user, ccl_tune_point* best,
+                                ccl_tune_report* report);
+
+/*
+ * Tune on the device: variants[v] is the program of subspace v (all with the same
+ * collective and nranks). Each evaluation creates a plan from `base` with the
+ * point's (k, nt, slice), runs space->warmup untimed and space->iters timed
+ * executions on `stream` over buffers the tuner allocates itself, and scores
+ * the algorithmic bus bandwidth. Returns the best point and its report.
+ */
+int ccl_tune(const ccl_program_desc* const* variants, int nvariants, int64_t count,
+             const ccl_plan_config* base, const ccl_tune_space* space, void* stream,
+             ccl_tune_point* best, ccl_tune_report* report);
+
+/* ---- measurement helper -------------------------------------------------- */
+/* Plain 16-byte-vector device copy of `bytes` (multiple of 16) from src to dst
+ * with `nblocks` x `nthreads`: the practical HBM streaming ceiling beside the
+ * nominal 8 TB/s, and the reference kernel for calibrating traffic counters. */
+int ccl_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int nthreads, void* stream);
+
+/* ---- errors --------------------------------------------------------------- */
+const char* ccl_error_string(int status);
+const char* ccl_last_error_detail(void);
+int ccl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CCL_H */
