@@ -50,7 +50,6 @@ struct ccl_plan {
   std::vector<void*> allocs;
   DevWG* d_wgs = nullptr;
   DevInstr* d_ins = nullptr;
-  DevXfer* d_xf = nullptr;
   int32_t* d_waits = nullptr;
   unsigned long long* d_xflags = nullptr;
   unsigned long long* d_dflags = nullptr;
@@ -61,6 +60,15 @@ struct ccl_plan {
   unsigned long long* d_trace = nullptr;
   hipEvent_t last = nullptr;
   bool launched = false;
+  // per-count instruction geometry, least recently used replaced first
+  struct GeoEntry {
+    int64_t count = -1;
+    DevGeo* d = nullptr;
+    uint64_t used = 0;
+  };
+  std::vector<GeoEntry> geo;
+  uint64_t geo_clock = 0;
+  std::vector<DevGeo> geo_host;
   unsigned long long epoch = 0;
   long long timeout_ticks = 0;
   int64_t scratch_stride = 0;  // bytes between ranks' scratch
@@ -76,11 +84,11 @@ struct ccl_plan {
   }
   void release() {
     if (last) {
-      hipEventSynchronize(last);
-      hipEventDestroy(last);
+      (void)hipEventSynchronize(last);
+      (void)hipEventDestroy(last);
       last = nullptr;
     }
-    for (void* p : allocs) hipFree(p);
+    for (void* p : allocs) (void)hipFree(p);
     allocs.clear();
   }
   ~ccl_plan() { release(); }
@@ -114,8 +122,9 @@ void setup_device(ccl_plan* p) {
   p->timeout_ticks = (long long)(hp.cfg.timeout_us * (rate_khz / 1000.0));
   p->d_wgs = upload(p, hp.dwg);
   p->d_ins = upload(p, hp.dins);
-  p->d_xf = upload(p, hp.dxf);
   p->d_waits = upload(p, hp.dwaits);
+  p->geo.resize(4);
+  for (auto& g : p->geo) g.d = static_cast<DevGeo*>(p->dev_alloc(std::max<size_t>(1, hp.dins.size()) * sizeof(DevGeo)));
   size_t nx = std::max<size_t>(1, hp.dxf.size());
   int nd = 0;
   for (const auto& D : hp.dins) nd = std::max(nd, D.done_flag + 1);
@@ -212,10 +221,26 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
     int dev = -1;
     HIP_TRY(hipGetDevice(&dev));
     if (dev != plan->device_id) fail(CCL_ERR_INVALID_ARGUMENT, "plan belongs to another device");
+    // geometry for this count: cached, else computed and uploaded (synchronously,
+    // after the plan's previous launch, since the replaced entry may be in use)
+    ccl_plan::GeoEntry* ge = nullptr;
+    for (auto& g : plan->geo)
+      if (g.count == count) ge = &g;
+    if (!ge) {
+      ge = &plan->geo[0];
+      for (auto& g : plan->geo)
+        if (g.used < ge->used) ge = &g;
+      compute_geometry(hp, count, plan->geo_host);
+      if (plan->launched) HIP_TRY(hipEventSynchronize(plan->last));
+      if (!plan->geo_host.empty())
+        HIP_TRY(hipMemcpy(ge->d, plan->geo_host.data(), plan->geo_host.size() * sizeof(DevGeo), hipMemcpyHostToDevice));
+      ge->count = count;
+    }
+    ge->used = ++plan->geo_clock;
     ExecArgs A{};
     A.wgs = plan->d_wgs;
     A.ins = plan->d_ins;
-    A.xf = plan->d_xf;
+    A.geo = ge->d;
     A.waits = plan->d_waits;
     A.xflags = plan->d_xflags;
     A.dflags = plan->d_dflags;
@@ -223,12 +248,9 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
     A.err = plan->d_err;
     A.abort_word = plan->d_abort;
     A.trace = plan->d_trace;
-    A.count = count;
     A.slice_elems = hp.slice_elems;
     A.epoch = plan->epoch + 1;
     A.timeout_ticks = plan->timeout_ticks;
-    A.nchunks = hp.C;
-    A.k = hp.k;
     for (int r = 0; r < hp.P; ++r) {
       A.base[CCL_BUF_INPUT][r] = const_cast<unsigned char*>(static_cast<const unsigned char*>(sendbufs[r]));
       A.base[CCL_BUF_OUTPUT][r] = static_cast<unsigned char*>(recvbufs[r]);

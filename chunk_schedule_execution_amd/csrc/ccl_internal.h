@@ -113,6 +113,8 @@ int64_t output_elems(const HostPlan& hp, int64_t count);
 void group_members(const ccl_program_desc& d, int r, std::vector<int>& members, int& pos);
 int group_count(const ccl_program_desc& d);
 
+void compute_geometry(const HostPlan& hp, int64_t count, std::vector<DevGeo>& out);
+
 // simulate.cpp
 void check_lowered(const HostPlan& hp, uint64_t seed, int nsims);
 

@@ -908,6 +908,34 @@ int64_t plan_bytes(const HostPlan& hp, int64_t count) {
   return total;
 }
 
+// Byte offsets, lengths and slice counts of every lowered instruction for `count`
+// elements per rank. Slot data starts at the slot's base plus the phase of the chunk
+// named by the transfer, so that slot and local operands share their 16-byte alignment.
+void compute_geometry(const HostPlan& hp, int64_t count, std::vector<DevGeo>& out) {
+  const int V = 16 / hp.esz;
+  out.resize(hp.dins.size());
+  auto slot_off = [&](int x) {
+    const DevXfer& X = hp.dxf[x];
+    int64_t ph = 0;
+    if (X.phase_idx >= 0) ph = op_range(X.phase_idx, X.cnt, X.instance, hp.k, count, hp.C).lo % V;
+    return int64_t(X.slot_off) + ph * hp.esz;
+  };
+  for (size_t j = 0; j < hp.dins.size(); ++j) {
+    const DevInstr& D = hp.dins[j];
+    DevGeo G{};
+    G.len = op_range(D.pad0, D.cnt, D.instance, hp.k, count, hp.C).len;
+    G.nsl = G.len == 0 ? 0 : (G.len + hp.slice_elems - 1) / hp.slice_elems;
+    if (D.op & OPB_RECV)
+      G.a_off = slot_off(D.xin);
+    else
+      G.a_off = op_range(D.a_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
+    if (D.op & OPB_SRCB) G.b_off = op_range(D.b_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
+    if (D.op & OPB_DSTA) G.d_off = op_range(D.d_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
+    if (D.op & OPB_SEND) G.t_off = slot_off(D.xout);
+    out[j] = G;
+  }
+}
+
 void compile_plan(HostPlan& hp, const ccl_program_desc* prog, int nranks, int nchunks, int k,
                   const ccl_plan_config* cfg) {
   auto t0 = Clock::now();

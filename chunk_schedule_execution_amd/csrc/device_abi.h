@@ -41,11 +41,21 @@ struct DevXfer {  // 32 bytes: one send -> recv transfer
   int32_t pad0, pad1, pad2;
 };
 
+// Per-instruction geometry for one element count, computed on the host when a count
+// is first used and cached on the device: byte offsets of every operand (inside the
+// rank's buffer, or inside the staging pool for slots, in-slot phase included),
+// the element length and the number of slices.
+struct DevGeo {  // 48 bytes
+  int64_t a_off, b_off, d_off, t_off;
+  int64_t len;
+  int64_t nsl;
+};
+
 // Kernel arguments, passed by value.
 struct ExecArgs {
   const DevWG* wgs;
   const DevInstr* ins;
-  const DevXfer* xf;
+  const DevGeo* geo;
   const int32_t* waits;
   unsigned long long* xflags;  // per transfer: epoch << 24 | slices completed
   unsigned long long* dflags;  // per completion flag: epoch when done
@@ -53,12 +63,9 @@ struct ExecArgs {
   unsigned int* err;           // [code, wg, instr, epoch_lo]
   unsigned long long* abort_word;  // epoch of an aborted launch
   unsigned long long* trace;   // 4 words per workgroup, or null
-  int64_t count;               // elements per rank input for this launch
   int64_t slice_elems;         // slice length in elements (multiple of 64)
   unsigned long long epoch;    // launch number, >= 1
   long long timeout_ticks;     // watchdog budget per wait, device wall-clock ticks
-  int32_t nchunks;             // chunk unit of the input
-  int32_t k;                   // parallel factor (instances)
   unsigned char* base[kNumBufs][kMaxRanks];  // per-rank buffer base pointers
 };
 

@@ -26,22 +26,6 @@
 namespace ccl {
 namespace {
 
-__device__ __forceinline__ int64_t cbound(int64_t j, int64_t N, int64_t C) { return (j * N) / C; }
-
-__device__ __forceinline__ void range_of(int idx, int cnt, int inst, int k, int64_t N, int64_t C, int64_t& lo,
-                                         int64_t& len) {
-  int64_t a = cbound(idx, N, C), b = cbound(idx + cnt, N, C);
-  if (k > 1) {
-    int64_t l = b - a;
-    int64_t s = a + (inst * l) / k, e = a + ((inst + 1) * l) / k;
-    lo = s;
-    len = e - s;
-  } else {
-    lo = a;
-    len = b - a;
-  }
-}
-
 // ---- element arithmetic --------------------------------------------------
 
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
@@ -93,120 +77,168 @@ struct Arith<CCL_BF16> {
 };
 
 // ---- one slice of one instruction ------------------------------------------
+//
+// Every access goes through a buffer descriptor whose size is the operand's slice, so
+// an address outside the operand is dropped by the hardware instead of touching
+// other memory. Staging-slot data (RECV loads, SEND stores) uses the sc1 cache policy:
+// agent-coherent, the same policy the compiler gives relaxed agent-scope atomics, so a
+// slot's data is visible across XCDs as soon as the store completes and no L2
+// writeback or invalidate is needed around the slot flags.
 
-// Indices inside a slice are 32-bit: a slice is at most 2^31 bytes.
-template <int DT, bool SRCB, bool DSTA, bool SEND>
-__device__ __attribute__((noinline)) void run_slice(const unsigned char* __restrict__ pa,
-                                                    const unsigned char* __restrict__ pb,
-                                                    unsigned char* __restrict__ pd, unsigned char* __restrict__ pt,
-                                                    int n, int tid, int nthr) {
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 data format
+constexpr int kCpolNone = 0;
+constexpr int kCpolSc1 = 16;  // agent-scope coherent
+
+// Slice pointers and sizes are wave-uniform; readfirstlane puts them in scalar
+// registers so the descriptor is scalar (no per-lane waterfall around each access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const unsigned char* p, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  void* u = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, 0, __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
+}
+
+template <int CP>
+__device__ __forceinline__ v4u ld16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
+}
+template <int CP>
+__device__ __forceinline__ void st16(__amdgpu_buffer_rsrc_t r, int off, v4u v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, CP);
+}
+template <int ESZ, int CP>
+__device__ __forceinline__ uint32_t ld_elem(__amdgpu_buffer_rsrc_t r, int off) {
+  if (ESZ == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, CP);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP);
+}
+template <int ESZ, int CP>
+__device__ __forceinline__ void st_elem(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
+  if (ESZ == 2)
+    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, CP);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, CP);
+}
+
+__device__ __forceinline__ uint4 to_u4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
+__device__ __forceinline__ v4u to_v4(uint4 v) {
+  v4u r = {v.x, v.y, v.z, v.w};
+  return r;
+}
+
+// Indices inside a slice are 32-bit: a slice is far below 2^31 bytes.
+template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND>
+__device__ __attribute__((noinline)) void run_slice(const unsigned char* pa, const unsigned char* pb, unsigned char* pd,
+                                                    unsigned char* pt, int n, int tid, int nthr) {
   typedef Arith<DT> Ar;
-  typedef typename Ar::S S;
   constexpr int esz = Ar::esz;
   constexpr int V = 16 / esz;
+  constexpr int CA = RECV ? kCpolSc1 : kCpolNone;  // first operand: slot or local buffer
+  constexpr int CT = kCpolSc1;                      // outgoing slot
+  const int bytes = n * esz;
+  const __amdgpu_buffer_rsrc_t rA = make_rsrc(pa, bytes);
+  const __amdgpu_buffer_rsrc_t rB = make_rsrc(SRCB ? pb : pa, bytes);
+  const __amdgpu_buffer_rsrc_t rD = make_rsrc(DSTA ? pd : pa, DSTA ? bytes : 0);
+  const __amdgpu_buffer_rsrc_t rT = make_rsrc(SEND ? pt : pa, SEND ? bytes : 0);
   const uintptr_t ra = uintptr_t(pa) & 15;
   bool same = true;
   if (SRCB) same &= (uintptr_t(pb) & 15) == ra;
   if (DSTA) same &= (uintptr_t(pd) & 15) == ra;
   if (SEND) same &= (uintptr_t(pt) & 15) == ra;
   auto scalar = [&](int e) {
-    S v = reinterpret_cast<const S*>(pa)[e];
-    if (SRCB) v = Ar::add(v, reinterpret_cast<const S*>(pb)[e]);
-    if (DSTA) reinterpret_cast<S*>(pd)[e] = v;
-    if (SEND) reinterpret_cast<S*>(pt)[e] = v;
+    const int o = e * esz;
+    uint32_t v = ld_elem<esz, CA>(rA, o);
+    if (SRCB) v = Ar::add(typename Ar::S(v), typename Ar::S(ld_elem<esz, kCpolNone>(rB, o)));
+    if (DSTA) st_elem<esz, kCpolNone>(rD, o, v);
+    if (SEND) st_elem<esz, CT>(rT, o, v);
   };
-  if (!same) {
-    // operands disagree on 16-byte alignment: element-wise, four in flight per thread
-    int e = tid;
-    for (; e + 3 * nthr < n; e += 4 * nthr) {
-      S v0 = reinterpret_cast<const S*>(pa)[e];
-      S v1 = reinterpret_cast<const S*>(pa)[e + nthr];
-      S v2 = reinterpret_cast<const S*>(pa)[e + 2 * nthr];
-      S v3 = reinterpret_cast<const S*>(pa)[e + 3 * nthr];
+  int tail0 = 0;
+  if (same) {
+    int head = int((16 - ra) & 15) / esz;
+    if (head > n) head = n;
+    if (tid < head) scalar(tid);
+    const int nvec = (n - head) / V;
+    const int base = head * esz;
+    int i = tid;
+    for (; i + 3 * nthr < nvec; i += 4 * nthr) {
+      const int o0 = base + 16 * i, o1 = o0 + 16 * nthr, o2 = o1 + 16 * nthr, o3 = o2 + 16 * nthr;
+      uint4 a0 = to_u4(ld16<CA>(rA, o0)), a1 = to_u4(ld16<CA>(rA, o1));
+      uint4 a2 = to_u4(ld16<CA>(rA, o2)), a3 = to_u4(ld16<CA>(rA, o3));
       if (SRCB) {
-        v0 = Ar::add(v0, reinterpret_cast<const S*>(pb)[e]);
-        v1 = Ar::add(v1, reinterpret_cast<const S*>(pb)[e + nthr]);
-        v2 = Ar::add(v2, reinterpret_cast<const S*>(pb)[e + 2 * nthr]);
-        v3 = Ar::add(v3, reinterpret_cast<const S*>(pb)[e + 3 * nthr]);
+        uint4 b0 = to_u4(ld16<kCpolNone>(rB, o0)), b1 = to_u4(ld16<kCpolNone>(rB, o1));
+        uint4 b2 = to_u4(ld16<kCpolNone>(rB, o2)), b3 = to_u4(ld16<kCpolNone>(rB, o3));
+        a0 = Ar::add4(a0, b0);
+        a1 = Ar::add4(a1, b1);
+        a2 = Ar::add4(a2, b2);
+        a3 = Ar::add4(a3, b3);
       }
       if (DSTA) {
-        reinterpret_cast<S*>(pd)[e] = v0;
-        reinterpret_cast<S*>(pd)[e + nthr] = v1;
-        reinterpret_cast<S*>(pd)[e + 2 * nthr] = v2;
-        reinterpret_cast<S*>(pd)[e + 3 * nthr] = v3;
+        st16<kCpolNone>(rD, o0, to_v4(a0));
+        st16<kCpolNone>(rD, o1, to_v4(a1));
+        st16<kCpolNone>(rD, o2, to_v4(a2));
+        st16<kCpolNone>(rD, o3, to_v4(a3));
       }
       if (SEND) {
-        reinterpret_cast<S*>(pt)[e] = v0;
-        reinterpret_cast<S*>(pt)[e + nthr] = v1;
-        reinterpret_cast<S*>(pt)[e + 2 * nthr] = v2;
-        reinterpret_cast<S*>(pt)[e + 3 * nthr] = v3;
+        st16<CT>(rT, o0, to_v4(a0));
+        st16<CT>(rT, o1, to_v4(a1));
+        st16<CT>(rT, o2, to_v4(a2));
+        st16<CT>(rT, o3, to_v4(a3));
       }
     }
-    for (; e < n; e += nthr) scalar(e);
-    return;
-  }
-  int head = int((16 - ra) & 15) / esz;
-  if (head > n) head = n;
-  if (tid < head) scalar(tid);
-  const int nvec = (n - head) / V;
-  const int off = head * esz;
-  const uint4* __restrict__ A4 = reinterpret_cast<const uint4*>(pa + off);
-  const uint4* __restrict__ B4 = reinterpret_cast<const uint4*>(SRCB ? pb + off : pa + off);
-  uint4* __restrict__ D4 = reinterpret_cast<uint4*>(DSTA ? pd + off : nullptr);
-  uint4* __restrict__ T4 = reinterpret_cast<uint4*>(SEND ? pt + off : nullptr);
-  int i = tid;
-  for (; i + 3 * nthr < nvec; i += 4 * nthr) {
-    uint4 a0 = A4[i], a1 = A4[i + nthr], a2 = A4[i + 2 * nthr], a3 = A4[i + 3 * nthr];
-    if (SRCB) {
-      uint4 b0 = B4[i], b1 = B4[i + nthr], b2 = B4[i + 2 * nthr], b3 = B4[i + 3 * nthr];
-      a0 = Ar::add4(a0, b0);
-      a1 = Ar::add4(a1, b1);
-      a2 = Ar::add4(a2, b2);
-      a3 = Ar::add4(a3, b3);
+    for (; i < nvec; i += nthr) {
+      const int o = base + 16 * i;
+      uint4 a = to_u4(ld16<CA>(rA, o));
+      if (SRCB) a = Ar::add4(a, to_u4(ld16<kCpolNone>(rB, o)));
+      if (DSTA) st16<kCpolNone>(rD, o, to_v4(a));
+      if (SEND) st16<CT>(rT, o, to_v4(a));
     }
-    if (DSTA) {
-      D4[i] = a0;
-      D4[i + nthr] = a1;
-      D4[i + 2 * nthr] = a2;
-      D4[i + 3 * nthr] = a3;
-    }
-    if (SEND) {
-      T4[i] = a0;
-      T4[i + nthr] = a1;
-      T4[i + 2 * nthr] = a2;
-      T4[i + 3 * nthr] = a3;
-    }
+    tail0 = head + nvec * V;
   }
-  for (; i < nvec; i += nthr) {
-    uint4 a = A4[i];
-    if (SRCB) a = Ar::add4(a, B4[i]);
-    if (DSTA) D4[i] = a;
-    if (SEND) T4[i] = a;
-  }
-  const int tail0 = head + nvec * V;
+  // unaligned operands, or the tail: element by element
   for (int e = tail0 + tid; e < n; e += nthr) scalar(e);
 }
 
 template <int DT>
 __device__ __forceinline__ void dispatch_slice(uint32_t op, const unsigned char* pa, const unsigned char* pb,
                                                unsigned char* pd, unsigned char* pt, int n, int tid, int nthr) {
-  switch (op & (OPB_SRCB | OPB_DSTA | OPB_SEND)) {
-    case OPB_DSTA: run_slice<DT, false, true, false>(pa, pb, pd, pt, n, tid, nthr); break;
-    case OPB_SEND: run_slice<DT, false, false, true>(pa, pb, pd, pt, n, tid, nthr); break;
-    case OPB_DSTA | OPB_SEND: run_slice<DT, false, true, true>(pa, pb, pd, pt, n, tid, nthr); break;
-    case OPB_SRCB | OPB_DSTA: run_slice<DT, true, true, false>(pa, pb, pd, pt, n, tid, nthr); break;
-    case OPB_SRCB | OPB_SEND: run_slice<DT, true, false, true>(pa, pb, pd, pt, n, tid, nthr); break;
-    case OPB_SRCB | OPB_DSTA | OPB_SEND: run_slice<DT, true, true, true>(pa, pb, pd, pt, n, tid, nthr); break;
+#define CCL_CASE(R, B, D, T)                                                                                     \
+  case ((R) ? OPB_RECV : 0u) | ((B) ? OPB_SRCB : 0u) | ((D) ? OPB_DSTA : 0u) | ((T) ? OPB_SEND : 0u):            \
+    run_slice<DT, R, B, D, T>(pa, pb, pd, pt, n, tid, nthr);                                                    \
+    break;
+  switch (op & 15u) {
+    CCL_CASE(false, false, true, false)
+    CCL_CASE(false, false, false, true)
+    CCL_CASE(false, false, true, true)
+    CCL_CASE(false, true, true, false)
+    CCL_CASE(false, true, false, true)
+    CCL_CASE(false, true, true, true)
+    CCL_CASE(true, false, true, false)
+    CCL_CASE(true, false, false, true)
+    CCL_CASE(true, false, true, true)
+    CCL_CASE(true, true, true, false)
+    CCL_CASE(true, true, false, true)
+    CCL_CASE(true, true, true, true)
     default: break;  // an instruction always stores somewhere; the compiler never emits this
   }
+#undef CCL_CASE
 }
 
 // ---- flags ------------------------------------------------------------------
 
+// Completion flags guard local-buffer data written with ordinary (L2-cached)
+// stores: a full agent-scope release / acquire.
 __device__ __forceinline__ void release_store(unsigned long long* p, unsigned long long v) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// Slot flags guard sc1 data whose stores every wave has already waited for.
+__device__ __forceinline__ void slot_flag_store(unsigned long long* p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 __device__ void report_timeout(const ExecArgs& A, int instr) {
   if (atomicCAS(&A.err[0], 0u, unsigned(-CCL_ERR_TIMEOUT)) == 0u) {
@@ -217,13 +249,15 @@ __device__ void report_timeout(const ExecArgs& A, int instr) {
   __hip_atomic_store(A.abort_word, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0 only: spin until *p >= target (acquire), the watchdog expires, or the
-// launch is aborted by another workgroup's watchdog. Returns false on the latter two.
+// Thread 0 only: spin until *p >= target, the watchdog expires, or the launch is
+// aborted by another workgroup's watchdog. Returns false on the latter two. With
+// ACQ the success path ends in an agent-scope acquire fence.
+template <bool ACQ>
 __device__ bool wait_geq(unsigned long long* p, unsigned long long target, const ExecArgs& A, int instr,
                          unsigned long long& wait_ticks) {
   unsigned long long v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (v >= target) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (ACQ) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     return true;
   }
   const long long t0 = wall_clock64();
@@ -231,7 +265,7 @@ __device__ bool wait_geq(unsigned long long* p, unsigned long long target, const
     __builtin_amdgcn_s_sleep(1);
     v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (v >= target) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (ACQ) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       wait_ticks += (unsigned long long)(wall_clock64() - t0);
       return true;
     }
@@ -250,7 +284,6 @@ __device__ bool wait_geq(unsigned long long* p, unsigned long long target, const
 template <int DT>
 __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
   constexpr int esz = Arith<DT>::esz;
-  constexpr int V = 16 / esz;
   __shared__ int s_ok;
   const DevWG W = A.wgs[blockIdx.x];
   const int tid = threadIdx.x, nthr = blockDim.x;
@@ -260,73 +293,40 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
   if (A.trace && tid == 0) t_begin = wall_clock64();
   int ran = 0;
   for (int ii = 0; ii < W.n; ++ii) {
-    const DevInstr D = A.ins[W.first + ii];
     const int gi = W.first + ii;
+    const DevInstr D = A.ins[gi];
+    const DevGeo G = A.geo[gi];
     if (D.nwaits > 0) {
       if (tid == 0) {
         int ok = 1;
         for (int w = 0; w < D.nwaits && ok; ++w)
-          ok = wait_geq(&A.dflags[A.waits[D.wait_begin + w]], A.epoch, A, gi, wait_ticks) ? 1 : 0;
+          ok = wait_geq<true>(&A.dflags[A.waits[D.wait_begin + w]], A.epoch, A, gi, wait_ticks) ? 1 : 0;
         s_ok = ok;
       }
       __syncthreads();
       if (!s_ok) return;
     }
-    int64_t lo, len;
-    range_of(D.pad0, D.cnt, D.instance, A.k, A.count, A.nchunks, lo, len);
-    const unsigned char* pa;
-    const unsigned char* pb = nullptr;
-    unsigned char* pd = nullptr;
-    unsigned char* pt = nullptr;
-    if (D.op & OPB_RECV) {
-      const DevXfer X = A.xf[D.xin];
-      int64_t ph = 0;
-      if (X.phase_idx >= 0) {
-        int64_t plo, plen;
-        range_of(X.phase_idx, X.cnt, X.instance, A.k, A.count, A.nchunks, plo, plen);
-        ph = plo % V;
-      }
-      pa = A.staging + X.slot_off + ph * esz;
-    } else {
-      int64_t l, n;
-      range_of(D.a_idx, D.cnt, D.instance, A.k, A.count, A.nchunks, l, n);
-      pa = A.base[D.a_buf][W.rank] + l * esz;
-    }
-    if (D.op & OPB_SRCB) {
-      int64_t l, n;
-      range_of(D.b_idx, D.cnt, D.instance, A.k, A.count, A.nchunks, l, n);
-      pb = A.base[D.b_buf][W.rank] + l * esz;
-    }
-    if (D.op & OPB_DSTA) {
-      int64_t l, n;
-      range_of(D.d_idx, D.cnt, D.instance, A.k, A.count, A.nchunks, l, n);
-      pd = A.base[D.d_buf][W.rank] + l * esz;
-    }
-    if (D.op & OPB_SEND) {
-      const DevXfer X = A.xf[D.xout];
-      int64_t ph = 0;
-      if (X.phase_idx >= 0) {
-        int64_t plo, plen;
-        range_of(X.phase_idx, X.cnt, X.instance, A.k, A.count, A.nchunks, plo, plen);
-        ph = plo % V;
-      }
-      pt = A.staging + X.slot_off + ph * esz;
-    }
+    const unsigned char* pa =
+        (D.op & OPB_RECV) ? A.staging + G.a_off : A.base[D.a_buf][W.rank] + G.a_off;
+    const unsigned char* pb = (D.op & OPB_SRCB) ? A.base[D.b_buf][W.rank] + G.b_off : nullptr;
+    unsigned char* pd = (D.op & OPB_DSTA) ? A.base[D.d_buf][W.rank] + G.d_off : nullptr;
+    unsigned char* pt = (D.op & OPB_SEND) ? A.staging + G.t_off : nullptr;
     const int64_t se = A.slice_elems;
-    const int64_t nsl = (len + se - 1) / se;
-    for (int64_t s = 0; s < nsl; ++s) {
+    for (int64_t s = 0; s < G.nsl; ++s) {
       if (D.op & OPB_RECV) {
-        if (tid == 0) s_ok = wait_geq(&A.xflags[D.xin], E + (unsigned long long)(s + 1), A, gi, wait_ticks) ? 1 : 0;
+        if (tid == 0)
+          s_ok = wait_geq<false>(&A.xflags[D.xin], E + (unsigned long long)(s + 1), A, gi, wait_ticks) ? 1 : 0;
         __syncthreads();
         if (!s_ok) return;
       }
       const int64_t o = s * se;
-      const int64_t n = (len - o < se) ? (len - o) : se;
+      const int n = int((G.len - o < se) ? (G.len - o) : se);
       const int64_t bo = o * esz;
-      dispatch_slice<DT>(D.op, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr, pt ? pt + bo : nullptr,
-                         int(n), tid, nthr);
+      dispatch_slice<DT>(D.op, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr, pt ? pt + bo : nullptr, n,
+                         tid, nthr);
+      if (D.op & OPB_SEND) wait_vm_stores();
       __syncthreads();
-      if ((D.op & OPB_SEND) && tid == 0) release_store(&A.xflags[D.xout], E + (unsigned long long)(s + 1));
+      if ((D.op & OPB_SEND) && tid == 0) slot_flag_store(&A.xflags[D.xout], E + (unsigned long long)(s + 1));
     }
     if (D.done_flag >= 0 && tid == 0) release_store(&A.dflags[D.done_flag], A.epoch);
     ++ran;

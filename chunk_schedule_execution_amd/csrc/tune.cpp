@@ -105,14 +105,14 @@ static double device_objective(const ccl_tune_point* pt, void* user) {
   if (rc) return -1.0;  // infeasible (e.g. not enough co-resident workgroups)
   for (int i = 0; i < c->warmup && rc == 0; ++i)
     rc = ccl_execute(plan, (const void* const*)c->in.data(), c->out.data(), c->count, c->stream);
-  hipEventRecord(c->e0, c->stream);
+  (void)hipEventRecord(c->e0, c->stream);
   for (int i = 0; i < c->iters && rc == 0; ++i)
     rc = ccl_execute(plan, (const void* const*)c->in.data(), c->out.data(), c->count, c->stream);
-  hipEventRecord(c->e1, c->stream);
-  hipEventSynchronize(c->e1);
+  (void)hipEventRecord(c->e1, c->stream);
+  (void)hipEventSynchronize(c->e1);
   if (rc == 0) rc = ccl_plan_status(plan);
   float ms = 0.f;
-  hipEventElapsedTime(&ms, c->e0, c->e1);
+  (void)hipEventElapsedTime(&ms, c->e0, c->e1);
   ccl_plan_destroy(plan);
   if (rc) {
     c->last_error = rc;
@@ -149,11 +149,11 @@ int ccl_tune(const ccl_program_desc* const* variants, int nvariants, int64_t cou
     void* a = nullptr;
     void* b = nullptr;
     if (hipMalloc(&a, size_t(count) * esz) != hipSuccess || hipMalloc(&b, size_t(out_elems) * esz) != hipSuccess) {
-      if (a) hipFree(a);
+      if (a) (void)hipFree(a);
       rc = CCL_ERR_OUT_OF_RESOURCES;
       break;
     }
-    hipMemset(a, 0, size_t(count) * esz);
+    (void)hipMemset(a, 0, size_t(count) * esz);
     c.in.push_back(a);
     c.out.push_back(b);
   }
@@ -161,11 +161,11 @@ int ccl_tune(const ccl_program_desc* const* variants, int nvariants, int64_t cou
   ccl_tune_space sp = *space;
   sp.nvariants = nvariants;
   if (rc == 0) rc = ccl_tune_coordinate_descent(&sp, nullptr, device_objective, &c, best, report);
-  hipDeviceSynchronize();
-  for (void* p : c.in) hipFree(p);
-  for (void* p : c.out) hipFree(p);
-  if (c.e0) hipEventDestroy(c.e0);
-  if (c.e1) hipEventDestroy(c.e1);
+  (void)hipDeviceSynchronize();
+  for (void* p : c.in) (void)hipFree(p);
+  for (void* p : c.out) (void)hipFree(p);
+  if (c.e0) (void)hipEventDestroy(c.e0);
+  if (c.e1) (void)hipEventDestroy(c.e1);
   return rc;
 }
 

@@ -149,3 +149,46 @@ def ring_allreduce_inter(xs, L, dtype):
         for i, r in enumerate(ranks):
             out[r] = res[i]
     return out
+
+
+# ---- the same folds at sampled element indices (checks at full sizes) --------------
+
+def chunk_of(idx, N: int, C: int):
+    """Chunk that holds each element index: the last chunk whose start is <= index."""
+    starts = np.array([(j * N) // C for j in range(C + 1)], dtype=np.int64)
+    return np.searchsorted(starts, np.asarray(idx, dtype=np.int64), side="right") - 1
+
+
+def ring_allreduce_at(xs, nchunks, idx, dtype):
+    """Ring AllReduce output at element indices ``idx`` (same for every rank)."""
+    P = len(xs)
+    N = len(xs[0])
+    c = nchunks // P
+    idx = np.asarray(idx, dtype=np.int64)
+    owner = chunk_of(idx, N, nchunks) // c
+    out = np.empty(len(idx), dtype=np.asarray(xs[0]).dtype)
+    for o in range(P):
+        sel = np.nonzero(owner == o)[0]
+        if sel.size == 0:
+            continue
+        order = [(o + 1 + t) % P for t in range(P)]
+        out[sel] = fold([np.asarray(xs[r])[idx[sel]] for r in order], dtype)
+    return out
+
+
+def hierarchical_allreduce_at(xs, G, L, idx, dtype):
+    N = len(xs[0])
+    C = L * G
+    idx = np.asarray(idx, dtype=np.int64)
+    j = chunk_of(idx, N, C)
+    out = np.empty(len(idx), dtype=np.asarray(xs[0]).dtype)
+    for jj in np.unique(j):
+        sel = np.nonzero(j == jj)[0]
+        l, gp = divmod(int(jj), G)
+        partial = []
+        for g in range(G):
+            lanes = [(l + 1 + t) % L for t in range(L)]
+            partial.append(fold([np.asarray(xs[g * L + ln])[idx[sel]] for ln in lanes], dtype))
+        groups = [(gp + 1 + t) % G for t in range(G)]
+        out[sel] = fold([partial[g] for g in groups], dtype)
+    return out

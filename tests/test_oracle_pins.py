@@ -434,3 +434,14 @@ def test_planted_mistakes_fail_the_pins(golden, monkeypatch):
         cases = golden("bf16_rne_cases.txt")
         x = np.array([int(c[0], 16) for c in cases], dtype=np.uint32).view(np.float32)
         assert [int(v) for v in nm.f32_to_bf16_rne(x)] != [int(c[1], 16) for c in cases]
+
+
+def test_sampled_folds_match_whole_folds():
+    P, N = 8, 1003
+    xs = W.make_inputs("normal_f32", N, P, cfg_id=85)
+    full = O2.ring_allreduce(xs, 16, "f32")[0]
+    idx = np.arange(N)
+    assert np.array_equal(O2.ring_allreduce_at(xs, 16, idx, "f32"), full)
+    xb = W.make_inputs("normal_bf16", 16 * 37, 16, cfg_id=85)
+    fullh = O2.hierarchical_allreduce(xb, 2, 8, "bf16")[0]
+    assert np.array_equal(O2.hierarchical_allreduce_at(xb, 2, 8, np.arange(16 * 37), "bf16"), fullh)
