@@ -32,7 +32,7 @@ CCL_F32, CCL_BF16, CCL_I32 = 0, 1, 2
 CCL_SCOPE_ALL, CCL_SCOPE_INTRA, CCL_SCOPE_INTER = 0, 1, 2
 CCL_SCHED_PROGRAM_ORDER, CCL_SCHED_HPDS, CCL_SCHED_RR = 0, 1, 2
 CCL_WG_CONNECTION, CCL_WG_STATE = 0, 1
-CCL_FLAG_TRACE, CCL_FLAG_HOST_ONLY, CCL_FLAG_NO_FUSION, CCL_FLAG_NO_VERIFY = 0x1, 0x2, 0x4, 0x8
+CCL_FLAG_TRACE, CCL_FLAG_HOST_ONLY, CCL_FLAG_NO_FUSION, CCL_FLAG_NO_VERIFY, CCL_FLAG_LL = 0x1, 0x2, 0x4, 0x8, 0x10
 CCL_I_RECV, CCL_I_SRCB, CCL_I_DSTA, CCL_I_SEND = 0x1, 0x2, 0x4, 0x8
 
 
@@ -63,7 +63,7 @@ class ccl_plan_info_t(C.Structure):
                 ("num_instructions", C.c_int32), ("num_subpipelines", C.c_int32),
                 ("num_connections", C.c_int32), ("num_transfers", C.c_int32), ("num_waits", C.c_int32),
                 ("count_granule", C.c_int32), ("nthreads", C.c_int32), ("slice_bytes", C.c_int32),
-                ("max_resident_wgs", C.c_int32), ("reserved", C.c_int32),
+                ("max_resident_wgs", C.c_int32), ("grid_workgroups", C.c_int32),
                 ("staging_bytes", C.c_int64), ("scratch_bytes", C.c_int64), ("flag_bytes", C.c_int64),
                 ("table_bytes", C.c_int64), ("compile_ms", C.c_double * 6), ("opcode_hist", C.c_int32 * 16)]
 
@@ -77,14 +77,15 @@ class ccl_instr_info(C.Structure):
 
 class ccl_tune_point(C.Structure):
     _fields_ = [("variant", C.c_int32), ("parallel_factor", C.c_int32), ("nthreads", C.c_int32),
-                ("slice_bytes", C.c_int32)]
+                ("slice_bytes", C.c_int32), ("protocol", C.c_int32), ("reserved", C.c_int32)]
 
 
 class ccl_tune_space(C.Structure):
     _fields_ = [("factors", C.POINTER(C.c_int32)), ("nfactors", C.c_int32),
                 ("nthreads", C.POINTER(C.c_int32)), ("nnthreads", C.c_int32),
                 ("slices", C.POINTER(C.c_int32)), ("nslices", C.c_int32),
-                ("nvariants", C.c_int32), ("warmup", C.c_int32), ("iters", C.c_int32)]
+                ("nvariants", C.c_int32), ("warmup", C.c_int32), ("iters", C.c_int32),
+                ("protocols", C.c_int32)]
 
 
 class ccl_tune_report(C.Structure):
@@ -220,10 +221,13 @@ def ccl_plan_status(plan: int) -> None:
     _check(_lib.ccl_plan_status(C.c_void_p(plan)), "ccl_plan_status")
 
 
-def ccl_plan_read_trace(plan: int, nwg: int):
-    buf = (C.c_uint64 * (4 * max(1, nwg)))()
+def ccl_plan_read_trace(plan: int, nwg: int, ninstr: int = 0):
+    """Per-workgroup records, and per-instruction records when ninstr > 0."""
+    n = nwg + ninstr
+    buf = (C.c_uint64 * (4 * max(1, n)))()
     _check(_lib.ccl_plan_read_trace(C.c_void_p(plan), buf, C.sizeof(buf)), "ccl_plan_read_trace")
-    return [tuple(buf[4 * w:4 * w + 4]) for w in range(nwg)]
+    recs = [tuple(buf[4 * w:4 * w + 4]) for w in range(n)]
+    return (recs[:nwg], recs[nwg:]) if ninstr else recs
 
 
 def ccl_tune_coordinate_descent(space: ccl_tune_space, objective, start: ccl_tune_point | None = None):

@@ -49,7 +49,6 @@ struct ccl_plan {
   int device_id = -1;
   std::vector<void*> allocs;
   DevWG* d_wgs = nullptr;
-  DevInstr* d_ins = nullptr;
   int32_t* d_waits = nullptr;
   unsigned long long* d_xflags = nullptr;
   unsigned long long* d_dflags = nullptr;
@@ -58,17 +57,18 @@ struct ccl_plan {
   unsigned int* d_err = nullptr;
   unsigned long long* d_abort = nullptr;
   unsigned long long* d_trace = nullptr;
-  hipEvent_t last = nullptr;
+  hipEvent_t last = nullptr;    // recorded on last_stream when another stream needs ordering
+  hipStream_t last_stream = nullptr;
   bool launched = false;
   // per-count instruction geometry, least recently used replaced first
   struct GeoEntry {
     int64_t count = -1;
-    DevGeo* d = nullptr;
+    DevExec* d = nullptr;
     uint64_t used = 0;
   };
   std::vector<GeoEntry> geo;
   uint64_t geo_clock = 0;
-  std::vector<DevGeo> geo_host;
+  std::vector<DevExec> geo_host;
   unsigned long long epoch = 0;
   long long timeout_ticks = 0;
   int64_t scratch_stride = 0;  // bytes between ranks' scratch
@@ -83,8 +83,8 @@ struct ccl_plan {
     return p;
   }
   void release() {
+    if (launched) (void)hipStreamSynchronize(last_stream);
     if (last) {
-      (void)hipEventSynchronize(last);
       (void)hipEventDestroy(last);
       last = nullptr;
     }
@@ -121,10 +121,9 @@ void setup_device(ccl_plan* p) {
   if (rate_khz <= 0) rate_khz = 100000;
   p->timeout_ticks = (long long)(hp.cfg.timeout_us * (rate_khz / 1000.0));
   p->d_wgs = upload(p, hp.dwg);
-  p->d_ins = upload(p, hp.dins);
   p->d_waits = upload(p, hp.dwaits);
   p->geo.resize(4);
-  for (auto& g : p->geo) g.d = static_cast<DevGeo*>(p->dev_alloc(std::max<size_t>(1, hp.dins.size()) * sizeof(DevGeo)));
+  for (auto& g : p->geo) g.d = static_cast<DevExec*>(p->dev_alloc(std::max<size_t>(1, hp.dins.size()) * sizeof(DevExec)));
   size_t nx = std::max<size_t>(1, hp.dxf.size());
   int nd = 0;
   for (const auto& D : hp.dins) nd = std::max(nd, D.done_flag + 1);
@@ -133,6 +132,7 @@ void setup_device(ccl_plan* p) {
   p->d_dflags = static_cast<unsigned long long*>(p->dev_alloc(std::max(1, nd) * 8));
   HIP_TRY(hipMemset(p->d_dflags, 0, std::max(1, nd) * 8));
   p->d_staging = static_cast<unsigned char*>(p->dev_alloc(size_t(hp.staging_bytes)));
+  HIP_TRY(hipMemset(p->d_staging, 0, size_t(hp.staging_bytes)));  // LL flags start at 0, never a launch's flag
   p->scratch_stride = ((hp.scratch_elems_per_rank * hp.esz) + 255) / 256 * 256;
   if (p->scratch_stride) p->d_scratch = static_cast<unsigned char*>(p->dev_alloc(size_t(p->scratch_stride) * hp.P));
   p->d_err = static_cast<unsigned int*>(p->dev_alloc(16));
@@ -140,8 +140,9 @@ void setup_device(ccl_plan* p) {
   p->d_abort = static_cast<unsigned long long*>(p->dev_alloc(8));
   HIP_TRY(hipMemset(p->d_abort, 0, 8));
   if (hp.cfg.flags & CCL_FLAG_TRACE) {
-    p->d_trace = static_cast<unsigned long long*>(p->dev_alloc(hp.dwg.size() * 32));
-    HIP_TRY(hipMemset(p->d_trace, 0, hp.dwg.size() * 32));
+    const size_t tb = (hp.dwg.size() + hp.dins.size()) * 32;
+    p->d_trace = static_cast<unsigned long long*>(p->dev_alloc(tb));
+    HIP_TRY(hipMemset(p->d_trace, 0, tb));
   }
   HIP_TRY(hipEventCreateWithFlags(&p->last, hipEventDisableTiming));
   HIP_TRY(hipDeviceSynchronize());
@@ -230,17 +231,16 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
       ge = &plan->geo[0];
       for (auto& g : plan->geo)
         if (g.used < ge->used) ge = &g;
-      compute_geometry(hp, count, plan->geo_host);
-      if (plan->launched) HIP_TRY(hipEventSynchronize(plan->last));
+      compute_exec_records(hp, count, plan->geo_host);
+      if (plan->launched) HIP_TRY(hipStreamSynchronize(plan->last_stream));
       if (!plan->geo_host.empty())
-        HIP_TRY(hipMemcpy(ge->d, plan->geo_host.data(), plan->geo_host.size() * sizeof(DevGeo), hipMemcpyHostToDevice));
+        HIP_TRY(hipMemcpy(ge->d, plan->geo_host.data(), plan->geo_host.size() * sizeof(DevExec), hipMemcpyHostToDevice));
       ge->count = count;
     }
     ge->used = ++plan->geo_clock;
     ExecArgs A{};
     A.wgs = plan->d_wgs;
-    A.ins = plan->d_ins;
-    A.geo = ge->d;
+    A.recs = ge->d;
     A.waits = plan->d_waits;
     A.xflags = plan->d_xflags;
     A.dflags = plan->d_dflags;
@@ -248,21 +248,29 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
     A.err = plan->d_err;
     A.abort_word = plan->d_abort;
     A.trace = plan->d_trace;
+    unsigned long long epoch = plan->epoch + 1;
+    if (uint32_t(epoch) == 0) ++epoch;  // LL units use the low 32 bits; zero is the slots' initial value
     A.slice_elems = hp.slice_elems;
-    A.epoch = plan->epoch + 1;
+    A.epoch = epoch;
     A.timeout_ticks = plan->timeout_ticks;
+    A.ll = (hp.cfg.flags & CCL_FLAG_LL) ? 1 : 0;
+    A.ll_flag = uint32_t(epoch);
     for (int r = 0; r < hp.P; ++r) {
       A.base[CCL_BUF_INPUT][r] = const_cast<unsigned char*>(static_cast<const unsigned char*>(sendbufs[r]));
       A.base[CCL_BUF_OUTPUT][r] = static_cast<unsigned char*>(recvbufs[r]);
       A.base[CCL_BUF_SCRATCH][r] = plan->d_scratch ? plan->d_scratch + size_t(plan->scratch_stride) * r : nullptr;
     }
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (plan->launched) HIP_TRY(hipStreamWaitEvent(s, plan->last, 0));
+    // launches of one plan are serialized: on a new stream, first wait for the old one
+    if (plan->launched && s != plan->last_stream) {
+      HIP_TRY(hipEventRecord(plan->last, plan->last_stream));
+      HIP_TRY(hipStreamWaitEvent(s, plan->last, 0));
+    }
     std::string err;
     int rc = launch_executor(A, hp.cfg.dtype, int(hp.dwg.size()), hp.cfg.nthreads, stream, &err);
     if (rc) fail(rc, err);
-    plan->epoch += 1;
-    HIP_TRY(hipEventRecord(plan->last, s));
+    plan->epoch = epoch;
+    plan->last_stream = s;
     plan->launched = true;
     return CCL_OK;
   });
@@ -277,7 +285,9 @@ int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info) {
     info->nchunks = hp.C;
     info->parallel_factor = hp.k;
     info->dtype = hp.cfg.dtype;
-    info->num_workgroups = int(hp.dwg.size());
+    info->num_workgroups = 0;
+    for (const auto& G : hp.dwg) info->num_workgroups += G.n > 0 ? 1 : 0;
+    info->grid_workgroups = int(hp.dwg.size());
     info->max_wg_per_rank = hp.max_wg_per_rank;
     info->num_instructions = int(hp.dins.size());
     info->num_subpipelines = hp.num_subpipes;
@@ -293,8 +303,8 @@ int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info) {
     int nd = 0;
     for (const auto& D : hp.dins) nd = std::max(nd, D.done_flag + 1);
     info->flag_bytes = int64_t(hp.dxf.size() + nd) * 8;
-    info->table_bytes = int64_t(hp.dwg.size() * sizeof(DevWG) + hp.dins.size() * sizeof(DevInstr) +
-                                hp.dxf.size() * sizeof(DevXfer) + hp.dwaits.size() * 4);
+    info->table_bytes = int64_t(hp.dwg.size() * sizeof(DevWG) + hp.dins.size() * sizeof(DevExec) * 4 +
+                                hp.dwaits.size() * 4);
     for (int i = 0; i < 6; ++i) info->compile_ms[i] = hp.ms[i];
     for (const auto& D : hp.dins) info->opcode_hist[D.op & 15]++;
     return CCL_OK;
@@ -363,7 +373,7 @@ int ccl_plan_status(ccl_plan* plan) {
   return guarded([&] {
     std::lock_guard<std::mutex> lk(plan->mu);
     if (!plan->device) return CCL_OK;
-    if (plan->launched) HIP_TRY(hipEventSynchronize(plan->last));
+    if (plan->launched) HIP_TRY(hipStreamSynchronize(plan->last_stream));
     unsigned int e[4] = {0, 0, 0, 0};
     HIP_TRY(hipMemcpy(e, plan->d_err, sizeof e, hipMemcpyDeviceToHost));
     if (e[0] == 0) return CCL_OK;
@@ -380,7 +390,9 @@ int ccl_plan_read_trace(ccl_plan* plan, void* host, size_t bytes) {
     if (!plan->d_trace) fail(CCL_ERR_INVALID_ARGUMENT, "plan was not created with CCL_FLAG_TRACE");
     size_t need = plan->hp.dwg.size() * 32;
     if (bytes < need) fail(CCL_ERR_INVALID_ARGUMENT, "trace buffer too small");
-    if (plan->launched) HIP_TRY(hipEventSynchronize(plan->last));
+    const size_t full = (plan->hp.dwg.size() + plan->hp.dins.size()) * 32;
+    if (bytes >= full) need = full;
+    if (plan->launched) HIP_TRY(hipStreamSynchronize(plan->last_stream));
     HIP_TRY(hipMemcpy(host, plan->d_trace, need, hipMemcpyDeviceToHost));
     return CCL_OK;
   });

@@ -101,6 +101,7 @@ struct HostPlan {
   int num_connections = 0;
   int max_wg_per_rank = 0;
   int max_resident_wgs = 0;
+  int wg_stride = 1;  // lowered ids per base workgroup (>= k; extra ids are empty)
   double ms[6] = {0, 0, 0, 0, 0, 0};
 };
 
@@ -113,7 +114,7 @@ int64_t output_elems(const HostPlan& hp, int64_t count);
 void group_members(const ccl_program_desc& d, int r, std::vector<int>& members, int& pos);
 int group_count(const ccl_program_desc& d);
 
-void compute_geometry(const HostPlan& hp, int64_t count, std::vector<DevGeo>& out);
+void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec>& out);
 
 // simulate.cpp
 void check_lowered(const HostPlan& hp, uint64_t seed, int nsims);

@@ -812,6 +812,7 @@ void lower(HostPlan& hp) {
     const Xfer& X = hp.xf[x];
     int64_t cap = (k == 1) ? (int64_t(X.cnt) * M) / hp.C + 2 : (M / hp.C + 2) / k + 2;
     int64_t bytes = ((cap + 16) * hp.esz + 255) / 256 * 256;
+    if (hp.cfg.flags & CCL_FLAG_LL) bytes *= 2;  // every 4 data bytes travel with a 4-byte flag
     for (int i = 0; i < k; ++i) {
       DevXfer& D = hp.dxf[size_t(x) * k + i];
       D.slot_off = uint64_t(off);
@@ -827,11 +828,25 @@ void lower(HostPlan& hp) {
     if (I.a.buf == CCL_BUF_SCRATCH || I.b.buf == CCL_BUF_SCRATCH || I.d.buf == CCL_BUF_SCRATCH) uses_scratch = true;
   hp.scratch_elems_per_rank = uses_scratch ? chunk_bound(hp.scr_chunks, M, hp.C) + 64 : 0;
   std::vector<int> per_rank(hp.P, 0);
-  // lowered workgroup (w, i) has id w*k + i
+  // Lowered workgroup (w, i) gets id w*stride + i. Workgroups are dispatched to the
+  // eight XCDs round robin by id, so with a stride that is a multiple of 8 every
+  // instance keeps all its workgroups -- the ones that hand slots to each other -- on
+  // one XCD (i mod 8). Padding ids run no instructions; padding is used only when the
+  // padded grid still fits a conservative residency estimate.
+  int stride = k;
+  const int padded = (k + 7) / 8 * 8;
+  const int est_resident = hp.cfg.num_cus * std::max(1, 1024 / hp.cfg.nthreads);
+  if (padded != k && int64_t(nW) * padded <= est_resident) stride = padded;
+  hp.wg_stride = stride;
   for (int w = 0; w < nW; ++w) {
     const BaseWG& W = hp.wgs[w];
     per_rank[W.rank] += k;
-    for (int i = 0; i < k; ++i) {
+    for (int i = 0; i < stride; ++i) {
+      if (i >= k) {
+        DevWG E{W.rank, int(hp.dins.size()), 0, int(hp.dwg.size())};
+        hp.dwg.push_back(E);
+        continue;
+      }
       DevWG G;
       G.rank = W.rank;
       G.first = int(hp.dins.size());
@@ -902,37 +917,52 @@ int64_t plan_bytes(const HostPlan& hp, int64_t count) {
   for (size_t j = 0; j < hp.dins.size(); ++j) {
     const DevInstr& D = hp.dins[j];
     Range r = op_range(D.pad0, D.cnt, D.instance, hp.k, count, hp.C);
-    int ops = 1 + ((D.op & OPB_SRCB) ? 1 : 0) + ((D.op & OPB_DSTA) ? 1 : 0) + ((D.op & OPB_SEND) ? 1 : 0);
+    // slot reads and writes carry one flag byte per data byte under the LL protocol
+    const int slot = (hp.cfg.flags & CCL_FLAG_LL) ? 2 : 1;
+    int ops = ((D.op & OPB_RECV) ? slot : 1) + ((D.op & OPB_SRCB) ? 1 : 0) + ((D.op & OPB_DSTA) ? 1 : 0) +
+              ((D.op & OPB_SEND) ? slot : 0);
     total += int64_t(ops) * r.len * hp.esz;
   }
   return total;
 }
 
-// Byte offsets, lengths and slice counts of every lowered instruction for `count`
-// elements per rank. Slot data starts at the slot's base plus the phase of the chunk
-// named by the transfer, so that slot and local operands share their 16-byte alignment.
-void compute_geometry(const HostPlan& hp, int64_t count, std::vector<DevGeo>& out) {
+// Exec records of every lowered instruction for `count` elements per rank: byte
+// offsets, lengths and slice counts. Slot data starts at the slot's base plus the phase
+// of the chunk named by the transfer, so that slot and local operands share their
+// 16-byte alignment (LL slots hold units from the base).
+void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec>& out) {
   const int V = 16 / hp.esz;
+  const bool ll = hp.cfg.flags & CCL_FLAG_LL;
   out.resize(hp.dins.size());
   auto slot_off = [&](int x) {
     const DevXfer& X = hp.dxf[x];
+    if (ll) return int64_t(X.slot_off);
     int64_t ph = 0;
     if (X.phase_idx >= 0) ph = op_range(X.phase_idx, X.cnt, X.instance, hp.k, count, hp.C).lo % V;
     return int64_t(X.slot_off) + ph * hp.esz;
   };
   for (size_t j = 0; j < hp.dins.size(); ++j) {
     const DevInstr& D = hp.dins[j];
-    DevGeo G{};
-    G.len = op_range(D.pad0, D.cnt, D.instance, hp.k, count, hp.C).len;
-    G.nsl = G.len == 0 ? 0 : (G.len + hp.slice_elems - 1) / hp.slice_elems;
+    DevExec E{};
+    E.op = D.op | (uint32_t(D.a_buf < 0 ? 0 : D.a_buf) << 8) | (uint32_t(D.b_buf < 0 ? 0 : D.b_buf) << 12) |
+           (uint32_t(D.d_buf < 0 ? 0 : D.d_buf) << 16);
+    E.xin = D.xin;
+    E.xout = D.xout;
+    E.done_flag = D.done_flag;
+    E.wait_begin = D.wait_begin;
+    E.nwaits = D.nwaits;
+    E.len = op_range(D.pad0, D.cnt, D.instance, hp.k, count, hp.C).len;
+    const int64_t nsl = E.len == 0 ? 0 : (E.len + hp.slice_elems - 1) / hp.slice_elems;
+    if (nsl >= (int64_t(1) << kEpochShift)) fail(CCL_ERR_INVALID_ARGUMENT, "too many slices for one transfer");
+    E.nsl = int32_t(nsl);
     if (D.op & OPB_RECV)
-      G.a_off = slot_off(D.xin);
+      E.a_off = slot_off(D.xin);
     else
-      G.a_off = op_range(D.a_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
-    if (D.op & OPB_SRCB) G.b_off = op_range(D.b_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
-    if (D.op & OPB_DSTA) G.d_off = op_range(D.d_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
-    if (D.op & OPB_SEND) G.t_off = slot_off(D.xout);
-    out[j] = G;
+      E.a_off = op_range(D.a_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
+    if (D.op & OPB_SRCB) E.b_off = op_range(D.b_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
+    if (D.op & OPB_DSTA) E.d_off = op_range(D.d_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
+    if (D.op & OPB_SEND) E.t_off = slot_off(D.xout);
+    out[j] = E;
   }
 }
 

@@ -41,21 +41,28 @@ struct DevXfer {  // 32 bytes: one send -> recv transfer
   int32_t pad0, pad1, pad2;
 };
 
-// Per-instruction geometry for one element count, computed on the host when a count
-// is first used and cached on the device: byte offsets of every operand (inside the
-// rank's buffer, or inside the staging pool for slots, in-slot phase included),
-// the element length and the number of slices.
-struct DevGeo {  // 48 bytes
+// What the kernel reads for one lowered instruction at one element count: the
+// opcode, buffers, transfer and completion-flag ids, and the byte offsets of every
+// operand (inside the rank's buffer, or inside the staging pool for slots, in-slot
+// phase included), its length and slice count. Built on the host from DevInstr and
+// the count when a count is first used, cached on the device, and copied into LDS by
+// each workgroup at launch.
+struct DevExec {  // 80 bytes
+  uint32_t op;     // OPB_* bits | a_buf << 8 | b_buf << 12 | d_buf << 16
+  int32_t xin, xout, done_flag;
+  int32_t wait_begin, nwaits;
+  int32_t nsl;     // slices (simple protocol)
+  int32_t pad0;
+  int64_t len;     // elements
   int64_t a_off, b_off, d_off, t_off;
-  int64_t len;
-  int64_t nsl;
+  int64_t pad1;
 };
+static_assert(sizeof(DevExec) == 80, "DevExec layout");
 
 // Kernel arguments, passed by value.
 struct ExecArgs {
   const DevWG* wgs;
-  const DevInstr* ins;
-  const DevGeo* geo;
+  const DevExec* recs;
   const int32_t* waits;
   unsigned long long* xflags;  // per transfer: epoch << 24 | slices completed
   unsigned long long* dflags;  // per completion flag: epoch when done
@@ -66,6 +73,8 @@ struct ExecArgs {
   int64_t slice_elems;         // slice length in elements (multiple of 64)
   unsigned long long epoch;    // launch number, >= 1
   long long timeout_ticks;     // watchdog budget per wait, device wall-clock ticks
+  int32_t ll;                  // low-latency protocol: slots hold {4 data bytes, 4-byte flag} units
+  uint32_t ll_flag;            // flag value of this launch's units (never 0)
   unsigned char* base[kNumBufs][kMaxRanks];  // per-rank buffer base pointers
 };
 

@@ -46,34 +46,56 @@ int ccl_tune_coordinate_descent(const ccl_tune_space* space, const ccl_tune_poin
   int evals = 0;
   bool have_best = false;
   double best_score = -1.0, start_score = -1.0;
+  const int protos = space->protocols ? space->protocols : 1;
+  bool first = true;
   for (int v = 0; v < space->nvariants; ++v) {
-    ccl_tune_point pt;
-    pt.variant = v;
-    int idx[3];
-    for (int c = 0; c < 3; ++c) {
-      idx[c] = start ? index_of(coords[c].vals, coords[c].n, start->*(coords[c].field)) : 0;
-      pt.*(coords[c].field) = coords[c].vals[idx[c]];
-    }
-    double score = objective(&pt, user);
-    ++evals;
-    if (v == 0) start_score = score;
-    for (int c = 0; c < 3; ++c) {
-      // step this coordinate up while the objective improves
-      while (idx[c] + 1 < coords[c].n) {
-        ccl_tune_point cand = pt;
-        cand.*(coords[c].field) = coords[c].vals[idx[c] + 1];
-        double s = objective(&cand, user);
-        ++evals;
-        if (!(s > score)) break;
-        pt = cand;
-        score = s;
-        idx[c] += 1;
+    for (int proto = 0; proto < 2; ++proto) {
+      if (!(protos & (1 << proto))) continue;
+      ccl_tune_point pt{};
+      pt.variant = v;
+      pt.protocol = proto;
+      int idx[3];
+      for (int c = 0; c < 3; ++c) {
+        idx[c] = start ? index_of(coords[c].vals, coords[c].n, start->*(coords[c].field)) : 0;
+        pt.*(coords[c].field) = coords[c].vals[idx[c]];
       }
-    }
-    if (score >= 0 && (!have_best || score > best_score)) {
-      have_best = true;
-      best_score = score;
-      *best = pt;
+      double score = objective(&pt, user);
+      ++evals;
+      if (first) start_score = score;
+      first = false;
+      for (int c = 0; c < 3; ++c) {
+        // step this coordinate up while the objective improves; one look-ahead step
+        // past a candidate that does not improve (resource counts that leave part of
+        // the machine idle can dip between two better values)
+        int i = idx[c];
+        while (i + 1 < coords[c].n) {
+          ccl_tune_point cand = pt;
+          cand.*(coords[c].field) = coords[c].vals[i + 1];
+          double s = objective(&cand, user);
+          ++evals;
+          if (s > score) {
+            pt = cand;
+            score = s;
+            i += 1;
+            continue;
+          }
+          if (i + 2 >= coords[c].n) break;
+          ccl_tune_point next = pt;
+          next.*(coords[c].field) = coords[c].vals[i + 2];
+          double s2 = objective(&next, user);
+          ++evals;
+          if (!(s2 > score)) break;
+          pt = next;
+          score = s2;
+          i += 2;
+        }
+        idx[c] = i;
+      }
+      if (score >= 0 && (!have_best || score > best_score)) {
+        have_best = true;
+        best_score = score;
+        *best = pt;
+      }
     }
   }
   report->evaluations = evals;
@@ -99,7 +121,8 @@ static double device_objective(const ccl_tune_point* pt, void* user) {
   ccl_plan_config cfg = c->base;
   cfg.nthreads = pt->nthreads;
   cfg.slice_bytes = pt->slice_bytes;
-  cfg.flags &= ~(CCL_FLAG_HOST_ONLY | CCL_FLAG_TRACE);
+  cfg.flags &= ~(CCL_FLAG_HOST_ONLY | CCL_FLAG_TRACE | CCL_FLAG_LL);
+  if (pt->protocol == 1) cfg.flags |= CCL_FLAG_LL;
   ccl_plan* plan = nullptr;
   int rc = ccl_plan_create(prog, prog->nranks, prog->in_chunks, pt->parallel_factor, &cfg, &plan);
   if (rc) return -1.0;  // infeasible (e.g. not enough co-resident workgroups)

@@ -23,6 +23,7 @@ class PlanConfig:
     max_count: int = 1 << 20
     nthreads: int = 512
     slice_bytes: int = 256 * 1024
+    protocol: str = "simple"  # "simple" (slice flags) or "ll" (flag in every 8-byte unit)
     scheduler: str = "hpds"
     wg_alloc: str = "state"
     trace: bool = False
@@ -39,6 +40,10 @@ class PlanConfig:
             flags |= capi.CCL_FLAG_HOST_ONLY
         if self.no_fusion:
             flags |= capi.CCL_FLAG_NO_FUSION
+        if self.protocol == "ll":
+            flags |= capi.CCL_FLAG_LL
+        elif self.protocol != "simple":
+            raise ValueError(f"unknown protocol {self.protocol!r}")
         return capi.ccl_plan_config(DTYPES[self.dtype], capi.CCL_REDOP_SUM, int(self.max_count), int(self.nthreads),
                                     int(self.slice_bytes), SCHEDULERS[self.scheduler], WG_ALLOC[self.wg_alloc],
                                     flags, int(self.num_cus), int(self.timeout_us))
@@ -74,8 +79,14 @@ class Plan:
     def status(self) -> None:
         capi.ccl_plan_status(self.handle)
 
-    def trace(self):
-        return capi.ccl_plan_read_trace(self.handle, self.info()["num_workgroups"])
+    def trace(self, instructions: bool = False):
+        """Per-workgroup trace of the last launch (plans built with trace=True), one
+        record per launch-grid workgroup (idle padding ids record zeros); with
+        ``instructions`` also the per-instruction {start, data ready, end} records."""
+        i = self.info()
+        if instructions:
+            return capi.ccl_plan_read_trace(self.handle, i["grid_workgroups"], i["num_instructions"])
+        return capi.ccl_plan_read_trace(self.handle, i["grid_workgroups"])
 
     def output_len(self, count: int) -> int:
         return (self.program.out_chunks * count) // self.program.in_chunks

@@ -17,6 +17,9 @@
  * in the same HBM, a "send" writes the receiving rank's staging slot and then
  * release-stores a flag, a "recv" acquire-polls that flag and reads the slot.
  *
+ * The stream of a plan's last launch must stay valid until the next execute, status or
+ * destroy call on that plan.
+ *
  * Conventions for every entry point:
  *   - Status codes: CCL_OK (0) on success, a negative CCL_ERR_* otherwise. No C++
  *     exception crosses this boundary. ccl_last_error_detail() gives a
@@ -118,6 +121,11 @@ typedef struct {
 #define CCL_FLAG_HOST_ONLY 0x2u  /* compile and lower on the host only; no HIP call, no execute */
 #define CCL_FLAG_NO_FUSION 0x4u  /* keep primitive send/recv/copy/reduce instructions */
 #define CCL_FLAG_NO_VERIFY 0x8u  /* skip the symbolic postcondition check at create */
+#define CCL_FLAG_LL 0x10u        /* low-latency protocol: every 4 data bytes in a staging slot travel with a
+                                    4-byte flag in one 8-byte store; receivers poll the data itself, there
+                                    are no per-slice flags (twice the slot traffic, far fewer round trips;
+                                    the protocol choice of the MSCCLang report, section 3.1 runtime, and the
+                                    AutoCCL report's Protocol parameter) */
 
 typedef struct {
   int32_t dtype;       /* CCL_F32, CCL_BF16 or CCL_I32 */
@@ -170,7 +178,7 @@ int ccl_plan_destroy(ccl_plan* plan);
 
 typedef struct {
   int32_t nranks, nchunks, parallel_factor, dtype;
-  int32_t num_workgroups;     /* total, all ranks and instances */
+  int32_t num_workgroups;     /* workgroups that run instructions, all ranks and instances */
   int32_t max_wg_per_rank;
   int32_t num_instructions;   /* lowered, all instances */
   int32_t num_subpipelines;   /* of the base schedule */
@@ -180,7 +188,7 @@ typedef struct {
   int32_t count_granule;      /* ccl_execute's count must be a multiple of this */
   int32_t nthreads, slice_bytes;
   int32_t max_resident_wgs;   /* co-residency bound the plan was checked against */
-  int32_t reserved;
+  int32_t grid_workgroups;    /* launch grid: num_workgroups plus idle ids that keep every instance on one XCD */
   int64_t staging_bytes, scratch_bytes, flag_bytes, table_bytes;
   double compile_ms[6];       /* verify, DAG, fusion, schedule, workgroup allocation, lowering */
   int32_t opcode_hist[16];    /* lowered instructions by opcode bits (see ccl_instr_info.opcode) */
@@ -235,7 +243,10 @@ int ccl_plan_status(ccl_plan* plan);
 /* Per-workgroup trace of the last launch of a CCL_FLAG_TRACE plan: for each
  * workgroup four uint64 values {first instruction start, last instruction end,
  * ticks spent waiting on flags, instructions run}, ticks of the 100 MHz device
- * wall clock. `bytes` must hold num_workgroups * 32. */
+ * wall clock. `bytes` must hold num_workgroups * 32; if it holds
+ * (num_workgroups + num_instructions) * 32, four more values follow for every
+ * lowered instruction in ccl_plan_export order {start, first slice's data ready,
+ * end, 0}. */
 int ccl_plan_read_trace(ccl_plan* plan, void* host, size_t bytes);
 
 /* ---- tuner (AutoCCL report, "Methods" 1-2: resource parameters tuned by
@@ -245,14 +256,17 @@ typedef struct {
   int32_t parallel_factor; /* channels / instances (nc) */
   int32_t nthreads;        /* threads per workgroup (nt) */
   int32_t slice_bytes;     /* chunk size of one pipelined step (c) */
+  int32_t protocol;        /* 0 = slice flags, 1 = low-latency units (CCL_FLAG_LL) */
+  int32_t reserved;
 } ccl_tune_point;
 
 typedef struct {
   const int32_t* factors;  int32_t nfactors;  /* ascending candidate values */
   const int32_t* nthreads; int32_t nnthreads;
   const int32_t* slices;   int32_t nslices;
-  int32_t nvariants;       /* subspaces 0..nvariants-1 */
+  int32_t nvariants;       /* algorithm subspaces 0..nvariants-1 */
   int32_t warmup, iters;   /* per device evaluation */
+  int32_t protocols;       /* protocol subspaces to search: bit 0 = slice flags, bit 1 = LL (0 = bit 0) */
 } ccl_tune_space;
 
 typedef struct {
@@ -266,11 +280,12 @@ typedef struct {
 typedef double (*ccl_tune_objective)(const ccl_tune_point* point, void* user);
 
 /*
- * Subspace coordinate descent: for every variant, starting from the smallest
- * candidate of each coordinate (or from `start` where it lies in the space),
- * optimize parallel_factor, then nthreads, then slice_bytes; each coordinate is
- * stepped up through its ascending candidates while the objective improves. The
- * best point over all variants is returned. Pure host logic.
+ * Subspace coordinate descent: for every (variant, protocol) subspace, starting
+ * from the smallest candidate of each coordinate (or from `start` where it lies in
+ * the space), optimize parallel_factor, then nthreads, then slice_bytes; each
+ * coordinate is stepped up through its ascending candidates while the objective
+ * improves, looking one candidate past a step that does not improve before
+ * stopping. The best point over all subspaces is returned. Pure host logic.
  */
 int ccl_tune_coordinate_descent(const ccl_tune_space* space, const ccl_tune_point* start,
                                 ccl_tune_objective objective, void* user, ccl_tune_point* best,

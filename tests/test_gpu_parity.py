@@ -258,3 +258,51 @@ def test_int32_reduction_wraps():
     ys, _ = _run(programs.ring_allreduce(P), xs, "i32", k=1)
     want = O1.allreduce(xs, "i32").exact
     assert_all_equal(ys, want)
+
+
+# ------------------------------------------------------------------ low-latency protocol
+
+@pytest.mark.parametrize("P,N,k", [(8, 8192, 1), (8, 786432, 24), (8, 1001, 3), (4, 262144, 1), (2, 5, 1)])
+def test_ll_ring_allreduce(P, N, k):
+    """Flag-in-data units instead of slice flags: same bits as the chain order."""
+    case(f"LL ring AR P={P} N={N} k={k}")
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 3)
+    ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=k, protocol="ll", nthreads=256)
+    assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
+
+
+@pytest.mark.parametrize("N", [(1 << 16) + 16, 8 * 1001 + 8])
+def test_ll_hierarchical_bf16_odd_lengths(N):
+    """bf16 pairs share a 4-byte unit: odd chunk lengths leave a half-filled last unit."""
+    G, L = 2, 8
+    case(f"LL hier AR bf16 N={N}")
+    xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 5)
+    ys, _ = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, protocol="ll")
+    assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
+
+
+def test_ll_alltoall_and_alltonext():
+    G, L = 4, 8
+    P, b = G * L, 1037
+    case("LL two-phase alltoall + alltonext")
+    xs = W.make_inputs("uniform_i32", P * b, P, W.CFG_A2A_32R_INT32, size_bytes=P * b * 4 + 9)
+    ys, _ = _run(programs.two_phase_alltoall(G, L), xs, "i32", k=1, protocol="ll", nthreads=256)
+    want = O1.alltoall(xs)
+    for r in range(P):
+        assert np.array_equal(ys[r], want[r]), r
+    G, L, N = 3, 8, 8 * 777
+    xs = W.make_inputs("normal_f32", N, G * L, W.CFG_A2NEXT_AGRS_24R, size_bytes=N * 4 + 9)
+    prior = [np.full(N, -3.0, np.float32) for _ in range(G * L)]
+    ys, _ = _run(programs.alltonext(G, L, split=True), xs, "f32", k=2, prior=prior, protocol="ll")
+    want = O1.alltonext(xs, prior)
+    for r in range(G * L):
+        assert np.array_equal(ys[r], want[r]), r
+
+
+def test_ll_repeated_launches():
+    """LL flags are the launch's epoch: repeated launches over the same slots stay exact."""
+    P, N = 8, 50_000
+    case("LL ring AR repeated")
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 11)
+    ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=4, protocol="ll", repeat=5)
+    assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
