@@ -1,0 +1,319 @@
+"""Host compiler: fusion, byte accounting, scheduling, workgroup allocation and the
+lowered-plan checker, on host-only plans (no GPU).
+
+The programs themselves are checked against the oracle's symbolic postcondition and
+its sequential interpreter, which share no code with the compiler."""
+
+import collections
+
+import numpy as np
+import pytest
+
+import workloads as W
+from chunk_schedule_execution_amd import Plan, PlanConfig, capi, programs
+from oracle import program as OP
+from oracle import schedule_order as O2
+
+SEND, RRS, RRCS, RCS, RECV, RRC, CS, RS = 8, 11, 15, 13, 5, 7, 12, 9
+
+
+def host_plan(prog, k=1, **cfg):
+    cfg.setdefault("max_count", 1 << 20)
+    return Plan(prog, k, PlanConfig(host_only=True, **cfg))
+
+
+def hist(plan):
+    return collections.Counter(e.opcode for e in plan.export())
+
+
+# ---------------------------------------------------------------- fusion
+
+@pytest.mark.parametrize("P", [2, 3, 4, 8])
+def test_ring_allreduce_fuses_to_the_rrcs_family(P):
+    """Every chunk chain becomes send, (P-2) x recv-reduce-send, recv-reduce-copy-send,
+    (P-2) x recv-copy-send, recv: 2P-1 instructions (MSCCLang report, section 3.1)."""
+    plan = host_plan(programs.ring_allreduce(P))
+    h = hist(plan)
+    want = collections.Counter({SEND: P, RRS: P * (P - 2), RRCS: P, RCS: P * (P - 2), RECV: P})
+    assert h == +want
+    per_rank = collections.Counter(e.rank for e in plan.export())
+    assert all(v == 2 * P - 1 for v in per_rank.values())
+    info = plan.info()
+    assert info["scratch_bytes"] == 0  # every scratch partial was forwarded in registers
+
+
+def test_no_fusion_keeps_primitives_and_costs_bytes():
+    P, N = 4, 4096
+    fused = host_plan(programs.ring_allreduce(P))
+    prim = host_plan(programs.ring_allreduce(P), no_fusion=True)
+    assert prim.info()["num_instructions"] > fused.info()["num_instructions"]
+    assert prim.bytes(N) > fused.bytes(N)
+    prim.check(seed=3, nsims=3)
+
+
+def test_two_phase_alltoall_keeps_batched_transfers():
+    G, L = 4, 8
+    plan = host_plan(programs.two_phase_alltoall(G, L))
+    big = [e for e in plan.export() if e.count == L and (e.opcode & capi.CCL_I_SEND)]
+    assert len(big) == G * L * (G - 1)  # one batched send per (rank, remote group)
+
+
+# ---------------------------------------------------------------- byte accounting
+
+@pytest.mark.parametrize("P", [2, 4, 8, 16])
+@pytest.mark.parametrize("k", [1, 3])
+def test_ring_bytes_closed_forms(P, k):
+    """Ring AllReduce moves S(6P-4) bytes over all ranks, ring ReduceScatter and
+    AllGather S(3P-1) (S = the larger per-rank buffer); instances do not change it."""
+    N = P * 1000
+    S = N * 4
+    assert host_plan(programs.ring_allreduce(P), k).bytes(N) == S * (6 * P - 4)
+    assert host_plan(programs.ring_reducescatter(P), k).bytes(N) == S * (3 * P - 1)
+    assert host_plan(programs.ring_allgather(P), k).bytes(N // P) == S * (3 * P - 1)
+
+
+def test_direct_alltoall_and_alltonext_bytes():
+    P, N = 8, 8 * 64
+    S = N * 4
+    assert host_plan(programs.direct_alltoall(P)).bytes(N) == S * (4 * P - 2)
+    G, L = 3, 8
+    P = G * L
+    N = L * 100
+    S = N * 4
+    assert host_plan(programs.alltonext(G, L, split=False)).bytes(N) == 4 * S * (P - 1)
+    assert host_plan(programs.alltonext(G, L, split=True)).bytes(N) == 4 * S * (P - G) + (G - 1) * S * (8 * L - 4) // L
+
+
+def test_hierarchical_bytes_and_phase_fusion():
+    """Three phases at k=1: intra-group reduce-scatter G*S(3L-1), cross-group ring
+    AllReduce S(7G-6) (its reductions land in the output, so they stay written), intra-group
+    all-gather G*S(3L-2): S(6P+4G-6) in all. With instances the ops are per chunk and the
+    phase boundaries fuse (a receive-reduce feeds the next phase's send)."""
+    for G, L in ((2, 8), (3, 4), (4, 2)):
+        P, N = G * L, G * L * 512
+        S = N * 2
+        assert host_plan(programs.hierarchical_allreduce(G, L), dtype="bf16").bytes(N) == S * (6 * P + 4 * G - 6)
+    G, L = 2, 8
+    P, N = G * L, 16 * 512
+    S = N * 2
+    p1 = host_plan(programs.hierarchical_allreduce(G, L), dtype="bf16")
+    p2 = host_plan(programs.hierarchical_allreduce(G, L), k=2, dtype="bf16")
+    assert p2.bytes(N) < p1.bytes(N)
+
+
+def test_ll_protocol_doubles_slot_traffic():
+    P, N = 8, 8000
+    S = N * 4
+    simple = host_plan(programs.ring_allreduce(P)).bytes(N)
+    ll = host_plan(programs.ring_allreduce(P), protocol="ll").bytes(N)
+    # every slot write and read carries 4 flag bytes per 4 data bytes: 4 slot ops per
+    # chain hop (send+recv of each of the 2(P-1) transfers per chunk)
+    assert ll - simple == 2 * (2 * (P - 1)) * S // P * P
+
+
+def test_count_granule():
+    assert host_plan(programs.ring_allreduce(8)).info()["count_granule"] == 1
+    assert host_plan(programs.two_phase_alltoall(4, 8)).info()["count_granule"] == 32
+    assert host_plan(programs.reducescatter_2d(3, 8)).info()["count_granule"] == 24
+
+
+# ---------------------------------------------------------------- scheduling
+
+def _subpipes_by_instr(plan):
+    return [e.subpipe for e in plan.export() if e.instance == 0]
+
+
+@pytest.mark.parametrize("name,args", [("ring_allreduce", (8,)), ("hierarchical_allreduce", (2, 4)),
+                                       ("two_phase_alltoall", (2, 4)), ("alltonext", (3, 4)),
+                                       ("allgather_2d", (3, 4)), ("reducescatter_2d", (3, 4))])
+@pytest.mark.parametrize("sched", ["hpds", "rr", "program"])
+def test_every_transfer_crosses_to_a_later_subpipeline(name, args, sched):
+    plan = host_plan(programs.REGISTRY[name](*args), scheduler=sched)
+    ex = [e for e in plan.export() if e.instance == 0]
+    assert all(e.subpipe >= 0 for e in ex)
+    sender = {e.xout: e for e in ex if e.xout >= 0}
+    for e in ex:
+        if e.xin >= 0:
+            assert sender[e.xin].subpipe < e.subpipe
+    if sched == "program":
+        assert plan.info()["num_subpipelines"] == len(ex)
+
+
+@pytest.mark.parametrize("name,args", [("ring_allreduce", (8,)), ("two_phase_alltoall", (2, 4)),
+                                       ("alltonext", (3, 8)), ("reducescatter_2d", (3, 4))])
+def test_hpds_subpipelines_have_no_link_conflict(name, args):
+    """ReSCCL report, section 2.2: a sub-pipeline holds tasks free of data and link
+    conflicts; the link of a task is the connection its send uses."""
+    plan = host_plan(programs.REGISTRY[name](*args), scheduler="hpds")
+    seen = set()
+    for e in plan.export():
+        if e.instance != 0 or e.send_peer < 0:
+            continue
+        key = (e.subpipe, e.rank, e.send_peer, e.channel)
+        assert key not in seen
+        seen.add(key)
+
+
+@pytest.mark.parametrize("P", [3, 4, 8, 16])
+def test_hpds_meets_the_critical_path_on_rings(P):
+    """A chunk's chain is 2P-1 dependent instructions, so no schedule has fewer than
+    2P-1 sub-pipelines; HPDS reaches that bound, and every workgroup runs the ring
+    step by step (chain of rank r at step t is (r - t))."""
+    plan = host_plan(programs.ring_allreduce(P), scheduler="hpds")
+    assert plan.info()["num_subpipelines"] == 2 * P - 1
+    prog_order = host_plan(programs.ring_allreduce(P), scheduler="program")
+    assert prog_order.info()["num_subpipelines"] == P * (2 * P - 1)
+
+
+def test_state_allocation_uses_fewer_workgroups():
+    """ReSCCL report, section 2.2 (state-based allocation): connections of one rank
+    that are never active in the same sub-pipeline share a workgroup."""
+    G, L = 3, 8
+    for prog in (programs.alltonext(G, L, split=True), programs.two_phase_alltoall(4, 8),
+                 programs.reducescatter_2d(G, L), programs.allgather_2d(G, L)):
+        conn = host_plan(prog, scheduler="hpds", wg_alloc="connection").info()["num_workgroups"]
+        state = host_plan(prog, scheduler="hpds", wg_alloc="state").info()["num_workgroups"]
+        assert state <= conn, prog.name
+    conn = host_plan(programs.alltonext(G, L), wg_alloc="connection").info()["num_workgroups"]
+    state = host_plan(programs.alltonext(G, L), wg_alloc="state").info()["num_workgroups"]
+    assert state < conn
+
+
+def test_workgroup_order_follows_subpipelines():
+    plan = host_plan(programs.allgather_2d(3, 4), scheduler="hpds", wg_alloc="state")
+    by_wg = collections.defaultdict(list)
+    for e in plan.export():
+        by_wg[e.wg].append(e.subpipe)
+    for sps in by_wg.values():
+        assert sps == sorted(sps)
+
+
+def test_instances_sit_on_one_xcd():
+    """Instance i of every rank gets a workgroup id congruent to i mod 8 (workgroups
+    are dispatched to the eight XCDs round robin)."""
+    for k in (1, 3, 8, 24):
+        plan = host_plan(programs.ring_allreduce(8), k=k)
+        for e in plan.export():
+            assert e.wg % 8 == e.instance % 8
+
+
+# ---------------------------------------------------------------- lowered-plan checker
+
+@pytest.mark.parametrize("name,args", [("ring_allreduce", (4,)), ("ring_allreduce", (5,)),
+                                       ("ring_reducescatter", (4,)), ("ring_allgather", (4,)),
+                                       ("hierarchical_allreduce", (2, 4)), ("direct_alltoall", (4,)),
+                                       ("two_phase_alltoall", (2, 4)), ("alltonext", (2, 4)),
+                                       ("allgather_2d", (2, 4)), ("reducescatter_2d", (2, 4))])
+@pytest.mark.parametrize("knobs", [dict(k=1, scheduler="hpds", wg_alloc="state"),
+                                   dict(k=2, scheduler="rr", wg_alloc="connection"),
+                                   dict(k=3, scheduler="program", wg_alloc="state", protocol="ll")])
+def test_lowered_plans_pass_random_interleavings(name, args, knobs):
+    knobs = dict(knobs)
+    k = knobs.pop("k")
+    plan = host_plan(programs.REGISTRY[name](*args), k=k, **knobs)
+    plan.check(seed=11, nsims=3)
+
+
+def test_hierarchical_stages_pass_the_checker():
+    for prog in (programs.hier_stage_reducescatter_intra(2, 4), programs.hier_stage_allreduce_inter(2, 4),
+                 programs.hier_stage_allgather_intra(2, 4)):
+        host_plan(prog, k=2).check(seed=5, nsims=2)
+
+
+# ---------------------------------------------------------------- programs vs the oracle
+
+ALL_PROGRAMS = [
+    ("allreduce", programs.ring_allreduce(5), None),
+    ("reducescatter", programs.ring_reducescatter(4), None),
+    ("allgather", programs.ring_allgather(4), None),
+    ("allreduce", programs.hierarchical_allreduce(3, 4), None),
+    ("alltoall", programs.direct_alltoall(5), None),
+    ("alltoall", programs.two_phase_alltoall(3, 4), None),
+    ("alltonext", programs.alltonext(3, 4, split=True), None),
+    ("alltonext", programs.alltonext(3, 4, split=False), None),
+    ("allgather", programs.allgather_2d(3, 4), None),
+    ("reducescatter", programs.reducescatter_2d(3, 4), None),
+    ("reducescatter_intra", programs.hier_stage_reducescatter_intra(3, 4), 4),
+    ("allreduce_inter", programs.hier_stage_allreduce_inter(3, 4), 4),
+    ("allgather_intra", programs.hier_stage_allgather_intra(3, 4), 4),
+]
+
+
+@pytest.mark.parametrize("coll,prog,L", ALL_PROGRAMS, ids=[p.name for _, p, _ in ALL_PROGRAMS])
+def test_library_programs_meet_the_oracles_postcondition(coll, prog, L):
+    assert OP.check_postcondition(prog.as_tuples(), coll, prog.nranks, prog.in_chunks, prog.scratch_chunks, L)
+
+
+@pytest.mark.parametrize("P", [2, 3, 4, 8])
+def test_ring_program_follows_the_documented_chain(P):
+    """The package's ring program, run by the oracle's sequential interpreter, gives
+    the same bits as the oracle's chain-order fold."""
+    N = P * 37 + 3
+    xs = W.make_inputs("normal_f32", N, P, 77, size_bytes=N)
+    prog = programs.ring_allreduce(P)
+    ys = OP.run_program(prog.as_tuples(), xs, "f32", prog.in_chunks, prog.out_chunks, prog.scratch_chunks)
+    want = O2.ring_allreduce(xs, P, "f32")
+    for r in range(P):
+        assert np.array_equal(ys[r], want[r])
+
+
+def test_hierarchical_and_2d_programs_follow_the_documented_chains():
+    G, L = 3, 4
+    P, N = G * L, 12 * 41
+    xb = W.make_inputs("normal_bf16", N, P, 78, size_bytes=N)
+    h = programs.hierarchical_allreduce(G, L)
+    ys = OP.run_program(h.as_tuples(), xb, "bf16", h.in_chunks, h.out_chunks, h.scratch_chunks)
+    want = O2.hierarchical_allreduce(xb, G, L, "bf16")
+    assert all(np.array_equal(ys[r], want[r]) for r in range(P))
+    xs = W.make_inputs("normal_f32", N, P, 79, size_bytes=N)
+    rs = programs.reducescatter_2d(G, L)
+    ys = OP.run_program(rs.as_tuples(), xs, "f32", rs.in_chunks, rs.out_chunks, rs.scratch_chunks)
+    want = O2.reducescatter_2d(xs, G, L, "f32")
+    assert all(np.array_equal(ys[r], want[r]) for r in range(P))
+
+
+# ---------------------------------------------------------------- tuner (host logic)
+
+def _space(factors, threads, slices, nvariants=1, protocols=1):
+    arrs = [(C * len(v))(*v) for C, v in ((capi.C.c_int32, factors), (capi.C.c_int32, threads),
+                                          (capi.C.c_int32, slices))]
+    sp = capi.ccl_tune_space(capi.C.cast(arrs[0], capi.C.POINTER(capi.C.c_int32)), len(factors),
+                             capi.C.cast(arrs[1], capi.C.POINTER(capi.C.c_int32)), len(threads),
+                             capi.C.cast(arrs[2], capi.C.POINTER(capi.C.c_int32)), len(slices),
+                             nvariants, 0, 1, protocols)
+    sp._keep = arrs
+    return sp
+
+
+def test_coordinate_descent_finds_the_peak_of_a_unimodal_objective():
+    """AutoCCL report, methods 1-2: each resource parameter is unimodal, so raising one
+    coordinate until the objective stops improving reaches the peak."""
+    F, T, S = [1, 2, 4, 8, 16, 24, 32], [64, 128, 256, 512, 1024], [4096 << i for i in range(8)]
+    peak = (16, 256, 4096 << 5)
+
+    def f(p):
+        return 100 - abs(np.log2(p.parallel_factor) - 4) - abs(np.log2(p.nthreads) - 8) - \
+            abs(np.log2(p.slice_bytes) - np.log2(peak[2]))
+    best, rep = capi.ccl_tune_coordinate_descent(_space(F, T, S), f)
+    assert (best.parallel_factor, best.nthreads, best.slice_bytes) == peak
+    assert rep.best_score == pytest.approx(100)
+    assert rep.evaluations <= 1 + len(F) + len(T) + len(S) + 3
+
+
+def test_coordinate_descent_looks_past_one_dip_and_picks_the_subspace():
+    F = [1, 2, 4, 8, 16, 24, 32]
+
+    def f(p):
+        # factor 24 is worse than 16 and 32 (idle compute units); protocol 1 is better
+        base = {1: 1, 2: 2, 4: 4, 8: 8, 16: 16, 24: 12, 32: 20}[p.parallel_factor]
+        return base + (5 if p.protocol == 1 else 0) + (3 if p.variant == 1 else 0)
+    best, rep = capi.ccl_tune_coordinate_descent(_space(F, [256], [65536], nvariants=2, protocols=3), f)
+    assert best.parallel_factor == 32 and best.protocol == 1 and best.variant == 1
+    assert rep.best_score == 28
+
+
+def test_coordinate_descent_stops_on_infeasible_points():
+    def f(p):
+        return -1.0 if p.parallel_factor > 4 else float(p.parallel_factor)
+    best, rep = capi.ccl_tune_coordinate_descent(_space([1, 2, 4, 8, 16], [256], [4096]), f)
+    assert best.parallel_factor == 4
