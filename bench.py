@@ -41,6 +41,8 @@ def parse():
                     help="k,nthreads,slice_bytes,protocol(0 simple, 1 LL): skip tuning (profiling runs)")
     ap.add_argument("--no-extras", action="store_true", help="headline only (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="also run the plain copy kernel this many times on 256 MiB (counter calibration)")
     return ap.parse_args()
 
 
@@ -217,6 +219,16 @@ def main():
         torch.cuda.synchronize()
         tc = e0.elapsed_time(e1) * 1e-3 / 10
         out["copy_probe_GBs"] = round(2 * nb / tc / 1e9, 1)
+
+    if args.copy_probe:
+        nb = 1 << 28
+        a = torch.zeros(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty(nb, dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+        for _ in range(args.copy_probe):
+            capi.ccl_copy_probe(b.data_ptr(), a.data_ptr(), nb, 1024, 512, stream.cuda_stream)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes_per_launch"] = 2 * nb
 
     # ---- CPU baseline: the oracle on the host, same workload, bounded time --------
     out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
