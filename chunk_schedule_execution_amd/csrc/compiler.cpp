@@ -871,6 +871,7 @@ void lower(HostPlan& hp) {
         D.done_flag = I.done_flag >= 0 ? I.done_flag * k + i : -1;
         D.instance = i;
         D.pad0 = len_idx_of(hp, t);
+        D.peer_wg = I.xout >= 0 ? hp.ins[hp.xf[I.xout].receiver].wg * stride + i : -1;
         hp.dins.push_back(D);
         hp.dins_base.push_back(t);
       }

@@ -30,7 +30,8 @@ struct DevInstr {  // 64 bytes, read wave-uniformly
   int32_t wait_begin, nwaits;  // completion flags to await, in DevExec::waits
   int32_t done_flag;           // completion flag to set (-1 = none)
   int32_t instance;            // instance sub-chunk index (0..k-1)
-  int32_t pad0, pad1;
+  int32_t pad0;                // chunk index that fixes the instruction's element range
+  int32_t peer_wg;             // OPB_SEND: launch-grid workgroup that receives (-1 = none)
 };
 
 struct DevXfer {  // 32 bytes: one send -> recv transfer
@@ -75,6 +76,10 @@ struct ExecArgs {
   long long timeout_ticks;     // watchdog budget per wait, device wall-clock ticks
   int32_t ll;                  // low-latency protocol: slots hold {4 data bytes, 4-byte flag} units
   uint32_t ll_flag;            // flag value of this launch's units (never 0)
+  // XCD-local launches: workgroup i must run on XCD i mod nxcd (the device's
+  // round-robin dispatch, checked at plan setup); each workgroup re-checks its own
+  // placement before touching any slot.
+  int32_t nxcd;
   unsigned char* base[kNumBufs][kMaxRanks];  // per-rank buffer base pointers
 };
 

@@ -140,7 +140,7 @@ __device__ __forceinline__ long long wait_slot_flag(unsigned long long* p, unsig
 // of the first pass is loaded before that wait so its latency hides behind it.
 // Returns the ticks waited, or -1 if the wait gave up (the whole workgroup returns
 // -1 together).
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND>
+template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL>
 __device__ __forceinline__ long long run_slice(const unsigned char* pa, const unsigned char* pb,
                                                          unsigned char* pd, unsigned char* pt, int n, int tid,
                                                          int nthr, unsigned long long* wflag,
@@ -152,7 +152,7 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
   constexpr int esz = Ar::esz;
   constexpr int V = 16 / esz;
   constexpr int CA = RECV ? kCpolSc1 : kCpolNone;  // first operand: slot or local buffer
-  constexpr int CT = kCpolSc1;                      // outgoing slot
+  constexpr int CT = XL ? kCpolNone : kCpolSc1;     // outgoing slot: XCD-local L2, or agent-coherent
   const int bytes = n * esz;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(pa, bytes);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(SRCB ? pb : pa, bytes);
@@ -237,18 +237,18 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
 
 // bf16 widening adds need more registers: its slice code stays an out-of-line call so
 // the register allocator sees one variant at a time (no spills); fp32 / int32 inline.
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND>
+template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL>
 __device__ __attribute__((noinline)) long long run_slice_call(const unsigned char* pa, const unsigned char* pb,
                                                               unsigned char* pd, unsigned char* pt, int n, int tid,
                                                               int nthr, unsigned long long* wflag,
                                                               unsigned long long wtarget, unsigned int* err,
                                                               unsigned long long* abort_word, unsigned long long epoch,
                                                               long long timeout_ticks, int instr) {
-  return run_slice<DT, RECV, SRCB, DSTA, SEND>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, err, abort_word, epoch,
-                                               timeout_ticks, instr);
+  return run_slice<DT, RECV, SRCB, DSTA, SEND, XL>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, err, abort_word,
+                                                   epoch, timeout_ticks, instr);
 }
 
-template <int DT>
+template <int DT, bool XL>
 __device__ __forceinline__ long long dispatch_slice(uint32_t op, const unsigned char* pa, const unsigned char* pb,
                                                     unsigned char* pd, unsigned char* pt, int n, int tid, int nthr,
                                                     unsigned long long* wflag, unsigned long long wtarget,
@@ -256,10 +256,10 @@ __device__ __forceinline__ long long dispatch_slice(uint32_t op, const unsigned 
 #define CCL_CASE(R, B, D, T)                                                                                     \
   case ((R) ? OPB_RECV : 0u) | ((B) ? OPB_SRCB : 0u) | ((D) ? OPB_DSTA : 0u) | ((T) ? OPB_SEND : 0u):            \
     return (DT == CCL_BF16)                                                                                      \
-               ? run_slice_call<DT, R, B, D, T>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err, A.abort_word,  \
-                                                A.epoch, A.timeout_ticks, instr)                                   \
-               : run_slice<DT, R, B, D, T>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err, A.abort_word,       \
-                                           A.epoch, A.timeout_ticks, instr);
+               ? run_slice_call<DT, R, B, D, T, XL>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err,          \
+                                                    A.abort_word, A.epoch, A.timeout_ticks, instr)                 \
+               : run_slice<DT, R, B, D, T, XL>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err, A.abort_word,   \
+                                               A.epoch, A.timeout_ticks, instr);
   switch (op & 15u) {
     CCL_CASE(false, false, true, false)
     CCL_CASE(false, false, false, true)
@@ -353,10 +353,11 @@ __device__ __forceinline__ bool ll_load_unit(__amdgpu_buffer_rsrc_t r, int off, 
   return true;
 }
 
+template <int CP>
 __device__ __forceinline__ void ll_store_quad(__amdgpu_buffer_rsrc_t r, int off, v4u v, uint32_t flag) {
   v4u a = {v.x, flag, v.y, flag}, b = {v.z, flag, v.w, flag};
-  st16<kCpolSc1>(r, off, a);
-  st16<kCpolSc1>(r, off + 16, b);
+  st16<CP>(r, off, a);
+  st16<CP>(r, off + 16, b);
 }
 
 // One data word (4 bytes of the transfer) of a local operand starting at byte `o`:
@@ -387,12 +388,13 @@ __device__ __forceinline__ uint32_t add_word(uint32_t a, uint32_t b) {
 
 // The wait context travels as separate scalars: a struct argument would go through
 // the stack.
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND>
+template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL>
 __device__ __forceinline__ bool run_ll(const unsigned char* pa, const unsigned char* pb, unsigned char* pd,
                                                  unsigned char* pt, int n, int tid, int nthr, uint32_t flag,
                                                  unsigned int* err, unsigned long long* abort_word,
                                                  unsigned long long epoch, long long timeout_ticks, int instr) {
   const WaitCtx w{err, abort_word, epoch, timeout_ticks, instr};
+  constexpr int CT = XL ? kCpolNone : kCpolSc1;  // outgoing slot: XCD-local L2, or agent-coherent
   typedef Arith<DT> Ar;
   constexpr int esz = Ar::esz;
   const int bytes = n * esz;
@@ -430,8 +432,8 @@ __device__ __forceinline__ bool run_ll(const unsigned char* pa, const unsigned c
       if (has1) st16<kCpolNone>(rD, 16 * q1, v1);
     }
     if (SEND) {
-      ll_store_quad(rT, 32 * q, v0, flag);
-      if (has1) ll_store_quad(rT, 32 * q1, v1, flag);
+      ll_store_quad<CT>(rT, 32 * q, v0, flag);
+      if (has1) ll_store_quad<CT>(rT, 32 * q1, v1, flag);
     }
   }
   for (int u = 4 * nquads + tid; u < nunits; u += nthr) {
@@ -448,31 +450,31 @@ __device__ __forceinline__ bool run_ll(const unsigned char* pa, const unsigned c
     if (DSTA) st_word<esz>(rD, o, v, second);
     if (SEND) {
       v2u unit = {v, flag};
-      __builtin_amdgcn_raw_buffer_store_b64(unit, rT, 8 * u, 0, kCpolSc1);
+      __builtin_amdgcn_raw_buffer_store_b64(unit, rT, 8 * u, 0, CT);
     }
   }
   return false;
 }
 
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND>
+template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL>
 __device__ __attribute__((noinline)) bool run_ll_call(const unsigned char* pa, const unsigned char* pb,
                                                       unsigned char* pd, unsigned char* pt, int n, int tid, int nthr,
                                                       uint32_t flag, unsigned int* err, unsigned long long* abort_word,
                                                       unsigned long long epoch, long long timeout_ticks, int instr) {
-  return run_ll<DT, RECV, SRCB, DSTA, SEND>(pa, pb, pd, pt, n, tid, nthr, flag, err, abort_word, epoch,
-                                            timeout_ticks, instr);
+  return run_ll<DT, RECV, SRCB, DSTA, SEND, XL>(pa, pb, pd, pt, n, tid, nthr, flag, err, abort_word, epoch,
+                                                timeout_ticks, instr);
 }
 
-template <int DT>
+template <int DT, bool XL>
 __device__ __forceinline__ bool dispatch_ll(uint32_t op, const unsigned char* pa, const unsigned char* pb,
                                             unsigned char* pd, unsigned char* pt, int n, int tid, int nthr,
                                             uint32_t flag, const WaitCtx& w) {
 #define CCL_CASE(R, B, D, T)                                                                                     \
   case ((R) ? OPB_RECV : 0u) | ((B) ? OPB_SRCB : 0u) | ((D) ? OPB_DSTA : 0u) | ((T) ? OPB_SEND : 0u):            \
-    return (DT == CCL_BF16) ? run_ll_call<DT, R, B, D, T>(pa, pb, pd, pt, n, tid, nthr, flag, w.err,            \
-                                                          w.abort_word, w.epoch, w.timeout_ticks, w.instr)       \
-                            : run_ll<DT, R, B, D, T>(pa, pb, pd, pt, n, tid, nthr, flag, w.err, w.abort_word,     \
-                                                     w.epoch, w.timeout_ticks, w.instr);
+    return (DT == CCL_BF16) ? run_ll_call<DT, R, B, D, T, XL>(pa, pb, pd, pt, n, tid, nthr, flag, w.err,        \
+                                                              w.abort_word, w.epoch, w.timeout_ticks, w.instr)   \
+                            : run_ll<DT, R, B, D, T, XL>(pa, pb, pd, pt, n, tid, nthr, flag, w.err, w.abort_word, \
+                                                         w.epoch, w.timeout_ticks, w.instr);
   switch (op & 15u) {
     CCL_CASE(false, false, true, false)
     CCL_CASE(false, false, false, true)
@@ -500,10 +502,19 @@ __device__ __forceinline__ void release_store(unsigned long long* p, unsigned lo
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Slot flags guard sc1 data whose stores every wave has already waited for.
+// Slot flags guard slot data whose stores every wave has already waited for: both
+// agent-coherent, or (XCD-local launches) both plain stores into the XCD's shared L2.
+// Receivers read flags and data with agent-coherent loads either way.
+template <bool XL>
 __device__ __forceinline__ void slot_flag_store(unsigned long long* p, unsigned long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (XL)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// XCD of the executing workgroup (hardware register XCC_ID, bits 3:0).
+__device__ __forceinline__ unsigned xcd_id() { return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)); }
 
 __device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
@@ -580,7 +591,9 @@ __device__ __forceinline__ int64_t uni64(int64_t v) {
   return int64_t((uint64_t(hi) << 32) | lo);
 }
 
-template <int DT>
+// XL: slots and their flags are written with plain stores, valid because the host
+// laid out the grid so that every transfer stays between workgroups of one XCD.
+template <int DT, bool XL>
 __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
   constexpr int esz = Arith<DT>::esz;
   // Set once by any thread that gives up (watchdog, or another workgroup's abort) and
@@ -591,6 +604,18 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
   const DevWG W = A.wgs[blockIdx.x];
   if (W.n == 0) return;  // padding id
   const int tid = threadIdx.x, nthr = blockDim.x;
+  if (XL && int(xcd_id()) != int(blockIdx.x % unsigned(A.nxcd))) {
+    // the layout this launch relies on does not hold: fail it before any slot is touched
+    if (tid == 0) {
+      if (atomicCAS(&A.err[0], 0u, unsigned(-CCL_ERR_PLACEMENT)) == 0u) {
+        A.err[1] = blockIdx.x;
+        A.err[2] = xcd_id();
+        A.err[3] = unsigned(A.epoch);
+      }
+      __hip_atomic_store(A.abort_word, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
   const unsigned long long E = A.epoch << kEpochShift;
   // this rank's buffers, kept in scalar registers
   unsigned char* const bufs[3] = {A.base[0][W.rank], A.base[1][W.rank], A.base[2][W.rank]};
@@ -636,7 +661,7 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
       if (A.ll) {
         // one pass over the whole range; receivers poll the units they consume
         const WaitCtx wc{A.err, A.abort_word, A.epoch, A.timeout_ticks, gi};
-        const bool gave_up = len > 0 && dispatch_ll<DT>(op, pa, pb, pd, pt, int(len), tid, nthr, A.ll_flag, wc);
+        const bool gave_up = len > 0 && dispatch_ll<DT, XL>(op, pa, pb, pd, pt, int(len), tid, nthr, A.ll_flag, wc);
         if (gave_up) s_abort = 1;
         __syncthreads();
         if (s_abort) return;
@@ -648,7 +673,7 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
           const int n = int((len - o < se) ? (len - o) : se);
           const int64_t bo = o * esz;
           const long long waited =
-              dispatch_slice<DT>(op, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr,
+              dispatch_slice<DT, XL>(op, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr,
                                  pt ? pt + bo : nullptr, n, tid, nthr, (op & OPB_RECV) ? &A.xflags[xin] : nullptr,
                                  E + (unsigned long long)(s + 1), A, gi);
           if (waited < 0) return;  // the wait gave up: uniform across the workgroup
@@ -656,7 +681,7 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
           if (itrace && tid == 0 && s == 0) itrace[4 * size_t(gi) + 1] = (unsigned long long)wall_clock64();
           if (op & OPB_SEND) wait_vm_stores();
           __syncthreads();
-          if ((op & OPB_SEND) && tid == 0) slot_flag_store(&A.xflags[xout], E + (unsigned long long)(s + 1));
+          if ((op & OPB_SEND) && tid == 0) slot_flag_store<XL>(&A.xflags[xout], E + (unsigned long long)(s + 1));
         }
       }
       if (done_flag >= 0 && tid == 0) release_store(&A.dflags[done_flag], A.epoch);
@@ -689,14 +714,29 @@ __global__ __launch_bounds__(1024) void copy_probe_kernel(uint4* __restrict__ ds
   for (; i < nvec; i += stride) dst[i] = src[i];
 }
 
+__global__ void xcd_probe_kernel(unsigned* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = xcd_id();
+}
+
 }  // namespace
 
-int launch_executor(const ExecArgs& args, int dtype, int nwg, int nthreads, void* stream, std::string* err) {
+int launch_executor(const ExecArgs& args, int dtype, bool xcd_local, int nwg, int nthreads, void* stream,
+                    std::string* err) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const dim3 g(nwg), b(nthreads);
   switch (dtype) {
-    case CCL_F32: hipLaunchKernelGGL(executor_kernel<CCL_F32>, dim3(nwg), dim3(nthreads), 0, s, args); break;
-    case CCL_BF16: hipLaunchKernelGGL(executor_kernel<CCL_BF16>, dim3(nwg), dim3(nthreads), 0, s, args); break;
-    case CCL_I32: hipLaunchKernelGGL(executor_kernel<CCL_I32>, dim3(nwg), dim3(nthreads), 0, s, args); break;
+    case CCL_F32:
+      if (xcd_local) hipLaunchKernelGGL((executor_kernel<CCL_F32, true>), g, b, 0, s, args);
+      else hipLaunchKernelGGL((executor_kernel<CCL_F32, false>), g, b, 0, s, args);
+      break;
+    case CCL_BF16:
+      if (xcd_local) hipLaunchKernelGGL((executor_kernel<CCL_BF16, true>), g, b, 0, s, args);
+      else hipLaunchKernelGGL((executor_kernel<CCL_BF16, false>), g, b, 0, s, args);
+      break;
+    case CCL_I32:
+      if (xcd_local) hipLaunchKernelGGL((executor_kernel<CCL_I32, true>), g, b, 0, s, args);
+      else hipLaunchKernelGGL((executor_kernel<CCL_I32, false>), g, b, 0, s, args);
+      break;
     default: *err = "dtype"; return CCL_ERR_UNSUPPORTED;
   }
   hipError_t e = hipGetLastError();
@@ -707,18 +747,31 @@ int launch_executor(const ExecArgs& args, int dtype, int nwg, int nthreads, void
   return CCL_OK;
 }
 
+// Both store variants of a dtype: the smaller occupancy bounds the plan.
 int executor_max_blocks_per_cu(int dtype, int nthreads, int* blocks, std::string* err) {
-  hipError_t e = hipSuccess;
+  int b0 = 0, b1 = 0;
+  hipError_t e0 = hipSuccess, e1 = hipSuccess;
   switch (dtype) {
-    case CCL_F32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, executor_kernel<CCL_F32>, nthreads, 0); break;
-    case CCL_BF16: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, executor_kernel<CCL_BF16>, nthreads, 0); break;
-    case CCL_I32: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, executor_kernel<CCL_I32>, nthreads, 0); break;
+    case CCL_F32:
+      e0 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, executor_kernel<CCL_F32, false>, nthreads, 0);
+      e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, executor_kernel<CCL_F32, true>, nthreads, 0);
+      break;
+    case CCL_BF16:
+      e0 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, executor_kernel<CCL_BF16, false>, nthreads, 0);
+      e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, executor_kernel<CCL_BF16, true>, nthreads, 0);
+      break;
+    case CCL_I32:
+      e0 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, executor_kernel<CCL_I32, false>, nthreads, 0);
+      e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, executor_kernel<CCL_I32, true>, nthreads, 0);
+      break;
     default: *err = "dtype"; return CCL_ERR_UNSUPPORTED;
   }
+  const hipError_t e = e0 != hipSuccess ? e0 : e1;
   if (e != hipSuccess) {
     *err = std::string("occupancy query: ") + hipGetErrorString(e);
     return CCL_ERR_HIP;
   }
+  *blocks = b0 < b1 ? b0 : b1;
   return CCL_OK;
 }
 
@@ -729,6 +782,20 @@ int launch_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     *err = std::string("copy probe launch: ") + hipGetErrorString(e);
+    return CCL_ERR_HIP;
+  }
+  return CCL_OK;
+}
+
+}  // namespace ccl
+
+namespace ccl {
+
+int launch_xcd_probe(unsigned* out, int nwg, std::string* err) {
+  hipLaunchKernelGGL(xcd_probe_kernel, dim3(nwg), dim3(64), 0, 0, out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    *err = std::string("XCD probe launch: ") + hipGetErrorString(e);
     return CCL_ERR_HIP;
   }
   return CCL_OK;

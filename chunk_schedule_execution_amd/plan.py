@@ -29,6 +29,7 @@ class PlanConfig:
     trace: bool = False
     host_only: bool = False
     no_fusion: bool = False
+    xcd_local: bool = True  # plain slot stores between workgroups verified to share an XCD
     num_cus: int = 0
     timeout_us: int = 0
 
@@ -40,6 +41,8 @@ class PlanConfig:
             flags |= capi.CCL_FLAG_HOST_ONLY
         if self.no_fusion:
             flags |= capi.CCL_FLAG_NO_FUSION
+        if not self.xcd_local:
+            flags |= capi.CCL_FLAG_COHERENT_ONLY
         if self.protocol == "ll":
             flags |= capi.CCL_FLAG_LL
         elif self.protocol != "simple":

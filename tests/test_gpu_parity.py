@@ -306,3 +306,49 @@ def test_ll_repeated_launches():
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 11)
     ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=4, protocol="ll", repeat=5)
     assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
+
+
+# ------------------------------------------------------------------ slot store policy
+
+@pytest.mark.parametrize("protocol", ["simple", "ll"])
+@pytest.mark.parametrize("k,nt,num_cus", [(8, 256, 0), (3, 512, 0), (32, 1024, 0), (5, 256, 8)])
+def test_xcd_local_and_coherent_stores_agree(protocol, k, nt, num_cus):
+    """A plan whose transfers all stay between workgroups of one XCD writes slots with
+    plain stores; with num_cus=8 the layout estimate rejects the XCD-aligned grid, the
+    instances spread over XCDs and the plan keeps coherent stores. Either way, and with
+    CCL_FLAG_COHERENT_ONLY, the bits are the chain order, launch after launch."""
+    P, N = 8, 3 * 65536 + 24
+    case(f"ring AR store policy {protocol} k={k} nt={nt} num_cus={num_cus}")
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 13)
+    want = O2.ring_allreduce(xs, P, "f32")[0]
+    for xcd_local in (True, False):
+        ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=k, protocol=protocol, nthreads=nt,
+                        slice_bytes=16 << 10, xcd_local=xcd_local, repeat=4, num_cus=num_cus)
+        info = plan.info()
+        assert info["num_xcds"] >= 1
+        if not xcd_local:
+            assert info["xcd_local"] == 0
+        elif info["num_xcds"] == 8:
+            assert info["xcd_local"] == (0 if num_cus == 8 else 1)
+        if num_cus == 8:
+            assert info["grid_workgroups"] == P * k  # no XCD padding
+        assert_all_equal(ys, want)
+
+
+def test_xcd_local_hierarchical_and_alltoall():
+    G, L, N = 2, 8, 8 * 4099
+    case("store policy: hierarchical bf16, two-phase alltoall")
+    xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 17)
+    want = O2.hierarchical_allreduce(xs, G, L, "bf16")[0]
+    for xcd_local in (True, False):
+        ys, _ = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, xcd_local=xcd_local, repeat=3,
+                     slice_bytes=8192)
+        assert_all_equal(ys, want)
+    G, L, b = 4, 8, 513
+    P = G * L
+    xs = W.make_inputs("uniform_i32", P * b, P, W.CFG_A2A_32R_INT32, size_bytes=P * b * 4 + 17)
+    want = O1.alltoall(xs)
+    for xcd_local in (True, False):
+        ys, _ = _run(programs.two_phase_alltoall(G, L), xs, "i32", k=1, xcd_local=xcd_local, repeat=3, nthreads=256)
+        for r in range(P):
+            assert np.array_equal(ys[r], want[r]), r
