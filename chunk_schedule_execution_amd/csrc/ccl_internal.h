@@ -46,6 +46,7 @@ struct Loc {
 struct Instr {
   int rank = 0, channel = 0, cnt = 1;
   bool recv = false;  // first operand is the staging slot of transfer xin
+  bool local_in = false;  // direct transport: the received data is written into `a` by the sender
   Loc a, b, d;        // local first operand (if !recv), added operand, local destination
   int xin = -1, xout = -1;
   int chunk_id = 0;
@@ -57,7 +58,7 @@ struct Instr {
   std::vector<int> waits;  // base instruction ids whose completion it awaits
   uint32_t opbits() const {
     return (recv ? OPB_RECV : 0u) | (b.valid() ? OPB_SRCB : 0u) | (d.valid() ? OPB_DSTA : 0u) |
-           (xout >= 0 ? OPB_SEND : 0u);
+           (xout >= 0 ? OPB_SEND : 0u) | (local_in ? OPB_LOCAL_IN : 0u);
   }
 };
 
@@ -65,6 +66,7 @@ struct Xfer {
   int src_rank = 0, dst_rank = 0, channel = 0, cnt = 1;
   int sender = -1, receiver = -1;  // base instruction ids
   int phase_idx = -1;
+  bool direct = false;  // the sender writes the receiver's destination, no staging slot
 };
 
 struct BaseWG {

@@ -536,6 +536,51 @@ int64_t link_of(const HostPlan& hp, const Instr& I) {
   return (int64_t(X.src_rank) * kMaxRanks + X.dst_rank) * 65536 + X.channel;
 }
 
+// ---------------------------------------------------------------- direct transport
+
+// A receive that only copies the incoming data into a local location (and perhaps
+// forwards it) can have the sender write that location itself, with no staging slot,
+// when no instruction of the receiving rank that could run before the receive touches
+// the location: every other accessor must be a descendant of the receive in the DAG.
+// The receive then waits for the transfer's flag and reads (forwards) from there.
+void choose_direct(HostPlan& hp, const std::vector<std::set<int>>& dag) {
+  if (!(hp.cfg.flags & CCL_FLAG_DIRECT) || (hp.cfg.flags & CCL_FLAG_LL)) return;
+  const size_t n = hp.ins.size();
+  std::vector<int> mark(n, -1), stack;
+  auto overlaps = [](const Loc& l, int lc, const Loc& m, int mc) {
+    return l.valid() && m.valid() && l.buf == m.buf && l.idx < m.idx + mc && m.idx < l.idx + lc;
+  };
+  for (size_t x = 0; x < hp.xf.size(); ++x) {
+    Xfer& X = hp.xf[x];
+    Instr& R = hp.ins[X.receiver];
+    if (!R.recv || R.local_in || R.b.valid() || !R.d.valid() || hp.ins[X.sender].rank == R.rank) continue;
+    stack.assign(1, X.receiver);
+    mark[X.receiver] = int(x);
+    while (!stack.empty()) {
+      int u = stack.back();
+      stack.pop_back();
+      for (int v : dag[u])
+        if (mark[v] != int(x)) {
+          mark[v] = int(x);
+          stack.push_back(v);
+        }
+    }
+    bool ok = true;
+    for (size_t i = 0; i < n && ok; ++i) {
+      if (mark[i] == int(x)) continue;  // the receive itself and its descendants
+      const Instr& I = hp.ins[i];
+      if (I.rank != R.rank) continue;
+      if (overlaps(I.a, I.cnt, R.d, R.cnt) || overlaps(I.b, I.cnt, R.d, R.cnt) || overlaps(I.d, I.cnt, R.d, R.cnt))
+        ok = false;
+    }
+    if (!ok) continue;
+    X.direct = true;
+    R.local_in = true;
+    R.a = R.d;
+    R.d = Loc{};
+  }
+}
+
 void schedule(HostPlan& hp, const std::vector<std::set<int>>& succ) {
   size_t n = hp.ins.size();
   std::vector<int> pos(n);
@@ -789,7 +834,7 @@ void compute_waits(HostPlan& hp, const std::vector<std::set<int>>& dag) {
 
 int len_idx_of(const HostPlan& hp, int t, int depth = 0) {
   const Instr& I = hp.ins[t];
-  if (!I.recv && I.a.valid()) return I.a.idx;
+  if ((!I.recv || I.local_in) && I.a.valid()) return I.a.idx;
   if (I.d.valid()) return I.d.idx;
   if (I.b.valid()) return I.b.idx;
   if (I.recv && depth < 1024) return len_idx_of(hp, hp.xf[I.xin].sender, depth + 1);
@@ -813,12 +858,14 @@ void lower(HostPlan& hp) {
     int64_t cap = (k == 1) ? (int64_t(X.cnt) * M) / hp.C + 2 : (M / hp.C + 2) / k + 2;
     int64_t bytes = ((cap + 16) * hp.esz + 255) / 256 * 256;
     if (hp.cfg.flags & CCL_FLAG_LL) bytes *= 2;  // every 4 data bytes travel with a 4-byte flag
+    if (X.direct) bytes = 0;                     // written straight into the receiver's buffer
     for (int i = 0; i < k; ++i) {
       DevXfer& D = hp.dxf[size_t(x) * k + i];
       D.slot_off = uint64_t(off);
       D.phase_idx = X.phase_idx;
       D.instance = i;
       D.cnt = X.cnt;
+      D.direct = X.direct ? 1 : 0;
       off += bytes;
     }
   }
@@ -872,6 +919,13 @@ void lower(HostPlan& hp) {
         D.instance = i;
         D.pad0 = len_idx_of(hp, t);
         D.peer_wg = I.xout >= 0 ? hp.ins[hp.xf[I.xout].receiver].wg * stride + i : -1;
+        D.t_buf = D.t_rank = D.t_idx = -1;
+        if (I.xout >= 0 && hp.xf[I.xout].direct) {
+          const Instr& R = hp.ins[hp.xf[I.xout].receiver];
+          D.t_buf = R.a.buf;
+          D.t_rank = R.rank;
+          D.t_idx = R.a.idx;
+        }
         hp.dins.push_back(D);
         hp.dins_base.push_back(t);
       }
@@ -917,6 +971,7 @@ int64_t plan_bytes(const HostPlan& hp, int64_t count) {
   int64_t total = 0;
   for (size_t j = 0; j < hp.dins.size(); ++j) {
     const DevInstr& D = hp.dins[j];
+    if (D.op == (OPB_RECV | OPB_LOCAL_IN)) continue;  // waits for data the sender already placed
     Range r = op_range(D.pad0, D.cnt, D.instance, hp.k, count, hp.C);
     // slot reads and writes carry one flag byte per data byte under the LL protocol
     const int slot = (hp.cfg.flags & CCL_FLAG_LL) ? 2 : 1;
@@ -946,7 +1001,8 @@ void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec
     const DevInstr& D = hp.dins[j];
     DevExec E{};
     E.op = D.op | (uint32_t(D.a_buf < 0 ? 0 : D.a_buf) << 8) | (uint32_t(D.b_buf < 0 ? 0 : D.b_buf) << 12) |
-           (uint32_t(D.d_buf < 0 ? 0 : D.d_buf) << 16);
+           (uint32_t(D.d_buf < 0 ? 0 : D.d_buf) << 16) | ((D.t_buf < 0 ? kStagingBuf : uint32_t(D.t_buf)) << 20) |
+           (uint32_t(D.t_rank < 0 ? 0 : D.t_rank) << 24);
     E.xin = D.xin;
     E.xout = D.xout;
     E.done_flag = D.done_flag;
@@ -956,13 +1012,14 @@ void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec
     const int64_t nsl = E.len == 0 ? 0 : (E.len + hp.slice_elems - 1) / hp.slice_elems;
     if (nsl >= (int64_t(1) << kEpochShift)) fail(CCL_ERR_INVALID_ARGUMENT, "too many slices for one transfer");
     E.nsl = int32_t(nsl);
-    if (D.op & OPB_RECV)
+    if ((D.op & OPB_RECV) && !(D.op & OPB_LOCAL_IN))
       E.a_off = slot_off(D.xin);
     else
       E.a_off = op_range(D.a_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
     if (D.op & OPB_SRCB) E.b_off = op_range(D.b_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
     if (D.op & OPB_DSTA) E.d_off = op_range(D.d_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
-    if (D.op & OPB_SEND) E.t_off = slot_off(D.xout);
+    if (D.op & OPB_SEND)
+      E.t_off = D.t_buf >= 0 ? op_range(D.t_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz : slot_off(D.xout);
     out[j] = E;
   }
 }
@@ -976,6 +1033,7 @@ void compile_plan(HostPlan& hp, const ccl_program_desc* prog, int nranks, int nc
   t0 = Clock::now();
   std::vector<std::set<int>> dag;
   fuse(hp, dag);  // DAG construction happens inside; split timing below is approximate
+  choose_direct(hp, dag);
   hp.ms[1] = 0.0;
   hp.ms[2] = ms_since(t0);
   t0 = Clock::now();

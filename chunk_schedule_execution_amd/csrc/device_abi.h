@@ -10,8 +10,12 @@ namespace ccl {
 constexpr int kMaxRanks = 64;
 constexpr int kNumBufs = 3;  // input, output, scratch
 
-// Opcode bits of a lowered instruction (same values as CCL_I_* in ccl.h).
-enum : uint32_t { OPB_RECV = 1u, OPB_SRCB = 2u, OPB_DSTA = 4u, OPB_SEND = 8u };
+// Opcode bits of a lowered instruction (same values as CCL_I_* in ccl.h). With
+// OPB_LOCAL_IN a receive's data is already in the local first operand, written there
+// by the sender (direct transport); the receive only waits for the transfer's flag
+// before reading it.
+enum : uint32_t { OPB_RECV = 1u, OPB_SRCB = 2u, OPB_DSTA = 4u, OPB_SEND = 8u, OPB_LOCAL_IN = 16u };
+constexpr uint32_t kStagingBuf = 15u;  // DevExec::op target-buffer field: the staging pool
 
 struct DevWG {  // one workgroup of the launch
   int32_t rank;
@@ -20,7 +24,7 @@ struct DevWG {  // one workgroup of the launch
   int32_t trace_slot;
 };
 
-struct DevInstr {  // 64 bytes, read wave-uniformly
+struct DevInstr {  // host-side lowered instruction
   uint32_t op;     // OPB_* bits
   int32_t cnt;     // chunks covered
   int32_t a_buf, a_idx;  // local first operand (unless OPB_RECV)
@@ -32,6 +36,8 @@ struct DevInstr {  // 64 bytes, read wave-uniformly
   int32_t instance;            // instance sub-chunk index (0..k-1)
   int32_t pad0;                // chunk index that fixes the instruction's element range
   int32_t peer_wg;             // OPB_SEND: launch-grid workgroup that receives (-1 = none)
+  int32_t t_buf, t_rank, t_idx;  // direct OPB_SEND: receiver's buffer, rank and chunk (t_buf -1: staging slot)
+  int32_t pad1;
 };
 
 struct DevXfer {  // 32 bytes: one send -> recv transfer
@@ -39,7 +45,8 @@ struct DevXfer {  // 32 bytes: one send -> recv transfer
   int32_t phase_idx;  // chunk whose range start fixes the data's offset inside the slot (-1: none)
   int32_t instance;
   int32_t cnt;
-  int32_t pad0, pad1, pad2;
+  int32_t direct;     // 1: written straight into the receiver's buffer, no slot
+  int32_t pad1, pad2;
 };
 
 // What the kernel reads for one lowered instruction at one element count: the
@@ -49,7 +56,9 @@ struct DevXfer {  // 32 bytes: one send -> recv transfer
 // the count when a count is first used, cached on the device, and copied into LDS by
 // each workgroup at launch.
 struct DevExec {  // 80 bytes
-  uint32_t op;     // OPB_* bits | a_buf << 8 | b_buf << 12 | d_buf << 16
+  // OPB_* bits | a_buf << 8 | b_buf << 12 | d_buf << 16 | t_buf << 20 | t_rank << 24, where
+  // t_buf / t_rank name the receiver's buffer of a direct send (t_buf kStagingBuf: a slot)
+  uint32_t op;
   int32_t xin, xout, done_flag;
   int32_t wait_begin, nwaits;
   int32_t nsl;     // slices (simple protocol)

@@ -197,6 +197,7 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
     waited = s_waited;
     if (waited < 0) return -1;
   }
+  if constexpr (!DSTA && !SEND) return waited;  // a receive whose data the sender already placed
   int tail0 = 0;
   if (same) {
     if (tid < head) scalar(tid);
@@ -267,13 +268,14 @@ __device__ __forceinline__ long long dispatch_slice(uint32_t op, const unsigned 
     CCL_CASE(false, true, true, false)
     CCL_CASE(false, true, false, true)
     CCL_CASE(false, true, true, true)
+    CCL_CASE(true, false, false, false)
     CCL_CASE(true, false, true, false)
     CCL_CASE(true, false, false, true)
     CCL_CASE(true, false, true, true)
     CCL_CASE(true, true, true, false)
     CCL_CASE(true, true, false, true)
     CCL_CASE(true, true, true, true)
-    default: return 0;  // an instruction always stores somewhere; the compiler never emits this
+    default: return 0;  // every other instruction stores somewhere; the compiler never emits these
   }
 #undef CCL_CASE
 }
@@ -654,10 +656,17 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
         __syncthreads();
         if (s_abort) return;
       }
-      const unsigned char* pa = (op & OPB_RECV) ? staging + uni64(R.a_off) : bufs[(opw >> 8) & 3u] + uni64(R.a_off);
+      // a receive reads its slot, or (direct transport) its own buffer where the sender wrote
+      const unsigned char* pa = ((op & OPB_RECV) && !(opw & OPB_LOCAL_IN)) ? staging + uni64(R.a_off)
+                                                                           : bufs[(opw >> 8) & 3u] + uni64(R.a_off);
       const unsigned char* pb = (op & OPB_SRCB) ? bufs[(opw >> 12) & 3u] + uni64(R.b_off) : nullptr;
       unsigned char* pd = (op & OPB_DSTA) ? bufs[(opw >> 16) & 3u] + uni64(R.d_off) : nullptr;
-      unsigned char* pt = (op & OPB_SEND) ? staging + uni64(R.t_off) : nullptr;
+      unsigned char* pt = nullptr;
+      if (op & OPB_SEND) {  // the receiver's slot, or (direct transport) the receiver's buffer
+        const uint32_t tb = (opw >> 20) & 15u, tr = opw >> 24;
+        pt = (tb == kStagingBuf ? staging : tb == 0u ? A.base[0][tr] : tb == 1u ? A.base[1][tr] : A.base[2][tr]) +
+             uni64(R.t_off);
+      }
       if (A.ll) {
         // one pass over the whole range; receivers poll the units they consume
         const WaitCtx wc{A.err, A.abort_word, A.epoch, A.timeout_ticks, gi};

@@ -72,19 +72,21 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
     std::vector<char> started(nW, 0);
     // instruction geometry at N
     struct Geo {
-      int64_t len, alo, blo, dlo, nsl;
+      int64_t len, alo, blo, dlo, tlo, nsl;
     };
     std::vector<Geo> geo(hp.dins.size());
     for (size_t j = 0; j < hp.dins.size(); ++j) {
       const DevInstr& D = hp.dins[j];
       Geo g{};
       g.len = op_range(D.pad0, D.cnt, D.instance, hp.k, N, hp.C).len;
-      if (!(D.op & OPB_RECV)) g.alo = op_range(D.a_idx, D.cnt, D.instance, hp.k, N, hp.C).lo;
+      const bool local_a = !(D.op & OPB_RECV) || (D.op & OPB_LOCAL_IN);
+      if (local_a) g.alo = op_range(D.a_idx, D.cnt, D.instance, hp.k, N, hp.C).lo;
+      if (D.t_buf >= 0) g.tlo = op_range(D.t_idx, D.cnt, D.instance, hp.k, N, hp.C).lo;
       if (D.op & OPB_SRCB) g.blo = op_range(D.b_idx, D.cnt, D.instance, hp.k, N, hp.C).lo;
       if (D.op & OPB_DSTA) g.dlo = op_range(D.d_idx, D.cnt, D.instance, hp.k, N, hp.C).lo;
       g.nsl = (g.len + se - 1) / se;
       geo[j] = g;
-      if (D.op & OPB_SEND) slot[D.xout].assign(g.len, Val{});
+      if ((D.op & OPB_SEND) && D.t_buf < 0) slot[D.xout].assign(g.len, Val{});
     }
     std::vector<int> runnable;
     for (;;) {
@@ -120,7 +122,8 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
       if (g.nsl > 0) {
         int64_t lo = sl[w] * se, hi = std::min(g.len, lo + se);
         for (int64_t e = lo; e < hi; ++e) {
-          Val v = (D.op & OPB_RECV) ? slot[D.xin][e] : buf[D.a_buf][G.rank][g.alo + e];
+          const bool from_slot = (D.op & OPB_RECV) && !(D.op & OPB_LOCAL_IN);
+          Val v = from_slot ? slot[D.xin][e] : buf[D.a_buf][G.rank][g.alo + e];
           if (D.op & OPB_SRCB) {
             const Val& b = buf[D.b_buf][G.rank][g.blo + e];
             if (!b.init) v.init = false;
@@ -134,7 +137,10 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
             fail(CCL_ERR_INVALID_PROGRAM, msg);
           }
           if (D.op & OPB_DSTA) buf[D.d_buf][G.rank][g.dlo + e] = v;
-          if (D.op & OPB_SEND) slot[D.xout][e] = v;
+          if ((D.op & OPB_SEND) && D.t_buf >= 0)
+            buf[D.t_buf][D.t_rank][g.tlo + e] = v;  // direct transport: the receiver's own location
+          else if (D.op & OPB_SEND)
+            slot[D.xout][e] = v;
         }
         if (D.op & OPB_SEND) xflag[D.xout] = sl[w] + 1;
         sl[w]++;

@@ -24,6 +24,7 @@ class PlanConfig:
     nthreads: int = 512
     slice_bytes: int = 256 * 1024
     protocol: str = "simple"  # "simple" (slice flags) or "ll" (flag in every 8-byte unit)
+    transport: str = "staged"  # "staged" (every transfer through a slot) or "direct" (copy receives skip it)
     scheduler: str = "hpds"
     wg_alloc: str = "state"
     trace: bool = False
@@ -41,6 +42,10 @@ class PlanConfig:
             flags |= capi.CCL_FLAG_HOST_ONLY
         if self.no_fusion:
             flags |= capi.CCL_FLAG_NO_FUSION
+        if self.transport == "direct":
+            flags |= capi.CCL_FLAG_DIRECT
+        elif self.transport != "staged":
+            raise ValueError(f"unknown transport {self.transport!r}")
         if not self.xcd_local:
             flags |= capi.CCL_FLAG_COHERENT_ONLY
         if self.protocol == "ll":

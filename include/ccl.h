@@ -129,6 +129,13 @@ typedef struct {
                                     are no per-slice flags (twice the slot traffic, far fewer round trips;
                                     the protocol choice of the MSCCLang report, section 3.1 runtime, and the
                                     AutoCCL report's Protocol parameter) */
+#define CCL_FLAG_DIRECT 0x40u     /* direct transport (simple protocol only): when a receive only copies the
+                                    incoming data into a local buffer (and perhaps forwards it), and no
+                                    other instruction touches that location before it, the sender writes
+                                    the location itself and the receive just waits for the transfer's flag
+                                    and forwards from there; such transfers use no staging slot. The
+                                    AutoCCL report's transport parameter; ring AllReduce moves S(5P-4)
+                                    bytes instead of S(6P-4) */
 #define CCL_FLAG_COHERENT_ONLY 0x20u /* always write staging slots and their flags with agent-coherent stores.
                                     By default, when every transfer of the lowered plan stays between
                                     workgroups that the device's round-robin dispatch puts on one XCD
@@ -219,7 +226,10 @@ int64_t ccl_plan_bytes(const ccl_plan* plan, int64_t count);
 #define CCL_I_RECV 0x1 /* first operand is the incoming transfer's staging slot */
 #define CCL_I_SRCB 0x2 /* a second, local operand is added (reduce) */
 #define CCL_I_DSTA 0x4 /* the result is stored to a local buffer */
-#define CCL_I_SEND 0x8 /* the result is stored to the outgoing transfer's staging slot */
+#define CCL_I_SEND 0x8 /* the result is stored to the outgoing transfer's staging slot (or, direct
+                          transport, straight into the receiver's buffer) */
+#define CCL_I_LOCAL_IN 0x10 /* with CCL_I_RECV: the data was written into the local first operand by the
+                               sender (direct transport); the receive waits for the flag, then reads it */
 
 typedef struct {
   int32_t rank, wg, subpipe, channel, instance;
@@ -271,7 +281,8 @@ typedef struct {
   int32_t parallel_factor; /* channels / instances (nc) */
   int32_t nthreads;        /* threads per workgroup (nt) */
   int32_t slice_bytes;     /* chunk size of one pipelined step (c) */
-  int32_t protocol;        /* 0 = slice flags, 1 = low-latency units (CCL_FLAG_LL) */
+  int32_t protocol;        /* 0 = slice flags, 1 = low-latency units (CCL_FLAG_LL), 2 = slice flags with
+                              direct transport (CCL_FLAG_DIRECT) */
   int32_t reserved;
 } ccl_tune_point;
 
@@ -281,7 +292,8 @@ typedef struct {
   const int32_t* slices;   int32_t nslices;
   int32_t nvariants;       /* algorithm subspaces 0..nvariants-1 */
   int32_t warmup, iters;   /* per device evaluation */
-  int32_t protocols;       /* protocol subspaces to search: bit 0 = slice flags, bit 1 = LL (0 = bit 0) */
+  int32_t protocols;       /* protocol subspaces to search: bit 0 = slice flags, bit 1 = LL, bit 2 = slice
+                              flags with direct transport (0 = bit 0) */
 } ccl_tune_space;
 
 typedef struct {

@@ -11,6 +11,7 @@ import pytest
 
 import workloads as W
 from chunk_schedule_execution_amd import Plan, PlanConfig, capi, programs
+from chunk_schedule_execution_amd.dsl import Buffer, Program
 from oracle import program as OP
 from oracle import schedule_order as O2
 
@@ -111,6 +112,46 @@ def test_ll_protocol_doubles_slot_traffic():
     assert ll - simple == 2 * (2 * (P - 1)) * S // P * P
 
 
+def test_direct_transport_bytes_and_opcodes():
+    """Direct transport: a receive that only copies (and forwards) the incoming data has
+    it written into place by the sender. Ring AllReduce then moves S(5P-4) bytes: every
+    all-gather hop but the owner's becomes wait-and-forward from the output, the last
+    one only waits; direct AllToAll reaches its floor 2PS with no staging slot at all."""
+    for P in (2, 3, 8):
+        N = P * 1000
+        S = N * 4
+        plan = host_plan(programs.ring_allreduce(P), 2, transport="direct")
+        assert plan.bytes(N) == S * (5 * P - 4)
+        LOCAL = capi.CCL_I_LOCAL_IN
+        want = collections.Counter({SEND: 2 * P, RRS: 2 * P * (P - 2), RRCS: 2 * P,
+                                    capi.CCL_I_RECV | capi.CCL_I_SEND | LOCAL: 2 * P * (P - 2),
+                                    capi.CCL_I_RECV | LOCAL: 2 * P})
+        assert hist(plan) == +want
+        staged = host_plan(programs.ring_allreduce(P), 2)
+        assert plan.info()["staging_bytes"] < staged.info()["staging_bytes"]
+        plan.check(seed=2, nsims=3)
+    P, N = 8, 8 * 64
+    S = N * 4
+    a2a = host_plan(programs.direct_alltoall(P), transport="direct")
+    assert a2a.bytes(N) == 2 * P * S and a2a.info()["staging_bytes"] == 0
+    # the LL protocol keeps its flag units in slots: direct transport does not apply
+    ll = host_plan(programs.ring_allreduce(8), protocol="ll", transport="direct")
+    assert ll.bytes(8000) == host_plan(programs.ring_allreduce(8), protocol="ll").bytes(8000)
+
+
+def test_direct_transport_skips_locations_touched_before_the_receive():
+    """Rank 1 writes its output chunk locally before receiving into it: a direct write
+    could land before that local copy, so the transfer keeps its slot."""
+    IN, OUT = Buffer.input, Buffer.output
+    p = Program("custom", 2, 1, 1)
+    p.chunk(1, IN, 0).copy(1, OUT, 0)
+    p.chunk(0, IN, 0).copy(1, OUT, 0)
+    plan = host_plan(p, transport="direct")
+    assert not any(e.opcode & capi.CCL_I_LOCAL_IN for e in plan.export())
+    assert plan.bytes(100) == host_plan(p).bytes(100)
+    plan.check(seed=1, nsims=4)
+
+
 def test_count_granule():
     assert host_plan(programs.ring_allreduce(8)).info()["count_granule"] == 1
     assert host_plan(programs.two_phase_alltoall(4, 8)).info()["count_granule"] == 32
@@ -206,7 +247,9 @@ def test_instances_sit_on_one_xcd():
                                        ("allgather_2d", (2, 4)), ("reducescatter_2d", (2, 4))])
 @pytest.mark.parametrize("knobs", [dict(k=1, scheduler="hpds", wg_alloc="state"),
                                    dict(k=2, scheduler="rr", wg_alloc="connection"),
-                                   dict(k=3, scheduler="program", wg_alloc="state", protocol="ll")])
+                                   dict(k=3, scheduler="program", wg_alloc="state", protocol="ll"),
+                                   dict(k=2, scheduler="hpds", wg_alloc="state", transport="direct"),
+                                   dict(k=1, scheduler="rr", wg_alloc="connection", transport="direct")])
 def test_lowered_plans_pass_random_interleavings(name, args, knobs):
     knobs = dict(knobs)
     k = knobs.pop("k")

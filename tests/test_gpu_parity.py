@@ -352,3 +352,57 @@ def test_xcd_local_hierarchical_and_alltoall():
         ys, _ = _run(programs.two_phase_alltoall(G, L), xs, "i32", k=1, xcd_local=xcd_local, repeat=3, nthreads=256)
         for r in range(P):
             assert np.array_equal(ys[r], want[r]), r
+
+
+# ------------------------------------------------------------------ direct transport
+
+@pytest.mark.parametrize("P,N,k", [(2, 4099, 2), (3, 7, 1), (8, 3 * 65536 + 24, 8), (8, 8 * 1001, 24), (5, 123457, 7)])
+@pytest.mark.parametrize("xcd_local", [True, False])
+def test_direct_ring_allreduce(P, N, k, xcd_local):
+    """Senders write the all-gather hops straight into the receivers' outputs; the
+    receivers forward from there. Same chain-order bits, repeated launches."""
+    case(f"direct ring AR P={P} N={N} k={k} xcd_local={xcd_local}")
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 19)
+    ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=k, transport="direct", xcd_local=xcd_local,
+                    slice_bytes=8192, repeat=3)
+    assert any(e.opcode & 0x10 for e in plan.export())
+    assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
+
+
+def test_direct_other_collectives():
+    """Hierarchical bf16, two-phase and direct AllToAll, split AllToNext, ring and 2-D
+    AllGather / ReduceScatter with direct transport."""
+    G, L, N = 2, 8, 8 * 4099
+    case("direct hierarchical bf16")
+    xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 23)
+    ys, _ = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, transport="direct", repeat=2)
+    assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
+    G, L, b = 4, 8, 257
+    P = G * L
+    xs = W.make_inputs("uniform_i32", P * b, P, W.CFG_A2A_32R_INT32, size_bytes=P * b * 4 + 23)
+    want = O1.alltoall(xs)
+    for prog in (programs.two_phase_alltoall(G, L), programs.direct_alltoall(P)):
+        case(f"direct {prog.name}")
+        ys, _ = _run(prog, xs, "i32", k=1, transport="direct", nthreads=256, repeat=2)
+        for r in range(P):
+            assert np.array_equal(ys[r], want[r]), r
+    G, L, N = 3, 8, 8 * 777
+    case("direct alltonext split")
+    xs = W.make_inputs("normal_f32", N, G * L, W.CFG_A2NEXT_AGRS_24R, size_bytes=N * 4 + 23)
+    prior = [np.full(N, -3.0, np.float32) for _ in range(G * L)]
+    ys, _ = _run(programs.alltonext(G, L, split=True), xs, "f32", k=2, prior=prior, transport="direct")
+    want = O1.alltonext(xs, prior)
+    for r in range(G * L):
+        assert np.array_equal(ys[r], want[r]), r
+    P, n = G * L, 24 * 41
+    xs = W.make_inputs("prov_i32", n, P, W.CFG_A2NEXT_AGRS_24R, size_bytes=n * 4 + 29)
+    for prog in (programs.ring_allgather(P), programs.allgather_2d(G, L)):
+        case(f"direct {prog.name}")
+        ys, _ = _run(prog, xs, "i32", k=2, transport="direct")
+        assert_all_equal(ys, O1.allgather(xs))
+    xs = W.make_inputs("normal_f32", n * P, P, W.CFG_A2NEXT_AGRS_24R, size_bytes=n * P * 4 + 29)
+    case("direct ring reducescatter")
+    ys, _ = _run(programs.ring_reducescatter(P), xs, "f32", k=2, transport="direct")
+    want = O2.ring_reducescatter(xs, P, "f32")
+    for r in range(P):
+        assert np.array_equal(ys[r], want[r]), r
