@@ -1,11 +1,18 @@
 """Benchmark: ring AllReduce over 8 virtual ranks on one MI355X (busbw and HBM fraction).
 
-Workload: the 8-rank fp32 ring AllReduce swept over 32 KiB .. 3 MiB per rank, with
-the parallelization factor, threads per workgroup and slice size chosen by the
-on-device coordinate-descent tuner. A timed step is one collective (one kernel
-launch) at the top of the sweep, 3 MiB per rank; the rest of the sweep, the
-32-256 MiB points and the tuned-vs-fixed comparison are reported beside it.
-Plan compilation and tuning happen before timing.
+Headline step: one 8-rank fp32 ring AllReduce of 3 MiB per rank (the top of the
+32 KiB .. 3 MiB sweep), one kernel launch per collective, inputs resident in HBM,
+with the parallelization factor, threads per workgroup, slice size and protocol /
+transport chosen by the on-device coordinate-descent tuner. Plan compilation and
+tuning happen before timing.
+
+Beside it (unless --no-extras): the rest of the sweep and 32-256 MiB, tuned versus
+fixed configurations, the other four workloads (4-rank integer ring AllReduce,
+16-rank bf16 hierarchical AllReduce fused versus three launches, 32-rank int32
+AllToAll two-phase versus direct, 24-rank AllToNext split / unsplit under HPDS with
+state allocation versus round robin with connection allocation, AllGather and
+ReduceScatter at 128 MiB), workgroup idle fractions from the device trace, cold
+runs over rotating buffer sets, and the plain-copy ceiling.
 
 Prints one JSON line. Only one GPU: --gpus above 1 exits with a message.
 """
@@ -16,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -30,6 +38,10 @@ HBM_PEAK_GBS = 8000.0
 TUNE_FACTORS = [1, 2, 4, 8, 16, 24, 32]
 TUNE_THREADS = [256, 512, 1024]
 TUNE_SLICES = [16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20]
+# tuner protocol ids: (protocol, transport, non-temporal local traffic)
+PROTOCOLS = {0: ("simple", "staged", False), 1: ("ll", "staged", False), 2: ("simple", "direct", False),
+             3: ("simple", "direct", True)}
+DEVICE_INPUT_BYTES = 32 << 20  # at or above this many bytes per rank, inputs are drawn on the device
 
 
 def parse():
@@ -38,7 +50,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--fixed", type=str, default="",
-                    help="k,nthreads,slice_bytes,protocol(0 simple, 1 LL): skip tuning (profiling runs)")
+                    help="k,nthreads,slice_bytes,protocol(0 simple, 1 LL, 2 simple+direct, 3 simple+direct+streaming): "
+                         "skip tuning (profiling runs)")
     ap.add_argument("--no-extras", action="store_true", help="headline only (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -52,6 +65,20 @@ def source_digest() -> str:
         with open(os.path.join(ROOT, "chunk_schedule_execution_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def same_launch(a, b, piece_bytes):
+    """Two (k, nthreads, slice_bytes, protocol) configurations run the same kernel work:
+    equal apart from slice sizes that both exceed every instruction's piece (one slice
+    each)."""
+    a, b = tuple(a), tuple(b)
+    if len(a) != 4 or len(b) != 4 or (a[0], a[1], a[3]) != (b[0], b[1], b[3]):
+        return False
+    return a[2] == b[2] or (a[2] >= piece_bytes + 64 and b[2] >= piece_bytes + 64)
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def main():
@@ -69,61 +96,94 @@ def main():
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    prog = programs.ring_allreduce(P)
+    TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}
+    ESZ = {"f32": 4, "bf16": 2, "i32": 4}
 
-    def inputs(S):
+    def device_inputs(kind, n, ranks, seed):
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        if kind == "i32":
+            return [torch.randint(-2**31, 2**31 - 1, (n,), generator=g, device=dev, dtype=torch.int32)
+                    for _ in range(ranks)]
+        return [torch.randn(n, generator=g, device=dev).to(TORCH[kind]) for _ in range(ranks)]
+
+    def ring_inputs(S):
         N = S // 4
         outs = [torch.empty(N, dtype=torch.float32, device=dev) for _ in range(P)]
-        if S >= (32 << 20):  # timing-only points: seeded N(0,1) drawn on the device
-            g = torch.Generator(device=dev)
-            g.manual_seed(2026 * 1000 + S // (1 << 20))
-            return N, [torch.randn(N, generator=g, device=dev) for _ in range(P)], outs
+        if S >= DEVICE_INPUT_BYTES:  # seeded N(0,1) drawn on the device
+            return N, device_inputs("f32", N, P, 2026 * 1000 + S // (1 << 20)), outs
         xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=S)
         return N, [torch.from_numpy(x).to(dev) for x in xs], outs
 
-    def tune(N):
+    def tune(prog, N, dtype="f32", protocols=15):
         desc = prog.to_desc()
-        base = PlanConfig(dtype="f32", max_count=N).to_c()
+        base = PlanConfig(dtype=dtype, max_count=N).to_c()
         arrs = [(capi.C.c_int32 * len(v))(*v) for v in (TUNE_FACTORS, TUNE_THREADS, TUNE_SLICES)]
         space = capi.ccl_tune_space(capi.C.cast(arrs[0], capi.C.POINTER(capi.C.c_int32)), len(TUNE_FACTORS),
                                     capi.C.cast(arrs[1], capi.C.POINTER(capi.C.c_int32)), len(TUNE_THREADS),
                                     capi.C.cast(arrs[2], capi.C.POINTER(capi.C.c_int32)), len(TUNE_SLICES),
-                                    1, 3, 10, 3)
+                                    1, 3, 10, protocols)
         best, rep = capi.ccl_tune([desc], N, base, space, stream.cuda_stream)
         return (best.parallel_factor, best.nthreads, best.slice_bytes, best.protocol), rep.evaluations
 
-    def make_plan(N, k, nt, sl, proto=0):
-        return Plan(prog, k, PlanConfig(dtype="f32", max_count=N, nthreads=nt, slice_bytes=sl,
-                                        protocol="ll" if proto else "simple"))
+    def make_plan(prog, N, k, nt, sl, proto=0, dtype="f32", **kw):
+        return Plan(prog, k, PlanConfig(dtype=dtype, max_count=N, nthreads=nt, slice_bytes=sl,
+                                        protocol=PROTOCOLS[proto][0], transport=PROTOCOLS[proto][1],
+                                        streaming=PROTOCOLS[proto][2], **kw))
 
-    def time_plan(plan, N, ins, outs, iters, warmup=3):
+    def time_launches(fn, iters, warmup=3):
+        """Mean seconds per call of fn() (which enqueues work on `stream`)."""
         for _ in range(warmup):
-            plan.execute(ins, outs, N, stream)
+            fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(iters):
-            plan.execute(ins, outs, N, stream)
+            fn()
         e1.record(stream)
         torch.cuda.synchronize()
-        plan.status()
         return e0.elapsed_time(e1) * 1e-3 / iters
 
-    def busbw(S, t):
-        return S / t * 2 * (P - 1) / P / 1e9
+    def busbw_ar(S, t, n=P):
+        return S / t * 2 * (n - 1) / n / 1e9
+
+    def stats(plan, N, t):
+        return {"us": round(t * 1e6, 2), "plan_bytes": plan.bytes(N),
+                "hbm_frac": round(plan.bytes(N) / t / 1e9 / HBM_PEAK_GBS, 4)}
+
+    def release(*objs):
+        for o in objs:
+            if hasattr(o, "destroy"):
+                o.destroy()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    def fitting(makers, ks=(8, 4, 2, 1)):
+        """The largest parallelization factor at which every maker(k) builds a plan (all
+        workgroups co-resident), with those plans; compared variants share it."""
+        for k in ks:
+            built = []
+            try:
+                for m in makers:
+                    built.append(m(k))
+                return k, built
+            except capi.CCLError:
+                release(*built)
+        raise RuntimeError("no parallelization factor fits")
 
     # ---- headline: tune, then warmup + timed steps ----------------------------------
+    prog = programs.ring_allreduce(P)
     S = HEADLINE_BYTES
-    N, ins, outs = inputs(S)
+    N, ins, outs = ring_inputs(S)
     t0 = time.perf_counter()
     if args.fixed:
         cfg = tuple(int(v) for v in args.fixed.split(","))
         cfg = cfg + (0,) * (4 - len(cfg))
         tune_evals = 0
     else:
-        cfg, tune_evals = tune(N)
+        cfg, tune_evals = tune(prog, N)
     tune_s = time.perf_counter() - t0
-    plan = make_plan(N, *cfg)
+    plan = make_plan(prog, N, *cfg)
     info = plan.info()
     plan_bytes = plan.bytes(N)
     for _ in range(args.warmup):
@@ -137,6 +197,14 @@ def main():
     torch.cuda.synchronize()
     plan.status()
     t_step = e0.elapsed_time(e1) * 1e-3 / args.steps
+    # per-launch spread from a separate, shorter pass (an event between launches costs time)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(51)]
+    ev[0].record(stream)
+    for i in range(50):
+        plan.execute(ins, outs, N, stream)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(50))
     # spot check of the timed output against the chain-order oracle
     from oracle import schedule_order as O2
     xs = [t.cpu().numpy() for t in ins]
@@ -149,12 +217,13 @@ def main():
     if os.path.exists(tpath):
         with open(tpath) as fh:
             tj = json.load(fh)
-        if tj.get("source_digest") == source_digest() and tuple(tj.get("config", [])) == tuple(cfg):
+        if tj.get("source_digest") == source_digest() and same_launch(tj.get("config", []), cfg, S // P // cfg[0]):
             traffic = tj.get("bytes_per_launch")
+    floor_bytes = 2 * P * S  # every rank reads its input once and writes its output once
 
     out = {
         "metric": "AllReduce busbw GB/s (8 virtual ranks, 1 GPU) and % of HBM peak",
-        "value": round(busbw(S, t_step), 2),
+        "value": round(busbw_ar(S, t_step), 2),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -169,56 +238,46 @@ def main():
                                "(top of the 32 KiB-3 MiB sweep), one kernel launch per collective",
                    "ranks": P, "bytes_per_rank": S, "elements_per_rank": N,
                    "parallel_factor": cfg[0], "nthreads": cfg[1], "slice_bytes": cfg[2],
-                   "protocol": "ll" if cfg[3] else "simple",
+                   "protocol": PROTOCOLS[cfg[3]][0], "transport": PROTOCOLS[cfg[3]][1],
+                   "streaming": PROTOCOLS[cfg[3]][2],
+                   "xcd_local_stores": bool(info["xcd_local"]),
                    "scheduler": "hpds", "wg_alloc": "state", "workgroups": info["num_workgroups"],
                    "tuner_evaluations": tune_evals, "tune_seconds": round(tune_s, 2),
                    "compile_ms": round(sum(info["compile_ms"]), 3), "parallelism": "virtual ranks, 1 GPU"},
         "hbm_frac": round(achieved / HBM_PEAK_GBS, 4),
+        "floor_frac": round(floor_bytes / t_step / 1e9 / HBM_PEAK_GBS, 4),
         "plan_bytes_per_launch": plan_bytes,
+        "us_per_launch": {"mean": round(t_step * 1e6, 2), "min_event_bracketed": round(per[0], 2),
+                          "median_event_bracketed": round(statistics.median(per), 2)},
         "oracle_spot_check": ok,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
-    plan.destroy()
+
+    progress(f"headline {t_step * 1e6:.2f} us per launch, config {cfg}")
+    if not args.no_extras:
+        # cold: rotate over buffer sets whose total exceeds the 256 MiB Infinity Cache twice
+        nsets = max(2, (512 << 20) // (2 * P * S) + 1)
+        sets = [(ins, outs)] + [ring_inputs(S)[1:] for _ in range(nsets - 1)]
+        rot = [0]
+
+        def cold_call():
+            i_, o_ = sets[rot[0] % nsets]
+            rot[0] += 1
+            plan.execute(i_, o_, N, stream)
+        t_cold = time_launches(cold_call, 4 * nsets, warmup=nsets)
+        out["cold"] = {"buffer_sets": nsets, "us": round(t_cold * 1e6, 2), "busbw": round(busbw_ar(S, t_cold), 2),
+                       "hbm_frac": round(plan_bytes / t_cold / 1e9 / HBM_PEAK_GBS, 4)}
+        del sets
+    release(plan)
     del ins, outs
 
     if not args.no_extras:
-        # ---- rest of the sweep and the large sizes, each tuned ----------------------
-        sweep = []
-        for Si in SWEEP + LARGE:
-            Ni, ii, oo = inputs(Si)
-            c, _ = tune(Ni)
-            p = make_plan(Ni, *c)
-            t = time_plan(p, Ni, ii, oo, 20 if Si >= (32 << 20) else 50)
-            sweep.append({"bytes_per_rank": Si, "k": c[0], "nthreads": c[1], "slice_bytes": c[2],
-                          "protocol": "ll" if c[3] else "simple",
-                          "us": round(t * 1e6, 2), "busbw": round(busbw(Si, t), 2),
-                          "hbm_frac": round(p.bytes(Ni) / t / 1e9 / HBM_PEAK_GBS, 4)})
-            # tuned vs fixed configurations at the same size
-            if Si in (1 << 20, 3 << 20, 32 << 20, 128 << 20):
-                for name, (k, nt, sl) in (("fixed_k1_nt256_slice128k", (1, 256, min(128 << 10, Si // P))),
-                                          ("fixed_k8_nt512_slice256k", (8, 512, 256 << 10))):
-                    pf = make_plan(Ni, k, nt, sl)
-                    tf = time_plan(pf, Ni, ii, oo, 10 if Si >= (32 << 20) else 30)
-                    sweep[-1][name + "_busbw"] = round(busbw(Si, tf), 2)
-                    pf.destroy()
-            p.destroy()
-            del ii, oo
-            torch.cuda.empty_cache()
-        out["sweep"] = sweep
-        # ---- practical streaming ceiling: a plain copy kernel ------------------------
-        nb = 1 << 28
-        a = torch.empty(nb, dtype=torch.uint8, device=dev)
-        b = torch.empty(nb, dtype=torch.uint8, device=dev)
-        for _ in range(3):
-            capi.ccl_copy_probe(b.data_ptr(), a.data_ptr(), nb, 1024, 512, stream.cuda_stream)
-        e0.record(stream)
-        for _ in range(10):
-            capi.ccl_copy_probe(b.data_ptr(), a.data_ptr(), nb, 1024, 512, stream.cuda_stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        tc = e0.elapsed_time(e1) * 1e-3 / 10
-        out["copy_probe_GBs"] = round(2 * nb / tc / 1e9, 1)
+        out.update(extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inputs, device_inputs,
+                          tune, make_plan, time_launches, busbw_ar, stats, release, fitting))
+        copy = out.get("copy_probe_GBs")
+        if copy:
+            out["copy_frac"] = round(achieved / copy, 4)
 
     if args.copy_probe:
         nb = 1 << 28
@@ -226,7 +285,7 @@ def main():
         b = torch.empty(nb, dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
         for _ in range(args.copy_probe):
-            capi.ccl_copy_probe(b.data_ptr(), a.data_ptr(), nb, 1024, 512, stream.cuda_stream)
+            capi.ccl_copy_probe(b.data_ptr(), a.data_ptr(), nb, 256, 256, stream.cuda_stream)
         torch.cuda.synchronize()
         out["copy_probe_bytes_per_launch"] = 2 * nb
 
@@ -234,6 +293,212 @@ def main():
     out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     out["source_digest"] = source_digest()
     print(json.dumps(out), flush=True)
+
+
+def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inputs, device_inputs, tune, make_plan,
+           time_launches, busbw_ar, stats, release, fitting):
+    res = {}
+    prog = programs.ring_allreduce(P)
+
+    # ---- the rest of the 8-rank sweep and the large sizes, each tuned ---------------
+    sweep = []
+    for S in SWEEP + LARGE:
+        N, ii, oo = ring_inputs(S)
+        c, _ = tune(prog, N)
+        p = make_plan(prog, N, *c)
+        t = time_launches(lambda: p.execute(ii, oo, N, stream), 20 if S >= DEVICE_INPUT_BYTES else 50)
+        row = {"bytes_per_rank": S, "k": c[0], "nthreads": c[1], "slice_bytes": c[2],
+               "protocol": PROTOCOLS[c[3]][0], "transport": PROTOCOLS[c[3]][1], "streaming": PROTOCOLS[c[3]][2],
+               "busbw": round(busbw_ar(S, t), 2), **stats(p, N, t)}
+        if S in (1 << 20, 3 << 20, 32 << 20, 128 << 20):  # tuned versus fixed configurations
+            for name, (k, nt, sl) in (("fixed_k1_nt256_slice128k", (1, 256, min(128 << 10, S // P))),
+                                      ("fixed_k8_nt512_slice256k", (8, 512, 256 << 10))):
+                pf = make_plan(prog, N, k, nt, sl)
+                tf = time_launches(lambda: pf.execute(ii, oo, N, stream), 10 if S >= DEVICE_INPUT_BYTES else 30)
+                row[name + "_busbw"] = round(busbw_ar(S, tf), 2)
+                release(pf)
+        sweep.append(row)
+        progress(f"ring AR 8 ranks {S >> 10} KiB: {row['us']} us")
+        release(p)
+        del ii, oo
+    res["sweep"] = sweep
+
+    # ---- 4 ranks, 1 MiB integer-valued fp32, 4 chunks, one channel, one slice -------
+    N = 262144
+    xs = W.make_inputs("int_f32", N, 4, W.CFG_RING_AR_4R_INT, size_bytes=N * 4)
+    ii = [torch.from_numpy(x).to(dev) for x in xs]
+    oo = [torch.empty(N, device=dev) for _ in range(4)]
+    p4 = make_plan(programs.ring_allreduce(4), N, 1, 512, N * 4)
+    t = time_launches(lambda: p4.execute(ii, oo, N, stream), 100)
+    exact = bool(np.array_equal(oo[0].cpu().numpy(), np.sum(np.stack(xs).astype(np.float64), 0).astype(np.float32)))
+    res["ring_ar_4r_1mib_int"] = {"busbw": round(busbw_ar(N * 4, t, 4), 2), "exact": exact, **stats(p4, N, t)}
+    release(p4)
+    del ii, oo
+
+    # ---- 16 ranks (2 x 8) bf16 hierarchical AllReduce: fused vs three launches -----
+    G, L = 2, 8
+    hier = []
+    fused_prog = programs.hierarchical_allreduce(G, L)
+    stages = (programs.hier_stage_reducescatter_intra(G, L), programs.hier_stage_allreduce_inter(G, L),
+              programs.hier_stage_allgather_intra(G, L))
+    for S in (1 << 20, 16 << 20, 64 << 20, 256 << 20):
+        N = S // 2
+        ii = device_inputs("bf16", N, G * L, 3000 + S // (1 << 20))
+        oo = [torch.empty(N, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
+        cf, _ = tune(fused_prog, N, "bf16")
+        pf = make_plan(fused_prog, N, *cf, dtype="bf16")
+        tf = time_launches(lambda: pf.execute(ii, oo, N, stream), 10)
+        sh = N // L
+        mid1 = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
+        mid2 = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
+        c1, _ = tune(stages[0], N, "bf16")
+        c2, _ = tune(stages[1], sh, "bf16")
+        c3, _ = tune(stages[2], sh, "bf16")
+        s1 = make_plan(stages[0], N, *c1, dtype="bf16")
+        s2 = make_plan(stages[1], sh, *c2, dtype="bf16")
+        s3 = make_plan(stages[2], sh, *c3, dtype="bf16")
+
+        def three():
+            s1.execute(ii, mid1, N, stream)
+            s2.execute(mid1, mid2, sh, stream)
+            s3.execute(mid2, oo, sh, stream)
+        t3 = time_launches(three, 10)
+        hier.append({"bytes_per_rank": S, "fused_config": list(cf), "stage_configs": [list(c1), list(c2), list(c3)],
+                     "fused_us": round(tf * 1e6, 2), "three_launch_us": round(t3 * 1e6, 2),
+                     "fused_busbw": round(busbw_ar(S, tf, G * L), 2), "three_launch_busbw": round(busbw_ar(S, t3, G * L), 2),
+                     "speedup": round(t3 / tf, 3), "fused_hbm_frac": stats(pf, N, tf)["hbm_frac"],
+                     "fused_workgroups": pf.info()["num_workgroups"]})
+        release(pf, s1, s2, s3)
+        del ii, oo, mid1, mid2
+    res["hier_ar_16r_bf16"] = hier
+    progress("hierarchical AllReduce done")
+
+    # ---- 32 ranks (4 x 8) int32 AllToAll: two-phase vs direct ----------------------
+    G, L = 4, 8
+    Pa = G * L
+    a2a = []
+    for S in (1 << 20, 4 << 20, 16 << 20, 64 << 20):
+        N = S // 4
+        ii = device_inputs("i32", N, Pa, 4000 + S // (1 << 20))
+        oo = [torch.empty(N, dtype=torch.int32, device=dev) for _ in range(Pa)]
+        row = {"bytes_per_rank": S}
+        for name, pr in (("two_phase", programs.two_phase_alltoall(G, L)), ("direct", programs.direct_alltoall(Pa))):
+            best = None
+            for k, nt in ((1, 256), (2, 256), (4, 256)):
+                try:
+                    pl = make_plan(pr, N, k, nt, 256 << 10, 2, dtype="i32")
+                except capi.CCLError:
+                    continue  # more workgroups than fit at once
+                t = time_launches(lambda: pl.execute(ii, oo, N, stream), 10)
+                if best is None or t < best[0]:
+                    best = (t, k, pl.info()["num_workgroups"], stats(pl, N, t)["hbm_frac"])
+                release(pl)
+            if best:
+                t, k, nwg, hf = best
+                row[name] = {"us": round(t * 1e6, 2), "k": k, "workgroups": nwg, "hbm_frac": hf,
+                             "busbw": round(S / t * (Pa - 1) / Pa / 1e9, 2)}
+        a2a.append(row)
+        del ii, oo
+        release()
+    res["alltoall_32r_int32"] = a2a
+    progress("AllToAll done")
+
+    # ---- 24 ranks (3 x 8): AllToNext split / unsplit, HPDS+state vs RR+connection ---
+    G, L = 3, 8
+    Pn = G * L
+    a2n = []
+    for S in (16 << 20, 64 << 20, 128 << 20):
+        N = S // 4
+        ii = device_inputs("f32", N, Pn, 5000 + S // (1 << 20))
+        oo = [torch.empty(N, device=dev) for _ in range(Pn)]
+        row = {"bytes_per_rank": S}
+        for split in (True, False):
+            modes = (("hpds", "state"), ("rr", "connection"))
+            k, pls = fitting([lambda k, sc=sc, al=al: make_plan(programs.alltonext(G, L, split=split), N, k, 512,
+                                                                  256 << 10, 2, scheduler=sc, wg_alloc=al)
+                              for sc, al in modes])
+            for (sched, alloc), pl in zip(modes, pls):
+                t = time_launches(lambda: pl.execute(ii, oo, N, stream), 10)
+                row[f"{'split' if split else 'unsplit'}_{sched}_{alloc}"] = {
+                    "us": round(t * 1e6, 2), "algbw": round(S / t / 1e9, 2), "k": k,
+                    "workgroups": pl.info()["num_workgroups"], "hbm_frac": stats(pl, N, t)["hbm_frac"]}
+            release(*pls)
+        a2n.append(row)
+        del ii, oo
+        release()
+    res["alltonext_24r"] = a2n
+    progress("AllToNext done")
+
+    # AllGather / ReduceScatter on the same 24 ranks, 128 MiB (the larger buffer)
+    n_big = Pn * ((32 << 20) // Pn)  # 33,554,424 fp32
+    agrs = {}
+    for coll in ("allgather", "reducescatter"):
+        for variant in ("ring", "2d"):
+            if coll == "allgather":
+                pr = programs.ring_allgather(Pn) if variant == "ring" else programs.allgather_2d(G, L)
+                count, nout = n_big // Pn, n_big
+            else:
+                pr = programs.ring_reducescatter(Pn) if variant == "ring" else programs.reducescatter_2d(G, L)
+                count, nout = n_big, n_big // Pn
+            ii = device_inputs("f32", count, Pn, 6000 + len(coll))
+            oo = [torch.empty(nout, device=dev) for _ in range(Pn)]
+            modes = (("hpds", "state"), ("rr", "connection"))
+            k, pls = fitting([lambda k, sc=sc, al=al: make_plan(pr, count, k, 512, 256 << 10, 2, scheduler=sc,
+                                                                  wg_alloc=al) for sc, al in modes],
+                             ks=(32, 16, 8, 4, 2, 1))
+            for (sched, alloc), pl in zip(modes, pls):
+                t = time_launches(lambda: pl.execute(ii, oo, count, stream), 5)
+                Sb = n_big * 4
+                agrs[f"{coll}_{variant}_{sched}_{alloc}"] = {
+                    "us": round(t * 1e6, 2), "busbw": round(Sb / t * (Pn - 1) / Pn / 1e9, 2), "k": k,
+                    "workgroups": pl.info()["num_workgroups"], "hbm_frac": stats(pl, count, t)["hbm_frac"]}
+            release(*pls)
+            del ii, oo
+            release()
+    res["allgather_reducescatter_24r_128mib"] = agrs
+    progress("AllGather / ReduceScatter done")
+
+    # ---- workgroup idle fraction from the device trace (one traced launch) ----------
+    def idle(pr, N, dtype, k, nt, sl, proto, ii, oo, **kw):
+        k, (pl,) = fitting([lambda kk: make_plan(pr, N, kk, nt, sl, proto, dtype=dtype, trace=True, **kw)],
+                           ks=[x for x in (k, 8, 4, 2, 1) if x <= k])
+        for _ in range(3):
+            pl.execute(ii, oo, N, stream)
+        torch.cuda.synchronize()
+        recs = [r for r in pl.trace() if r[3] > 0]
+        t0 = min(r[0] for r in recs)
+        span = max(r[1] for r in recs) - t0
+        # waiting on flags, plus the time a workgroup is not yet started or already done
+        fr = [(r[2] + (r[0] - t0) + (t0 + span - r[1])) / span for r in recs]
+        out = {"workgroups": len(recs), "k": k, "mean": round(float(np.mean(fr)), 4),
+               "max": round(float(np.max(fr)), 4)}
+        release(pl)
+        return out
+
+    N, ii, oo = ring_inputs(HEADLINE_BYTES)
+    c, _ = tune(prog, N)
+    idle_rows = {"ring_ar_8r_3mib_tuned": idle(prog, N, "f32", *c, ii, oo)}
+    del ii, oo
+    N = (64 << 20) // 4
+    ii = device_inputs("f32", N, Pn, 5064)
+    oo = [torch.empty(N, device=dev) for _ in range(Pn)]
+    for sched, alloc in (("hpds", "state"), ("rr", "connection")):
+        idle_rows[f"alltonext_24r_64mib_split_{sched}_{alloc}"] = idle(
+            programs.alltonext(G, L, split=True), N, "f32", 8, 512, 256 << 10, 2, ii, oo, scheduler=sched,
+            wg_alloc=alloc)
+    del ii, oo
+    release()
+    res["wg_idle_fraction"] = idle_rows
+
+    # ---- practical streaming ceiling: a plain copy kernel, 1 GiB (beyond every cache) --
+    nb = 1 << 30
+    a = torch.empty(nb, dtype=torch.uint8, device=dev)
+    b = torch.empty(nb, dtype=torch.uint8, device=dev)
+    tc = time_launches(lambda: capi.ccl_copy_probe(b.data_ptr(), a.data_ptr(), nb, 256, 256, stream.cuda_stream), 10)
+    res["copy_probe_GBs"] = round(2 * nb / tc / 1e9, 1)
+    del a, b
+    release()
+    return res
 
 
 def cpu_baseline(budget_s: float):
@@ -259,10 +524,17 @@ def cpu_baseline(budget_s: float):
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": round(S / t * 2 * (P - 1) / P / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
             "sample": f"schedule-order oracle, ring AllReduce 8 ranks x 3 MiB fp32, {reps} repetitions "
-                      f"({t * 1e3:.1f} ms each); numpy elementwise adds run on one thread; host has {cores} cores"}
+                      f"({t * 1e3:.1f} ms each); numpy elementwise adds run on one thread; host has {cores} "
+                      f"cores available ({cpu})"}
 
 
 if __name__ == "__main__":

@@ -36,6 +36,7 @@ CCL_WG_CONNECTION, CCL_WG_STATE = 0, 1
 CCL_FLAG_TRACE, CCL_FLAG_HOST_ONLY, CCL_FLAG_NO_FUSION, CCL_FLAG_NO_VERIFY, CCL_FLAG_LL = 0x1, 0x2, 0x4, 0x8, 0x10
 CCL_FLAG_COHERENT_ONLY = 0x20
 CCL_FLAG_DIRECT = 0x40
+CCL_FLAG_STREAMING = 0x80
 CCL_I_RECV, CCL_I_SRCB, CCL_I_DSTA, CCL_I_SEND, CCL_I_LOCAL_IN = 0x1, 0x2, 0x4, 0x8, 0x10
 
 

@@ -311,7 +311,8 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
       HIP_TRY(hipStreamWaitEvent(s, plan->last, 0));
     }
     std::string err;
-    int rc = launch_executor(A, hp.cfg.dtype, plan->xcd_local, int(hp.dwg.size()), hp.cfg.nthreads, stream, &err);
+    int rc = launch_executor(A, hp.cfg.dtype, plan->xcd_local, (hp.cfg.flags & CCL_FLAG_STREAMING) != 0,
+                             int(hp.dwg.size()), hp.cfg.nthreads, stream, &err);
     if (rc) fail(rc, err);
     plan->epoch = epoch;
     plan->last_stream = s;

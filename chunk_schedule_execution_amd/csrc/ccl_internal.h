@@ -124,8 +124,9 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims);
 // executor.hip
 // xcd_local: the kernel variant that writes slots and their flags with plain stores
 // (every transfer stays on one XCD; each workgroup checks its placement first).
-int launch_executor(const ExecArgs& args, int dtype, bool xcd_local, int nwg, int nthreads, void* stream,
-                    std::string* err);
+// streaming: the variant whose local-buffer loads and stores are non-temporal.
+int launch_executor(const ExecArgs& args, int dtype, bool xcd_local, bool streaming, int nwg, int nthreads,
+                    void* stream, std::string* err);
 int executor_max_blocks_per_cu(int dtype, int nthreads, int* blocks, std::string* err);
 // Records the XCD of each of `nwg` single-wave workgroups into out[0..nwg) (synchronous use).
 int launch_xcd_probe(unsigned* out, int nwg, std::string* err);

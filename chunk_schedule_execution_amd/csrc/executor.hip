@@ -89,6 +89,7 @@ typedef unsigned v4u __attribute__((ext_vector_type(4)));
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 data format
 constexpr int kCpolNone = 0;
 constexpr int kCpolSc1 = 16;  // agent-scope coherent
+constexpr int kCpolNt = 2;    // non-temporal: streamed lines are not kept
 
 // Slice pointers and sizes are wave-uniform; readfirstlane puts them in scalar
 // registers so the descriptor is scalar (no per-lane waterfall around each access).
@@ -140,7 +141,7 @@ __device__ __forceinline__ long long wait_slot_flag(unsigned long long* p, unsig
 // of the first pass is loaded before that wait so its latency hides behind it.
 // Returns the ticks waited, or -1 if the wait gave up (the whole workgroup returns
 // -1 together).
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL>
+template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL, bool NT>
 __device__ __forceinline__ long long run_slice(const unsigned char* pa, const unsigned char* pb,
                                                          unsigned char* pd, unsigned char* pt, int n, int tid,
                                                          int nthr, unsigned long long* wflag,
@@ -151,7 +152,8 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
   typedef Arith<DT> Ar;
   constexpr int esz = Ar::esz;
   constexpr int V = 16 / esz;
-  constexpr int CA = RECV ? kCpolSc1 : kCpolNone;  // first operand: slot or local buffer
+  constexpr int CL = NT ? kCpolNt : kCpolNone;      // local-buffer loads and stores
+  constexpr int CA = RECV ? kCpolSc1 : CL;          // first operand: slot or local buffer
   constexpr int CT = XL ? kCpolNone : kCpolSc1;     // outgoing slot: XCD-local L2, or agent-coherent
   const int bytes = n * esz;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(pa, bytes);
@@ -166,8 +168,8 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
   auto scalar = [&](int e) {
     const int o = e * esz;
     uint32_t v = ld_elem<esz, CA>(rA, o);
-    if (SRCB) v = Ar::add(typename Ar::S(v), typename Ar::S(ld_elem<esz, kCpolNone>(rB, o)));
-    if (DSTA) st_elem<esz, kCpolNone>(rD, o, v);
+    if (SRCB) v = Ar::add(typename Ar::S(v), typename Ar::S(ld_elem<esz, CL>(rB, o)));
+    if (DSTA) st_elem<esz, CL>(rD, o, v);
     if (SEND) st_elem<esz, CT>(rT, o, v);
   };
   int head = 0, nvec = 0, base = 0;
@@ -188,7 +190,7 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
   if (SRCB && RECV && same) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (tid + u * nthr < nvec) pf[u] = to_u4(ld16<kCpolNone>(rB, base + 16 * (tid + u * nthr)));
+      if (tid + u * nthr < nvec) pf[u] = to_u4(ld16<CL>(rB, base + 16 * (tid + u * nthr)));
   }
   long long waited = 0;
   if (RECV) {
@@ -216,7 +218,7 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
           if (RECV && i == tid)
             bb[u] = pf[u];
           else if (i + u * nthr < nvec)
-            bb[u] = to_u4(ld16<kCpolNone>(rB, base + 16 * (i + u * nthr)));
+            bb[u] = to_u4(ld16<CL>(rB, base + 16 * (i + u * nthr)));
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) a[u] = Ar::add4(a[u], bb[u]);
@@ -225,7 +227,7 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
       for (int u = 0; u < U; ++u) {
         if (i + u * nthr >= nvec) continue;
         const int o = base + 16 * (i + u * nthr);
-        if (DSTA) st16<kCpolNone>(rD, o, to_v4(a[u]));
+        if (DSTA) st16<CL>(rD, o, to_v4(a[u]));
         if (SEND) st16<CT>(rT, o, to_v4(a[u]));
       }
     }
@@ -238,18 +240,18 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
 
 // bf16 widening adds need more registers: its slice code stays an out-of-line call so
 // the register allocator sees one variant at a time (no spills); fp32 / int32 inline.
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL>
+template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL, bool NT>
 __device__ __attribute__((noinline)) long long run_slice_call(const unsigned char* pa, const unsigned char* pb,
                                                               unsigned char* pd, unsigned char* pt, int n, int tid,
                                                               int nthr, unsigned long long* wflag,
                                                               unsigned long long wtarget, unsigned int* err,
                                                               unsigned long long* abort_word, unsigned long long epoch,
                                                               long long timeout_ticks, int instr) {
-  return run_slice<DT, RECV, SRCB, DSTA, SEND, XL>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, err, abort_word,
-                                                   epoch, timeout_ticks, instr);
+  return run_slice<DT, RECV, SRCB, DSTA, SEND, XL, NT>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, err, abort_word,
+                                                       epoch, timeout_ticks, instr);
 }
 
-template <int DT, bool XL>
+template <int DT, bool XL, bool NT>
 __device__ __forceinline__ long long dispatch_slice(uint32_t op, const unsigned char* pa, const unsigned char* pb,
                                                     unsigned char* pd, unsigned char* pt, int n, int tid, int nthr,
                                                     unsigned long long* wflag, unsigned long long wtarget,
@@ -257,10 +259,10 @@ __device__ __forceinline__ long long dispatch_slice(uint32_t op, const unsigned 
 #define CCL_CASE(R, B, D, T)                                                                                     \
   case ((R) ? OPB_RECV : 0u) | ((B) ? OPB_SRCB : 0u) | ((D) ? OPB_DSTA : 0u) | ((T) ? OPB_SEND : 0u):            \
     return (DT == CCL_BF16)                                                                                      \
-               ? run_slice_call<DT, R, B, D, T, XL>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err,          \
-                                                    A.abort_word, A.epoch, A.timeout_ticks, instr)                 \
-               : run_slice<DT, R, B, D, T, XL>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err, A.abort_word,   \
-                                               A.epoch, A.timeout_ticks, instr);
+               ? run_slice_call<DT, R, B, D, T, XL, NT>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err,      \
+                                                        A.abort_word, A.epoch, A.timeout_ticks, instr)             \
+               : run_slice<DT, R, B, D, T, XL, NT>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err,           \
+                                                   A.abort_word, A.epoch, A.timeout_ticks, instr);
   switch (op & 15u) {
     CCL_CASE(false, false, true, false)
     CCL_CASE(false, false, false, true)
@@ -595,7 +597,8 @@ __device__ __forceinline__ int64_t uni64(int64_t v) {
 
 // XL: slots and their flags are written with plain stores, valid because the host
 // laid out the grid so that every transfer stays between workgroups of one XCD.
-template <int DT, bool XL>
+// NT: local-buffer loads and local stores carry the non-temporal hint (simple protocol).
+template <int DT, bool XL, bool NT>
 __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
   constexpr int esz = Arith<DT>::esz;
   // Set once by any thread that gives up (watchdog, or another workgroup's abort) and
@@ -682,7 +685,7 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
           const int n = int((len - o < se) ? (len - o) : se);
           const int64_t bo = o * esz;
           const long long waited =
-              dispatch_slice<DT, XL>(op, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr,
+              dispatch_slice<DT, XL, NT>(op, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr,
                                  pt ? pt + bo : nullptr, n, tid, nthr, (op & OPB_RECV) ? &A.xflags[xin] : nullptr,
                                  E + (unsigned long long)(s + 1), A, gi);
           if (waited < 0) return;  // the wait gave up: uniform across the workgroup
@@ -708,17 +711,20 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
   }
 }
 
-// Plain streaming copy: the HBM ceiling a single kernel reaches on this part.
-__global__ __launch_bounds__(1024) void copy_probe_kernel(uint4* __restrict__ dst, const uint4* __restrict__ src,
+// Plain streaming copy: the HBM ceiling a single kernel reaches on this part. Four
+// 16-byte vectors per thread in flight, non-temporal loads and stores (the lines are
+// not reused), grid-stride; one workgroup per CU streams best here.
+__global__ __launch_bounds__(1024) void copy_probe_kernel(v4u* __restrict__ dst, const v4u* __restrict__ src,
                                                           int64_t nvec) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
   int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   for (; i + 3 * stride < nvec; i += 4 * stride) {
-    uint4 a0 = src[i], a1 = src[i + stride], a2 = src[i + 2 * stride], a3 = src[i + 3 * stride];
-    dst[i] = a0;
-    dst[i + stride] = a1;
-    dst[i + 2 * stride] = a2;
-    dst[i + 3 * stride] = a3;
+    v4u a0 = __builtin_nontemporal_load(src + i), a1 = __builtin_nontemporal_load(src + i + stride);
+    v4u a2 = __builtin_nontemporal_load(src + i + 2 * stride), a3 = __builtin_nontemporal_load(src + i + 3 * stride);
+    __builtin_nontemporal_store(a0, dst + i);
+    __builtin_nontemporal_store(a1, dst + i + stride);
+    __builtin_nontemporal_store(a2, dst + i + 2 * stride);
+    __builtin_nontemporal_store(a3, dst + i + 3 * stride);
   }
   for (; i < nvec; i += stride) dst[i] = src[i];
 }
@@ -729,23 +735,22 @@ __global__ void xcd_probe_kernel(unsigned* out) {
 
 }  // namespace
 
-int launch_executor(const ExecArgs& args, int dtype, bool xcd_local, int nwg, int nthreads, void* stream,
-                    std::string* err) {
+template <int DT>
+static void launch_dt(const ExecArgs& args, bool xl, bool nt, dim3 g, dim3 b, hipStream_t s) {
+  if (xl && nt) hipLaunchKernelGGL((executor_kernel<DT, true, true>), g, b, 0, s, args);
+  else if (xl) hipLaunchKernelGGL((executor_kernel<DT, true, false>), g, b, 0, s, args);
+  else if (nt) hipLaunchKernelGGL((executor_kernel<DT, false, true>), g, b, 0, s, args);
+  else hipLaunchKernelGGL((executor_kernel<DT, false, false>), g, b, 0, s, args);
+}
+
+int launch_executor(const ExecArgs& args, int dtype, bool xcd_local, bool streaming, int nwg, int nthreads,
+                    void* stream, std::string* err) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 g(nwg), b(nthreads);
   switch (dtype) {
-    case CCL_F32:
-      if (xcd_local) hipLaunchKernelGGL((executor_kernel<CCL_F32, true>), g, b, 0, s, args);
-      else hipLaunchKernelGGL((executor_kernel<CCL_F32, false>), g, b, 0, s, args);
-      break;
-    case CCL_BF16:
-      if (xcd_local) hipLaunchKernelGGL((executor_kernel<CCL_BF16, true>), g, b, 0, s, args);
-      else hipLaunchKernelGGL((executor_kernel<CCL_BF16, false>), g, b, 0, s, args);
-      break;
-    case CCL_I32:
-      if (xcd_local) hipLaunchKernelGGL((executor_kernel<CCL_I32, true>), g, b, 0, s, args);
-      else hipLaunchKernelGGL((executor_kernel<CCL_I32, false>), g, b, 0, s, args);
-      break;
+    case CCL_F32: launch_dt<CCL_F32>(args, xcd_local, streaming, g, b, s); break;
+    case CCL_BF16: launch_dt<CCL_BF16>(args, xcd_local, streaming, g, b, s); break;
+    case CCL_I32: launch_dt<CCL_I32>(args, xcd_local, streaming, g, b, s); break;
     default: *err = "dtype"; return CCL_ERR_UNSUPPORTED;
   }
   hipError_t e = hipGetLastError();
@@ -756,38 +761,42 @@ int launch_executor(const ExecArgs& args, int dtype, bool xcd_local, int nwg, in
   return CCL_OK;
 }
 
-// Both store variants of a dtype: the smaller occupancy bounds the plan.
+template <int DT>
+static hipError_t min_blocks(int nthreads, int* blocks) {
+  int b[4] = {0, 0, 0, 0};
+  hipError_t e[4] = {hipOccupancyMaxActiveBlocksPerMultiprocessor(&b[0], executor_kernel<DT, false, false>, nthreads, 0),
+                     hipOccupancyMaxActiveBlocksPerMultiprocessor(&b[1], executor_kernel<DT, false, true>, nthreads, 0),
+                     hipOccupancyMaxActiveBlocksPerMultiprocessor(&b[2], executor_kernel<DT, true, false>, nthreads, 0),
+                     hipOccupancyMaxActiveBlocksPerMultiprocessor(&b[3], executor_kernel<DT, true, true>, nthreads, 0)};
+  int m = b[0];
+  for (int i = 0; i < 4; ++i) {
+    if (e[i] != hipSuccess) return e[i];
+    m = b[i] < m ? b[i] : m;
+  }
+  *blocks = m;
+  return hipSuccess;
+}
+
+// Every kernel variant of a dtype: the smallest occupancy bounds the plan.
 int executor_max_blocks_per_cu(int dtype, int nthreads, int* blocks, std::string* err) {
-  int b0 = 0, b1 = 0;
-  hipError_t e0 = hipSuccess, e1 = hipSuccess;
+  hipError_t e = hipSuccess;
   switch (dtype) {
-    case CCL_F32:
-      e0 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, executor_kernel<CCL_F32, false>, nthreads, 0);
-      e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, executor_kernel<CCL_F32, true>, nthreads, 0);
-      break;
-    case CCL_BF16:
-      e0 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, executor_kernel<CCL_BF16, false>, nthreads, 0);
-      e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, executor_kernel<CCL_BF16, true>, nthreads, 0);
-      break;
-    case CCL_I32:
-      e0 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b0, executor_kernel<CCL_I32, false>, nthreads, 0);
-      e1 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&b1, executor_kernel<CCL_I32, true>, nthreads, 0);
-      break;
+    case CCL_F32: e = min_blocks<CCL_F32>(nthreads, blocks); break;
+    case CCL_BF16: e = min_blocks<CCL_BF16>(nthreads, blocks); break;
+    case CCL_I32: e = min_blocks<CCL_I32>(nthreads, blocks); break;
     default: *err = "dtype"; return CCL_ERR_UNSUPPORTED;
   }
-  const hipError_t e = e0 != hipSuccess ? e0 : e1;
   if (e != hipSuccess) {
     *err = std::string("occupancy query: ") + hipGetErrorString(e);
     return CCL_ERR_HIP;
   }
-  *blocks = b0 < b1 ? b0 : b1;
   return CCL_OK;
 }
 
 int launch_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int nthreads, void* stream,
                       std::string* err) {
   hipLaunchKernelGGL(copy_probe_kernel, dim3(nblocks), dim3(nthreads), 0, reinterpret_cast<hipStream_t>(stream),
-                     reinterpret_cast<uint4*>(dst), reinterpret_cast<const uint4*>(src), int64_t(bytes / 16));
+                     reinterpret_cast<v4u*>(dst), reinterpret_cast<const v4u*>(src), int64_t(bytes / 16));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     *err = std::string("copy probe launch: ") + hipGetErrorString(e);

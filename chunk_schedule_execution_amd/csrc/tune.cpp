@@ -49,7 +49,7 @@ int ccl_tune_coordinate_descent(const ccl_tune_space* space, const ccl_tune_poin
   const int protos = space->protocols ? space->protocols : 1;
   bool first = true;
   for (int v = 0; v < space->nvariants; ++v) {
-    for (int proto = 0; proto < 3; ++proto) {
+    for (int proto = 0; proto < 4; ++proto) {
       if (!(protos & (1 << proto))) continue;
       ccl_tune_point pt{};
       pt.variant = v;
@@ -121,9 +121,10 @@ static double device_objective(const ccl_tune_point* pt, void* user) {
   ccl_plan_config cfg = c->base;
   cfg.nthreads = pt->nthreads;
   cfg.slice_bytes = pt->slice_bytes;
-  cfg.flags &= ~(CCL_FLAG_HOST_ONLY | CCL_FLAG_TRACE | CCL_FLAG_LL | CCL_FLAG_DIRECT);
+  cfg.flags &= ~(CCL_FLAG_HOST_ONLY | CCL_FLAG_TRACE | CCL_FLAG_LL | CCL_FLAG_DIRECT | CCL_FLAG_STREAMING);
   if (pt->protocol == 1) cfg.flags |= CCL_FLAG_LL;
-  if (pt->protocol == 2) cfg.flags |= CCL_FLAG_DIRECT;
+  if (pt->protocol >= 2) cfg.flags |= CCL_FLAG_DIRECT;
+  if (pt->protocol == 3) cfg.flags |= CCL_FLAG_STREAMING;
   ccl_plan* plan = nullptr;
   int rc = ccl_plan_create(prog, prog->nranks, prog->in_chunks, pt->parallel_factor, &cfg, &plan);
   if (rc) return -1.0;  // infeasible (e.g. not enough co-resident workgroups)

@@ -25,6 +25,7 @@ class PlanConfig:
     slice_bytes: int = 256 * 1024
     protocol: str = "simple"  # "simple" (slice flags) or "ll" (flag in every 8-byte unit)
     transport: str = "staged"  # "staged" (every transfer through a slot) or "direct" (copy receives skip it)
+    streaming: bool = False  # non-temporal hints on local-buffer traffic (large working sets)
     scheduler: str = "hpds"
     wg_alloc: str = "state"
     trace: bool = False
@@ -46,6 +47,8 @@ class PlanConfig:
             flags |= capi.CCL_FLAG_DIRECT
         elif self.transport != "staged":
             raise ValueError(f"unknown transport {self.transport!r}")
+        if self.streaming:
+            flags |= capi.CCL_FLAG_STREAMING
         if not self.xcd_local:
             flags |= capi.CCL_FLAG_COHERENT_ONLY
         if self.protocol == "ll":

@@ -136,6 +136,9 @@ typedef struct {
                                     and forwards from there; such transfers use no staging slot. The
                                     AutoCCL report's transport parameter; ring AllReduce moves S(5P-4)
                                     bytes instead of S(6P-4) */
+#define CCL_FLAG_STREAMING 0x80u  /* non-temporal hint on local-buffer loads and stores (simple protocol):
+                                    streamed lines are not kept in the caches. Helps when the working set is
+                                    far larger than the caches, costs when it fits */
 #define CCL_FLAG_COHERENT_ONLY 0x20u /* always write staging slots and their flags with agent-coherent stores.
                                     By default, when every transfer of the lowered plan stays between
                                     workgroups that the device's round-robin dispatch puts on one XCD
@@ -282,7 +285,8 @@ typedef struct {
   int32_t nthreads;        /* threads per workgroup (nt) */
   int32_t slice_bytes;     /* chunk size of one pipelined step (c) */
   int32_t protocol;        /* 0 = slice flags, 1 = low-latency units (CCL_FLAG_LL), 2 = slice flags with
-                              direct transport (CCL_FLAG_DIRECT) */
+                              direct transport (CCL_FLAG_DIRECT), 3 = 2 with non-temporal local traffic
+                              (CCL_FLAG_DIRECT | CCL_FLAG_STREAMING) */
   int32_t reserved;
 } ccl_tune_point;
 
@@ -292,8 +296,7 @@ typedef struct {
   const int32_t* slices;   int32_t nslices;
   int32_t nvariants;       /* algorithm subspaces 0..nvariants-1 */
   int32_t warmup, iters;   /* per device evaluation */
-  int32_t protocols;       /* protocol subspaces to search: bit 0 = slice flags, bit 1 = LL, bit 2 = slice
-                              flags with direct transport (0 = bit 0) */
+  int32_t protocols;       /* protocol subspaces to search, bit p = protocol p of ccl_tune_point (0 = bit 0) */
 } ccl_tune_space;
 
 typedef struct {

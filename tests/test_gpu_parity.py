@@ -406,3 +406,19 @@ def test_direct_other_collectives():
     want = O2.ring_reducescatter(xs, P, "f32")
     for r in range(P):
         assert np.array_equal(ys[r], want[r]), r
+
+
+@pytest.mark.parametrize("transport", ["staged", "direct"])
+def test_streaming_hints_keep_the_bits(transport):
+    """Non-temporal hints on local traffic are cache policy only: same bits."""
+    P, N = 8, 3 * 65536 + 40
+    case(f"streaming ring AR {transport}")
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 31)
+    ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=8, transport=transport, streaming=True, repeat=2,
+                 slice_bytes=16 << 10)
+    assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
+    G, L, N = 2, 8, 8 * 2051
+    case(f"streaming hierarchical bf16 {transport}")
+    xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 31)
+    ys, _ = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, transport=transport, streaming=True)
+    assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
