@@ -58,8 +58,7 @@ struct ccl_plan {
   unsigned int* d_err = nullptr;
   unsigned long long* d_abort = nullptr;
   unsigned long long* d_trace = nullptr;
-  bool xcd_local = false;  // launch the kernel that writes slots with plain XCD-local stores
-  int nxcd = 0;            // XCDs of the device's round-robin dispatch (0 = unknown)
+  unsigned long long* d_xcd = nullptr;  // per launch-grid workgroup: XCD tag of the latest launch
   hipEvent_t last = nullptr;    // recorded on last_stream when another stream needs ordering
   hipStream_t last_stream = nullptr;
   bool launched = false;
@@ -106,35 +105,6 @@ T* upload(ccl_plan* p, const std::vector<T>& v) {
   return d;
 }
 
-// XCDs the device dispatches workgroups over, round robin by workgroup id: measured
-// once per device with a probe launch that records each workgroup's XCD. 0 if the
-// placement is not exactly id mod n (then no plan uses XCD-local stores).
-int device_xcd_count(int device) {
-  static std::mutex mu;
-  static std::map<int, int> known;
-  std::lock_guard<std::mutex> lk(mu);
-  auto it = known.find(device);
-  if (it != known.end()) return it->second;
-  constexpr int kProbeWGs = 256;
-  unsigned* d = nullptr;
-  HIP_TRY(hipMalloc(&d, kProbeWGs * sizeof(unsigned)));
-  std::vector<unsigned> h(kProbeWGs, 0);
-  std::string err;
-  int rc = launch_xcd_probe(d, kProbeWGs, &err);
-  hipError_t e = rc ? hipSuccess : hipDeviceSynchronize();
-  if (!rc && e == hipSuccess) e = hipMemcpy(h.data(), d, h.size() * sizeof(unsigned), hipMemcpyDeviceToHost);
-  (void)hipFree(d);
-  if (rc) fail(rc, err);
-  if (e != hipSuccess) fail(CCL_ERR_HIP, std::string("XCD probe: ") + hipGetErrorString(e));
-  unsigned n = 0;
-  for (unsigned x : h) n = std::max(n, x + 1);
-  int result = int(n);
-  for (int i = 0; i < kProbeWGs; ++i)
-    if (h[i] != unsigned(i) % n) result = 0;
-  known[device] = result;
-  return result;
-}
-
 void setup_device(ccl_plan* p) {
   HostPlan& hp = p->hp;
   HIP_TRY(hipGetDevice(&p->device_id));
@@ -171,16 +141,19 @@ void setup_device(ccl_plan* p) {
   HIP_TRY(hipMemset(p->d_err, 0, 16));
   p->d_abort = static_cast<unsigned long long*>(p->dev_alloc(8));
   HIP_TRY(hipMemset(p->d_abort, 0, 8));
-  // XCD-local slot stores: every transfer must stay between workgroups that the
-  // device's round-robin dispatch puts on one XCD.
-  p->nxcd = device_xcd_count(p->device_id);
-  bool local = p->nxcd > 0 && !(hp.cfg.flags & CCL_FLAG_COHERENT_ONLY);
-  for (size_t w = 0; w < hp.dwg.size() && local; ++w)
+  // XCD-local layout: every transfer between workgroups whose launch ids are congruent
+  // mod 8, which the round-robin dispatch over the eight XCDs places on one XCD (the
+  // kernel checks each launch's actual placement through the published tags).
+  bool local = !(hp.cfg.flags & CCL_FLAG_COHERENT_ONLY);
+  for (size_t w = 0; w < hp.dwg.size() && local && !(hp.cfg.flags & CCL_FLAG_FORCE_XCD_LOCAL); ++w)
     for (int t = 0; t < hp.dwg[w].n && local; ++t) {
       const DevInstr& D = hp.dins[hp.dwg[w].first + t];
-      if (D.peer_wg >= 0 && int(w) % p->nxcd != D.peer_wg % p->nxcd) local = false;
+      if (D.peer_wg >= 0 && int(w) % 8 != D.peer_wg % 8) local = false;
     }
-  p->xcd_local = local;
+  if (local) {
+    p->d_xcd = static_cast<unsigned long long*>(p->dev_alloc(std::max<size_t>(1, hp.dwg.size()) * 8));
+    HIP_TRY(hipMemset(p->d_xcd, 0, std::max<size_t>(1, hp.dwg.size()) * 8));  // no tag matches an epoch >= 1
+  }
   if (hp.cfg.flags & CCL_FLAG_TRACE) {
     const size_t tb = (hp.dwg.size() + hp.dins.size()) * 32;
     p->d_trace = static_cast<unsigned long long*>(p->dev_alloc(tb));
@@ -207,7 +180,6 @@ const char* ccl_error_string(int status) {
     case CCL_ERR_HIP: return "HIP runtime error";
     case CCL_ERR_TIMEOUT: return "device wait timed out";
     case CCL_ERR_INTERNAL: return "internal error";
-    case CCL_ERR_PLACEMENT: return "workgroup ran on an unexpected XCD";
   }
   return "unknown status";
 }
@@ -262,6 +234,13 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
       if (sendbufs[r] == recvbufs[r]) fail(CCL_ERR_INVALID_ARGUMENT, "in-place execution is not supported");
     }
     if (count == 0) return CCL_OK;
+    // The launch epoch is a kernel argument: a captured launch replayed from a graph
+    // would reuse it and find its flags already set by the previous replay. Checked
+    // before any other HIP call, so a capture in progress is left untouched.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap));
+    if (cap != hipStreamCaptureStatusNone)
+      fail(CCL_ERR_UNSUPPORTED, "ccl_execute cannot be captured into a graph (each launch needs a fresh epoch)");
     int dev = -1;
     HIP_TRY(hipGetDevice(&dev));
     if (dev != plan->device_id) fail(CCL_ERR_INVALID_ARGUMENT, "plan belongs to another device");
@@ -291,7 +270,7 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
     A.err = plan->d_err;
     A.abort_word = plan->d_abort;
     A.trace = plan->d_trace;
-    A.nxcd = plan->nxcd;
+    A.xcd_tags = plan->d_xcd;
     unsigned long long epoch = plan->epoch + 1;
     if (uint32_t(epoch) == 0) ++epoch;  // LL units use the low 32 bits; zero is the slots' initial value
     A.slice_elems = hp.slice_elems;
@@ -311,7 +290,7 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
       HIP_TRY(hipStreamWaitEvent(s, plan->last, 0));
     }
     std::string err;
-    int rc = launch_executor(A, hp.cfg.dtype, plan->xcd_local, (hp.cfg.flags & CCL_FLAG_STREAMING) != 0,
+    int rc = launch_executor(A, hp.cfg.dtype, plan->d_xcd != nullptr, (hp.cfg.flags & CCL_FLAG_STREAMING) != 0,
                              int(hp.dwg.size()), hp.cfg.nthreads, stream, &err);
     if (rc) fail(rc, err);
     plan->epoch = epoch;
@@ -333,8 +312,7 @@ int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info) {
     info->num_workgroups = 0;
     for (const auto& G : hp.dwg) info->num_workgroups += G.n > 0 ? 1 : 0;
     info->grid_workgroups = int(hp.dwg.size());
-    info->xcd_local = plan->xcd_local ? 1 : 0;
-    info->num_xcds = plan->nxcd;
+    info->xcd_local = plan->d_xcd ? 1 : 0;
     info->max_wg_per_rank = hp.max_wg_per_rank;
     info->num_instructions = int(hp.dins.size());
     info->num_subpipelines = hp.num_subpipes;
@@ -425,12 +403,6 @@ int ccl_plan_status(ccl_plan* plan) {
     HIP_TRY(hipMemcpy(e, plan->d_err, sizeof e, hipMemcpyDeviceToHost));
     if (e[0] == 0) return CCL_OK;
     HIP_TRY(hipMemset(plan->d_err, 0, sizeof e));
-    if (-int(e[0]) == CCL_ERR_PLACEMENT) {
-      plan->xcd_local = false;
-      fail(CCL_ERR_PLACEMENT, "launch " + std::to_string(e[3]) + ": workgroup " + std::to_string(e[1]) + " ran on XCD " +
-                                  std::to_string(e[2]) + ", not " + std::to_string(int(e[1]) % std::max(1, plan->nxcd)) +
-                                  "; later launches use coherent slot stores");
-    }
     fail(-int(e[0]), "launch " + std::to_string(e[3]) + ": workgroup " + std::to_string(e[1]) + " timed out at instruction " +
                          std::to_string(e[2]));
   });

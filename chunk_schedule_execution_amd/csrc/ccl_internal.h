@@ -122,14 +122,11 @@ void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec
 void check_lowered(const HostPlan& hp, uint64_t seed, int nsims);
 
 // executor.hip
-// xcd_local: the kernel variant that writes slots and their flags with plain stores
-// (every transfer stays on one XCD; each workgroup checks its placement first).
-// streaming: the variant whose local-buffer loads and stores are non-temporal.
+// xcd_local: the variant for XCD-local layouts (plain transfer stores, flags checked
+// against the receivers' published XCDs); streaming: non-temporal local traffic.
 int launch_executor(const ExecArgs& args, int dtype, bool xcd_local, bool streaming, int nwg, int nthreads,
                     void* stream, std::string* err);
 int executor_max_blocks_per_cu(int dtype, int nthreads, int* blocks, std::string* err);
-// Records the XCD of each of `nwg` single-wave workgroups into out[0..nwg) (synchronous use).
-int launch_xcd_probe(unsigned* out, int nwg, std::string* err);
 int launch_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int nthreads,
                       void* stream, std::string* err);
 

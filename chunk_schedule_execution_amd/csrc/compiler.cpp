@@ -1012,6 +1012,7 @@ void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec
     const int64_t nsl = E.len == 0 ? 0 : (E.len + hp.slice_elems - 1) / hp.slice_elems;
     if (nsl >= (int64_t(1) << kEpochShift)) fail(CCL_ERR_INVALID_ARGUMENT, "too many slices for one transfer");
     E.nsl = int32_t(nsl);
+    E.peer_wg = D.peer_wg;
     if ((D.op & OPB_RECV) && !(D.op & OPB_LOCAL_IN))
       E.a_off = slot_off(D.xin);
     else

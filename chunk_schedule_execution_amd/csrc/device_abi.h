@@ -62,7 +62,7 @@ struct DevExec {  // 80 bytes
   int32_t xin, xout, done_flag;
   int32_t wait_begin, nwaits;
   int32_t nsl;     // slices (simple protocol)
-  int32_t pad0;
+  int32_t peer_wg; // OPB_SEND: launch-grid workgroup of the receiver (-1 = none)
   int64_t len;     // elements
   int64_t a_off, b_off, d_off, t_off;
   int64_t pad1;
@@ -85,10 +85,11 @@ struct ExecArgs {
   long long timeout_ticks;     // watchdog budget per wait, device wall-clock ticks
   int32_t ll;                  // low-latency protocol: slots hold {4 data bytes, 4-byte flag} units
   uint32_t ll_flag;            // flag value of this launch's units (never 0)
-  // XCD-local launches: workgroup i must run on XCD i mod nxcd (the device's
-  // round-robin dispatch, checked at plan setup); each workgroup re-checks its own
-  // placement before touching any slot.
-  int32_t nxcd;
+  // Per launch-grid workgroup: epoch << 8 | 0x10 | XCD id, published at the start of
+  // each launch. A sender whose receiver's entry names the sender's own XCD for this
+  // launch sets the transfer's flag with a plain store; otherwise (or when null) with a
+  // full agent-scope release.
+  unsigned long long* xcd_tags;
   unsigned char* base[kNumBufs][kMaxRanks];  // per-rank buffer base pointers
 };
 

@@ -154,7 +154,7 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
   constexpr int V = 16 / esz;
   constexpr int CL = NT ? kCpolNt : kCpolNone;      // local-buffer loads and stores
   constexpr int CA = RECV ? kCpolSc1 : CL;          // first operand: slot or local buffer
-  constexpr int CT = XL ? kCpolNone : kCpolSc1;     // outgoing slot: XCD-local L2, or agent-coherent
+  constexpr int CT = XL ? kCpolNone : kCpolSc1;     // outgoing data: plain (XCD-local layout) or coherent
   const int bytes = n * esz;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(pa, bytes);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(SRCB ? pb : pa, bytes);
@@ -398,7 +398,7 @@ __device__ __forceinline__ bool run_ll(const unsigned char* pa, const unsigned c
                                                  unsigned int* err, unsigned long long* abort_word,
                                                  unsigned long long epoch, long long timeout_ticks, int instr) {
   const WaitCtx w{err, abort_word, epoch, timeout_ticks, instr};
-  constexpr int CT = XL ? kCpolNone : kCpolSc1;  // outgoing slot: XCD-local L2, or agent-coherent
+  constexpr int CT = XL ? kCpolNone : kCpolSc1;  // outgoing units: plain (XCD-local layout) or coherent
   typedef Arith<DT> Ar;
   constexpr int esz = Ar::esz;
   const int bytes = n * esz;
@@ -506,15 +506,29 @@ __device__ __forceinline__ void release_store(unsigned long long* p, unsigned lo
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Slot flags guard slot data whose stores every wave has already waited for: both
-// agent-coherent, or (XCD-local launches) both plain stores into the XCD's shared L2.
+// Transfer flags. Coherent layouts write the data with agent-coherent stores, so a
+// relaxed agent-scope flag store after every wave's stores are acknowledged suffices.
+// XCD-local layouts write the data with plain stores, which stay in the writer's XCD
+// L2: when the receiving workgroup runs on the same XCD (its tag for this launch says
+// so) that L2 is the point both sides share and the flag is a plain store too;
+// otherwise the flag store is a full agent-scope release (L2 writeback first).
 // Receivers read flags and data with agent-coherent loads either way.
 template <bool XL>
-__device__ __forceinline__ void slot_flag_store(unsigned long long* p, unsigned long long v) {
-  if (XL)
+__device__ __forceinline__ void slot_flag_store(unsigned long long* p, unsigned long long v, bool colocated) {
+  if (XL && colocated) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  else
+  } else {
+    if (XL) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Keeps the compiler from moving the first use of a loaded value above this point (the
+// wait for the load lands here, after the instruction's own memory traffic).
+__device__ __forceinline__ unsigned long long use_here(unsigned long long v) {
+  uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
+  asm volatile("" : "+v"(lo), "+v"(hi));
+  return (uint64_t(hi) << 32) | lo;
 }
 
 // XCD of the executing workgroup (hardware register XCC_ID, bits 3:0).
@@ -595,8 +609,9 @@ __device__ __forceinline__ int64_t uni64(int64_t v) {
   return int64_t((uint64_t(hi) << 32) | lo);
 }
 
-// XL: slots and their flags are written with plain stores, valid because the host
-// laid out the grid so that every transfer stays between workgroups of one XCD.
+// XL: XCD-local layout (every transfer between workgroups whose ids are congruent mod
+// 8, which the round-robin dispatch puts on one XCD): transfer data travels with plain
+// stores and flags are checked against the receiver's published XCD (slot_flag_store).
 // NT: local-buffer loads and local stores carry the non-temporal hint (simple protocol).
 template <int DT, bool XL, bool NT>
 __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
@@ -609,18 +624,10 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
   const DevWG W = A.wgs[blockIdx.x];
   if (W.n == 0) return;  // padding id
   const int tid = threadIdx.x, nthr = blockDim.x;
-  if (XL && int(xcd_id()) != int(blockIdx.x % unsigned(A.nxcd))) {
-    // the layout this launch relies on does not hold: fail it before any slot is touched
-    if (tid == 0) {
-      if (atomicCAS(&A.err[0], 0u, unsigned(-CCL_ERR_PLACEMENT)) == 0u) {
-        A.err[1] = blockIdx.x;
-        A.err[2] = xcd_id();
-        A.err[3] = unsigned(A.epoch);
-      }
-      __hip_atomic_store(A.abort_word, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    return;
-  }
+  // This workgroup's XCD for this launch, published for the workgroups that send to it.
+  const unsigned long long my_tag = (A.epoch << 8) | 0x10ull | xcd_id();
+  if (XL && A.xcd_tags && tid == 0)
+    __hip_atomic_store(&A.xcd_tags[blockIdx.x], my_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const unsigned long long E = A.epoch << kEpochShift;
   // this rank's buffers, kept in scalar registers
   unsigned char* const bufs[3] = {A.base[0][W.rank], A.base[1][W.rank], A.base[2][W.rank]};
@@ -670,13 +677,23 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
         pt = (tb == kStagingBuf ? staging : tb == 0u ? A.base[0][tr] : tb == 1u ? A.base[1][tr] : A.base[2][tr]) +
              uni64(R.t_off);
       }
+      // the receiver's XCD tag: loaded now, first used after this instruction's stores
+      unsigned long long peer_tag = 0;
+      if (XL && (op & OPB_SEND) && A.xcd_tags) {
+        const int peer = uni(R.peer_wg);
+        if (peer >= 0) peer_tag = __hip_atomic_load(&A.xcd_tags[peer], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       if (A.ll) {
         // one pass over the whole range; receivers poll the units they consume
         const WaitCtx wc{A.err, A.abort_word, A.epoch, A.timeout_ticks, gi};
         const bool gave_up = len > 0 && dispatch_ll<DT, XL>(op, pa, pb, pd, pt, int(len), tid, nthr, A.ll_flag, wc);
+        // plain units for a receiver on another XCD leave this XCD's L2 with a release
+        const bool colocated = !XL || use_here(peer_tag) == my_tag;
+        if ((op & OPB_SEND) && !colocated) wait_vm_stores();
         if (gave_up) s_abort = 1;
         __syncthreads();
         if (s_abort) return;
+        if ((op & OPB_SEND) && !colocated && tid == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       } else {
         const int64_t se = A.slice_elems;
         const int nsl = uni(R.nsl);
@@ -693,7 +710,8 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
           if (itrace && tid == 0 && s == 0) itrace[4 * size_t(gi) + 1] = (unsigned long long)wall_clock64();
           if (op & OPB_SEND) wait_vm_stores();
           __syncthreads();
-          if ((op & OPB_SEND) && tid == 0) slot_flag_store<XL>(&A.xflags[xout], E + (unsigned long long)(s + 1));
+          if ((op & OPB_SEND) && tid == 0)
+            slot_flag_store<XL>(&A.xflags[xout], E + (unsigned long long)(s + 1), XL && use_here(peer_tag) == my_tag);
         }
       }
       if (done_flag >= 0 && tid == 0) release_store(&A.dflags[done_flag], A.epoch);
@@ -727,10 +745,6 @@ __global__ __launch_bounds__(1024) void copy_probe_kernel(v4u* __restrict__ dst,
     __builtin_nontemporal_store(a3, dst + i + 3 * stride);
   }
   for (; i < nvec; i += stride) dst[i] = src[i];
-}
-
-__global__ void xcd_probe_kernel(unsigned* out) {
-  if (threadIdx.x == 0) out[blockIdx.x] = xcd_id();
 }
 
 }  // namespace
@@ -807,16 +821,3 @@ int launch_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int
 
 }  // namespace ccl
 
-namespace ccl {
-
-int launch_xcd_probe(unsigned* out, int nwg, std::string* err) {
-  hipLaunchKernelGGL(xcd_probe_kernel, dim3(nwg), dim3(64), 0, 0, out);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) {
-    *err = std::string("XCD probe launch: ") + hipGetErrorString(e);
-    return CCL_ERR_HIP;
-  }
-  return CCL_OK;
-}
-
-}  // namespace ccl

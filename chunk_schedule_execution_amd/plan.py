@@ -31,7 +31,8 @@ class PlanConfig:
     trace: bool = False
     host_only: bool = False
     no_fusion: bool = False
-    xcd_local: bool = True  # plain slot stores between workgroups verified to share an XCD
+    xcd_local: bool = True  # plain transfer stores when the layout keeps transfers on one XCD
+    force_xcd_local: bool = False  # that variant even for spread layouts (tests its release path)
     num_cus: int = 0
     timeout_us: int = 0
 
@@ -49,6 +50,8 @@ class PlanConfig:
             raise ValueError(f"unknown transport {self.transport!r}")
         if self.streaming:
             flags |= capi.CCL_FLAG_STREAMING
+        if self.force_xcd_local:
+            flags |= capi.CCL_FLAG_FORCE_XCD_LOCAL
         if not self.xcd_local:
             flags |= capi.CCL_FLAG_COHERENT_ONLY
         if self.protocol == "ll":
@@ -73,7 +76,7 @@ class Plan:
     def info(self) -> dict:
         i = capi.ccl_plan_info(self.handle)
         d = {name: getattr(i, name) for name, _ in capi.ccl_plan_info_t._fields_
-             if name not in ("compile_ms", "opcode_hist", "reserved")}
+             if name not in ("compile_ms", "opcode_hist", "reserved", "reserved0")}
         d["compile_ms"] = list(i.compile_ms)
         d["opcode_hist"] = list(i.opcode_hist)
         return d

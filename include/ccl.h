@@ -50,9 +50,6 @@ extern "C" {
 #define CCL_ERR_HIP (-5)              /* a HIP runtime call failed */
 #define CCL_ERR_TIMEOUT (-6)          /* a device spin-wait exceeded its watchdog budget */
 #define CCL_ERR_INTERNAL (-7)
-#define CCL_ERR_PLACEMENT (-8)        /* a workgroup of an XCD-local launch ran on another XCD than the device's
-                                         round-robin dispatch puts it on; the launch's outputs are invalid and
-                                         the plan uses coherent slot stores from then on */
 
 /* ---- program description (MSCCLang report, section 3.1: chunks, buffers, copy/reduce) ---- */
 #define CCL_OP_COPY 0   /* dst <- src */
@@ -139,13 +136,16 @@ typedef struct {
 #define CCL_FLAG_STREAMING 0x80u  /* non-temporal hint on local-buffer loads and stores (simple protocol):
                                     streamed lines are not kept in the caches. Helps when the working set is
                                     far larger than the caches, costs when it fits */
-#define CCL_FLAG_COHERENT_ONLY 0x20u /* always write staging slots and their flags with agent-coherent stores.
-                                    By default, when every transfer of the lowered plan stays between
-                                    workgroups that the device's round-robin dispatch puts on one XCD
-                                    (checked once per device at setup), launches write slots and flags with
-                                    plain stores that stay in that XCD's shared L2: shorter hand-offs,
-                                    fewer HBM writes. Every workgroup of such a launch checks its own XCD
-                                    first and fails the launch with CCL_ERR_PLACEMENT if it differs */
+#define CCL_FLAG_FORCE_XCD_LOCAL 0x100u /* use the XCD-local variant even when the layout spreads transfers over
+                                    XCDs: senders then find most receivers on other XCDs and release each
+                                    flag. Slow; exists to exercise that path */
+#define CCL_FLAG_COHERENT_ONLY 0x20u /* write transfers and their flags with agent-coherent stores. By default a
+                                    plan whose lowered layout keeps every transfer on one XCD (workgroup ids
+                                    congruent mod 8, which the round-robin dispatch places together) writes
+                                    transfer data with plain stores; each sender then checks the XCD its
+                                    receiving workgroup published at the start of the launch and, when it is
+                                    its own, sets the flag with a plain store (data and flag meet in that
+                                    XCD's shared L2); otherwise the flag store is a full agent-scope release */
 
 typedef struct {
   int32_t dtype;       /* CCL_F32, CCL_BF16 or CCL_I32 */
@@ -187,8 +187,9 @@ int ccl_plan_create(const ccl_program_desc* prog, int nranks, int nchunks, int p
  * plan are serialized: a launch on another stream first waits for the previous one.
  * Errors: INVALID_ARGUMENT (count > max_count, count not a multiple of the plan's
  * count granule or of P where the collective needs it, null pointers, HOST_ONLY
- * plan), HIP. Device-side failures of a launch (watchdog, placement) are reported
- * by ccl_plan_status.
+ * plan), UNSUPPORTED when `stream` is capturing a graph (every launch carries a fresh
+ * epoch, which a graph replay would repeat), HIP. A watchdog expiry during a launch is
+ * reported by ccl_plan_status.
  */
 int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbufs, int64_t count,
                 void* stream);
@@ -209,8 +210,8 @@ typedef struct {
   int32_t nthreads, slice_bytes;
   int32_t max_resident_wgs;   /* co-residency bound the plan was checked against */
   int32_t grid_workgroups;    /* launch grid: num_workgroups plus idle ids that keep every instance on one XCD */
-  int32_t xcd_local;          /* 1: launches write slots and flags with plain XCD-local stores (see CCL_FLAG_COHERENT_ONLY) */
-  int32_t num_xcds;           /* XCDs the device's round-robin dispatch cycles through (0 = not established) */
+  int32_t xcd_local;          /* 1: XCD-local layout, plain transfer stores (see CCL_FLAG_COHERENT_ONLY) */
+  int32_t reserved0;
   int64_t staging_bytes, scratch_bytes, flag_bytes, table_bytes;
   double compile_ms[6];       /* verify, DAG, fusion, schedule, workgroup allocation, lowering */
   int32_t opcode_hist[16];    /* lowered instructions by opcode bits (see ccl_instr_info.opcode) */
@@ -261,11 +262,9 @@ int ccl_plan_export(const ccl_plan* plan, ccl_instr_info* out, size_t cap, size_
  */
 int ccl_plan_check(const ccl_plan* plan, uint64_t seed, int nsims);
 
-/* After the plan's last launch: CCL_OK, CCL_ERR_TIMEOUT if a watchdog fired, or
- * CCL_ERR_PLACEMENT if a workgroup of an XCD-local launch found itself on an
- * unexpected XCD (the plan then switches to coherent slot stores). The error is
- * cleared once reported; the failed launch's outputs are invalid. Synchronizes with
- * the plan's last launch. */
+/* After the plan's last launch: CCL_OK, or CCL_ERR_TIMEOUT if a watchdog fired (the
+ * error is then cleared; that launch's outputs are invalid). Synchronizes with the
+ * plan's last launch. */
 int ccl_plan_status(ccl_plan* plan);
 
 /* Per-workgroup trace of the last launch of a CCL_FLAG_TRACE plan: for each

@@ -313,23 +313,25 @@ def test_ll_repeated_launches():
 @pytest.mark.parametrize("protocol", ["simple", "ll"])
 @pytest.mark.parametrize("k,nt,num_cus", [(8, 256, 0), (3, 512, 0), (32, 1024, 0), (5, 256, 8)])
 def test_xcd_local_and_coherent_stores_agree(protocol, k, nt, num_cus):
-    """A plan whose transfers all stay between workgroups of one XCD writes slots with
-    plain stores; with num_cus=8 the layout estimate rejects the XCD-aligned grid, the
-    instances spread over XCDs and the plan keeps coherent stores. Either way, and with
-    CCL_FLAG_COHERENT_ONLY, the bits are the chain order, launch after launch."""
+    """An XCD-aligned layout writes transfers with plain stores and sets each flag with a
+    plain store when the receiving workgroup published the sender's own XCD, else with a
+    release. With num_cus=8 the layout estimate rejects the aligned grid: the plan keeps
+    coherent stores, or (forced) runs the XCD-local variant with most receivers on other
+    XCDs, so both flag kinds occur. Every way the bits are the chain order, launch after
+    launch."""
     P, N = 8, 3 * 65536 + 24
     case(f"ring AR store policy {protocol} k={k} nt={nt} num_cus={num_cus}")
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 13)
     want = O2.ring_allreduce(xs, P, "f32")[0]
-    for xcd_local in (True, False):
+    modes = [dict(xcd_local=True), dict(xcd_local=False)]
+    if num_cus == 8:
+        modes.append(dict(xcd_local=True, force_xcd_local=True))
+    for mode in modes:
         ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=k, protocol=protocol, nthreads=nt,
-                        slice_bytes=16 << 10, xcd_local=xcd_local, repeat=4, num_cus=num_cus)
+                        slice_bytes=16 << 10, repeat=4, num_cus=num_cus, **mode)
         info = plan.info()
-        assert info["num_xcds"] >= 1
-        if not xcd_local:
-            assert info["xcd_local"] == 0
-        elif info["num_xcds"] == 8:
-            assert info["xcd_local"] == (0 if num_cus == 8 else 1)
+        aligned = num_cus != 8
+        assert info["xcd_local"] == (1 if mode["xcd_local"] and (aligned or mode.get("force_xcd_local")) else 0)
         if num_cus == 8:
             assert info["grid_workgroups"] == P * k  # no XCD padding
         assert_all_equal(ys, want)
@@ -422,3 +424,31 @@ def test_streaming_hints_keep_the_bits(transport):
     xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 31)
     ys, _ = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, transport=transport, streaming=True)
     assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
+
+
+def test_execute_refuses_graph_capture():
+    """Each launch carries a fresh epoch: a graph would replay a stale one."""
+    import torch
+    from chunk_schedule_execution_amd import Plan, PlanConfig, capi
+    P, N = 4, 1024
+    case("graph capture refused")
+    plan = Plan(programs.ring_allreduce(P), 1, PlanConfig(max_count=N))
+    ins = [torch.zeros(N, device="cuda:0") for _ in range(P)]
+    outs = [torch.empty(N, device="cuda:0") for _ in range(P)]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    err = None
+    try:
+        with torch.cuda.graph(g, stream=s):
+            try:
+                plan.execute(ins, outs, N, s)
+            except capi.CCLError as e:
+                err = e
+    except RuntimeError:
+        pass  # torch may reject the empty capture itself
+    assert err is not None and err.status == capi.CCL_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    plan.execute(ins, outs, N)  # the plan still works outside the capture
+    torch.cuda.synchronize()
+    plan.status()
+    plan.destroy()
