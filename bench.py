@@ -115,16 +115,20 @@ def main():
         xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=S)
         return N, [torch.from_numpy(x).to(dev) for x in xs], outs
 
-    def tune(prog, N, dtype="f32", protocols=15):
-        desc = prog.to_desc()
+    def tune(prog, N, dtype="f32", protocols=15, variants=None):
+        """Tuned (k, nthreads, slice_bytes, protocol) of prog, or, given a list of
+        programs as `variants`, the best over those algorithm subspaces with
+        (..., variant index) appended."""
+        progs = variants if variants is not None else [prog]
         base = PlanConfig(dtype=dtype, max_count=N).to_c()
         arrs = [(capi.C.c_int32 * len(v))(*v) for v in (TUNE_FACTORS, TUNE_THREADS, TUNE_SLICES)]
         space = capi.ccl_tune_space(capi.C.cast(arrs[0], capi.C.POINTER(capi.C.c_int32)), len(TUNE_FACTORS),
                                     capi.C.cast(arrs[1], capi.C.POINTER(capi.C.c_int32)), len(TUNE_THREADS),
                                     capi.C.cast(arrs[2], capi.C.POINTER(capi.C.c_int32)), len(TUNE_SLICES),
-                                    1, 3, 10, protocols)
-        best, rep = capi.ccl_tune([desc], N, base, space, stream.cuda_stream)
-        return (best.parallel_factor, best.nthreads, best.slice_bytes, best.protocol), rep.evaluations
+                                    len(progs), 3, 10, protocols)
+        best, rep = capi.ccl_tune([p.to_desc() for p in progs], N, base, space, stream.cuda_stream)
+        c = (best.parallel_factor, best.nthreads, best.slice_bytes, best.protocol)
+        return (c + (best.variant,) if variants is not None else c), rep.evaluations
 
     def make_plan(prog, N, k, nt, sl, proto=0, dtype="f32", **kw):
         return Plan(prog, k, PlanConfig(dtype=dtype, max_count=N, nthreads=nt, slice_bytes=sl,
@@ -322,6 +326,35 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         release(p)
         del ii, oo
     res["sweep"] = sweep
+
+    # ---- tree versus ring AllReduce at small sizes, and the tuner choosing -----------
+    from oracle import schedule_order as O2
+    trees = []
+    for R, S in ((8, 64 << 10), (8, 256 << 10), (8, 1 << 20), (8, 3 << 20), (24, 1 << 20)):
+        N = S // 4
+        ii = device_inputs("f32", N, R, 77000 + R * 64 + S // 65536)
+        oo = [torch.empty(N, device=dev) for _ in range(R)]
+        ring, tree = programs.ring_allreduce(R), programs.tree_allreduce(R)
+        row = {"ranks": R, "bytes_per_rank": S}
+        for name, pr in (("ring", ring), ("tree", tree)):
+            c, _ = tune(pr, N)
+            p = make_plan(pr, N, *c)
+            t = time_launches(lambda: p.execute(ii, oo, N, stream), 50)
+            row[name] = {"k": c[0], "nthreads": c[1], "slice_bytes": c[2], "protocol": PROTOCOLS[c[3]][0],
+                         "transport": PROTOCOLS[c[3]][1], "busbw": round(busbw_ar(S, t, R), 2), **stats(p, N, t)}
+            if name == "tree":  # sampled check of the tree's own association order
+                xs = [x.cpu().numpy() for x in ii]
+                want = O2.tree_allreduce(xs, R, "f32")[0]
+                idx = np.random.default_rng(1).integers(0, N, 256)
+                row[name]["oracle_spot_check"] = bool(np.array_equal(oo[R - 1].cpu().numpy()[idx], want[idx]))
+            release(p)
+        c, ev = tune(None, N, variants=[ring, tree])
+        row["tuner_picks"] = ("ring", "tree")[c[4]]
+        row["tuner_evaluations"] = ev
+        trees.append(row)
+        progress(f"tree vs ring {R} ranks {S >> 10} KiB: {row['tree']['us']} vs {row['ring']['us']} us")
+        del ii, oo
+    res["tree_vs_ring"] = trees
 
     # ---- 4 ranks, 1 MiB integer-valued fp32, 4 chunks, one channel, one slice -------
     N = 262144

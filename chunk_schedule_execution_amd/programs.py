@@ -140,6 +140,41 @@ def hier_stage_allgather_intra(G: int, L: int) -> Program:
     return prog
 
 
+def tree_allreduce(P: int, c: int = 1) -> Program:
+    """Binary-tree AllReduce: chunk j (owner o = j // c) is reduced up a heap-ordered
+    tree over the ranks o, o+1, ..., o-1 (position t has children 2t+1 and 2t+2; the
+    owner is the root), then copied back down it. A node's partial is (child 2t+2's
+    partial + its own input) + child 2t+1's partial: the shallower subtree arrives
+    first. About 2*log2(P) dependent hops
+    per chunk instead of the ring's 2(P-1), for more bytes (two-child nodes keep a
+    scratch partial); every rank is the root of c chunks. (The AutoCCL report finds
+    tree above ring AllReduce in one setting, "other value" and its Table 5.)"""
+    C = P * c
+    prog = Program("allreduce", P, C, C, scratch_chunks=C, name=f"tree_allreduce_p{P}")
+    for j in range(C):
+        o = j // c
+        rank = [(o + t) % P for t in range(P)]
+        part = {}
+        for t in reversed(range(P)):  # children (larger t) before parents
+            kids = [u for u in (2 * t + 2, 2 * t + 1) if u < P]
+            if not kids:
+                part[t] = prog.chunk(rank[t], IN, j)
+                continue
+            buf = OUT if t == 0 else SCR
+            acc = part[kids[0]].copy(rank[t], buf, j)
+            acc.reduce(prog.chunk(rank[t], IN, j))
+            for u in kids[1:]:
+                acc.reduce(part[u])
+            part[t] = acc
+        if P == 1:
+            prog.chunk(rank[0], IN, j).copy(rank[0], OUT, j)
+        for t in range(P):  # broadcast, parents before children
+            for u in (2 * t + 1, 2 * t + 2):
+                if u < P:
+                    prog.chunk(rank[t], OUT, j).copy(rank[u], OUT, j)
+    return prog
+
+
 def direct_alltoall(P: int) -> Program:
     """Every block straight to its destination (the single-phase baseline)."""
     prog = Program("alltoall", P, P, P, name=f"direct_alltoall_p{P}")
@@ -256,6 +291,7 @@ def reducescatter_2d(G: int, L: int) -> Program:
 
 REGISTRY = {
     "ring_allreduce": ring_allreduce,
+    "tree_allreduce": tree_allreduce,
     "ring_reducescatter": ring_reducescatter,
     "ring_allgather": ring_allgather,
     "hierarchical_allreduce": hierarchical_allreduce,

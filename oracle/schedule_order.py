@@ -27,6 +27,14 @@ taken):
   shards inside each group. (MSCCLang report, §4.2 "Hierarchical AllReduce"; the
   same three-step shape as the cluster primitives of the HetCCL page, "Methodology"
   item 3.)
+* Tree AllReduce (P ranks, C = P*c chunks, chunk j owned by o = j // c). Position t
+  holds rank (o + t) mod P; its children are positions 2t+1 and 2t+2 (a heap). A
+  leaf's partial is its input; a node with one child (2t+1) adds that child's
+  partial to its input; a node with two adds child 2t+2's partial to its input, then
+  child 2t+1's partial (the subtree at 2t+2 is never the deeper one, so its partial
+  is ready first). The root's partial is the result, which every rank receives
+  unchanged. The pages fix no order inside the tree; this one is the reading taken.
+  (The AutoCCL report, "other value", compares tree and ring AllReduce.)
 * Two-dimensional ReduceScatter (P = G*L, C = P blocks, block b = h*L + l belongs
   to rank b). Step 1: inside each group, block b's chain runs over the lanes
   l+1, ..., l (so lane l holds the group's partial of every block of lane l).
@@ -68,6 +76,34 @@ def ring_allreduce(xs, nchunks, dtype):
     y = np.empty_like(np.asarray(xs[0]))
     for j, (lo, hi) in enumerate(chunk_bounds(N, nchunks)):
         y[lo:hi] = _ring_chunk(xs, lo, hi, j // c, dtype)
+    return [y.copy() for _ in range(P)]
+
+
+def _tree_chunk(xs, lo, hi, owner, dtype):
+    P = len(xs)
+
+    def partial(t):
+        x = np.asarray(xs[(owner + t) % P][lo:hi])
+        kids = [u for u in (2 * t + 2, 2 * t + 1) if u < P]  # shallower subtree first
+        if not kids:
+            return x.copy()
+        acc = add_stored(partial(kids[0]), x, dtype)
+        for u in kids[1:]:
+            acc = add_stored(acc, partial(u), dtype)
+        return acc
+    return partial(0)
+
+
+def tree_allreduce(xs, nchunks, dtype):
+    """Every rank's output of the tree AllReduce (they are all the same array)."""
+    P = len(xs)
+    N = len(xs[0])
+    if nchunks % P:
+        raise ValueError("tree programs use a multiple of P chunks")
+    c = nchunks // P
+    y = np.empty_like(np.asarray(xs[0]))
+    for j, (lo, hi) in enumerate(chunk_bounds(N, nchunks)):
+        y[lo:hi] = _tree_chunk(xs, lo, hi, j // c, dtype)
     return [y.copy() for _ in range(P)]
 
 

@@ -158,6 +158,46 @@ def test_count_granule():
     assert host_plan(programs.reducescatter_2d(3, 8)).info()["count_granule"] == 24
 
 
+def _tree_shape(P):
+    internal = P // 2              # heap nodes t with 2t+1 < P
+    two_kids = (P - 1) // 2        # heap nodes t with 2t+2 < P
+    return P - internal, internal, two_kids
+
+
+@pytest.mark.parametrize("P", [2, 3, 4, 5, 7, 8, 9, 16])
+@pytest.mark.parametrize("c", [1, 2])
+def test_tree_allreduce_bytes_closed_form(P, c):
+    """Per chunk of s elements, counted from the fused instructions: each of the L
+    leaves sends its input (read + slot write) and, in the broadcast, receives into
+    its output (slot read + write); a two-child node stores its first receive plus its
+    own input to scratch (3 accesses) and sends its second child's data once more
+    (SEND, 2); every non-root interior node sends up with a reduce-send (3) and
+    forwards the broadcast with a receive-copy-send (3); the root's last receive writes
+    the output and starts the broadcast (4). That is 4L + 5T + 6I - 2 slices of s,
+    I interior and T two-child nodes, and P*c chunks of S/(P*c) make it a multiple of
+    S. Direct transport drops the 2 accesses of each leaf's copy-only receive and the
+    slot read of every forwarding node: minus 2L + (I - 1)."""
+    L, I, T = _tree_shape(P)
+    N = P * c * 64
+    S = 4 * N
+    staged = host_plan(programs.tree_allreduce(P, c)).bytes(N)
+    direct = host_plan(programs.tree_allreduce(P, c), transport="direct").bytes(N)
+    assert staged == S * (4 * L + 5 * T + 6 * I - 2)
+    assert direct == staged - S * (2 * L + I - 1)
+
+
+@pytest.mark.parametrize("P", [5, 8, 16, 24])
+def test_tree_is_shallower_than_the_ring(P):
+    """The point of the tree: its dependent chain grows with log P where the ring's is
+    2P - 1 instructions (at P = 4 both come to 7 sub-pipelines, the tree's being
+    stretched by link conflicts between the trees of different chunks)."""
+    tree = host_plan(programs.tree_allreduce(P)).info()["num_subpipelines"]
+    ring = host_plan(programs.ring_allreduce(P)).info()["num_subpipelines"]
+    assert tree < ring
+    depth = P.bit_length() - 1
+    assert tree <= 4 * depth + 2
+
+
 # ---------------------------------------------------------------- scheduling
 
 def _subpipes_by_instr(plan):
@@ -244,7 +284,8 @@ def test_instances_sit_on_one_xcd():
                                        ("ring_reducescatter", (4,)), ("ring_allgather", (4,)),
                                        ("hierarchical_allreduce", (2, 4)), ("direct_alltoall", (4,)),
                                        ("two_phase_alltoall", (2, 4)), ("alltonext", (2, 4)),
-                                       ("allgather_2d", (2, 4)), ("reducescatter_2d", (2, 4))])
+                                       ("allgather_2d", (2, 4)), ("reducescatter_2d", (2, 4)),
+                                       ("tree_allreduce", (6,)), ("tree_allreduce", (3, 2))])
 @pytest.mark.parametrize("knobs", [dict(k=1, scheduler="hpds", wg_alloc="state"),
                                    dict(k=2, scheduler="rr", wg_alloc="connection"),
                                    dict(k=3, scheduler="program", wg_alloc="state", protocol="ll"),
@@ -279,6 +320,9 @@ ALL_PROGRAMS = [
     ("reducescatter_intra", programs.hier_stage_reducescatter_intra(3, 4), 4),
     ("allreduce_inter", programs.hier_stage_allreduce_inter(3, 4), 4),
     ("allgather_intra", programs.hier_stage_allgather_intra(3, 4), 4),
+    ("allreduce", programs.tree_allreduce(5), None),
+    ("allreduce", programs.tree_allreduce(8, 2), None),
+    ("allreduce", programs.tree_allreduce(1), None),
 ]
 
 

@@ -356,6 +356,31 @@ def test_xcd_local_hierarchical_and_alltoall():
             assert np.array_equal(ys[r], want[r]), r
 
 
+# ------------------------------------------------------------------ tree AllReduce
+
+@pytest.mark.parametrize("P,c,N,k,dtype", [(8, 1, 786432, 8, "f32"), (8, 2, 8 * 1001 + 5, 3, "f32"),
+                                           (5, 1, 123457, 7, "f32"), (3, 1, 7, 1, "f32"), (1, 1, 1000, 1, "f32"),
+                                           (16, 1, 16 * 4099, 2, "bf16"), (24, 1, 24 * 513, 1, "f32")])
+@pytest.mark.parametrize("mode", ["staged", "direct", "ll"])
+def test_tree_allreduce(P, c, N, k, dtype, mode):
+    """Heap tree per chunk rooted at its owner: the bits of the documented tree order,
+    for every transport and protocol, over repeated launches."""
+    case(f"tree AR P={P} c={c} N={N} k={k} {dtype} {mode}")
+    kind = "normal_bf16" if dtype == "bf16" else "normal_f32"
+    xs = W.make_inputs(kind, N, P, W.CFG_TREE_AR, size_bytes=N * 4 + P)
+    knobs = dict(protocol="ll") if mode == "ll" else dict(transport=mode)
+    ys, _ = _run(programs.tree_allreduce(P, c), xs, dtype, k=k, slice_bytes=8192, repeat=2, **knobs)
+    assert_all_equal(ys, O2.tree_allreduce(xs, P * c, dtype)[0])
+
+
+def test_tree_allreduce_integer_exact():
+    P, N = 8, 1 << 18
+    case(f"tree AR P={P} N={N} int-valued")
+    xs = W.make_inputs("int_f32", N, P, W.CFG_TREE_AR, size_bytes=N * 4)
+    ys, _ = _run(programs.tree_allreduce(P), xs, "f32", k=4)
+    assert_all_equal(ys, O1.allreduce(xs, "f32").exact.astype(np.float32))
+
+
 # ------------------------------------------------------------------ direct transport
 
 @pytest.mark.parametrize("P,N,k", [(2, 4099, 2), (3, 7, 1), (8, 3 * 65536 + 24, 8), (8, 8 * 1001, 24), (5, 123457, 7)])

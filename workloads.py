@@ -26,6 +26,7 @@ CFG_RING_AR_8R = 2            # ring AllReduce, 8 ranks, fp32 N(0,1)
 CFG_HIER_AR_16R_BF16 = 3      # hierarchical AllReduce, 2x8 ranks, bf16
 CFG_A2A_32R_INT32 = 4         # two-phase AllToAll, 4x8 ranks, int32
 CFG_A2NEXT_AGRS_24R = 5       # AllToNext / AllGather / ReduceScatter, 3x8 ranks, fp32
+CFG_TREE_AR = 6               # tree AllReduce, 1..24 ranks, fp32 / bf16 N(0,1)
 
 DTYPES = ("f32", "bf16", "i32")
 ELEM_SIZE = {"f32": 4, "bf16": 2, "i32": 4}
