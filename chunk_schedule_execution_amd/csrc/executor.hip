@@ -136,9 +136,8 @@ __device__ __forceinline__ long long wait_slot_flag(unsigned long long* p, unsig
 
 // Inlined into the kernel: a call would reload its target and arguments through the
 // scalar cache on every slice. Indices inside a slice are 32-bit: a slice is far below
-// 2^31 bytes. With RECV, the
-// slice first waits for the incoming slot flag (*wflag >= wtarget); the local operand
-// of the first pass is loaded before that wait so its latency hides behind it.
+// 2^31 bytes. With RECV, the slice first waits for the incoming slot flag (*wflag >=
+// wtarget).
 // Returns the ticks waited, or -1 if the wait gave up (the whole workgroup returns
 // -1 together).
 template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL, bool NT>
@@ -183,11 +182,15 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
   // registers per vector for its widening adds, so it takes two per pass.
   constexpr int U = (DT == CCL_BF16) ? 2 : 4;
   const uint4 zero = {0, 0, 0, 0};
-  // first pass of the second operand, in flight during the wait
+  // First pass of the second operand, loaded before the wait only in the streaming
+  // variant (large transfers): a wave's loads complete in order, so the polling wave's
+  // flag loads queue behind such early loads, and at latency-bound sizes the steps
+  // measured slower with it than without.
   uint4 pf[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) pf[u] = zero;
-  if (SRCB && RECV && same) {
+  constexpr bool kPrefetch = SRCB && RECV && NT;
+  if (kPrefetch && same) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
       if (tid + u * nthr < nvec) pf[u] = to_u4(ld16<CL>(rB, base + 16 * (tid + u * nthr)));
@@ -215,7 +218,7 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           bb[u] = zero;
-          if (RECV && i == tid)
+          if (kPrefetch && i == tid)
             bb[u] = pf[u];
           else if (i + u * nthr < nvec)
             bb[u] = to_u4(ld16<CL>(rB, base + 16 * (i + u * nthr)));
