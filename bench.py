@@ -53,6 +53,8 @@ def parse():
                     help="k,nthreads,slice_bytes,protocol(0 simple, 1 LL, 2 simple+direct, 3 simple+direct+streaming): "
                          "skip tuning (profiling runs)")
     ap.add_argument("--no-extras", action="store_true", help="headline only (profiling runs)")
+    ap.add_argument("--section", choices=["interference"], default="",
+                    help="after the headline run only this part of the extras")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also run the plain copy kernel this many times on 256 MiB (counter calibration)")
@@ -259,7 +261,7 @@ def main():
     }
 
     progress(f"headline {t_step * 1e6:.2f} us per launch, config {cfg}")
-    if not args.no_extras:
+    if not args.no_extras and not args.section:
         # cold: rotate over buffer sets whose total exceeds the 256 MiB Infinity Cache twice
         nsets = max(2, (512 << 20) // (2 * P * S) + 1)
         sets = [(ins, outs)] + [ring_inputs(S)[1:] for _ in range(nsets - 1)]
@@ -276,7 +278,9 @@ def main():
     release(plan)
     del ins, outs
 
-    if not args.no_extras:
+    if args.section == "interference":
+        out["interference"] = interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release)
+    elif not args.no_extras:
         out.update(extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inputs, device_inputs,
                           tune, make_plan, time_launches, busbw_ar, stats, release, fitting))
         copy = out.get("copy_probe_GBs")
@@ -355,6 +359,10 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         progress(f"tree vs ring {R} ranks {S >> 10} KiB: {row['tree']['us']} vs {row['ring']['us']} us")
         del ii, oo
     res["tree_vs_ring"] = trees
+
+    # ---- tuning under compute interference: bf16 GEMMs on a second stream ----------
+    res["interference"] = interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release)
+    progress("interference done")
 
     # ---- 4 ranks, 1 MiB integer-valued fp32, 4 chunks, one channel, one slice -------
     N = 262144
@@ -532,6 +540,92 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
     del a, b
     release()
     return res
+
+
+def interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release):
+    """AutoCCL tunes inside the running job, where computation competes for the GPU.
+    Here a loop of 8192^3 bf16 GEMMs (hipBLASLt through torch) runs on a second stream
+    (default priority) while the ring AllReduce is tuned and timed; the config tuned in
+    isolation and the one tuned under the GEMMs are both timed under the GEMMs."""
+    side = torch.cuda.Stream(device=dev)
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+
+    def gemms(count):
+        with torch.cuda.stream(side):
+            for _ in range(count):
+                torch.matmul(a, b, out=c)
+
+    def on_side(count):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(side)
+        gemms(count)
+        e1.record(side)
+        return e0, e1
+
+    gemms(3)
+    torch.cuda.synchronize()
+    g0, g1 = on_side(20)
+    torch.cuda.synchronize()
+    t_gemm = g0.elapsed_time(g1) * 1e-3 / 20
+    out = {"gemm": "bf16 8192x8192x8192, torch.matmul on a second stream",
+           "gemm_alone_tflops": round(2 * n ** 3 / t_gemm / 1e12, 1), "sizes": []}
+
+    def timed_under_gemms(fn, iters):
+        """Mean seconds per fn() on `stream` while GEMMs keep the second stream busy;
+        also the GEMM rate over the same span."""
+        for _ in range(3):
+            fn()
+        stream.synchronize()
+        # enough GEMMs to outlast the timed launches (estimated from an isolated run)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        alone = e0.elapsed_time(e1) * 1e-3 / iters
+        cover = int(3 * alone * iters / t_gemm) + 8
+        gemms(2)  # the GEMMs are running when the timed launches start
+        g0, g1 = on_side(cover)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3 / iters
+        tg = g0.elapsed_time(g1) * 1e-3 / cover
+        return alone, t, 2 * n ** 3 / tg / 1e12
+
+    for S in (3 << 20, 32 << 20):
+        N, ii, oo = ring_inputs(S)
+        t0 = time.perf_counter()
+        c_pure, _ = tune(prog, N)
+        torch.cuda.synchronize()
+        tune_s = time.perf_counter() - t0
+        # a GEMM backlog that outlasts the tuning under interference (slower than alone)
+        gemms(int(6 * tune_s / t_gemm) + 16)
+        t0 = time.perf_counter()
+        c_int, ev = tune(prog, N)
+        tune_int_s = time.perf_counter() - t0
+        torch.cuda.synchronize()
+        row = {"bytes_per_rank": S, "tuner_evaluations_under_gemms": ev, "tune_seconds_alone": round(tune_s, 2),
+               "tune_seconds_under_gemms": round(tune_int_s, 2)}
+        for name, cfg in (("tuned_alone", c_pure), ("tuned_under_gemms", c_int)):
+            p = make_plan(prog, N, *cfg)
+            alone, t, tf = timed_under_gemms(lambda: p.execute(ii, oo, N, stream), 50 if S < (32 << 20) else 20)
+            row[name] = {"k": cfg[0], "nthreads": cfg[1], "slice_bytes": cfg[2], "protocol": cfg[3],
+                         "workgroups": p.info()["num_workgroups"],
+                         "us_alone": round(alone * 1e6, 2), "us_under_gemms": round(t * 1e6, 2),
+                         "busbw_under_gemms": round(busbw_ar(S, t), 2), "gemm_tflops_meanwhile": round(tf, 1)}
+            release(p)
+        out["sizes"].append(row)
+        del ii, oo
+    del a, b, c
+    release()
+    return out
 
 
 def cpu_baseline(budget_s: float):

@@ -381,6 +381,31 @@ def test_tree_allreduce_integer_exact():
     assert_all_equal(ys, O1.allreduce(xs, "f32").exact.astype(np.float32))
 
 
+# ------------------------------------------------------------------ under compute interference
+
+def test_collectives_under_concurrent_gemms():
+    """bf16 GEMMs keep a second stream (default priority) busy while ring and tree
+    AllReduce plans run on the main one: the bits stay those of the oracle and no wait
+    times out, although the GEMMs hold compute units the executor's workgroups wait for."""
+    import torch
+    side = torch.cuda.Stream()
+    a = torch.randn(4096, 4096, device="cuda:0").to(torch.bfloat16)
+    b = torch.randn(4096, 4096, device="cuda:0").to(torch.bfloat16).contiguous()
+    c = torch.empty(4096, 4096, device="cuda:0", dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    P, N = 8, 3 * 65536 + 24
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 31)
+    for prog, want, knobs in ((programs.ring_allreduce(P), O2.ring_allreduce(xs, P, "f32")[0], dict(k=32, transport="direct")),
+                              (programs.tree_allreduce(P), O2.tree_allreduce(xs, P, "f32")[0], dict(k=8)),
+                              (programs.ring_allreduce(P), O2.ring_allreduce(xs, P, "f32")[0], dict(k=8, protocol="ll"))):
+        case(f"{prog.name} {knobs} under GEMMs")
+        with torch.cuda.stream(side):
+            for _ in range(40):
+                torch.matmul(a, b, out=c)
+        ys, _ = _run(prog, xs, "f32", repeat=4, **knobs)
+        assert_all_equal(ys, want)
+
+
 # ------------------------------------------------------------------ direct transport
 
 @pytest.mark.parametrize("P,N,k", [(2, 4099, 2), (3, 7, 1), (8, 3 * 65536 + 24, 8), (8, 8 * 1001, 24), (5, 123457, 7)])
