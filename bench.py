@@ -63,7 +63,7 @@ def parse():
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("executor.hip", "device_abi.h"):
+    for f in ("executor.hip", "executor_device.h", "device_abi.h"):
         with open(os.path.join(ROOT, "chunk_schedule_execution_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

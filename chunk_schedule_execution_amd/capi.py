@@ -37,6 +37,8 @@ CCL_FLAG_COHERENT_ONLY = 0x20
 CCL_FLAG_DIRECT = 0x40
 CCL_FLAG_STREAMING = 0x80
 CCL_FLAG_FORCE_XCD_LOCAL = 0x100
+CCL_FLAG_SPECIALIZE = 0x200
+CCL_FLAG_LAZY = 0x400
 CCL_I_RECV, CCL_I_SRCB, CCL_I_DSTA, CCL_I_SEND, CCL_I_LOCAL_IN = 0x1, 0x2, 0x4, 0x8, 0x10
 
 
@@ -68,7 +70,7 @@ class ccl_plan_info_t(C.Structure):
                 ("num_connections", C.c_int32), ("num_transfers", C.c_int32), ("num_waits", C.c_int32),
                 ("count_granule", C.c_int32), ("nthreads", C.c_int32), ("slice_bytes", C.c_int32),
                 ("max_resident_wgs", C.c_int32), ("grid_workgroups", C.c_int32),
-                ("xcd_local", C.c_int32), ("reserved0", C.c_int32),
+                ("xcd_local", C.c_int32), ("specialized_shapes", C.c_int32),
                 ("staging_bytes", C.c_int64), ("scratch_bytes", C.c_int64), ("flag_bytes", C.c_int64),
                 ("table_bytes", C.c_int64), ("compile_ms", C.c_double * 6), ("opcode_hist", C.c_int32 * 16)]
 

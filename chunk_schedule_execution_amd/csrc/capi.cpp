@@ -59,6 +59,8 @@ struct ccl_plan {
   unsigned long long* d_abort = nullptr;
   unsigned long long* d_trace = nullptr;
   unsigned long long* d_xcd = nullptr;  // per launch-grid workgroup: XCD tag of the latest launch
+  void* spec_fn = nullptr;              // generated kernel (CCL_FLAG_SPECIALIZE / LAZY), or the interpreter
+  int spec_shapes = 0;
   hipEvent_t last = nullptr;    // recorded on last_stream when another stream needs ordering
   hipStream_t last_stream = nullptr;
   bool launched = false;
@@ -154,6 +156,16 @@ void setup_device(ccl_plan* p) {
     p->d_xcd = static_cast<unsigned long long*>(p->dev_alloc(std::max<size_t>(1, hp.dwg.size()) * 8));
     HIP_TRY(hipMemset(p->d_xcd, 0, std::max<size_t>(1, hp.dwg.size()) * 8));  // no tag matches an epoch >= 1
   }
+  if (hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY)) {
+    const std::string src = specialized_source(hp, local, (hp.cfg.flags & CCL_FLAG_LAZY) != 0, &p->spec_shapes);
+    int spec_blocks = 0;
+    p->spec_fn = load_specialized(src, p->device_id, hp.cfg.nthreads, &spec_blocks);
+    hp.max_resident_wgs = std::min(hp.max_resident_wgs, spec_blocks * cus);
+    if (int(hp.dwg.size()) > spec_blocks * cus)
+      fail(CCL_ERR_OUT_OF_RESOURCES, "plan needs " + std::to_string(hp.dwg.size()) +
+                                         " co-resident workgroups, the device holds " + std::to_string(spec_blocks * cus) +
+                                         " of the specialized kernel");
+  }
   if (hp.cfg.flags & CCL_FLAG_TRACE) {
     const size_t tb = (hp.dwg.size() + hp.dins.size()) * 32;
     p->d_trace = static_cast<unsigned long long*>(p->dev_alloc(tb));
@@ -201,6 +213,11 @@ int ccl_plan_create(const ccl_program_desc* prog, int nranks, int nchunks, int p
         p->hp.max_resident_wgs = blocks * p->hp.cfg.num_cus;
         if (int(p->hp.dwg.size()) > p->hp.max_resident_wgs)
           fail(CCL_ERR_OUT_OF_RESOURCES, "plan needs more co-resident workgroups than the assumed device holds");
+        if (p->hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY)) {  // generate and compile, load nothing
+          bool local = !(p->hp.cfg.flags & CCL_FLAG_COHERENT_ONLY);
+          compile_specialized(specialized_source(p->hp, local, (p->hp.cfg.flags & CCL_FLAG_LAZY) != 0,
+                                                 &p->spec_shapes));
+        }
       }
     } catch (...) {
       delete p;
@@ -290,8 +307,10 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
       HIP_TRY(hipStreamWaitEvent(s, plan->last, 0));
     }
     std::string err;
-    int rc = launch_executor(A, hp.cfg.dtype, plan->d_xcd != nullptr, (hp.cfg.flags & CCL_FLAG_STREAMING) != 0,
-                             int(hp.dwg.size()), hp.cfg.nthreads, stream, &err);
+    int rc = plan->spec_fn ? launch_specialized(plan->spec_fn, A, int(hp.dwg.size()), hp.cfg.nthreads, stream, &err)
+                           : launch_executor(A, hp.cfg.dtype, plan->d_xcd != nullptr,
+                                             (hp.cfg.flags & CCL_FLAG_STREAMING) != 0, int(hp.dwg.size()),
+                                             hp.cfg.nthreads, stream, &err);
     if (rc) fail(rc, err);
     plan->epoch = epoch;
     plan->last_stream = s;
@@ -313,6 +332,7 @@ int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info) {
     for (const auto& G : hp.dwg) info->num_workgroups += G.n > 0 ? 1 : 0;
     info->grid_workgroups = int(hp.dwg.size());
     info->xcd_local = plan->d_xcd ? 1 : 0;
+    info->specialized_shapes = plan->spec_shapes;
     info->max_wg_per_rank = hp.max_wg_per_rank;
     info->num_instructions = int(hp.dins.size());
     info->num_subpipelines = hp.num_subpipes;

@@ -22,715 +22,10 @@
 
 #include "../../include/ccl.h"
 #include "device_abi.h"
+#include "executor_device.h"
 
 namespace ccl {
 namespace {
-
-// ---- element arithmetic --------------------------------------------------
-
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-template <int DT>
-struct Arith;
-
-template <>
-struct Arith<CCL_F32> {
-  static constexpr int esz = 4;
-  typedef uint32_t S;
-  static __device__ __forceinline__ S add(S a, S b) { return __float_as_uint(__uint_as_float(a) + __uint_as_float(b)); }
-  static __device__ __forceinline__ uint4 add4(uint4 a, uint4 b) {
-    return make_uint4(add(a.x, b.x), add(a.y, b.y), add(a.z, b.z), add(a.w, b.w));
-  }
-};
-
-template <>
-struct Arith<CCL_I32> {
-  static constexpr int esz = 4;
-  typedef uint32_t S;
-  static __device__ __forceinline__ S add(S a, S b) { return a + b; }  // two's-complement wrap
-  static __device__ __forceinline__ uint4 add4(uint4 a, uint4 b) {
-    return make_uint4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
-  }
-};
-
-template <>
-struct Arith<CCL_BF16> {
-  static constexpr int esz = 2;
-  typedef uint16_t S;
-  static __device__ __forceinline__ S add(S a, S b) {
-    float s = __uint_as_float(uint32_t(a) << 16) + __uint_as_float(uint32_t(b) << 16);
-    return S(f32_to_bf16_bits(s));
-  }
-  static __device__ __forceinline__ uint32_t add2(uint32_t a, uint32_t b) {
-    float lo = __uint_as_float(a << 16) + __uint_as_float(b << 16);
-    float hi = __uint_as_float(a & 0xffff0000u) + __uint_as_float(b & 0xffff0000u);
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
-  }
-  static __device__ __forceinline__ uint4 add4(uint4 a, uint4 b) {
-    return make_uint4(add2(a.x, b.x), add2(a.y, b.y), add2(a.z, b.z), add2(a.w, b.w));
-  }
-};
-
-// ---- one slice of one instruction ------------------------------------------
-//
-// Every access goes through a buffer descriptor whose size is the operand's slice, so
-// an address outside the operand is dropped by the hardware instead of touching
-// other memory. Staging-slot data (RECV loads, SEND stores) uses the sc1 cache policy:
-// agent-coherent, the same policy the compiler gives relaxed agent-scope atomics, so a
-// slot's data is visible across XCDs as soon as the store completes and no L2
-// writeback or invalidate is needed around the slot flags.
-
-typedef unsigned v4u __attribute__((ext_vector_type(4)));
-constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, gfx9 data format
-constexpr int kCpolNone = 0;
-constexpr int kCpolSc1 = 16;  // agent-scope coherent
-constexpr int kCpolNt = 2;    // non-temporal: streamed lines are not kept
-
-// Slice pointers and sizes are wave-uniform; readfirstlane puts them in scalar
-// registers so the descriptor is scalar (no per-lane waterfall around each access).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const unsigned char* p, int bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
-  void* u = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
-  return __builtin_amdgcn_make_buffer_rsrc(u, 0, __builtin_amdgcn_readfirstlane(bytes), kRsrcWord3);
-}
-
-template <int CP>
-__device__ __forceinline__ v4u ld16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, CP);
-}
-template <int CP>
-__device__ __forceinline__ void st16(__amdgpu_buffer_rsrc_t r, int off, v4u v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, CP);
-}
-template <int ESZ, int CP>
-__device__ __forceinline__ uint32_t ld_elem(__amdgpu_buffer_rsrc_t r, int off) {
-  if (ESZ == 2) return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, CP);
-  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, CP);
-}
-template <int ESZ, int CP>
-__device__ __forceinline__ void st_elem(__amdgpu_buffer_rsrc_t r, int off, uint32_t v) {
-  if (ESZ == 2)
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)v, r, off, 0, CP);
-  else
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, CP);
-}
-
-__device__ __forceinline__ uint4 to_u4(v4u v) { return make_uint4(v.x, v.y, v.z, v.w); }
-__device__ __forceinline__ v4u to_v4(uint4 v) {
-  v4u r = {v.x, v.y, v.z, v.w};
-  return r;
-}
-
-// Thread 0 only: spin until *p >= target, the watchdog expires, or the launch is
-// aborted; returns the ticks spent, or -1 on the latter two.
-__device__ __forceinline__ long long wait_slot_flag(unsigned long long* p, unsigned long long target,
-                                                    unsigned int* err, unsigned long long* abort_word,
-                                                    unsigned long long epoch, long long timeout_ticks, int instr);
-
-// Inlined into the kernel: a call would reload its target and arguments through the
-// scalar cache on every slice. Indices inside a slice are 32-bit: a slice is far below
-// 2^31 bytes. With RECV, the slice first waits for the incoming slot flag (*wflag >=
-// wtarget).
-// Returns the ticks waited, or -1 if the wait gave up (the whole workgroup returns
-// -1 together).
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL, bool NT>
-__device__ __forceinline__ long long run_slice(const unsigned char* pa, const unsigned char* pb,
-                                                         unsigned char* pd, unsigned char* pt, int n, int tid,
-                                                         int nthr, unsigned long long* wflag,
-                                                         unsigned long long wtarget, unsigned int* err,
-                                                         unsigned long long* abort_word, unsigned long long epoch,
-                                                         long long timeout_ticks, int instr) {
-  __shared__ long long s_waited;
-  typedef Arith<DT> Ar;
-  constexpr int esz = Ar::esz;
-  constexpr int V = 16 / esz;
-  constexpr int CL = NT ? kCpolNt : kCpolNone;      // local-buffer loads and stores
-  constexpr int CA = RECV ? kCpolSc1 : CL;          // first operand: slot or local buffer
-  constexpr int CT = XL ? kCpolNone : kCpolSc1;     // outgoing data: plain (XCD-local layout) or coherent
-  const int bytes = n * esz;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(pa, bytes);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(SRCB ? pb : pa, bytes);
-  const __amdgpu_buffer_rsrc_t rD = make_rsrc(DSTA ? pd : pa, DSTA ? bytes : 0);
-  const __amdgpu_buffer_rsrc_t rT = make_rsrc(SEND ? pt : pa, SEND ? bytes : 0);
-  const uintptr_t ra = uintptr_t(pa) & 15;
-  bool same = true;
-  if (SRCB) same &= (uintptr_t(pb) & 15) == ra;
-  if (DSTA) same &= (uintptr_t(pd) & 15) == ra;
-  if (SEND) same &= (uintptr_t(pt) & 15) == ra;
-  auto scalar = [&](int e) {
-    const int o = e * esz;
-    uint32_t v = ld_elem<esz, CA>(rA, o);
-    if (SRCB) v = Ar::add(typename Ar::S(v), typename Ar::S(ld_elem<esz, CL>(rB, o)));
-    if (DSTA) st_elem<esz, CL>(rD, o, v);
-    if (SEND) st_elem<esz, CT>(rT, o, v);
-  };
-  int head = 0, nvec = 0, base = 0;
-  if (same) {
-    head = int((16 - ra) & 15) / esz;
-    if (head > n) head = n;
-    nvec = (n - head) / V;
-    base = head * esz;
-  }
-  // Vectors per thread per pass: all issued before any is consumed. bf16 needs more
-  // registers per vector for its widening adds, so it takes two per pass.
-  constexpr int U = (DT == CCL_BF16) ? 2 : 4;
-  const uint4 zero = {0, 0, 0, 0};
-  // First pass of the second operand, loaded before the wait only in the streaming
-  // variant (large transfers): a wave's loads complete in order, so the polling wave's
-  // flag loads queue behind such early loads, and at latency-bound sizes the steps
-  // measured slower with it than without.
-  uint4 pf[U];
-#pragma unroll
-  for (int u = 0; u < U; ++u) pf[u] = zero;
-  constexpr bool kPrefetch = SRCB && RECV && NT;
-  if (kPrefetch && same) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (tid + u * nthr < nvec) pf[u] = to_u4(ld16<CL>(rB, base + 16 * (tid + u * nthr)));
-  }
-  long long waited = 0;
-  if (RECV) {
-    if (tid == 0) s_waited = wait_slot_flag(wflag, wtarget, err, abort_word, epoch, timeout_ticks, instr);
-    __syncthreads();
-    waited = s_waited;
-    if (waited < 0) return -1;
-  }
-  if constexpr (!DSTA && !SEND) return waited;  // a receive whose data the sender already placed
-  int tail0 = 0;
-  if (same) {
-    if (tid < head) scalar(tid);
-    for (int i = tid; i < nvec; i += U * nthr) {
-      uint4 a[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        a[u] = zero;
-        if (i + u * nthr < nvec) a[u] = to_u4(ld16<CA>(rA, base + 16 * (i + u * nthr)));
-      }
-      if (SRCB) {
-        uint4 bb[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          bb[u] = zero;
-          if (kPrefetch && i == tid)
-            bb[u] = pf[u];
-          else if (i + u * nthr < nvec)
-            bb[u] = to_u4(ld16<CL>(rB, base + 16 * (i + u * nthr)));
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) a[u] = Ar::add4(a[u], bb[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (i + u * nthr >= nvec) continue;
-        const int o = base + 16 * (i + u * nthr);
-        if (DSTA) st16<CL>(rD, o, to_v4(a[u]));
-        if (SEND) st16<CT>(rT, o, to_v4(a[u]));
-      }
-    }
-    tail0 = head + nvec * V;
-  }
-  // unaligned operands, or the tail: element by element
-  for (int e = tail0 + tid; e < n; e += nthr) scalar(e);
-  return waited;
-}
-
-// bf16 widening adds need more registers: its slice code stays an out-of-line call so
-// the register allocator sees one variant at a time (no spills); fp32 / int32 inline.
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL, bool NT>
-__device__ __attribute__((noinline)) long long run_slice_call(const unsigned char* pa, const unsigned char* pb,
-                                                              unsigned char* pd, unsigned char* pt, int n, int tid,
-                                                              int nthr, unsigned long long* wflag,
-                                                              unsigned long long wtarget, unsigned int* err,
-                                                              unsigned long long* abort_word, unsigned long long epoch,
-                                                              long long timeout_ticks, int instr) {
-  return run_slice<DT, RECV, SRCB, DSTA, SEND, XL, NT>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, err, abort_word,
-                                                       epoch, timeout_ticks, instr);
-}
-
-template <int DT, bool XL, bool NT>
-__device__ __forceinline__ long long dispatch_slice(uint32_t op, const unsigned char* pa, const unsigned char* pb,
-                                                    unsigned char* pd, unsigned char* pt, int n, int tid, int nthr,
-                                                    unsigned long long* wflag, unsigned long long wtarget,
-                                                    const ExecArgs& A, int instr) {
-#define CCL_CASE(R, B, D, T)                                                                                     \
-  case ((R) ? OPB_RECV : 0u) | ((B) ? OPB_SRCB : 0u) | ((D) ? OPB_DSTA : 0u) | ((T) ? OPB_SEND : 0u):            \
-    return (DT == CCL_BF16)                                                                                      \
-               ? run_slice_call<DT, R, B, D, T, XL, NT>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err,      \
-                                                        A.abort_word, A.epoch, A.timeout_ticks, instr)             \
-               : run_slice<DT, R, B, D, T, XL, NT>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err,           \
-                                                   A.abort_word, A.epoch, A.timeout_ticks, instr);
-  switch (op & 15u) {
-    CCL_CASE(false, false, true, false)
-    CCL_CASE(false, false, false, true)
-    CCL_CASE(false, false, true, true)
-    CCL_CASE(false, true, true, false)
-    CCL_CASE(false, true, false, true)
-    CCL_CASE(false, true, true, true)
-    CCL_CASE(true, false, false, false)
-    CCL_CASE(true, false, true, false)
-    CCL_CASE(true, false, false, true)
-    CCL_CASE(true, false, true, true)
-    CCL_CASE(true, true, true, false)
-    CCL_CASE(true, true, false, true)
-    CCL_CASE(true, true, true, true)
-    default: return 0;  // every other instruction stores somewhere; the compiler never emits these
-  }
-#undef CCL_CASE
-}
-
-// ---- low-latency protocol ------------------------------------------------------
-//
-// A slot holds 8-byte units {4 data bytes, 4-byte flag}; the flag of every unit of
-// this launch is A.ll_flag. A sender writes units with sc1 stores and needs no
-// barrier or separate flag; a receiver thread polls exactly the units it consumes.
-// Each thread handles quads (4 units = 16 data bytes) when every local operand is
-// 16-byte aligned, else single units. Returns true if this thread gave up
-// (watchdog or another workgroup's abort); the caller makes the workgroup leave
-// together at its next barrier.
-
-typedef unsigned v2u __attribute__((ext_vector_type(2)));
-
-struct WaitCtx {
-  unsigned int* err;
-  unsigned long long* abort_word;
-  unsigned long long epoch;
-  long long timeout_ticks;
-  int instr;
-};
-
-__device__ __noinline__ bool ll_give_up_slow(unsigned int* err, unsigned long long* abort_word,
-                                             unsigned long long epoch, long long timeout_ticks, int instr,
-                                             long long t0) {
-  if (timeout_ticks < 0 || wall_clock64() - t0 > timeout_ticks) {
-    if (atomicCAS(&err[0], 0u, unsigned(-CCL_ERR_TIMEOUT)) == 0u) {
-      err[1] = blockIdx.x;
-      err[2] = unsigned(instr);
-      err[3] = unsigned(epoch);
-    }
-    __hip_atomic_store(abort_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
-  }
-  return __hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
-}
-__device__ __forceinline__ bool ll_give_up(const WaitCtx& w, long long t0) {
-  return ll_give_up_slow(w.err, w.abort_word, w.epoch, w.timeout_ticks, w.instr, t0);
-}
-
-// 4 units (32 bytes) at byte offset off; returns their data words.
-__device__ __forceinline__ bool ll_load_quad(__amdgpu_buffer_rsrc_t r, int off, uint32_t flag, const WaitCtx& w,
-                                             v4u& out) {
-  v4u x = ld16<kCpolSc1>(r, off), y = ld16<kCpolSc1>(r, off + 16);
-  if (x.y != flag || x.w != flag || y.y != flag || y.w != flag) {
-    const long long t0 = wall_clock64();
-    for (unsigned it = 1;; ++it) {
-      __builtin_amdgcn_s_sleep(1);
-      x = ld16<kCpolSc1>(r, off);
-      y = ld16<kCpolSc1>(r, off + 16);
-      if (x.y == flag && x.w == flag && y.y == flag && y.w == flag) break;
-      if ((it & 63) == 0 && ll_give_up(w, t0)) return false;
-    }
-  }
-  out.x = x.x;
-  out.y = x.z;
-  out.z = y.x;
-  out.w = y.z;
-  return true;
-}
-
-__device__ __forceinline__ bool ll_load_unit(__amdgpu_buffer_rsrc_t r, int off, uint32_t flag, const WaitCtx& w,
-                                             uint32_t& out) {
-  v2u x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolSc1);
-  if (x.y != flag) {
-    const long long t0 = wall_clock64();
-    for (unsigned it = 1;; ++it) {
-      __builtin_amdgcn_s_sleep(1);
-      x = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCpolSc1);
-      if (x.y == flag) break;
-      if ((it & 63) == 0 && ll_give_up(w, t0)) return false;
-    }
-  }
-  out = x.x;
-  return true;
-}
-
-template <int CP>
-__device__ __forceinline__ void ll_store_quad(__amdgpu_buffer_rsrc_t r, int off, v4u v, uint32_t flag) {
-  v4u a = {v.x, flag, v.y, flag}, b = {v.z, flag, v.w, flag};
-  st16<CP>(r, off, a);
-  st16<CP>(r, off + 16, b);
-}
-
-// One data word (4 bytes of the transfer) of a local operand starting at byte `o`:
-// whole for 4-byte types, assembled from two bf16 elements otherwise (the second only
-// if it exists).
-template <int ESZ>
-__device__ __forceinline__ uint32_t ld_word(__amdgpu_buffer_rsrc_t r, int o, bool second) {
-  if (ESZ == 4) return __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, kCpolNone);
-  uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, o, 0, kCpolNone);
-  uint32_t hi = second ? uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, o + 2, 0, kCpolNone)) : 0u;
-  return lo | (hi << 16);
-}
-template <int ESZ>
-__device__ __forceinline__ void st_word(__amdgpu_buffer_rsrc_t r, int o, uint32_t v, bool second) {
-  if (ESZ == 4) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, o, 0, kCpolNone);
-  } else {
-    __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v & 0xffffu), r, o, 0, kCpolNone);
-    if (second) __builtin_amdgcn_raw_buffer_store_b16((unsigned short)(v >> 16), r, o + 2, 0, kCpolNone);
-  }
-}
-
-template <int DT>
-__device__ __forceinline__ uint32_t add_word(uint32_t a, uint32_t b) {
-  if (DT == CCL_BF16) return Arith<CCL_BF16>::add2(a, b);
-  return Arith<DT>::add(a, b);
-}
-
-// The wait context travels as separate scalars: a struct argument would go through
-// the stack.
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL>
-__device__ __forceinline__ bool run_ll(const unsigned char* pa, const unsigned char* pb, unsigned char* pd,
-                                                 unsigned char* pt, int n, int tid, int nthr, uint32_t flag,
-                                                 unsigned int* err, unsigned long long* abort_word,
-                                                 unsigned long long epoch, long long timeout_ticks, int instr) {
-  const WaitCtx w{err, abort_word, epoch, timeout_ticks, instr};
-  constexpr int CT = XL ? kCpolNone : kCpolSc1;  // outgoing units: plain (XCD-local layout) or coherent
-  typedef Arith<DT> Ar;
-  constexpr int esz = Ar::esz;
-  const int bytes = n * esz;
-  const int nunits = (bytes + 3) / 4;
-  const __amdgpu_buffer_rsrc_t rA = make_rsrc(pa, RECV ? nunits * 8 : bytes);
-  const __amdgpu_buffer_rsrc_t rB = make_rsrc(SRCB ? pb : pa, SRCB ? bytes : 0);
-  const __amdgpu_buffer_rsrc_t rD = make_rsrc(DSTA ? pd : pa, DSTA ? bytes : 0);
-  const __amdgpu_buffer_rsrc_t rT = make_rsrc(SEND ? pt : pa, SEND ? nunits * 8 : 0);
-  bool aligned = true;
-  if (!RECV) aligned &= (uintptr_t(pa) & 15) == 0;
-  if (SRCB) aligned &= (uintptr_t(pb) & 15) == 0;
-  if (DSTA) aligned &= (uintptr_t(pd) & 15) == 0;
-  const int nquads = aligned ? bytes / 16 : 0;
-  for (int q = tid; q < nquads; q += 2 * nthr) {
-    const int q1 = q + nthr;
-    const bool has1 = q1 < nquads;
-    v4u v0, v1 = {0, 0, 0, 0}, b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
-    if (SRCB) {  // the local operand is in flight while the units are polled
-      b0 = ld16<kCpolNone>(rB, 16 * q);
-      if (has1) b1 = ld16<kCpolNone>(rB, 16 * q1);
-    }
-    if (RECV) {
-      if (!ll_load_quad(rA, 32 * q, flag, w, v0)) return true;
-      if (has1 && !ll_load_quad(rA, 32 * q1, flag, w, v1)) return true;
-    } else {
-      v0 = ld16<kCpolNone>(rA, 16 * q);
-      if (has1) v1 = ld16<kCpolNone>(rA, 16 * q1);
-    }
-    if (SRCB) {
-      v0 = to_v4(Ar::add4(to_u4(v0), to_u4(b0)));
-      v1 = to_v4(Ar::add4(to_u4(v1), to_u4(b1)));
-    }
-    if (DSTA) {
-      st16<kCpolNone>(rD, 16 * q, v0);
-      if (has1) st16<kCpolNone>(rD, 16 * q1, v1);
-    }
-    if (SEND) {
-      ll_store_quad<CT>(rT, 32 * q, v0, flag);
-      if (has1) ll_store_quad<CT>(rT, 32 * q1, v1, flag);
-    }
-  }
-  for (int u = 4 * nquads + tid; u < nunits; u += nthr) {
-    const int o = 4 * u;
-    const bool second = (esz == 2) && (o + 2 < bytes);
-    uint32_t v, b = 0;
-    if (SRCB) b = ld_word<esz>(rB, o, second);
-    if (RECV) {
-      if (!ll_load_unit(rA, 8 * u, flag, w, v)) return true;
-    } else {
-      v = ld_word<esz>(rA, o, second);
-    }
-    if (SRCB) v = add_word<DT>(v, b);
-    if (DSTA) st_word<esz>(rD, o, v, second);
-    if (SEND) {
-      v2u unit = {v, flag};
-      __builtin_amdgcn_raw_buffer_store_b64(unit, rT, 8 * u, 0, CT);
-    }
-  }
-  return false;
-}
-
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL>
-__device__ __attribute__((noinline)) bool run_ll_call(const unsigned char* pa, const unsigned char* pb,
-                                                      unsigned char* pd, unsigned char* pt, int n, int tid, int nthr,
-                                                      uint32_t flag, unsigned int* err, unsigned long long* abort_word,
-                                                      unsigned long long epoch, long long timeout_ticks, int instr) {
-  return run_ll<DT, RECV, SRCB, DSTA, SEND, XL>(pa, pb, pd, pt, n, tid, nthr, flag, err, abort_word, epoch,
-                                                timeout_ticks, instr);
-}
-
-template <int DT, bool XL>
-__device__ __forceinline__ bool dispatch_ll(uint32_t op, const unsigned char* pa, const unsigned char* pb,
-                                            unsigned char* pd, unsigned char* pt, int n, int tid, int nthr,
-                                            uint32_t flag, const WaitCtx& w) {
-#define CCL_CASE(R, B, D, T)                                                                                     \
-  case ((R) ? OPB_RECV : 0u) | ((B) ? OPB_SRCB : 0u) | ((D) ? OPB_DSTA : 0u) | ((T) ? OPB_SEND : 0u):            \
-    return (DT == CCL_BF16) ? run_ll_call<DT, R, B, D, T, XL>(pa, pb, pd, pt, n, tid, nthr, flag, w.err,        \
-                                                              w.abort_word, w.epoch, w.timeout_ticks, w.instr)   \
-                            : run_ll<DT, R, B, D, T, XL>(pa, pb, pd, pt, n, tid, nthr, flag, w.err, w.abort_word, \
-                                                         w.epoch, w.timeout_ticks, w.instr);
-  switch (op & 15u) {
-    CCL_CASE(false, false, true, false)
-    CCL_CASE(false, false, false, true)
-    CCL_CASE(false, false, true, true)
-    CCL_CASE(false, true, true, false)
-    CCL_CASE(false, true, false, true)
-    CCL_CASE(false, true, true, true)
-    CCL_CASE(true, false, true, false)
-    CCL_CASE(true, false, false, true)
-    CCL_CASE(true, false, true, true)
-    CCL_CASE(true, true, true, false)
-    CCL_CASE(true, true, false, true)
-    CCL_CASE(true, true, true, true)
-    default: return false;
-  }
-#undef CCL_CASE
-}
-
-// ---- flags ------------------------------------------------------------------
-
-// Completion flags guard local-buffer data written with ordinary (L2-cached)
-// stores: a full agent-scope release / acquire.
-__device__ __forceinline__ void release_store(unsigned long long* p, unsigned long long v) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Transfer flags. Coherent layouts write the data with agent-coherent stores, so a
-// relaxed agent-scope flag store after every wave's stores are acknowledged suffices.
-// XCD-local layouts write the data with plain stores, which stay in the writer's XCD
-// L2: when the receiving workgroup runs on the same XCD (its tag for this launch says
-// so) that L2 is the point both sides share and the flag is a plain store too;
-// otherwise the flag store is a full agent-scope release (L2 writeback first).
-// Receivers read flags and data with agent-coherent loads either way.
-template <bool XL>
-__device__ __forceinline__ void slot_flag_store(unsigned long long* p, unsigned long long v, bool colocated) {
-  if (XL && colocated) {
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  } else {
-    if (XL) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-}
-
-// Keeps the compiler from moving the first use of a loaded value above this point (the
-// wait for the load lands here, after the instruction's own memory traffic).
-__device__ __forceinline__ unsigned long long use_here(unsigned long long v) {
-  uint32_t lo = uint32_t(v), hi = uint32_t(v >> 32);
-  asm volatile("" : "+v"(lo), "+v"(hi));
-  return (uint64_t(hi) << 32) | lo;
-}
-
-// XCD of the executing workgroup (hardware register XCC_ID, bits 3:0).
-__device__ __forceinline__ unsigned xcd_id() { return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11)); }
-
-__device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-
-__device__ void report_timeout(const ExecArgs& A, int instr) {
-  if (atomicCAS(&A.err[0], 0u, unsigned(-CCL_ERR_TIMEOUT)) == 0u) {
-    A.err[1] = blockIdx.x;
-    A.err[2] = unsigned(instr);
-    A.err[3] = unsigned(A.epoch);
-  }
-  __hip_atomic_store(A.abort_word, A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ long long wait_slot_flag(unsigned long long* p, unsigned long long target,
-                                                    unsigned int* err, unsigned long long* abort_word,
-                                                    unsigned long long epoch, long long timeout_ticks, int instr) {
-  unsigned long long v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (v >= target) return 0;
-  const long long t0 = wall_clock64();
-  for (unsigned it = 1;; ++it) {
-    __builtin_amdgcn_s_sleep(1);
-    v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (v >= target) return wall_clock64() - t0;
-    if ((it & 15) == 0) {
-      if (wall_clock64() - t0 > timeout_ticks) {
-        ll_give_up_slow(err, abort_word, epoch, -1, instr, t0);  // records the timeout and aborts
-        return -1;
-      }
-      if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) return -1;
-    }
-  }
-}
-
-// Thread 0 only: spin until *p >= target, the watchdog expires, or the launch is
-// aborted by another workgroup's watchdog. Returns false on the latter two. With
-// ACQ the success path ends in an agent-scope acquire fence.
-template <bool ACQ>
-__device__ bool wait_geq(unsigned long long* p, unsigned long long target, const ExecArgs& A, int instr,
-                         unsigned long long& wait_ticks) {
-  unsigned long long v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (v >= target) {
-    if (ACQ) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    return true;
-  }
-  const long long t0 = wall_clock64();
-  for (unsigned it = 1;; ++it) {
-    __builtin_amdgcn_s_sleep(1);
-    v = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (v >= target) {
-      if (ACQ) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      wait_ticks += (unsigned long long)(wall_clock64() - t0);
-      return true;
-    }
-    if ((it & 15) == 0) {
-      if (wall_clock64() - t0 > A.timeout_ticks) {
-        report_timeout(A, instr);
-        return false;
-      }
-      if (__hip_atomic_load(A.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == A.epoch) return false;
-    }
-  }
-}
-
-// ---- the kernel ---------------------------------------------------------------
-
-// Records held in LDS at a time: each workgroup copies its instruction records in
-// blocks of this many (80 bytes each) and reads them from LDS, so the per-instruction
-// path touches no global table.
-constexpr int kLdsRecs = 128;
-
-__device__ __forceinline__ int32_t uni(int32_t v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ int64_t uni64(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
-  return int64_t((uint64_t(hi) << 32) | lo);
-}
-
-// XL: XCD-local layout (every transfer between workgroups whose ids are congruent mod
-// 8, which the round-robin dispatch puts on one XCD): transfer data travels with plain
-// stores and flags are checked against the receiver's published XCD (slot_flag_store).
-// NT: local-buffer loads and local stores carry the non-temporal hint (simple protocol).
-template <int DT, bool XL, bool NT>
-__global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
-  constexpr int esz = Arith<DT>::esz;
-  // Set once by any thread that gives up (watchdog, or another workgroup's abort) and
-  // never cleared, so a wave that reads it early only leaves a launch that is failing
-  // anyway; waves that have ended no longer hold a workgroup barrier.
-  __shared__ int s_abort;
-  __shared__ DevExec s_rec[kLdsRecs];
-  const DevWG W = A.wgs[blockIdx.x];
-  if (W.n == 0) return;  // padding id
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  // This workgroup's XCD for this launch, published for the workgroups that send to it.
-  const unsigned long long my_tag = (A.epoch << 8) | 0x10ull | xcd_id();
-  if (XL && A.xcd_tags && tid == 0)
-    __hip_atomic_store(&A.xcd_tags[blockIdx.x], my_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const unsigned long long E = A.epoch << kEpochShift;
-  // this rank's buffers, kept in scalar registers
-  unsigned char* const bufs[3] = {A.base[0][W.rank], A.base[1][W.rank], A.base[2][W.rank]};
-  unsigned char* const staging = A.staging;
-  unsigned long long wait_ticks = 0;
-  long long t_begin = 0;
-  if (A.trace && tid == 0) t_begin = wall_clock64();
-  unsigned long long* itrace = A.trace ? A.trace + 4 * size_t(gridDim.x) : nullptr;
-  int ran = 0;
-  if (tid == 0) s_abort = 0;
-  for (int c0 = 0; c0 < W.n; c0 += kLdsRecs) {
-    const int cnt = (W.n - c0 < kLdsRecs) ? (W.n - c0) : kLdsRecs;
-    {
-      const uint4* src = reinterpret_cast<const uint4*>(A.recs + W.first + c0);
-      uint4* dst = reinterpret_cast<uint4*>(s_rec);
-      for (int t = tid; t < cnt * 5; t += nthr) dst[t] = src[t];
-    }
-    __syncthreads();
-    for (int j = 0; j < cnt; ++j) {
-      const int gi = W.first + c0 + j;
-      if (itrace && tid == 0) itrace[4 * size_t(gi)] = (unsigned long long)wall_clock64();
-      const DevExec& R = s_rec[j];
-      const uint32_t opw = uint32_t(uni(int32_t(R.op)));
-      const uint32_t op = opw & 15u;
-      const int xin = uni(R.xin), xout = uni(R.xout), done_flag = uni(R.done_flag);
-      const int nwaits = uni(R.nwaits);
-      const int64_t len = uni64(R.len);
-      if (nwaits > 0) {
-        const int wait_begin = uni(R.wait_begin);
-        if (tid == 0) {
-          int ok = 1;
-          for (int w = 0; w < nwaits && ok; ++w)
-            ok = wait_geq<true>(&A.dflags[A.waits[wait_begin + w]], A.epoch, A, gi, wait_ticks) ? 1 : 0;
-          if (!ok) s_abort = 1;
-        }
-        __syncthreads();
-        if (s_abort) return;
-      }
-      // a receive reads its slot, or (direct transport) its own buffer where the sender wrote
-      const unsigned char* pa = ((op & OPB_RECV) && !(opw & OPB_LOCAL_IN)) ? staging + uni64(R.a_off)
-                                                                           : bufs[(opw >> 8) & 3u] + uni64(R.a_off);
-      const unsigned char* pb = (op & OPB_SRCB) ? bufs[(opw >> 12) & 3u] + uni64(R.b_off) : nullptr;
-      unsigned char* pd = (op & OPB_DSTA) ? bufs[(opw >> 16) & 3u] + uni64(R.d_off) : nullptr;
-      unsigned char* pt = nullptr;
-      if (op & OPB_SEND) {  // the receiver's slot, or (direct transport) the receiver's buffer
-        const uint32_t tb = (opw >> 20) & 15u, tr = opw >> 24;
-        pt = (tb == kStagingBuf ? staging : tb == 0u ? A.base[0][tr] : tb == 1u ? A.base[1][tr] : A.base[2][tr]) +
-             uni64(R.t_off);
-      }
-      // the receiver's XCD tag: loaded now, first used after this instruction's stores
-      unsigned long long peer_tag = 0;
-      if (XL && (op & OPB_SEND) && A.xcd_tags) {
-        const int peer = uni(R.peer_wg);
-        if (peer >= 0) peer_tag = __hip_atomic_load(&A.xcd_tags[peer], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (A.ll) {
-        // one pass over the whole range; receivers poll the units they consume
-        const WaitCtx wc{A.err, A.abort_word, A.epoch, A.timeout_ticks, gi};
-        const bool gave_up = len > 0 && dispatch_ll<DT, XL>(op, pa, pb, pd, pt, int(len), tid, nthr, A.ll_flag, wc);
-        // plain units for a receiver on another XCD leave this XCD's L2 with a release
-        const bool colocated = !XL || use_here(peer_tag) == my_tag;
-        if ((op & OPB_SEND) && !colocated) wait_vm_stores();
-        if (gave_up) s_abort = 1;
-        __syncthreads();
-        if (s_abort) return;
-        if ((op & OPB_SEND) && !colocated && tid == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      } else {
-        const int64_t se = A.slice_elems;
-        const int nsl = uni(R.nsl);
-        for (int s = 0; s < nsl; ++s) {
-          const int64_t o = int64_t(s) * se;
-          const int n = int((len - o < se) ? (len - o) : se);
-          const int64_t bo = o * esz;
-          const long long waited =
-              dispatch_slice<DT, XL, NT>(op, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr,
-                                 pt ? pt + bo : nullptr, n, tid, nthr, (op & OPB_RECV) ? &A.xflags[xin] : nullptr,
-                                 E + (unsigned long long)(s + 1), A, gi);
-          if (waited < 0) return;  // the wait gave up: uniform across the workgroup
-          wait_ticks += (unsigned long long)waited;
-          if (itrace && tid == 0 && s == 0) itrace[4 * size_t(gi) + 1] = (unsigned long long)wall_clock64();
-          if (op & OPB_SEND) wait_vm_stores();
-          __syncthreads();
-          if ((op & OPB_SEND) && tid == 0)
-            slot_flag_store<XL>(&A.xflags[xout], E + (unsigned long long)(s + 1), XL && use_here(peer_tag) == my_tag);
-        }
-      }
-      if (done_flag >= 0 && tid == 0) release_store(&A.dflags[done_flag], A.epoch);
-      if (itrace && tid == 0) itrace[4 * size_t(gi) + 2] = (unsigned long long)wall_clock64();
-      ++ran;
-    }
-    if (c0 + kLdsRecs < W.n) __syncthreads();  // all reads of this block done before it is overwritten
-  }
-  if (A.trace && tid == 0) {
-    unsigned long long* t = A.trace + 4 * size_t(W.trace_slot);
-    t[0] = (unsigned long long)t_begin;
-    t[1] = (unsigned long long)wall_clock64();
-    t[2] = wait_ticks;
-    t[3] = (unsigned long long)ran;
-  }
-}
 
 // Plain streaming copy: the HBM ceiling a single kernel reaches on this part. Four
 // 16-byte vectors per thread in flight, non-temporal loads and stores (the lines are

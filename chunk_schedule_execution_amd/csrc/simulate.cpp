@@ -70,6 +70,12 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
     std::vector<int> ip(nW, 0);
     std::vector<int64_t> sl(nW, 0);
     std::vector<char> started(nW, 0);
+    // Lazy loop order (CCL_FLAG_LAZY): iteration it runs slice it of every instruction of
+    // the workgroup in order; an instruction with e = max(slices, 1) takes part in
+    // iterations 0 .. e-1, its completion waits at 0 and its completion flag at e-1.
+    // (an LL instruction is one pass either way, so LL plans run in task order)
+    const bool lazy = (hp.cfg.flags & CCL_FLAG_LAZY) && !(hp.cfg.flags & CCL_FLAG_LL);
+    std::vector<int64_t> iters(nW, 1), lit(nW, 0);
     // instruction geometry at N
     struct Geo {
       int64_t len, alo, blo, dlo, tlo, nsl;
@@ -88,23 +94,45 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
       geo[j] = g;
       if ((D.op & OPB_SEND) && D.t_buf < 0) slot[D.xout].assign(g.len, Val{});
     }
+    auto eff = [&](int j) { return std::max<int64_t>(1, geo[j].nsl); };
+    if (lazy) {
+      for (int w = 0; w < nW; ++w)
+        for (int t = 0; t < hp.dwg[w].n; ++t) iters[w] = std::max(iters[w], eff(hp.dwg[w].first + t));
+    }
+    // lazy: skip instructions that take no part in the current iteration
+    auto lazy_settle = [&](int w) {
+      const DevWG& G = hp.dwg[w];
+      for (;;) {
+        if (lit[w] >= iters[w]) return;
+        if (ip[w] >= G.n) {
+          ip[w] = 0;
+          ++lit[w];
+          continue;
+        }
+        if (lit[w] < eff(G.first + ip[w])) return;
+        ++ip[w];
+      }
+    };
+    if (lazy)
+      for (int w = 0; w < nW; ++w) lazy_settle(w);
     std::vector<int> runnable;
     for (;;) {
       runnable.clear();
       bool all_done = true;
       for (int w = 0; w < nW; ++w) {
         const DevWG& G = hp.dwg[w];
-        if (ip[w] >= G.n) continue;
+        if (lazy ? lit[w] >= iters[w] || G.n == 0 : ip[w] >= G.n) continue;
         all_done = false;
         int j = G.first + ip[w];
         const DevInstr& D = hp.dins[j];
-        if (!started[w]) {
+        const int64_t s_now = lazy ? lit[w] : sl[w];
+        if (lazy ? s_now == 0 : !started[w]) {
           bool ok = true;
           for (int q = 0; q < D.nwaits; ++q)
             if (!dflag[hp.dwaits[D.wait_begin + q]]) ok = false;
           if (!ok) continue;
         }
-        if ((D.op & OPB_RECV) && geo[j].nsl > 0 && xflag[D.xin] < sl[w] + 1) continue;
+        if ((D.op & OPB_RECV) && s_now < geo[j].nsl && xflag[D.xin] < s_now + 1) continue;
         runnable.push_back(w);
       }
       if (all_done) break;
@@ -119,7 +147,8 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
       const DevInstr& D = hp.dins[j];
       const Geo& g = geo[j];
       started[w] = 1;
-      if (g.nsl > 0) {
+      if (lazy) sl[w] = lit[w];
+      if (sl[w] < g.nsl) {
         int64_t lo = sl[w] * se, hi = std::min(g.len, lo + se);
         for (int64_t e = lo; e < hi; ++e) {
           const bool from_slot = (D.op & OPB_RECV) && !(D.op & OPB_LOCAL_IN);
@@ -145,7 +174,11 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
         if (D.op & OPB_SEND) xflag[D.xout] = sl[w] + 1;
         sl[w]++;
       }
-      if (sl[w] >= g.nsl) {
+      if (lazy) {
+        if (lit[w] == eff(j) - 1 && D.done_flag >= 0) dflag[D.done_flag] = 1;
+        ip[w]++;
+        lazy_settle(w);
+      } else if (sl[w] >= g.nsl) {
         if (D.done_flag >= 0) dflag[D.done_flag] = 1;
         ip[w]++;
         sl[w] = 0;

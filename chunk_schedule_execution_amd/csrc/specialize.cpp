@@ -1,0 +1,246 @@
+// Plan-specialized executor kernels, generated and compiled when a plan is created.
+//
+// The interpreting kernel reads every instruction's operation and buffers from its
+// record and branches on them. ReSCCL compiles each algorithm's pipelines into a
+// kernel of its own instead, so that no instruction stream is parsed at run time
+// (ReSCCL report, section 2.2, lightweight kernel generation). Here a plan's
+// workgroups are grouped by the sequence of operation words they run (the "shape";
+// all instances of a base workgroup share one), and each shape becomes straight-line
+// code: one call of the executor's per-instruction step per instruction, with the
+// operation and its buffers as template constants. Offsets, lengths and flag indices
+// still come from the count-dependent records, so one kernel serves every count.
+//
+// The lazy variant runs the same code in the other loop order: slice s of every
+// instruction before slice s + 1 of any (the whole algorithm once per slice, as an
+// interpreter that repeats the algorithm per chunk slice does; ReSCCL report, section
+// 2.1, lazy execution), instead of all slices of one instruction before the next.
+//
+// The device code is the library's own executor source, embedded at build time and
+// compiled with hiprtc for gfx950; code objects are cached per source text and
+// modules per device for the life of the process.
+#include <hip/hip_runtime.h>
+#include <hip/hiprtc.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ccl_internal.h"
+
+namespace ccl {
+
+extern const char kEmbeddedExecutorSource[];  // generated at build time
+
+namespace {
+
+constexpr int kMaxSpecializedInstructions = 160;
+
+std::string hex32(uint32_t v) {
+  char b[16];
+  snprintf(b, sizeof b, "0x%06xLL", v);
+  return b;
+}
+
+struct CodeCache {
+  std::mutex mu;
+  std::map<std::string, std::vector<char>> code;                   // source -> code object
+  std::map<std::pair<std::string, int>, hipFunction_t> functions;  // (source, device) -> kernel
+};
+CodeCache& cache() {
+  static CodeCache* c = new CodeCache();  // never destroyed: modules stay loaded
+  return *c;
+}
+
+const std::vector<char>& compile_cached(const std::string& src) {
+  CodeCache& c = cache();
+  {
+    std::lock_guard<std::mutex> g(c.mu);
+    auto it = c.code.find(src);
+    if (it != c.code.end()) return it->second;
+  }
+  hiprtcProgram prog;
+  if (hiprtcCreateProgram(&prog, src.c_str(), "ccl_specialized.hip", 0, nullptr, nullptr) != HIPRTC_SUCCESS)
+    fail(CCL_ERR_HIP, "hiprtcCreateProgram failed");
+  const char* opts[] = {"--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+                        "-packed-fp32-ops"};
+  const hiprtcResult r = hiprtcCompileProgram(prog, int(sizeof(opts) / sizeof(opts[0])), opts);
+  if (r != HIPRTC_SUCCESS) {
+    size_t n = 0;
+    hiprtcGetProgramLogSize(prog, &n);
+    std::string log(n, '\0');
+    if (n) hiprtcGetProgramLog(prog, &log[0]);
+    hiprtcDestroyProgram(&prog);
+    fail(CCL_ERR_HIP, std::string("specialized kernel does not compile: ") + hiprtcGetErrorString(r) + "\n" +
+                          log.substr(0, 4000));
+  }
+  size_t n = 0;
+  hiprtcGetCodeSize(prog, &n);
+  std::vector<char> obj(n);
+  hiprtcGetCode(prog, obj.data());
+  hiprtcDestroyProgram(&prog);
+  std::lock_guard<std::mutex> g(c.mu);
+  return c.code.emplace(src, std::move(obj)).first->second;
+}
+
+}  // namespace
+
+std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, int* num_shapes) {
+  const bool ll = hp.cfg.flags & CCL_FLAG_LL;
+  const bool nt = hp.cfg.flags & CCL_FLAG_STREAMING;
+  // operation words (operation and buffers, not the peer rank) are count-independent
+  std::vector<DevExec> recs;
+  compute_exec_records(hp, hp.cfg.max_count, recs);
+  const int ngrid = int(hp.dwg.size());
+  const int stride = hp.wg_stride;
+  const int nbase = (ngrid + stride - 1) / stride;
+  std::map<std::vector<uint32_t>, int> shape_of;
+  std::vector<std::vector<uint32_t>> shapes;
+  std::vector<int> base_shape(nbase, -1);
+  int max_n = 1;
+  for (int w = 0; w < nbase; ++w) {
+    const int g = w * stride;  // instance 0 of base workgroup w
+    if (g >= ngrid || hp.dwg[g].n == 0) continue;
+    const DevWG& G = hp.dwg[g];
+    std::vector<uint32_t> seq(G.n);
+    for (int j = 0; j < G.n; ++j) seq[j] = recs[G.first + j].op & 0x00ffffffu;
+    for (int i = 1; i < stride && g + i < ngrid; ++i) {  // every instance runs the same operations
+      const DevWG& H = hp.dwg[g + i];
+      if (H.n == 0) continue;
+      if (H.n != G.n) fail(CCL_ERR_INTERNAL, "instances of a workgroup differ in length");
+      for (int j = 0; j < H.n; ++j)
+        if ((recs[H.first + j].op & 0x00ffffffu) != seq[j]) fail(CCL_ERR_INTERNAL, "instances of a workgroup differ");
+    }
+    max_n = std::max(max_n, G.n);
+    auto it = shape_of.find(seq);
+    if (it == shape_of.end()) {
+      it = shape_of.emplace(seq, int(shapes.size())).first;
+      shapes.push_back(seq);
+    }
+    base_shape[w] = it->second;
+  }
+  if (max_n > 512) fail(CCL_ERR_UNSUPPORTED, "specialized kernels hold at most 512 instructions per workgroup");
+  // Every generated instruction is a fully inlined copy of the per-instruction step:
+  // compile time and code size grow with the total, so plans with many distinct
+  // workgroup programs stay on the interpreter.
+  size_t total = 0;
+  for (const auto& sh : shapes) total += sh.size();
+  if (total > size_t(kMaxSpecializedInstructions))
+    fail(CCL_ERR_UNSUPPORTED, "plan has " + std::to_string(shapes.size()) + " distinct workgroup programs with " +
+                                  std::to_string(total) + " instructions in all; specialized kernels take at most " +
+                                  std::to_string(kMaxSpecializedInstructions));
+  if (lazy)
+    for (const auto& D : hp.dins)
+      if (D.nwaits > 0)
+        fail(CCL_ERR_UNSUPPORTED,
+             "the lazy loop order needs a plan without cross-workgroup completion waits (one would wait for a "
+             "whole instruction while its workgroup is still at an earlier slice of others)");
+  if (num_shapes) *num_shapes = int(shapes.size());
+
+  const std::string targs = std::to_string(hp.cfg.dtype) + ", " + (xcd_local ? "true" : "false") + ", " +
+                            (nt ? "true" : "false");
+  const std::string llk = ll ? "1" : "0";
+  std::string s;
+  s += "// generated: plan-specialized executor kernel\n#include <stdint.h>\n";
+  s += kEmbeddedExecutorSource;
+  s += "\nnamespace ccl {\nnamespace {\n";
+  s += "__constant__ int kSpecShape[" + std::to_string(std::max(1, nbase)) + "] = {";
+  for (int w = 0; w < nbase; ++w) s += (w ? ", " : "") + std::to_string(base_shape[w]);
+  if (nbase == 0) s += "-1";
+  s += "};\n";
+  for (size_t sh = 0; sh < shapes.size(); ++sh) {
+    const auto& seq = shapes[sh];
+    const int n = int(seq.size());
+    s += "__device__ __forceinline__ int spec_shape_" + std::to_string(sh) +
+         "(const ExecArgs& A, WgState& S, const DevExec* r, int g) {\n";
+    if (!lazy) {
+      for (int j = 0; j < n; ++j)
+        s += "  if (!run_instr<" + targs + ", " + hex32(seq[j]) + ", " + llk + ">(A, S, r[" + std::to_string(j) +
+             "], g + " + std::to_string(j) + ", 0, -1, true, true)) return -1;\n";
+    } else {
+      // one slice of every instruction per iteration; an LL instruction is one pass
+      s += "  int iters = 1;\n";
+      for (int j = 0; j < n; ++j) {
+        const std::string e = "e" + std::to_string(j);
+        if (ll)
+          s += "  const int " + e + " = 1;\n";
+        else
+          s += "  const int " + e + " = uni(r[" + std::to_string(j) + "].nsl) > 1 ? uni(r[" + std::to_string(j) +
+               "].nsl) : 1;\n";
+        s += "  iters = iters > " + e + " ? iters : " + e + ";\n";
+      }
+      s += "  for (int it = 0; it < iters; ++it) {\n";
+      for (int j = 0; j < n; ++j) {
+        const std::string e = "e" + std::to_string(j);
+        s += "    if (it < " + e + " && !run_instr<" + targs + ", " + hex32(seq[j]) + ", " + llk + ">(A, S, r[" +
+             std::to_string(j) + "], g + " + std::to_string(j) + ", it, it + 1, it == 0, it == " + e +
+             " - 1)) return -1;\n";
+      }
+      s += "  }\n";
+    }
+    s += "  return " + std::to_string(n) + ";\n}\n";
+  }
+  s += "}  // namespace\n}  // namespace ccl\n\n";
+  s += "extern \"C\" __global__ __launch_bounds__(" + std::to_string(hp.cfg.nthreads) +
+       ") void ccl_spec_kernel(ccl::ExecArgs A) {\n";
+  s += "  using namespace ccl;\n";
+  s += "  __shared__ int s_abort;\n";
+  s += "  __shared__ DevExec s_rec[" + std::to_string(max_n) + "];\n";
+  s += "  const DevWG W = A.wgs[blockIdx.x];\n";
+  s += "  if (W.n == 0) return;  // padding id\n";
+  s += "  WgState S;\n";
+  s += "  wg_begin<" + std::string(xcd_local ? "true" : "false") + ">(A, W, S, &s_abort);\n";
+  s += "  stage_records(A, W.first, W.n, s_rec, S.tid, S.nthr);\n";
+  s += "  __syncthreads();\n";
+  s += "  int ran = -1;\n";
+  s += "  switch (kSpecShape[blockIdx.x / " + std::to_string(stride) + "]) {\n";
+  for (size_t sh = 0; sh < shapes.size(); ++sh)
+    s += "    case " + std::to_string(sh) + ": ran = spec_shape_" + std::to_string(sh) + "(A, S, s_rec, W.first); break;\n";
+  s += "    default: break;\n  }\n";
+  s += "  if (ran < 0) return;\n";
+  s += "  wg_end(A, W, S, ran);\n}\n";
+  return s;
+}
+
+void compile_specialized(const std::string& src) { (void)compile_cached(src); }
+
+void* load_specialized(const std::string& src, int device, int nthreads, int* blocks_per_cu) {
+  const std::vector<char>& obj = compile_cached(src);
+  CodeCache& c = cache();
+  hipFunction_t fn = nullptr;
+  {
+    std::lock_guard<std::mutex> g(c.mu);
+    auto it = c.functions.find({src, device});
+    if (it != c.functions.end()) fn = it->second;
+  }
+  if (!fn) {
+    hipModule_t mod = nullptr;
+    hipError_t e = hipModuleLoadData(&mod, obj.data());
+    if (e != hipSuccess) fail(CCL_ERR_HIP, std::string("hipModuleLoadData: ") + hipGetErrorString(e));
+    e = hipModuleGetFunction(&fn, mod, "ccl_spec_kernel");
+    if (e != hipSuccess) fail(CCL_ERR_HIP, std::string("hipModuleGetFunction: ") + hipGetErrorString(e));
+    std::lock_guard<std::mutex> g(c.mu);
+    c.functions[{src, device}] = fn;
+  }
+  int b = 0;
+  hipError_t e = hipModuleOccupancyMaxActiveBlocksPerMultiprocessor(&b, fn, nthreads, 0);
+  if (e != hipSuccess) fail(CCL_ERR_HIP, std::string("occupancy query: ") + hipGetErrorString(e));
+  *blocks_per_cu = b;
+  return reinterpret_cast<void*>(fn);
+}
+
+int launch_specialized(void* fn, const ExecArgs& args, int nwg, int nthreads, void* stream, std::string* err) {
+  ExecArgs a = args;
+  void* params[] = {&a};
+  hipError_t e = hipModuleLaunchKernel(reinterpret_cast<hipFunction_t>(fn), nwg, 1, 1, nthreads, 1, 1, 0,
+                                       reinterpret_cast<hipStream_t>(stream), params, nullptr);
+  if (e != hipSuccess) {
+    *err = std::string("specialized kernel launch: ") + hipGetErrorString(e);
+    return CCL_ERR_HIP;
+  }
+  return CCL_OK;
+}
+
+}  // namespace ccl

@@ -35,6 +35,9 @@ class PlanConfig:
     force_xcd_local: bool = False  # that variant even for spread layouts (tests its release path)
     num_cus: int = 0
     timeout_us: int = 0
+    # "interpreter" (one kernel for every plan), "specialized" (a kernel generated for
+    # this plan) or "lazy" (a generated kernel in the slice-outer loop order)
+    kernel: str = "interpreter"
 
     def to_c(self) -> capi.ccl_plan_config:
         flags = 0
@@ -54,6 +57,12 @@ class PlanConfig:
             flags |= capi.CCL_FLAG_FORCE_XCD_LOCAL
         if not self.xcd_local:
             flags |= capi.CCL_FLAG_COHERENT_ONLY
+        if self.kernel == "specialized":
+            flags |= capi.CCL_FLAG_SPECIALIZE
+        elif self.kernel == "lazy":
+            flags |= capi.CCL_FLAG_SPECIALIZE | capi.CCL_FLAG_LAZY
+        elif self.kernel != "interpreter":
+            raise ValueError(f"unknown kernel {self.kernel!r}")
         if self.protocol == "ll":
             flags |= capi.CCL_FLAG_LL
         elif self.protocol != "simple":

@@ -139,6 +139,18 @@ typedef struct {
 #define CCL_FLAG_FORCE_XCD_LOCAL 0x100u /* use the XCD-local variant even when the layout spreads transfers over
                                     XCDs: senders then find most receivers on other XCDs and release each
                                     flag. Slow; exists to exercise that path */
+#define CCL_FLAG_SPECIALIZE 0x200u /* run a kernel generated for this plan instead of the interpreting one
+                                    (ReSCCL report, section 2.2, lightweight kernel generation): each distinct
+                                    sequence of instructions becomes straight-line code with the operations
+                                    and buffers as constants, compiled with hiprtc at create (code objects
+                                    cached per process). Same records, flags and results; with HOST_ONLY the
+                                    kernel is generated and compiled but not loaded. Compile failures give
+                                    CCL_ERR_HIP */
+#define CCL_FLAG_LAZY 0x400u      /* with or without SPECIALIZE: a generated kernel that runs the lazy loop
+                                    order, slice s of every instruction of a workgroup before slice s + 1 of
+                                    any (the algorithm once per slice; ReSCCL report, section 2.1), instead of
+                                    every slice of an instruction before the next. CCL_ERR_UNSUPPORTED for
+                                    plans with cross-workgroup completion waits */
 #define CCL_FLAG_COHERENT_ONLY 0x20u /* write transfers and their flags with agent-coherent stores. By default a
                                     plan whose lowered layout keeps every transfer on one XCD (workgroup ids
                                     congruent mod 8, which the round-robin dispatch places together) writes
@@ -211,7 +223,8 @@ typedef struct {
   int32_t max_resident_wgs;   /* co-residency bound the plan was checked against */
   int32_t grid_workgroups;    /* launch grid: num_workgroups plus idle ids that keep every instance on one XCD */
   int32_t xcd_local;          /* 1: XCD-local layout, plain transfer stores (see CCL_FLAG_COHERENT_ONLY) */
-  int32_t reserved0;
+  int32_t specialized_shapes; /* generated kernel (CCL_FLAG_SPECIALIZE / LAZY): distinct instruction
+                                 sequences in it; 0 for the interpreting kernel */
   int64_t staging_bytes, scratch_bytes, flag_bytes, table_bytes;
   double compile_ms[6];       /* verify, DAG, fusion, schedule, workgroup allocation, lowering */
   int32_t opcode_hist[16];    /* lowered instructions by opcode bits (see ccl_instr_info.opcode) */

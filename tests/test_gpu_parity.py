@@ -381,6 +381,67 @@ def test_tree_allreduce_integer_exact():
     assert_all_equal(ys, O1.allreduce(xs, "f32").exact.astype(np.float32))
 
 
+# ------------------------------------------------------------------ plan-specialized kernels
+
+@pytest.mark.parametrize("kernel", ["specialized", "lazy"])
+@pytest.mark.parametrize("P,N,k,sl,knobs", [(8, 3 * 65536 + 24, 8, 8192, dict(transport="direct")),
+                                            (5, 123457, 3, 4096, {}),
+                                            (8, 8 * 1001, 2, 65536, dict(protocol="ll")),
+                                            (8, 1 << 20, 4, 65536, dict(transport="direct", streaming=True))])
+def test_specialized_ring_allreduce(kernel, P, N, k, sl, knobs):
+    """Generated kernels (task order and the lazy slice-outer order, which here runs up
+    to dozens of slices per instruction) give the chain-order bits."""
+    case(f"{kernel} ring AR P={P} N={N} k={k} slice={sl} {knobs}")
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 37)
+    ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=k, slice_bytes=sl, kernel=kernel, repeat=3, **knobs)
+    assert plan.info()["specialized_shapes"] == 1
+    assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
+
+
+@pytest.mark.parametrize("kernel", ["specialized", "lazy"])
+def test_specialized_other_collectives(kernel):
+    G, L, N = 2, 8, 8 * 4099
+    case(f"{kernel} hierarchical bf16")
+    xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 41)
+    ys, plan = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, slice_bytes=4096, kernel=kernel, repeat=2)
+    assert plan.info()["specialized_shapes"] >= 2
+    assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
+    G, L, N = 3, 8, 8 * 777
+    case(f"{kernel} alltonext split")
+    xs = W.make_inputs("normal_f32", N, G * L, W.CFG_A2NEXT_AGRS_24R, size_bytes=N * 4 + 41)
+    prior = [np.full(N, -3.0, np.float32) for _ in range(G * L)]
+    ys, _ = _run(programs.alltonext(G, L, split=True), xs, "f32", k=2, prior=prior, slice_bytes=4096, kernel=kernel)
+    want = O1.alltonext(xs, prior)
+    for r in range(G * L):
+        assert np.array_equal(ys[r], want[r]), r
+    P, n = G * L, 24 * 41
+    xs = W.make_inputs("prov_i32", n, P, W.CFG_A2NEXT_AGRS_24R, size_bytes=n * 4 + 43)
+    # the 3 x 8 two-dimensional AllGather has completion waits, which the lazy order refuses
+    prog = programs.allgather_2d(G, L) if kernel == "specialized" else programs.ring_allgather(P)
+    case(f"{kernel} {prog.name}")
+    ys, _ = _run(prog, xs, "i32", k=2, kernel=kernel)
+    assert_all_equal(ys, O1.allgather(xs))
+    if kernel == "specialized":  # completion waits: task order only
+        P, N = 8, 8 * 3001
+        case("specialized tree AR")
+        xs = W.make_inputs("normal_f32", N, P, W.CFG_TREE_AR, size_bytes=N * 4 + 43)
+        ys, _ = _run(programs.tree_allreduce(P), xs, "f32", k=4, kernel=kernel, repeat=2)
+        assert_all_equal(ys, O2.tree_allreduce(xs, P, "f32")[0])
+
+
+def test_specialized_kernel_trace():
+    """The generated kernel keeps the per-workgroup and per-instruction trace."""
+    P, N = 8, 8 * 4096
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 47)
+    ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=2, kernel="specialized", trace=True)
+    assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
+    wg, it = plan.trace(instructions=True)
+    ran = [w for w in wg if w[3] > 0]
+    assert len(ran) == plan.info()["num_workgroups"]
+    assert sum(w[3] for w in ran) == plan.info()["num_instructions"]
+    assert all(r[2] >= r[0] > 0 for r in it)
+
+
 # ------------------------------------------------------------------ under compute interference
 
 def test_collectives_under_concurrent_gemms():

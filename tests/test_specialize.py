@@ -1,0 +1,55 @@
+"""Plan-specialized kernels (generated per plan, compiled with hiprtc at create) and the
+lazy loop order, on the host: generation, compilation for gfx950 (no GPU needed),
+refusals, and the plan checker's interleavings in the lazy order."""
+
+import pytest
+
+from chunk_schedule_execution_amd import Plan, PlanConfig, capi, programs
+
+
+def host_plan(prog, k=1, **cfg):
+    cfg.setdefault("max_count", 1 << 16)
+    return Plan(prog, k, PlanConfig(host_only=True, **cfg))
+
+
+@pytest.mark.parametrize("kernel", ["specialized", "lazy"])
+def test_ring_allreduce_compiles_to_one_shape(kernel):
+    """Every rank's workgroups of a ring run the same operations, so one straight-line
+    sequence serves all 8k workgroups."""
+    plan = host_plan(programs.ring_allreduce(8), 4, transport="direct", kernel=kernel)
+    assert plan.info()["specialized_shapes"] == 1
+    assert host_plan(programs.ring_allreduce(8), 4).info()["specialized_shapes"] == 0
+
+
+def test_other_dtypes_and_protocols_compile():
+    assert host_plan(programs.hierarchical_allreduce(2, 4), 2, dtype="bf16", kernel="specialized").info()[
+        "specialized_shapes"] >= 2
+    assert host_plan(programs.ring_allreduce(4), 2, protocol="ll", kernel="lazy").info()["specialized_shapes"] == 1
+    assert host_plan(programs.direct_alltoall(4), 1, dtype="i32", kernel="specialized").info()["specialized_shapes"] >= 1
+
+
+def test_lazy_order_refuses_completion_waits():
+    """A completion wait covers a whole instruction; in the lazy order its workgroup may
+    still be at an earlier slice of others, so such plans are refused."""
+    assert host_plan(programs.tree_allreduce(8), 1).info()["num_waits"] > 0
+    with pytest.raises(capi.CCLError) as e:
+        host_plan(programs.tree_allreduce(8), 1, kernel="lazy")
+    assert e.value.status == capi.CCL_ERR_UNSUPPORTED
+
+
+def test_large_programs_stay_on_the_interpreter():
+    with pytest.raises(capi.CCLError) as e:
+        host_plan(programs.two_phase_alltoall(4, 8), 1, dtype="i32", nthreads=256, kernel="specialized")
+    assert e.value.status == capi.CCL_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("name,args,k,knobs", [("ring_allreduce", (5,), 2, dict(transport="direct")),
+                                               ("ring_allreduce", (4,), 3, {}),
+                                               ("hierarchical_allreduce", (2, 4), 2, {}),
+                                               ("alltonext", (2, 4), 2, {}),
+                                               ("allgather_2d", (2, 4), 1, {})])
+def test_lazy_plans_pass_random_interleavings(name, args, k, knobs):
+    """The plan checker runs the lazy order too: iteration s takes slice s of every
+    instruction of a workgroup; no interleaving deadlocks or reads unwritten data, and
+    the postcondition holds."""
+    host_plan(programs.REGISTRY[name](*args), k, kernel="lazy", **knobs).check(seed=7, nsims=3)
