@@ -42,6 +42,10 @@ TUNE_SLICES = [16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 
 PROTOCOLS = {0: ("simple", "staged", False), 1: ("ll", "staged", False), 2: ("simple", "direct", False),
              3: ("simple", "direct", True)}
 DEVICE_INPUT_BYTES = 32 << 20  # at or above this many bytes per rank, inputs are drawn on the device
+# executor kernels: the interpreting kernel, a kernel generated for the plan, and the
+# generated kernel in the lazy (slice-outer) loop order
+KERNELS = {0: "interpreter", 1: "specialized", 2: "lazy"}
+RING_KERNEL = 1  # the ring AllReduce workloads run generated kernels
 
 
 def parse():
@@ -50,10 +54,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--fixed", type=str, default="",
-                    help="k,nthreads,slice_bytes,protocol(0 simple, 1 LL, 2 simple+direct, 3 simple+direct+streaming): "
-                         "skip tuning (profiling runs)")
+                    help="k,nthreads,slice_bytes,protocol(0 simple, 1 LL, 2 simple+direct, 3 simple+direct+streaming)"
+                         "[,kernel(0 interpreter, 1 specialized, 2 lazy; default 1)]: skip tuning (profiling runs)")
     ap.add_argument("--no-extras", action="store_true", help="headline only (profiling runs)")
-    ap.add_argument("--section", choices=["interference"], default="",
+    ap.add_argument("--section", choices=["interference", "kernels"], default="",
                     help="after the headline run only this part of the extras")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -63,18 +67,18 @@ def parse():
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("executor.hip", "executor_device.h", "device_abi.h"):
+    for f in ("executor.hip", "executor_device.h", "device_abi.h", "specialize.cpp"):
         with open(os.path.join(ROOT, "chunk_schedule_execution_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def same_launch(a, b, piece_bytes):
-    """Two (k, nthreads, slice_bytes, protocol) configurations run the same kernel work:
-    equal apart from slice sizes that both exceed every instruction's piece (one slice
-    each)."""
+    """Two (k, nthreads, slice_bytes, protocol, kernel) configurations run the same
+    kernel work: equal apart from slice sizes that both exceed every instruction's piece
+    (one slice each)."""
     a, b = tuple(a), tuple(b)
-    if len(a) != 4 or len(b) != 4 or (a[0], a[1], a[3]) != (b[0], b[1], b[3]):
+    if len(a) != 5 or len(b) != 5 or (a[0], a[1], a[3], a[4]) != (b[0], b[1], b[3], b[4]):
         return False
     return a[2] == b[2] or (a[2] >= piece_bytes + 64 and b[2] >= piece_bytes + 64)
 
@@ -117,25 +121,25 @@ def main():
         xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=S)
         return N, [torch.from_numpy(x).to(dev) for x in xs], outs
 
-    def tune(prog, N, dtype="f32", protocols=15, variants=None):
-        """Tuned (k, nthreads, slice_bytes, protocol) of prog, or, given a list of
-        programs as `variants`, the best over those algorithm subspaces with
-        (..., variant index) appended."""
+    def tune(prog, N, dtype="f32", protocols=15, variants=None, kernel=0):
+        """Tuned (k, nthreads, slice_bytes, protocol, kernel) of prog with the given
+        executor kernel, or, given a list of programs as `variants`, the best over those
+        algorithm subspaces with (..., variant index) appended."""
         progs = variants if variants is not None else [prog]
-        base = PlanConfig(dtype=dtype, max_count=N).to_c()
+        base = PlanConfig(dtype=dtype, max_count=N, kernel=KERNELS[kernel]).to_c()
         arrs = [(capi.C.c_int32 * len(v))(*v) for v in (TUNE_FACTORS, TUNE_THREADS, TUNE_SLICES)]
         space = capi.ccl_tune_space(capi.C.cast(arrs[0], capi.C.POINTER(capi.C.c_int32)), len(TUNE_FACTORS),
                                     capi.C.cast(arrs[1], capi.C.POINTER(capi.C.c_int32)), len(TUNE_THREADS),
                                     capi.C.cast(arrs[2], capi.C.POINTER(capi.C.c_int32)), len(TUNE_SLICES),
                                     len(progs), 3, 10, protocols)
         best, rep = capi.ccl_tune([p.to_desc() for p in progs], N, base, space, stream.cuda_stream)
-        c = (best.parallel_factor, best.nthreads, best.slice_bytes, best.protocol)
+        c = (best.parallel_factor, best.nthreads, best.slice_bytes, best.protocol, kernel)
         return (c + (best.variant,) if variants is not None else c), rep.evaluations
 
-    def make_plan(prog, N, k, nt, sl, proto=0, dtype="f32", **kw):
+    def make_plan(prog, N, k, nt, sl, proto=0, kern=0, dtype="f32", **kw):
         return Plan(prog, k, PlanConfig(dtype=dtype, max_count=N, nthreads=nt, slice_bytes=sl,
                                         protocol=PROTOCOLS[proto][0], transport=PROTOCOLS[proto][1],
-                                        streaming=PROTOCOLS[proto][2], **kw))
+                                        streaming=PROTOCOLS[proto][2], kernel=KERNELS[kern], **kw))
 
     def time_launches(fn, iters, warmup=3):
         """Mean seconds per call of fn() (which enqueues work on `stream`)."""
@@ -184,10 +188,10 @@ def main():
     t0 = time.perf_counter()
     if args.fixed:
         cfg = tuple(int(v) for v in args.fixed.split(","))
-        cfg = cfg + (0,) * (4 - len(cfg))
+        cfg = cfg + (0, 0, RING_KERNEL)[len(cfg) - 2:] if len(cfg) < 5 else cfg
         tune_evals = 0
     else:
-        cfg, tune_evals = tune(prog, N)
+        cfg, tune_evals = tune(prog, N, kernel=RING_KERNEL)
     tune_s = time.perf_counter() - t0
     plan = make_plan(prog, N, *cfg)
     info = plan.info()
@@ -245,7 +249,7 @@ def main():
                    "ranks": P, "bytes_per_rank": S, "elements_per_rank": N,
                    "parallel_factor": cfg[0], "nthreads": cfg[1], "slice_bytes": cfg[2],
                    "protocol": PROTOCOLS[cfg[3]][0], "transport": PROTOCOLS[cfg[3]][1],
-                   "streaming": PROTOCOLS[cfg[3]][2],
+                   "streaming": PROTOCOLS[cfg[3]][2], "kernel": KERNELS[cfg[4]],
                    "xcd_local_stores": bool(info["xcd_local"]),
                    "scheduler": "hpds", "wg_alloc": "state", "workgroups": info["num_workgroups"],
                    "tuner_evaluations": tune_evals, "tune_seconds": round(tune_s, 2),
@@ -280,6 +284,8 @@ def main():
 
     if args.section == "interference":
         out["interference"] = interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release)
+    elif args.section == "kernels":
+        out["kernels"] = kernels(prog, ring_inputs, make_plan, time_launches, release, stream)
     elif not args.no_extras:
         out.update(extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inputs, device_inputs,
                           tune, make_plan, time_launches, busbw_ar, stats, release, fitting))
@@ -312,16 +318,16 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
     sweep = []
     for S in SWEEP + LARGE:
         N, ii, oo = ring_inputs(S)
-        c, _ = tune(prog, N)
+        c, _ = tune(prog, N, kernel=RING_KERNEL)
         p = make_plan(prog, N, *c)
         t = time_launches(lambda: p.execute(ii, oo, N, stream), 20 if S >= DEVICE_INPUT_BYTES else 50)
         row = {"bytes_per_rank": S, "k": c[0], "nthreads": c[1], "slice_bytes": c[2],
                "protocol": PROTOCOLS[c[3]][0], "transport": PROTOCOLS[c[3]][1], "streaming": PROTOCOLS[c[3]][2],
-               "busbw": round(busbw_ar(S, t), 2), **stats(p, N, t)}
+               "kernel": KERNELS[c[4]], "busbw": round(busbw_ar(S, t), 2), **stats(p, N, t)}
         if S in (1 << 20, 3 << 20, 32 << 20, 128 << 20):  # tuned versus fixed configurations
             for name, (k, nt, sl) in (("fixed_k1_nt256_slice128k", (1, 256, min(128 << 10, S // P))),
                                       ("fixed_k8_nt512_slice256k", (8, 512, 256 << 10))):
-                pf = make_plan(prog, N, k, nt, sl)
+                pf = make_plan(prog, N, k, nt, sl, 0, c[4])  # the tuned point's kernel
                 tf = time_launches(lambda: pf.execute(ii, oo, N, stream), 10 if S >= DEVICE_INPUT_BYTES else 30)
                 row[name + "_busbw"] = round(busbw_ar(S, tf), 2)
                 release(pf)
@@ -363,6 +369,9 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
     # ---- tuning under compute interference: bf16 GEMMs on a second stream ----------
     res["interference"] = interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release)
     progress("interference done")
+
+    # ---- interpreting vs generated kernels, and the lazy loop order ------------------
+    res["kernels"] = kernels(prog, ring_inputs, make_plan, time_launches, release, stream)
 
     # ---- 4 ranks, 1 MiB integer-valued fp32, 4 chunks, one channel, one slice -------
     N = 262144
@@ -500,8 +509,8 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
     progress("AllGather / ReduceScatter done")
 
     # ---- workgroup idle fraction from the device trace (one traced launch) ----------
-    def idle(pr, N, dtype, k, nt, sl, proto, ii, oo, **kw):
-        k, (pl,) = fitting([lambda kk: make_plan(pr, N, kk, nt, sl, proto, dtype=dtype, trace=True, **kw)],
+    def idle(pr, N, dtype, k, nt, sl, proto, kern, ii, oo, **kw):
+        k, (pl,) = fitting([lambda kk: make_plan(pr, N, kk, nt, sl, proto, kern, dtype=dtype, trace=True, **kw)],
                            ks=[x for x in (k, 8, 4, 2, 1) if x <= k])
         for _ in range(3):
             pl.execute(ii, oo, N, stream)
@@ -517,7 +526,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         return out
 
     N, ii, oo = ring_inputs(HEADLINE_BYTES)
-    c, _ = tune(prog, N)
+    c, _ = tune(prog, N, kernel=RING_KERNEL)
     idle_rows = {"ring_ar_8r_3mib_tuned": idle(prog, N, "f32", *c, ii, oo)}
     del ii, oo
     N = (64 << 20) // 4
@@ -525,7 +534,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
     oo = [torch.empty(N, device=dev) for _ in range(Pn)]
     for sched, alloc in (("hpds", "state"), ("rr", "connection")):
         idle_rows[f"alltonext_24r_64mib_split_{sched}_{alloc}"] = idle(
-            programs.alltonext(G, L, split=True), N, "f32", 8, 512, 256 << 10, 2, ii, oo, scheduler=sched,
+            programs.alltonext(G, L, split=True), N, "f32", 8, 512, 256 << 10, 2, 0, ii, oo, scheduler=sched,
             wg_alloc=alloc)
     del ii, oo
     release()
@@ -602,13 +611,13 @@ def interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_a
     for S in (3 << 20, 32 << 20):
         N, ii, oo = ring_inputs(S)
         t0 = time.perf_counter()
-        c_pure, _ = tune(prog, N)
+        c_pure, _ = tune(prog, N, kernel=RING_KERNEL)
         torch.cuda.synchronize()
         tune_s = time.perf_counter() - t0
         # a GEMM backlog that outlasts the tuning under interference (slower than alone)
         gemms(int(6 * tune_s / t_gemm) + 16)
         t0 = time.perf_counter()
-        c_int, ev = tune(prog, N)
+        c_int, ev = tune(prog, N, kernel=RING_KERNEL)
         tune_int_s = time.perf_counter() - t0
         torch.cuda.synchronize()
         row = {"bytes_per_rank": S, "tuner_evaluations_under_gemms": ev, "tune_seconds_alone": round(tune_s, 2),
@@ -617,6 +626,7 @@ def interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_a
             p = make_plan(prog, N, *cfg)
             alone, t, tf = timed_under_gemms(lambda: p.execute(ii, oo, N, stream), 50 if S < (32 << 20) else 20)
             row[name] = {"k": cfg[0], "nthreads": cfg[1], "slice_bytes": cfg[2], "protocol": cfg[3],
+                         "kernel": KERNELS[cfg[4]],
                          "workgroups": p.info()["num_workgroups"],
                          "us_alone": round(alone * 1e6, 2), "us_under_gemms": round(t * 1e6, 2),
                          "busbw_under_gemms": round(busbw_ar(S, t), 2), "gemm_tflops_meanwhile": round(tf, 1)}
@@ -626,6 +636,38 @@ def interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_a
     del a, b, c
     release()
     return out
+
+
+def kernels(prog, ring_inputs, make_plan, time_launches, release, stream):
+    """The interpreting kernel against kernels generated for the plan (ReSCCL's
+    lightweight kernel generation) and the generated kernel in the lazy loop order
+    (slice s of every instruction before slice s + 1 of any), on identical plans of the
+    8-rank ring AllReduce; several slices per instruction show the lazy order's bubbles."""
+    rows = []
+    for S, k, nt, sl, proto in ((32 << 10, 4, 256, 64 << 10, 1), (1 << 20, 32, 256, 128 << 10, 1),
+                                (1 << 20, 32, 256, 64 << 10, 2), (3 << 20, 32, 256, 64 << 10, 2),
+                                (3 << 20, 8, 256, 16 << 10, 2), (3 << 20, 2, 512, 16 << 10, 2),
+                                (32 << 20, 32, 512, 64 << 10, 3), (32 << 20, 32, 512, 16 << 10, 3)):
+        N, ii, oo = ring_inputs(S)
+        row = {"bytes_per_rank": S, "k": k, "nthreads": nt, "slice_bytes": sl, "protocol": PROTOCOLS[proto][0],
+               "transport": PROTOCOLS[proto][1], "streaming": PROTOCOLS[proto][2],
+               "slices_per_instruction": -(-(S // P // k) // sl)}
+        for kern, name in KERNELS.items():
+            t0 = time.perf_counter()
+            p = make_plan(prog, N, k, nt, sl, proto, kern)
+            create = time.perf_counter() - t0
+            t = min(time_launches(lambda: p.execute(ii, oo, N, stream), 30 if S >= DEVICE_INPUT_BYTES else 200)
+                    for _ in range(3))
+            p.status()
+            row[name + "_us"] = round(t * 1e6, 2)
+            row[name + "_create_s"] = round(create, 2)
+            release(p)
+        row["specialized_speedup"] = round(row["interpreter_us"] / row["specialized_us"], 3)
+        row["lazy_vs_specialized"] = round(row["lazy_us"] / row["specialized_us"], 3)
+        rows.append(row)
+        progress(f"kernels {S >> 10} KiB k={k}: {row['interpreter_us']} / {row['specialized_us']} / {row['lazy_us']} us")
+        del ii, oo
+    return rows
 
 
 def cpu_baseline(budget_s: float):
