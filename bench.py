@@ -413,12 +413,25 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
             s2.execute(mid1, mid2, sh, stream)
             s3.execute(mid2, oo, sh, stream)
         t3 = time_launches(three, 10)
-        hier.append({"bytes_per_rank": S, "fused_config": list(cf), "stage_configs": [list(c1), list(c2), list(c3)],
-                     "fused_us": round(tf * 1e6, 2), "three_launch_us": round(t3 * 1e6, 2),
-                     "fused_busbw": round(busbw_ar(S, tf, G * L), 2), "three_launch_busbw": round(busbw_ar(S, t3, G * L), 2),
-                     "speedup": round(t3 / tf, 3), "fused_hbm_frac": stats(pf, N, tf)["hbm_frac"],
-                     "fused_workgroups": pf.info()["num_workgroups"]})
+        row = {"bytes_per_rank": S, "fused_config": list(cf), "stage_configs": [list(c1), list(c2), list(c3)],
+               "fused_us": round(tf * 1e6, 2), "three_launch_us": round(t3 * 1e6, 2),
+               "fused_busbw": round(busbw_ar(S, tf, G * L), 2), "three_launch_busbw": round(busbw_ar(S, t3, G * L), 2),
+               "speedup": round(t3 / tf, 3), "fused_hbm_frac": stats(pf, N, tf)["hbm_frac"],
+               "fused_workgroups": pf.info()["num_workgroups"]}
         release(pf, s1, s2, s3)
+        if S <= (16 << 20):
+            # The stages' tuned points with generated kernels (tuning itself stays on the
+            # interpreter: a generated candidate compiles for about a second). The fused
+            # plan's workgroup programs are too long to generate (its code would outgrow
+            # the instruction cache), so it stays on the interpreter.
+            s1 = make_plan(stages[0], N, *c1[:4], 1, dtype="bf16")
+            s2 = make_plan(stages[1], sh, *c2[:4], 1, dtype="bf16")
+            s3 = make_plan(stages[2], sh, *c3[:4], 1, dtype="bf16")
+            t3g = time_launches(three, 10)
+            row.update({"generated_three_launch_us": round(t3g * 1e6, 2),
+                        "fused_vs_generated_three_launch": round(t3g / tf, 3)})
+            release(s1, s2, s3)
+        hier.append(row)
         del ii, oo, mid1, mid2
     res["hier_ar_16r_bf16"] = hier
     progress("hierarchical AllReduce done")

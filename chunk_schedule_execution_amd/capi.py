@@ -72,7 +72,9 @@ class ccl_plan_info_t(C.Structure):
                 ("max_resident_wgs", C.c_int32), ("grid_workgroups", C.c_int32),
                 ("xcd_local", C.c_int32), ("specialized_shapes", C.c_int32),
                 ("staging_bytes", C.c_int64), ("scratch_bytes", C.c_int64), ("flag_bytes", C.c_int64),
-                ("table_bytes", C.c_int64), ("compile_ms", C.c_double * 6), ("opcode_hist", C.c_int32 * 16)]
+                ("table_bytes", C.c_int64), ("compile_ms", C.c_double * 6), ("opcode_hist", C.c_int32 * 16),
+                ("specialized_instructions", C.c_int32), ("reserved1", C.c_int32),
+                ("specialized_code_bytes", C.c_int64)]
 
 
 class ccl_instr_info(C.Structure):

@@ -60,7 +60,8 @@ struct ccl_plan {
   unsigned long long* d_trace = nullptr;
   unsigned long long* d_xcd = nullptr;  // per launch-grid workgroup: XCD tag of the latest launch
   void* spec_fn = nullptr;              // generated kernel (CCL_FLAG_SPECIALIZE / LAZY), or the interpreter
-  int spec_shapes = 0;
+  int spec_shapes = 0, spec_instructions = 0;
+  int64_t spec_code_bytes = 0;
   hipEvent_t last = nullptr;    // recorded on last_stream when another stream needs ordering
   hipStream_t last_stream = nullptr;
   bool launched = false;
@@ -157,9 +158,10 @@ void setup_device(ccl_plan* p) {
     HIP_TRY(hipMemset(p->d_xcd, 0, std::max<size_t>(1, hp.dwg.size()) * 8));  // no tag matches an epoch >= 1
   }
   if (hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY)) {
-    const std::string src = specialized_source(hp, local, (hp.cfg.flags & CCL_FLAG_LAZY) != 0, &p->spec_shapes);
+    const std::string src = specialized_source(hp, local, (hp.cfg.flags & CCL_FLAG_LAZY) != 0, &p->spec_shapes,
+                                               &p->spec_instructions);
     int spec_blocks = 0;
-    p->spec_fn = load_specialized(src, p->device_id, hp.cfg.nthreads, &spec_blocks);
+    p->spec_fn = load_specialized(src, p->device_id, hp.cfg.nthreads, &spec_blocks, &p->spec_code_bytes);
     hp.max_resident_wgs = std::min(hp.max_resident_wgs, spec_blocks * cus);
     if (int(hp.dwg.size()) > spec_blocks * cus)
       fail(CCL_ERR_OUT_OF_RESOURCES, "plan needs " + std::to_string(hp.dwg.size()) +
@@ -215,8 +217,8 @@ int ccl_plan_create(const ccl_program_desc* prog, int nranks, int nchunks, int p
           fail(CCL_ERR_OUT_OF_RESOURCES, "plan needs more co-resident workgroups than the assumed device holds");
         if (p->hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY)) {  // generate and compile, load nothing
           bool local = !(p->hp.cfg.flags & CCL_FLAG_COHERENT_ONLY);
-          compile_specialized(specialized_source(p->hp, local, (p->hp.cfg.flags & CCL_FLAG_LAZY) != 0,
-                                                 &p->spec_shapes));
+          p->spec_code_bytes = compile_specialized(specialized_source(
+              p->hp, local, (p->hp.cfg.flags & CCL_FLAG_LAZY) != 0, &p->spec_shapes, &p->spec_instructions));
         }
       }
     } catch (...) {
@@ -333,6 +335,8 @@ int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info) {
     info->grid_workgroups = int(hp.dwg.size());
     info->xcd_local = plan->d_xcd ? 1 : 0;
     info->specialized_shapes = plan->spec_shapes;
+    info->specialized_instructions = plan->spec_instructions;
+    info->specialized_code_bytes = plan->spec_code_bytes;
     info->max_wg_per_rank = hp.max_wg_per_rank;
     info->num_instructions = int(hp.dins.size());
     info->num_subpipelines = hp.num_subpipes;

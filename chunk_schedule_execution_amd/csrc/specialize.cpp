@@ -36,7 +36,7 @@ extern const char kEmbeddedExecutorSource[];  // generated at build time
 
 namespace {
 
-constexpr int kMaxSpecializedInstructions = 160;
+constexpr int kMaxSpecializedInstructions = 32;
 
 std::string hex32(uint32_t v) {
   char b[16];
@@ -87,7 +87,7 @@ const std::vector<char>& compile_cached(const std::string& src) {
 
 }  // namespace
 
-std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, int* num_shapes) {
+std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, int* num_shapes, int* num_instructions) {
   const bool ll = hp.cfg.flags & CCL_FLAG_LL;
   const bool nt = hp.cfg.flags & CCL_FLAG_STREAMING;
   // operation words (operation and buffers, not the peer rank) are count-independent
@@ -122,9 +122,11 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, in
     base_shape[w] = it->second;
   }
   if (max_n > 512) fail(CCL_ERR_UNSUPPORTED, "specialized kernels hold at most 512 instructions per workgroup");
-  // Every generated instruction is a fully inlined copy of the per-instruction step:
-  // compile time and code size grow with the total, so plans with many distinct
-  // workgroup programs stay on the interpreter.
+  // Every generated instruction is a fully inlined copy of the per-instruction step
+  // (about 3 KB of code). Measured: kernels of up to 24 instructions (a ring of 24
+  // ranks, 80 KB code objects) beat the interpreter; from about 50 (150 KB and more,
+  // beyond the 64 KB instruction cache two CUs share) they lose by 1.3-1.8x. Larger
+  // plans therefore stay on the interpreter.
   size_t total = 0;
   for (const auto& sh : shapes) total += sh.size();
   if (total > size_t(kMaxSpecializedInstructions))
@@ -138,6 +140,7 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, in
              "the lazy loop order needs a plan without cross-workgroup completion waits (one would wait for a "
              "whole instruction while its workgroup is still at an earlier slice of others)");
   if (num_shapes) *num_shapes = int(shapes.size());
+  if (num_instructions) *num_instructions = int(total);
 
   const std::string targs = std::to_string(hp.cfg.dtype) + ", " + (xcd_local ? "true" : "false") + ", " +
                             (nt ? "true" : "false");
@@ -204,10 +207,11 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, in
   return s;
 }
 
-void compile_specialized(const std::string& src) { (void)compile_cached(src); }
+int64_t compile_specialized(const std::string& src) { return int64_t(compile_cached(src).size()); }
 
-void* load_specialized(const std::string& src, int device, int nthreads, int* blocks_per_cu) {
+void* load_specialized(const std::string& src, int device, int nthreads, int* blocks_per_cu, int64_t* code_bytes) {
   const std::vector<char>& obj = compile_cached(src);
+  *code_bytes = int64_t(obj.size());
   CodeCache& c = cache();
   hipFunction_t fn = nullptr;
   {

@@ -300,4 +300,7 @@ REGISTRY = {
     "alltonext": alltonext,
     "allgather_2d": allgather_2d,
     "reducescatter_2d": reducescatter_2d,
+    "hier_stage_reducescatter_intra": hier_stage_reducescatter_intra,
+    "hier_stage_allreduce_inter": hier_stage_allreduce_inter,
+    "hier_stage_allgather_intra": hier_stage_allgather_intra,
 }

@@ -145,7 +145,9 @@ typedef struct {
                                     and buffers as constants, compiled with hiprtc at create (code objects
                                     cached per process). Same records, flags and results; with HOST_ONLY the
                                     kernel is generated and compiled but not loaded. Compile failures give
-                                    CCL_ERR_HIP */
+                                    CCL_ERR_HIP; plans whose distinct sequences hold more than 32 instructions
+                                    in all give CCL_ERR_UNSUPPORTED (the code would outgrow the instruction
+                                    cache, and the interpreter is faster there) */
 #define CCL_FLAG_LAZY 0x400u      /* with or without SPECIALIZE: a generated kernel that runs the lazy loop
                                     order, slice s of every instruction of a workgroup before slice s + 1 of
                                     any (the algorithm once per slice; ReSCCL report, section 2.1), instead of
@@ -228,6 +230,9 @@ typedef struct {
   int64_t staging_bytes, scratch_bytes, flag_bytes, table_bytes;
   double compile_ms[6];       /* verify, DAG, fusion, schedule, workgroup allocation, lowering */
   int32_t opcode_hist[16];    /* lowered instructions by opcode bits (see ccl_instr_info.opcode) */
+  int32_t specialized_instructions; /* generated kernel: instructions over its distinct sequences */
+  int32_t reserved1;
+  int64_t specialized_code_bytes;   /* generated kernel: size of its code object */
 } ccl_plan_info_t;
 
 int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info);

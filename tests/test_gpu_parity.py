@@ -400,33 +400,47 @@ def test_specialized_ring_allreduce(kernel, P, N, k, sl, knobs):
 
 @pytest.mark.parametrize("kernel", ["specialized", "lazy"])
 def test_specialized_other_collectives(kernel):
+    """Generated kernels for the other small programs: the three hierarchical stages
+    (bf16, chained like the three-launch composition), 24-rank ring AllGather and
+    ReduceScatter, direct AllToAll and unsplit AllToNext."""
     G, L, N = 2, 8, 8 * 4099
-    case(f"{kernel} hierarchical bf16")
-    xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 41)
-    ys, plan = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, slice_bytes=4096, kernel=kernel, repeat=2)
-    assert plan.info()["specialized_shapes"] >= 2
+    P = G * L
+    case(f"{kernel} hierarchical stages bf16")
+    xs = W.make_inputs("normal_bf16", N, P, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 41)
+    sh = N // L
+    mid, _ = _run(programs.hier_stage_reducescatter_intra(G, L), xs, "bf16", k=2, slice_bytes=4096, kernel=kernel)
+    mid2, _ = _run(programs.hier_stage_allreduce_inter(G, L), mid, "bf16", k=2, count=sh, kernel=kernel)
+    ys, plan = _run(programs.hier_stage_allgather_intra(G, L), mid2, "bf16", k=2, count=sh, slice_bytes=4096,
+                    kernel=kernel)
+    assert plan.info()["specialized_shapes"] >= 1
     assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
-    G, L, N = 3, 8, 8 * 777
-    case(f"{kernel} alltonext split")
-    xs = W.make_inputs("normal_f32", N, G * L, W.CFG_A2NEXT_AGRS_24R, size_bytes=N * 4 + 41)
+    G, L = 3, 8
+    P, n = G * L, 24 * 41
+    xs = W.make_inputs("prov_i32", n, P, W.CFG_A2NEXT_AGRS_24R, size_bytes=n * 4 + 43)
+    case(f"{kernel} ring allgather 24")
+    ys, _ = _run(programs.ring_allgather(P), xs, "i32", k=2, transport="direct", kernel=kernel)
+    assert_all_equal(ys, O1.allgather(xs))
+    xs = W.make_inputs("normal_f32", n * P, P, W.CFG_A2NEXT_AGRS_24R, size_bytes=n * P * 4 + 43)
+    case(f"{kernel} ring reducescatter 24")
+    ys, _ = _run(programs.ring_reducescatter(P), xs, "f32", k=2, slice_bytes=4096, kernel=kernel)
+    want = O2.ring_reducescatter(xs, P, "f32")
+    for r in range(P):
+        assert np.array_equal(ys[r], want[r]), r
+    P, b = 8, 1031
+    xs = W.make_inputs("uniform_i32", P * b, P, W.CFG_A2A_32R_INT32, size_bytes=P * b * 4 + 43)
+    case(f"{kernel} direct alltoall 8")
+    ys, _ = _run(programs.direct_alltoall(P), xs, "i32", k=1, transport="direct", kernel=kernel)
+    want = O1.alltoall(xs)
+    for r in range(P):
+        assert np.array_equal(ys[r], want[r]), r
+    N = 8 * 777
+    case(f"{kernel} alltonext unsplit")
+    xs = W.make_inputs("normal_f32", N, G * L, W.CFG_A2NEXT_AGRS_24R, size_bytes=N * 4 + 43)
     prior = [np.full(N, -3.0, np.float32) for _ in range(G * L)]
-    ys, _ = _run(programs.alltonext(G, L, split=True), xs, "f32", k=2, prior=prior, slice_bytes=4096, kernel=kernel)
+    ys, _ = _run(programs.alltonext(G, L, split=False), xs, "f32", k=2, prior=prior, slice_bytes=4096, kernel=kernel)
     want = O1.alltonext(xs, prior)
     for r in range(G * L):
         assert np.array_equal(ys[r], want[r]), r
-    P, n = G * L, 24 * 41
-    xs = W.make_inputs("prov_i32", n, P, W.CFG_A2NEXT_AGRS_24R, size_bytes=n * 4 + 43)
-    # the 3 x 8 two-dimensional AllGather has completion waits, which the lazy order refuses
-    prog = programs.allgather_2d(G, L) if kernel == "specialized" else programs.ring_allgather(P)
-    case(f"{kernel} {prog.name}")
-    ys, _ = _run(prog, xs, "i32", k=2, kernel=kernel)
-    assert_all_equal(ys, O1.allgather(xs))
-    if kernel == "specialized":  # completion waits: task order only
-        P, N = 8, 8 * 3001
-        case("specialized tree AR")
-        xs = W.make_inputs("normal_f32", N, P, W.CFG_TREE_AR, size_bytes=N * 4 + 43)
-        ys, _ = _run(programs.tree_allreduce(P), xs, "f32", k=4, kernel=kernel, repeat=2)
-        assert_all_equal(ys, O2.tree_allreduce(xs, P, "f32")[0])
 
 
 def test_specialized_kernel_trace():
