@@ -44,8 +44,8 @@ PROTOCOLS = {0: ("simple", "staged", False), 1: ("ll", "staged", False), 2: ("si
 DEVICE_INPUT_BYTES = 32 << 20  # at or above this many bytes per rank, inputs are drawn on the device
 # executor kernels: the interpreting kernel, a kernel generated for the plan, and the
 # generated kernel in the lazy (slice-outer) loop order
-KERNELS = {0: "interpreter", 1: "specialized", 2: "lazy"}
-RING_KERNEL = 1  # the ring AllReduce workloads run generated kernels
+KERNELS = {0: "interpreter", 1: "specialized", 2: "lazy", 3: "specialized_loop"}
+KERNEL = 1  # every workload runs kernels generated for its plans (compiled when the plan is created)
 
 
 def parse():
@@ -121,7 +121,7 @@ def main():
         xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=S)
         return N, [torch.from_numpy(x).to(dev) for x in xs], outs
 
-    def tune(prog, N, dtype="f32", protocols=15, variants=None, kernel=0):
+    def tune(prog, N, dtype="f32", protocols=15, variants=None, kernel=KERNEL):
         """Tuned (k, nthreads, slice_bytes, protocol, kernel) of prog with the given
         executor kernel, or, given a list of programs as `variants`, the best over those
         algorithm subspaces with (..., variant index) appended."""
@@ -136,7 +136,7 @@ def main():
         c = (best.parallel_factor, best.nthreads, best.slice_bytes, best.protocol, kernel)
         return (c + (best.variant,) if variants is not None else c), rep.evaluations
 
-    def make_plan(prog, N, k, nt, sl, proto=0, kern=0, dtype="f32", **kw):
+    def make_plan(prog, N, k, nt, sl, proto=0, kern=KERNEL, dtype="f32", **kw):
         return Plan(prog, k, PlanConfig(dtype=dtype, max_count=N, nthreads=nt, slice_bytes=sl,
                                         protocol=PROTOCOLS[proto][0], transport=PROTOCOLS[proto][1],
                                         streaming=PROTOCOLS[proto][2], kernel=KERNELS[kern], **kw))
@@ -188,10 +188,10 @@ def main():
     t0 = time.perf_counter()
     if args.fixed:
         cfg = tuple(int(v) for v in args.fixed.split(","))
-        cfg = cfg + (0, 0, RING_KERNEL)[len(cfg) - 2:] if len(cfg) < 5 else cfg
+        cfg = cfg + (0, 0, KERNEL)[len(cfg) - 2:] if len(cfg) < 5 else cfg
         tune_evals = 0
     else:
-        cfg, tune_evals = tune(prog, N, kernel=RING_KERNEL)
+        cfg, tune_evals = tune(prog, N, kernel=KERNEL)
     tune_s = time.perf_counter() - t0
     plan = make_plan(prog, N, *cfg)
     info = plan.info()
@@ -286,6 +286,8 @@ def main():
         out["interference"] = interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release)
     elif args.section == "kernels":
         out["kernels"] = kernels(prog, ring_inputs, make_plan, time_launches, release, stream)
+        out["kernels_other"] = kernels_other(programs, device_inputs, make_plan, time_launches, release, stream,
+                                             torch, dev)
     elif not args.no_extras:
         out.update(extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inputs, device_inputs,
                           tune, make_plan, time_launches, busbw_ar, stats, release, fitting))
@@ -318,7 +320,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
     sweep = []
     for S in SWEEP + LARGE:
         N, ii, oo = ring_inputs(S)
-        c, _ = tune(prog, N, kernel=RING_KERNEL)
+        c, _ = tune(prog, N, kernel=KERNEL)
         p = make_plan(prog, N, *c)
         t = time_launches(lambda: p.execute(ii, oo, N, stream), 20 if S >= DEVICE_INPUT_BYTES else 50)
         row = {"bytes_per_rank": S, "k": c[0], "nthreads": c[1], "slice_bytes": c[2],
@@ -372,6 +374,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
 
     # ---- interpreting vs generated kernels, and the lazy loop order ------------------
     res["kernels"] = kernels(prog, ring_inputs, make_plan, time_launches, release, stream)
+    res["kernels_other"] = kernels_other(programs, device_inputs, make_plan, time_launches, release, stream, torch, dev)
 
     # ---- 4 ranks, 1 MiB integer-valued fp32, 4 chunks, one channel, one slice -------
     N = 262144
@@ -419,18 +422,6 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
                "speedup": round(t3 / tf, 3), "fused_hbm_frac": stats(pf, N, tf)["hbm_frac"],
                "fused_workgroups": pf.info()["num_workgroups"]}
         release(pf, s1, s2, s3)
-        if S <= (16 << 20):
-            # The stages' tuned points with generated kernels (tuning itself stays on the
-            # interpreter: a generated candidate compiles for about a second). The fused
-            # plan's workgroup programs are too long to generate (its code would outgrow
-            # the instruction cache), so it stays on the interpreter.
-            s1 = make_plan(stages[0], N, *c1[:4], 1, dtype="bf16")
-            s2 = make_plan(stages[1], sh, *c2[:4], 1, dtype="bf16")
-            s3 = make_plan(stages[2], sh, *c3[:4], 1, dtype="bf16")
-            t3g = time_launches(three, 10)
-            row.update({"generated_three_launch_us": round(t3g * 1e6, 2),
-                        "fused_vs_generated_three_launch": round(t3g / tf, 3)})
-            release(s1, s2, s3)
         hier.append(row)
         del ii, oo, mid1, mid2
     res["hier_ar_16r_bf16"] = hier
@@ -539,7 +530,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         return out
 
     N, ii, oo = ring_inputs(HEADLINE_BYTES)
-    c, _ = tune(prog, N, kernel=RING_KERNEL)
+    c, _ = tune(prog, N, kernel=KERNEL)
     idle_rows = {"ring_ar_8r_3mib_tuned": idle(prog, N, "f32", *c, ii, oo)}
     del ii, oo
     N = (64 << 20) // 4
@@ -547,7 +538,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
     oo = [torch.empty(N, device=dev) for _ in range(Pn)]
     for sched, alloc in (("hpds", "state"), ("rr", "connection")):
         idle_rows[f"alltonext_24r_64mib_split_{sched}_{alloc}"] = idle(
-            programs.alltonext(G, L, split=True), N, "f32", 8, 512, 256 << 10, 2, 0, ii, oo, scheduler=sched,
+            programs.alltonext(G, L, split=True), N, "f32", 8, 512, 256 << 10, 2, KERNEL, ii, oo, scheduler=sched,
             wg_alloc=alloc)
     del ii, oo
     release()
@@ -624,13 +615,13 @@ def interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_a
     for S in (3 << 20, 32 << 20):
         N, ii, oo = ring_inputs(S)
         t0 = time.perf_counter()
-        c_pure, _ = tune(prog, N, kernel=RING_KERNEL)
+        c_pure, _ = tune(prog, N, kernel=KERNEL)
         torch.cuda.synchronize()
         tune_s = time.perf_counter() - t0
         # a GEMM backlog that outlasts the tuning under interference (slower than alone)
         gemms(int(6 * tune_s / t_gemm) + 16)
         t0 = time.perf_counter()
-        c_int, ev = tune(prog, N, kernel=RING_KERNEL)
+        c_int, ev = tune(prog, N, kernel=KERNEL)
         tune_int_s = time.perf_counter() - t0
         torch.cuda.synchronize()
         row = {"bytes_per_rank": S, "tuner_evaluations_under_gemms": ev, "tune_seconds_alone": round(tune_s, 2),
@@ -679,6 +670,37 @@ def kernels(prog, ring_inputs, make_plan, time_launches, release, stream):
         row["lazy_vs_specialized"] = round(row["lazy_us"] / row["specialized_us"], 3)
         rows.append(row)
         progress(f"kernels {S >> 10} KiB k={k}: {row['interpreter_us']} / {row['specialized_us']} / {row['lazy_us']} us")
+        del ii, oo
+    return rows
+
+
+def kernels_other(programs, device_inputs, make_plan, time_launches, release, stream, torch, dev):
+    """Interpreting vs generated kernels (the loop form: these programs are too long for
+    straight-line code) on the other collectives, identical plans."""
+    TT = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}
+    rows = []
+    for name, pr, dt, N, k, nt, proto in (
+            ("hierarchical AR 2x8, 1 MiB bf16", programs.hierarchical_allreduce(2, 8), "bf16", 1 << 19, 16, 512, 1),
+            ("hierarchical AR 2x8, 16 MiB bf16", programs.hierarchical_allreduce(2, 8), "bf16", 1 << 23, 32, 512, 2),
+            ("tree AR 8 ranks, 64 KiB", programs.tree_allreduce(8), "f32", 1 << 14, 4, 256, 1),
+            ("two-phase AllToAll 4x8, 1 MiB int32", programs.two_phase_alltoall(4, 8), "i32", 1 << 18, 2, 256, 2),
+            ("2-D ReduceScatter 3x8, 768 KiB", programs.reducescatter_2d(3, 8), "f32", 24 * 8192, 4, 512, 0)):
+        P = pr.nranks
+        ii = device_inputs(dt, N, P, 8100 + len(rows))
+        oo = [torch.empty(max(1, pr.out_chunks * N // pr.in_chunks), dtype=TT[dt], device=dev) for _ in range(P)]
+        row = {"workload": name, "k": k, "nthreads": nt, "protocol": PROTOCOLS[proto][0],
+               "transport": PROTOCOLS[proto][1]}
+        for kern in (0, 1):
+            p = make_plan(pr, N, k, nt, 256 << 10, proto, kern, dtype=dt)
+            t = min(time_launches(lambda: p.execute(ii, oo, N, stream), 50) for _ in range(2))
+            p.status()
+            row[KERNELS[kern] + "_us"] = round(t * 1e6, 2)
+            if kern:
+                row["generated_instructions"] = p.info()["specialized_instructions"]
+            release(p)
+        row["specialized_speedup"] = round(row["interpreter_us"] / row["specialized_us"], 3)
+        rows.append(row)
+        progress(f"kernels: {name}: {row['interpreter_us']} / {row['specialized_us']} us")
         del ii, oo
     return rows
 

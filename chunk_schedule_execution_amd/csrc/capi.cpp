@@ -157,8 +157,9 @@ void setup_device(ccl_plan* p) {
     p->d_xcd = static_cast<unsigned long long*>(p->dev_alloc(std::max<size_t>(1, hp.dwg.size()) * 8));
     HIP_TRY(hipMemset(p->d_xcd, 0, std::max<size_t>(1, hp.dwg.size()) * 8));  // no tag matches an epoch >= 1
   }
-  if (hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY)) {
-    const std::string src = specialized_source(hp, local, (hp.cfg.flags & CCL_FLAG_LAZY) != 0, &p->spec_shapes,
+  if (hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY | CCL_FLAG_SPECIALIZE_LOOP)) {
+    const std::string src = specialized_source(hp, local, (hp.cfg.flags & CCL_FLAG_LAZY) != 0,
+                                               (hp.cfg.flags & CCL_FLAG_SPECIALIZE_LOOP) != 0, &p->spec_shapes,
                                                &p->spec_instructions);
     int spec_blocks = 0;
     p->spec_fn = load_specialized(src, p->device_id, hp.cfg.nthreads, &spec_blocks, &p->spec_code_bytes);
@@ -215,10 +216,12 @@ int ccl_plan_create(const ccl_program_desc* prog, int nranks, int nchunks, int p
         p->hp.max_resident_wgs = blocks * p->hp.cfg.num_cus;
         if (int(p->hp.dwg.size()) > p->hp.max_resident_wgs)
           fail(CCL_ERR_OUT_OF_RESOURCES, "plan needs more co-resident workgroups than the assumed device holds");
-        if (p->hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY)) {  // generate and compile, load nothing
+        if (p->hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY | CCL_FLAG_SPECIALIZE_LOOP)) {
+          // generate and compile, load nothing
           bool local = !(p->hp.cfg.flags & CCL_FLAG_COHERENT_ONLY);
           p->spec_code_bytes = compile_specialized(specialized_source(
-              p->hp, local, (p->hp.cfg.flags & CCL_FLAG_LAZY) != 0, &p->spec_shapes, &p->spec_instructions));
+              p->hp, local, (p->hp.cfg.flags & CCL_FLAG_LAZY) != 0, (p->hp.cfg.flags & CCL_FLAG_SPECIALIZE_LOOP) != 0,
+              &p->spec_shapes, &p->spec_instructions));
         }
       }
     } catch (...) {

@@ -131,7 +131,7 @@ int launch_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int
                       void* stream, std::string* err);
 
 // specialize.cpp: plan-specialized kernels (CCL_FLAG_SPECIALIZE / CCL_FLAG_LAZY)
-std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, int* num_shapes,
+std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bool force_loop, int* num_shapes,
                                int* num_instructions);
 int64_t compile_specialized(const std::string& src);  // compile only (no device needed); code bytes
 void* load_specialized(const std::string& src, int device, int nthreads, int* blocks_per_cu, int64_t* code_bytes);

@@ -36,7 +36,7 @@ extern const char kEmbeddedExecutorSource[];  // generated at build time
 
 namespace {
 
-constexpr int kMaxSpecializedInstructions = 32;
+constexpr int kMaxStraightInstructions = 32;
 
 std::string hex32(uint32_t v) {
   char b[16];
@@ -87,7 +87,8 @@ const std::vector<char>& compile_cached(const std::string& src) {
 
 }  // namespace
 
-std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, int* num_shapes, int* num_instructions) {
+std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bool force_loop, int* num_shapes,
+                               int* num_instructions) {
   const bool ll = hp.cfg.flags & CCL_FLAG_LL;
   const bool nt = hp.cfg.flags & CCL_FLAG_STREAMING;
   // operation words (operation and buffers, not the peer rank) are count-independent
@@ -122,17 +123,20 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, in
     base_shape[w] = it->second;
   }
   if (max_n > 512) fail(CCL_ERR_UNSUPPORTED, "specialized kernels hold at most 512 instructions per workgroup");
-  // Every generated instruction is a fully inlined copy of the per-instruction step
-  // (about 3 KB of code). Measured: kernels of up to 24 instructions (a ring of 24
-  // ranks, 80 KB code objects) beat the interpreter; from about 50 (150 KB and more,
-  // beyond the 64 KB instruction cache two CUs share) they lose by 1.3-1.8x. Larger
-  // plans therefore stay on the interpreter.
+  // Straight-line code inlines a copy of the per-instruction step (about 3 KB of code)
+  // for every instruction of every distinct workgroup program. Measured: up to 24
+  // instructions (a 24-rank ring, 80 KB code objects) it beats the interpreter; from
+  // about 50 (150 KB and more, beyond the 64 KB instruction cache two CUs share) it
+  // loses by 1.3-1.8x. Longer plans get the loop form instead: each workgroup walks its
+  // records and switches over the plan's distinct operation words, one inlined step
+  // per distinct word (a handful: 3 to 9 in the library's programs).
   size_t total = 0;
   for (const auto& sh : shapes) total += sh.size();
-  if (total > size_t(kMaxSpecializedInstructions))
-    fail(CCL_ERR_UNSUPPORTED, "plan has " + std::to_string(shapes.size()) + " distinct workgroup programs with " +
-                                  std::to_string(total) + " instructions in all; specialized kernels take at most " +
-                                  std::to_string(kMaxSpecializedInstructions));
+  std::vector<uint32_t> ops;
+  for (const auto& sh : shapes)
+    for (uint32_t o : sh)
+      if (std::find(ops.begin(), ops.end(), o) == ops.end()) ops.push_back(o);
+  const bool loop_form = force_loop || total > size_t(kMaxStraightInstructions);
   if (lazy)
     for (const auto& D : hp.dins)
       if (D.nwaits > 0)
@@ -140,50 +144,80 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, in
              "the lazy loop order needs a plan without cross-workgroup completion waits (one would wait for a "
              "whole instruction while its workgroup is still at an earlier slice of others)");
   if (num_shapes) *num_shapes = int(shapes.size());
-  if (num_instructions) *num_instructions = int(total);
+  if (num_instructions) *num_instructions = int(loop_form ? ops.size() : total);
 
   const std::string targs = std::to_string(hp.cfg.dtype) + ", " + (xcd_local ? "true" : "false") + ", " +
                             (nt ? "true" : "false");
   const std::string llk = ll ? "1" : "0";
+  auto step = [&](uint32_t opw, const std::string& rj, const std::string& gj, const std::string& tail) {
+    return "run_instr<" + targs + ", " + hex32(opw) + ", " + llk + ">(A, S, " + rj + ", " + gj + ", " + tail + ")";
+  };
   std::string s;
   s += "// generated: plan-specialized executor kernel\n#include <stdint.h>\n";
   s += kEmbeddedExecutorSource;
   s += "\nnamespace ccl {\nnamespace {\n";
-  s += "__constant__ int kSpecShape[" + std::to_string(std::max(1, nbase)) + "] = {";
-  for (int w = 0; w < nbase; ++w) s += (w ? ", " : "") + std::to_string(base_shape[w]);
-  if (nbase == 0) s += "-1";
-  s += "};\n";
-  for (size_t sh = 0; sh < shapes.size(); ++sh) {
-    const auto& seq = shapes[sh];
-    const int n = int(seq.size());
-    s += "__device__ __forceinline__ int spec_shape_" + std::to_string(sh) +
-         "(const ExecArgs& A, WgState& S, const DevExec* r, int g) {\n";
+  if (loop_form) {
+    // one step per distinct operation word; j-th record's word selects it
+    s += "__device__ __forceinline__ bool spec_step(const ExecArgs& A, WgState& S, const DevExec& R, int gi, int s0, "
+         "int s1, bool first, bool last) {\n";
+    s += "  switch (uint32_t(uni(int32_t(R.op))) & 0xffffffu) {\n";
+    for (uint32_t o : ops)
+      s += "    case " + hex32(o).substr(0, 8) + "u: return " + step(o, "R", "gi", "s0, s1, first, last") + ";\n";
+    s += "    default: return false;  // every word of the plan has a case\n  }\n}\n";
+    s += "__device__ __forceinline__ int spec_loop(const ExecArgs& A, WgState& S, const DevExec* r, int g, int n) {\n";
     if (!lazy) {
-      for (int j = 0; j < n; ++j)
-        s += "  if (!run_instr<" + targs + ", " + hex32(seq[j]) + ", " + llk + ">(A, S, r[" + std::to_string(j) +
-             "], g + " + std::to_string(j) + ", 0, -1, true, true)) return -1;\n";
+      s += "  for (int j = 0; j < n; ++j)\n";
+      s += "    if (!spec_step(A, S, r[j], g + j, 0, -1, true, true)) return -1;\n";
     } else {
-      // one slice of every instruction per iteration; an LL instruction is one pass
       s += "  int iters = 1;\n";
-      for (int j = 0; j < n; ++j) {
-        const std::string e = "e" + std::to_string(j);
-        if (ll)
-          s += "  const int " + e + " = 1;\n";
-        else
-          s += "  const int " + e + " = uni(r[" + std::to_string(j) + "].nsl) > 1 ? uni(r[" + std::to_string(j) +
-               "].nsl) : 1;\n";
-        s += "  iters = iters > " + e + " ? iters : " + e + ";\n";
-      }
-      s += "  for (int it = 0; it < iters; ++it) {\n";
-      for (int j = 0; j < n; ++j) {
-        const std::string e = "e" + std::to_string(j);
-        s += "    if (it < " + e + " && !run_instr<" + targs + ", " + hex32(seq[j]) + ", " + llk + ">(A, S, r[" +
-             std::to_string(j) + "], g + " + std::to_string(j) + ", it, it + 1, it == 0, it == " + e +
-             " - 1)) return -1;\n";
-      }
-      s += "  }\n";
+      s += "  for (int j = 0; j < n; ++j) {\n";
+      s += std::string("    const int e = ") + (ll ? "1" : "uni(r[j].nsl) > 1 ? uni(r[j].nsl) : 1") + ";\n";
+      s += "    iters = iters > e ? iters : e;\n  }\n";
+      s += "  for (int it = 0; it < iters; ++it)\n";
+      s += "    for (int j = 0; j < n; ++j) {\n";
+      s += std::string("      const int e = ") + (ll ? "1" : "uni(r[j].nsl) > 1 ? uni(r[j].nsl) : 1") + ";\n";
+      s += "      if (it < e && !spec_step(A, S, r[j], g + j, it, it + 1, it == 0, it == e - 1)) return -1;\n";
+      s += "    }\n";
     }
-    s += "  return " + std::to_string(n) + ";\n}\n";
+    s += "  return n;\n}\n";
+  } else {
+    s += "__constant__ int kSpecShape[" + std::to_string(std::max(1, nbase)) + "] = {";
+    for (int w = 0; w < nbase; ++w) s += (w ? ", " : "") + std::to_string(base_shape[w]);
+    if (nbase == 0) s += "-1";
+    s += "};\n";
+    for (size_t sh = 0; sh < shapes.size(); ++sh) {
+      const auto& seq = shapes[sh];
+      const int n = int(seq.size());
+      s += "__device__ __forceinline__ int spec_shape_" + std::to_string(sh) +
+           "(const ExecArgs& A, WgState& S, const DevExec* r, int g) {\n";
+      if (!lazy) {
+        for (int j = 0; j < n; ++j)
+          s += "  if (!" + step(seq[j], "r[" + std::to_string(j) + "]", "g + " + std::to_string(j), "0, -1, true, true") +
+               ") return -1;\n";
+      } else {
+        // one slice of every instruction per iteration; an LL instruction is one pass
+        s += "  int iters = 1;\n";
+        for (int j = 0; j < n; ++j) {
+          const std::string e = "e" + std::to_string(j);
+          if (ll)
+            s += "  const int " + e + " = 1;\n";
+          else
+            s += "  const int " + e + " = uni(r[" + std::to_string(j) + "].nsl) > 1 ? uni(r[" + std::to_string(j) +
+                 "].nsl) : 1;\n";
+          s += "  iters = iters > " + e + " ? iters : " + e + ";\n";
+        }
+        s += "  for (int it = 0; it < iters; ++it) {\n";
+        for (int j = 0; j < n; ++j) {
+          const std::string e = "e" + std::to_string(j);
+          s += "    if (it < " + e + " && !" +
+               step(seq[j], "r[" + std::to_string(j) + "]", "g + " + std::to_string(j),
+                    "it, it + 1, it == 0, it == " + e + " - 1") +
+               ") return -1;\n";
+        }
+        s += "  }\n";
+      }
+      s += "  return " + std::to_string(n) + ";\n}\n";
+    }
   }
   s += "}  // namespace\n}  // namespace ccl\n\n";
   s += "extern \"C\" __global__ __launch_bounds__(" + std::to_string(hp.cfg.nthreads) +
@@ -198,10 +232,14 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, in
   s += "  stage_records(A, W.first, W.n, s_rec, S.tid, S.nthr);\n";
   s += "  __syncthreads();\n";
   s += "  int ran = -1;\n";
-  s += "  switch (kSpecShape[blockIdx.x / " + std::to_string(stride) + "]) {\n";
-  for (size_t sh = 0; sh < shapes.size(); ++sh)
-    s += "    case " + std::to_string(sh) + ": ran = spec_shape_" + std::to_string(sh) + "(A, S, s_rec, W.first); break;\n";
-  s += "    default: break;\n  }\n";
+  if (loop_form) {
+    s += "  ran = spec_loop(A, S, s_rec, W.first, W.n);\n";
+  } else {
+    s += "  switch (kSpecShape[blockIdx.x / " + std::to_string(stride) + "]) {\n";
+    for (size_t sh = 0; sh < shapes.size(); ++sh)
+      s += "    case " + std::to_string(sh) + ": ran = spec_shape_" + std::to_string(sh) + "(A, S, s_rec, W.first); break;\n";
+    s += "    default: break;\n  }\n";
+  }
   s += "  if (ran < 0) return;\n";
   s += "  wg_end(A, W, S, ran);\n}\n";
   return s;

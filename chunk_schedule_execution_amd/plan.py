@@ -36,7 +36,9 @@ class PlanConfig:
     num_cus: int = 0
     timeout_us: int = 0
     # "interpreter" (one kernel for every plan), "specialized" (a kernel generated for
-    # this plan) or "lazy" (a generated kernel in the slice-outer loop order)
+    # this plan: straight-line code for short plans, the loop form for long ones),
+    # "specialized_loop" (the loop form always) or "lazy" (a generated kernel in the
+    # slice-outer loop order)
     kernel: str = "interpreter"
 
     def to_c(self) -> capi.ccl_plan_config:
@@ -59,6 +61,8 @@ class PlanConfig:
             flags |= capi.CCL_FLAG_COHERENT_ONLY
         if self.kernel == "specialized":
             flags |= capi.CCL_FLAG_SPECIALIZE
+        elif self.kernel == "specialized_loop":
+            flags |= capi.CCL_FLAG_SPECIALIZE | capi.CCL_FLAG_SPECIALIZE_LOOP
         elif self.kernel == "lazy":
             flags |= capi.CCL_FLAG_SPECIALIZE | capi.CCL_FLAG_LAZY
         elif self.kernel != "interpreter":

@@ -140,14 +140,17 @@ typedef struct {
                                     XCDs: senders then find most receivers on other XCDs and release each
                                     flag. Slow; exists to exercise that path */
 #define CCL_FLAG_SPECIALIZE 0x200u /* run a kernel generated for this plan instead of the interpreting one
-                                    (ReSCCL report, section 2.2, lightweight kernel generation): each distinct
-                                    sequence of instructions becomes straight-line code with the operations
-                                    and buffers as constants, compiled with hiprtc at create (code objects
-                                    cached per process). Same records, flags and results; with HOST_ONLY the
-                                    kernel is generated and compiled but not loaded. Compile failures give
-                                    CCL_ERR_HIP; plans whose distinct sequences hold more than 32 instructions
-                                    in all give CCL_ERR_UNSUPPORTED (the code would outgrow the instruction
-                                    cache, and the interpreter is faster there) */
+                                    (ReSCCL report, section 2.2, lightweight kernel generation), compiled with
+                                    hiprtc at create (code objects cached per process). When the plan's
+                                    distinct workgroup programs hold at most 32 instructions in all, each
+                                    becomes straight-line code with the operations and buffers as constants;
+                                    longer plans get the loop form (CCL_FLAG_SPECIALIZE_LOOP), whose code stays
+                                    within the instruction cache. Same records, flags and results; with
+                                    HOST_ONLY the kernel is generated and compiled but not loaded. Compile
+                                    failures give CCL_ERR_HIP */
+#define CCL_FLAG_SPECIALIZE_LOOP 0x800u /* a generated kernel in the loop form: each workgroup walks its
+                                    records and switches over the plan's distinct operation words, one step
+                                    with constant operation and buffers per word */
 #define CCL_FLAG_LAZY 0x400u      /* with or without SPECIALIZE: a generated kernel that runs the lazy loop
                                     order, slice s of every instruction of a workgroup before slice s + 1 of
                                     any (the algorithm once per slice; ReSCCL report, section 2.1), instead of

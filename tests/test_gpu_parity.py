@@ -443,6 +443,49 @@ def test_specialized_other_collectives(kernel):
         assert np.array_equal(ys[r], want[r]), r
 
 
+@pytest.mark.parametrize("kernel", ["specialized_loop", "lazy"])
+def test_generated_loop_form_long_programs(kernel):
+    """The loop form (one step per distinct operation word) on the long programs:
+    fused hierarchical bf16, split AllToNext, 2-D ReduceScatter, and with the task order
+    also the tree (completion waits) and the two-phase AllToAll."""
+    G, L, N = 2, 8, 8 * 4099
+    case(f"{kernel} fused hierarchical bf16")
+    xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 53)
+    ys, plan = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, slice_bytes=4096, kernel=kernel, repeat=2)
+    assert 0 < plan.info()["specialized_instructions"] <= 12
+    assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
+    G, L, N = 3, 8, 8 * 777
+    case(f"{kernel} alltonext split")
+    xs = W.make_inputs("normal_f32", N, G * L, W.CFG_A2NEXT_AGRS_24R, size_bytes=N * 4 + 53)
+    prior = [np.full(N, -3.0, np.float32) for _ in range(G * L)]
+    ys, _ = _run(programs.alltonext(G, L, split=True), xs, "f32", k=2, prior=prior, slice_bytes=4096, kernel=kernel)
+    want = O1.alltonext(xs, prior)
+    for r in range(G * L):
+        assert np.array_equal(ys[r], want[r]), r
+    P, n = G * L, 24 * 41
+    xs = W.make_inputs("normal_f32", n * P, P, W.CFG_A2NEXT_AGRS_24R, size_bytes=n * P * 4 + 53)
+    case(f"{kernel} reducescatter 2d")
+    ys, _ = _run(programs.reducescatter_2d(G, L), xs, "f32", k=2, kernel=kernel)
+    want = O2.reducescatter_2d(xs, G, L, "f32")
+    for r in range(P):
+        assert np.array_equal(ys[r], want[r]), r
+    if kernel == "lazy":
+        return
+    P, N = 8, 8 * 3001
+    case(f"{kernel} tree AR")
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_TREE_AR, size_bytes=N * 4 + 53)
+    ys, _ = _run(programs.tree_allreduce(P), xs, "f32", k=4, kernel=kernel, repeat=2)
+    assert_all_equal(ys, O2.tree_allreduce(xs, P, "f32")[0])
+    G, L, b = 4, 8, 257
+    P = G * L
+    case(f"{kernel} two-phase alltoall")
+    xs = W.make_inputs("uniform_i32", P * b, P, W.CFG_A2A_32R_INT32, size_bytes=P * b * 4 + 53)
+    ys, _ = _run(programs.two_phase_alltoall(G, L), xs, "i32", k=1, transport="direct", nthreads=256, kernel=kernel)
+    want = O1.alltoall(xs)
+    for r in range(P):
+        assert np.array_equal(ys[r], want[r]), r
+
+
 def test_specialized_kernel_trace():
     """The generated kernel keeps the per-workgroup and per-instruction trace."""
     P, N = 8, 8 * 4096

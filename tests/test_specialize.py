@@ -37,18 +37,20 @@ def test_lazy_order_refuses_completion_waits():
     assert e.value.status == capi.CCL_ERR_UNSUPPORTED
 
 
-@pytest.mark.parametrize("name,args", [("two_phase_alltoall", (4, 8)), ("hierarchical_allreduce", (2, 8)),
-                                       ("tree_allreduce", (8,))])
-def test_large_programs_stay_on_the_interpreter(name, args):
-    """Generated code is one inlined step per instruction of every distinct workgroup
-    program; past 32 instructions it outgrows the instruction cache (measured slower
-    than the interpreter), so such plans are refused."""
-    plan = host_plan(programs.REGISTRY[name](*args), 2, dtype="i32" if "alltoall" in name else "f32", nthreads=256)
-    with pytest.raises(capi.CCLError) as e:
-        host_plan(programs.REGISTRY[name](*args), 2, dtype="i32" if "alltoall" in name else "f32", nthreads=256,
-                  kernel="specialized")
-    assert e.value.status == capi.CCL_ERR_UNSUPPORTED
-    assert plan.info()["specialized_shapes"] == 0
+@pytest.mark.parametrize("name,args,dtype", [("two_phase_alltoall", (4, 8), "i32"),
+                                             ("hierarchical_allreduce", (2, 8), "bf16"), ("tree_allreduce", (8,), "f32")])
+def test_long_programs_get_the_loop_form(name, args, dtype):
+    """Straight-line code inlines one step per instruction of every distinct workgroup
+    program; past 32 instructions it would outgrow the instruction cache, so long plans
+    get the loop form: one step per distinct operation word, selected per record."""
+    prog = programs.REGISTRY[name](*args)
+    loop = host_plan(prog, 2, dtype=dtype, nthreads=256, kernel="specialized").info()
+    assert 3 <= loop["specialized_instructions"] <= 12  # distinct operation words
+    assert loop["specialized_code_bytes"] < 64 << 10
+    short = host_plan(programs.ring_allreduce(8), 2, kernel="specialized").info()
+    assert short["specialized_instructions"] == 15  # straight-line: every instruction
+    forced = host_plan(programs.ring_allreduce(8), 2, kernel="specialized_loop").info()
+    assert forced["specialized_instructions"] == len({e.opcode for e in host_plan(programs.ring_allreduce(8), 2).export()})
 
 
 @pytest.mark.parametrize("name,args,k,knobs", [("ring_allreduce", (5,), 2, dict(transport="direct")),
