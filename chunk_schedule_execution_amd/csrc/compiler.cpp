@@ -848,6 +848,18 @@ void lower(HostPlan& hp) {
   hp.dwg.clear();
   hp.dins.clear();
   hp.dxf.assign(size_t(nX) * k, DevXfer{});
+  // the base workgroup that waits for each instruction's completion flag, if only one does
+  std::vector<int> waiter_wg(hp.ins.size(), -1);
+  {
+    std::vector<char> several(hp.ins.size(), 0);
+    for (const auto& V : hp.ins)
+      for (int u : V.waits) {
+        if (waiter_wg[u] >= 0 && waiter_wg[u] != V.wg) several[u] = 1;
+        waiter_wg[u] = V.wg;
+      }
+    for (size_t u = 0; u < hp.ins.size(); ++u)
+      if (several[u]) waiter_wg[u] = -1;
+  }
   hp.dwaits.clear();
   hp.dins_base.clear();
   int64_t M = hp.cfg.max_count;
@@ -919,6 +931,7 @@ void lower(HostPlan& hp) {
         D.instance = i;
         D.pad0 = len_idx_of(hp, t);
         D.peer_wg = I.xout >= 0 ? hp.ins[hp.xf[I.xout].receiver].wg * stride + i : -1;
+        D.done_peer = I.done_flag >= 0 && waiter_wg[t] >= 0 ? waiter_wg[t] * stride + i : -1;
         D.t_buf = D.t_rank = D.t_idx = -1;
         if (I.xout >= 0 && hp.xf[I.xout].direct) {
           const Instr& R = hp.ins[hp.xf[I.xout].receiver];
@@ -1013,6 +1026,7 @@ void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec
     if (nsl >= (int64_t(1) << kEpochShift)) fail(CCL_ERR_INVALID_ARGUMENT, "too many slices for one transfer");
     E.nsl = int32_t(nsl);
     E.peer_wg = D.peer_wg;
+    E.done_peer = D.done_peer;
     if ((D.op & OPB_RECV) && !(D.op & OPB_LOCAL_IN))
       E.a_off = slot_off(D.xin);
     else

@@ -37,7 +37,7 @@ struct DevInstr {  // host-side lowered instruction
   int32_t pad0;                // chunk index that fixes the instruction's element range
   int32_t peer_wg;             // OPB_SEND: launch-grid workgroup that receives (-1 = none)
   int32_t t_buf, t_rank, t_idx;  // direct OPB_SEND: receiver's buffer, rank and chunk (t_buf -1: staging slot)
-  int32_t pad1;
+  int32_t done_peer;             // done_flag >= 0: the one workgroup that waits for it (-1: several)
 };
 
 struct DevXfer {  // 32 bytes: one send -> recv transfer
@@ -65,7 +65,10 @@ struct DevExec {  // 80 bytes
   int32_t peer_wg; // OPB_SEND: launch-grid workgroup of the receiver (-1 = none)
   int64_t len;     // elements
   int64_t a_off, b_off, d_off, t_off;
-  int64_t pad1;
+  // done_flag >= 0: launch-grid workgroup of the only waiter (-1: several); a waiter on
+  // the producer's XCD (its tag says so) lets an XCD-local layout skip the L2 writeback
+  int32_t done_peer;
+  int32_t pad1;
 };
 static_assert(sizeof(DevExec) == 80, "DevExec layout");
 

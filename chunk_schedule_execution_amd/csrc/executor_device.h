@@ -695,6 +695,10 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
     const int peer = uni(R.peer_wg);
     if (peer >= 0) peer_tag = __hip_atomic_load(&A.xcd_tags[peer], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // likewise the tag of the one workgroup that waits for this instruction's completion
+  unsigned long long done_tag = 0;
+  const int done_peer = (XL && last && done_flag >= 0 && A.xcd_tags) ? uni(R.done_peer) : -1;
+  if (done_peer >= 0) done_tag = __hip_atomic_load(&A.xcd_tags[done_peer], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const bool ll = LLK < 0 ? A.ll != 0 : LLK == 1;
   if (ll) {
     // one pass over the whole range (at s_begin 0); receivers poll the units they consume
@@ -731,7 +735,15 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
     }
   }
   if (last) {
-    if (done_flag >= 0 && tid == 0) release_store(&A.dflags[done_flag], A.epoch);
+    if (done_peer >= 0 && use_here(done_tag) == S.my_tag) {
+      // The waiter shares this XCD's L2, where this instruction's plain stores land:
+      // every wave's stores complete, then a plain flag store (no L2 writeback).
+      wait_vm_stores();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_store(&A.dflags[done_flag], A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    } else if (done_flag >= 0 && tid == 0) {
+      release_store(&A.dflags[done_flag], A.epoch);
+    }
     if (S.itrace && tid == 0) S.itrace[4 * size_t(gi) + 2] = (unsigned long long)wall_clock64();
   }
   return true;

@@ -445,15 +445,17 @@ def test_specialized_other_collectives(kernel):
 
 @pytest.mark.parametrize("kernel", ["specialized_loop", "lazy"])
 def test_generated_loop_form_long_programs(kernel):
-    """The loop form (one step per distinct operation word) on the long programs:
-    fused hierarchical bf16, split AllToNext, 2-D ReduceScatter, and with the task order
-    also the tree (completion waits) and the two-phase AllToAll."""
+    """The loop form (one step per distinct operation word) on the long programs: split
+    AllToNext and 2-D ReduceScatter, and with the task order also the plans with
+    completion waits: fused hierarchical bf16, tree and two-phase AllToAll."""
     G, L, N = 2, 8, 8 * 4099
-    case(f"{kernel} fused hierarchical bf16")
-    xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 53)
-    ys, plan = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, slice_bytes=4096, kernel=kernel, repeat=2)
-    assert 0 < plan.info()["specialized_instructions"] <= 12
-    assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
+    if kernel != "lazy":  # the fused hierarchical plan has completion waits
+        case(f"{kernel} fused hierarchical bf16")
+        xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 53)
+        ys, plan = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, slice_bytes=4096, kernel=kernel,
+                        repeat=2)
+        assert 0 < plan.info()["specialized_instructions"] <= 12
+        assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
     G, L, N = 3, 8, 8 * 777
     case(f"{kernel} alltonext split")
     xs = W.make_inputs("normal_f32", N, G * L, W.CFG_A2NEXT_AGRS_24R, size_bytes=N * 4 + 53)
