@@ -438,7 +438,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         row = {"bytes_per_rank": S}
         for name, pr in (("two_phase", programs.two_phase_alltoall(G, L)), ("direct", programs.direct_alltoall(Pa))):
             best = None
-            for k, nt in ((1, 256), (2, 256), (4, 256)):
+            for k, nt in ((1, 256), (2, 256), (2, 128), (4, 128)):
                 try:
                     pl = make_plan(pr, N, k, nt, 256 << 10, 2, dtype="i32")
                 except capi.CCLError:

@@ -249,8 +249,8 @@ def test_state_allocation_uses_fewer_workgroups():
     G, L = 3, 8
     for prog in (programs.alltonext(G, L, split=True), programs.two_phase_alltoall(4, 8),
                  programs.reducescatter_2d(G, L), programs.allgather_2d(G, L)):
-        conn = host_plan(prog, scheduler="hpds", wg_alloc="connection").info()["num_workgroups"]
-        state = host_plan(prog, scheduler="hpds", wg_alloc="state").info()["num_workgroups"]
+        conn = host_plan(prog, scheduler="hpds", wg_alloc="connection", nthreads=128).info()["num_workgroups"]
+        state = host_plan(prog, scheduler="hpds", wg_alloc="state", nthreads=128).info()["num_workgroups"]
         assert state <= conn, prog.name
     conn = host_plan(programs.alltonext(G, L), wg_alloc="connection").info()["num_workgroups"]
     state = host_plan(programs.alltonext(G, L), wg_alloc="state").info()["num_workgroups"]

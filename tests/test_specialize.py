@@ -58,7 +58,7 @@ def test_long_programs_get_the_loop_form(name, args, dtype):
                                                ("ring_reducescatter", (6,), 2, {}),
                                                ("hier_stage_reducescatter_intra", (2, 4), 2, {}),
                                                ("alltonext", (3, 4, False), 2, {}),
-                                               ("allgather_2d", (2, 4), 1, {})])
+                                               ("ring_allgather", (6,), 2, {})])
 def test_lazy_plans_pass_random_interleavings(name, args, k, knobs):
     """The plan checker runs the lazy order too: iteration s takes slice s of every
     instruction of a workgroup; no interleaving deadlocks or reads unwritten data, and
