@@ -675,15 +675,16 @@ def kernels(prog, ring_inputs, make_plan, time_launches, release, stream):
 
 
 def kernels_other(programs, device_inputs, make_plan, time_launches, release, stream, torch, dev):
+    from chunk_schedule_execution_amd import capi
     """Interpreting vs generated kernels (the loop form: these programs are too long for
     straight-line code) on the other collectives, identical plans."""
     TT = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}
     rows = []
     for name, pr, dt, N, k, nt, proto in (
             ("hierarchical AR 2x8, 1 MiB bf16", programs.hierarchical_allreduce(2, 8), "bf16", 1 << 19, 16, 512, 1),
-            ("hierarchical AR 2x8, 16 MiB bf16", programs.hierarchical_allreduce(2, 8), "bf16", 1 << 23, 32, 512, 2),
+            ("hierarchical AR 2x8, 16 MiB bf16", programs.hierarchical_allreduce(2, 8), "bf16", 1 << 23, 16, 512, 2),
             ("tree AR 8 ranks, 64 KiB", programs.tree_allreduce(8), "f32", 1 << 14, 4, 256, 1),
-            ("two-phase AllToAll 4x8, 1 MiB int32", programs.two_phase_alltoall(4, 8), "i32", 1 << 18, 2, 256, 2),
+            ("two-phase AllToAll 4x8, 1 MiB int32", programs.two_phase_alltoall(4, 8), "i32", 1 << 18, 1, 256, 2),
             ("2-D ReduceScatter 3x8, 768 KiB", programs.reducescatter_2d(3, 8), "f32", 24 * 8192, 4, 512, 0)):
         P = pr.nranks
         ii = device_inputs(dt, N, P, 8100 + len(rows))
@@ -691,16 +692,21 @@ def kernels_other(programs, device_inputs, make_plan, time_launches, release, st
         row = {"workload": name, "k": k, "nthreads": nt, "protocol": PROTOCOLS[proto][0],
                "transport": PROTOCOLS[proto][1]}
         for kern in (0, 1):
-            p = make_plan(pr, N, k, nt, 256 << 10, proto, kern, dtype=dt)
+            try:
+                p = make_plan(pr, N, k, nt, 256 << 10, proto, kern, dtype=dt)
+            except capi.CCLError as e:  # e.g. more workgroups than fit at once
+                row[KERNELS[kern] + "_skipped"] = str(e)[:120]
+                continue
             t = min(time_launches(lambda: p.execute(ii, oo, N, stream), 50) for _ in range(2))
             p.status()
             row[KERNELS[kern] + "_us"] = round(t * 1e6, 2)
             if kern:
                 row["generated_instructions"] = p.info()["specialized_instructions"]
             release(p)
-        row["specialized_speedup"] = round(row["interpreter_us"] / row["specialized_us"], 3)
+        if "interpreter_us" in row and "specialized_us" in row:
+            row["specialized_speedup"] = round(row["interpreter_us"] / row["specialized_us"], 3)
         rows.append(row)
-        progress(f"kernels: {name}: {row['interpreter_us']} / {row['specialized_us']} us")
+        progress(f"kernels: {name}: {row.get('interpreter_us')} / {row.get('specialized_us')} us")
         del ii, oo
     return rows
 

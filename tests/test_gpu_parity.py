@@ -126,15 +126,19 @@ def test_repeated_launches_and_counts():
     plan.destroy()
 
 
-@pytest.mark.parametrize("S,k", [(3 << 20, 8), (32 << 20, 32)])
-def test_ring_allreduce_8r_full_size_sampled(S, k):
-    """Full sizes in the benchmark's launch configuration: 4096 sampled elements
-    against the chain-order oracle, the fp32 bound everywhere sampled, and all ranks
-    identical over the whole buffer."""
+@pytest.mark.parametrize("S,k,nt,sl,knobs", [
+    (3 << 20, 8, 512, 256 << 10, dict(kernel="interpreter")),
+    (3 << 20, 32, 256, 64 << 10, dict(transport="direct", kernel="specialized")),  # the benchmark's headline point
+    (32 << 20, 32, 512, 64 << 10, dict(transport="direct", streaming=True, kernel="specialized")),
+    (256 << 20, 32, 512, 256 << 10, dict(transport="direct", streaming=True, kernel="specialized"))])
+def test_ring_allreduce_8r_full_size_sampled(S, k, nt, sl, knobs):
+    """Full sizes in the benchmark's launch configurations: sampled elements against the
+    chain-order oracle, the fp32 bound everywhere sampled, and all ranks identical over
+    the whole buffer."""
     P, N = 8, S // 4
-    case(f"ring AR full size S={S} k={k}")
+    case(f"ring AR full size S={S} k={k} nt={nt} {knobs}")
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=S)
-    ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=k, nthreads=512, slice_bytes=256 << 10)
+    ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=k, nthreads=nt, slice_bytes=sl, repeat=2, **knobs)
     for r in range(1, P):
         assert np.array_equal(ys[r], ys[0])
     rng = np.random.default_rng(1)
@@ -142,6 +146,23 @@ def test_ring_allreduce_8r_full_size_sampled(S, k):
     assert np.array_equal(ys[0][idx], O2.ring_allreduce_at(xs, P, idx, "f32"))
     ref = O1.allreduce_at(xs, idx, "f32")
     assert nm.scaled_error(ys[0][idx], ref.exact, ref.abs_sum, "f32") <= F32_TOL(P)
+
+
+def test_hierarchical_allreduce_16r_bf16_64mib_sampled():
+    """The 2 x 8 bf16 hierarchical AllReduce at 64 MiB per rank in the benchmark's kind
+    of launch (generated kernel, direct transport, k=16): sampled elements against the
+    oracle's chain order, all ranks identical."""
+    G, L = 2, 8
+    P, N = G * L, (64 << 20) // 2
+    case(f"hierarchical bf16 64 MiB sampled")
+    xs = W.make_inputs("normal_bf16", N, P, W.CFG_HIER_AR_16R_BF16, size_bytes=64 << 20)
+    ys, _ = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=16, nthreads=512, slice_bytes=256 << 10,
+                 transport="direct", kernel="specialized")
+    for r in range(1, P):
+        assert np.array_equal(ys[r], ys[0])
+    rng = np.random.default_rng(2)
+    idx = np.unique(np.concatenate([rng.integers(0, N, 4000), [0, N - 1]]))
+    assert np.array_equal(ys[0][idx], O2.hierarchical_allreduce_at(xs, G, L, idx, "bf16"))
 
 
 # ------------------------------------------------------------------ hierarchical, bf16
