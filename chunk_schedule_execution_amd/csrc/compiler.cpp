@@ -543,41 +543,100 @@ int64_t link_of(const HostPlan& hp, const Instr& I) {
 // when no instruction of the receiving rank that could run before the receive touches
 // the location: every other accessor must be a descendant of the receive in the DAG.
 // The receive then waits for the transfer's flag and reads (forwards) from there.
+// Direct transport: the sender writes the received data straight into a location of
+// the receiving rank (its landing), so the transfer needs no staging slot. The landing
+// is the receive's destination; a receive that reduces without storing locally (it only
+// forwards the sum) lands in the same chunk of the rank's output, else of its scratch.
+// Legal when every other instruction of that rank that touches the landing is either a
+// DAG descendant of the receive (it runs after the data was consumed) or a DAG ancestor
+// of the sender (it is done with it before the sender writes), and touches exactly the
+// landing's chunk range if the DAG orders it only slice by slice. Every DAG edge is
+// enforced at run time: program order and completion flags order a whole instruction
+// before the next, but a transfer (and program order under the lazy loop order) only
+// orders slice s after slice s. Along a path of such edges alone, slice s of one end
+// comes before slice s of the other, which covers the same elements only when both
+// operate on the same range. A copy-only receive then only waits (and forwards from its
+// landing); a reducing one reads its landing in place of the slot.
 void choose_direct(HostPlan& hp, const std::vector<std::set<int>>& dag) {
   if (!(hp.cfg.flags & CCL_FLAG_DIRECT) || (hp.cfg.flags & CCL_FLAG_LL)) return;
   const size_t n = hp.ins.size();
-  std::vector<int> mark(n, -1), stack;
+  std::vector<std::vector<int>> pred(n);
+  for (size_t u = 0; u < n; ++u)
+    for (int v : dag[u]) pred[v].push_back(int(u));
+  std::vector<int> below(n, -1), above(n, -1), stack;
+  // transfer chains: the instruction a sender feeds and the one a receiver is fed by
+  std::vector<int> feeds(n, -1), fed_by(n, -1);
+  for (const Xfer& X : hp.xf) {
+    feeds[X.sender] = X.receiver;
+    fed_by[X.receiver] = X.sender;
+  }
+  const bool lazy = (hp.cfg.flags & CCL_FLAG_LAZY) != 0;
+  std::vector<int> slicewise(n, -1);
   auto overlaps = [](const Loc& l, int lc, const Loc& m, int mc) {
     return l.valid() && m.valid() && l.buf == m.buf && l.idx < m.idx + mc && m.idx < l.idx + lc;
+  };
+  auto mark_from = [&](int root, int tag, std::vector<int>& mark, bool down) {
+    stack.assign(1, root);
+    mark[root] = tag;
+    while (!stack.empty()) {
+      int u = stack.back();
+      stack.pop_back();
+      const auto visit = [&](int v) {
+        if (mark[v] != tag) {
+          mark[v] = tag;
+          stack.push_back(v);
+        }
+      };
+      if (down)
+        for (int v : dag[u]) visit(v);
+      else
+        for (int v : pred[u]) visit(v);
+    }
   };
   for (size_t x = 0; x < hp.xf.size(); ++x) {
     Xfer& X = hp.xf[x];
     Instr& R = hp.ins[X.receiver];
-    if (!R.recv || R.local_in || R.b.valid() || !R.d.valid() || hp.ins[X.sender].rank == R.rank) continue;
-    stack.assign(1, X.receiver);
-    mark[X.receiver] = int(x);
-    while (!stack.empty()) {
-      int u = stack.back();
-      stack.pop_back();
-      for (int v : dag[u])
-        if (mark[v] != int(x)) {
-          mark[v] = int(x);
-          stack.push_back(v);
-        }
+    if (!R.recv || R.local_in || hp.ins[X.sender].rank == R.rank) continue;
+    std::vector<Loc> cands;
+    if (R.d.valid()) {
+      cands.push_back(R.d);
+    } else if (R.b.valid()) {
+      if (R.b.idx + R.cnt <= hp.out_chunks) cands.push_back(Loc{CCL_BUF_OUTPUT, R.b.idx});
+      if (R.b.idx + R.cnt <= hp.scr_chunks) cands.push_back(Loc{CCL_BUF_SCRATCH, R.b.idx});
     }
-    bool ok = true;
-    for (size_t i = 0; i < n && ok; ++i) {
-      if (mark[i] == int(x)) continue;  // the receive itself and its descendants
-      const Instr& I = hp.ins[i];
-      if (I.rank != R.rank) continue;
-      if (overlaps(I.a, I.cnt, R.d, R.cnt) || overlaps(I.b, I.cnt, R.d, R.cnt) || overlaps(I.d, I.cnt, R.d, R.cnt))
-        ok = false;
+    if (cands.empty()) continue;
+    mark_from(X.receiver, int(x), below, true);
+    mark_from(X.sender, int(x), above, false);
+    for (const Loc& land : cands) {
+      if (R.b.valid() && overlaps(land, R.cnt, R.b, R.cnt)) continue;  // the operand is read as data lands
+      bool ok = true;
+      for (size_t i = 0; i < n && ok; ++i) {
+        if (below[i] == int(x) || above[i] == int(x)) continue;
+        const Instr& I = hp.ins[i];
+        if (I.rank != R.rank) continue;
+        if (overlaps(I.a, I.cnt, land, R.cnt) || overlaps(I.b, I.cnt, land, R.cnt) ||
+            overlaps(I.d, I.cnt, land, R.cnt))
+          ok = false;
+      }
+      // instructions ordered against the transfer only slice by slice
+      for (int u = feeds[X.receiver]; u >= 0 && slicewise[u] != int(x); u = feeds[u]) slicewise[u] = int(x);
+      for (int u = X.sender; u >= 0 && slicewise[u] != int(x); u = fed_by[u]) slicewise[u] = int(x);
+      for (size_t i = 0; i < n && ok; ++i) {
+        if (i == size_t(X.receiver) || (below[i] != int(x) && above[i] != int(x))) continue;
+        if (!lazy && slicewise[i] != int(x)) continue;
+        const Instr& I = hp.ins[i];
+        if (I.rank != R.rank) continue;
+        for (const Loc* l : {&I.a, &I.b, &I.d})
+          if (overlaps(*l, I.cnt, land, R.cnt) && !(l->buf == land.buf && l->idx == land.idx && I.cnt == R.cnt))
+            ok = false;  // ordered by the DAG, but its slices cover other elements
+      }
+      if (!ok) continue;
+      X.direct = true;
+      R.local_in = true;
+      R.a = land;
+      if (!R.b.valid()) R.d = Loc{};  // copy-only: the data is already in place
+      break;
     }
-    if (!ok) continue;
-    X.direct = true;
-    R.local_in = true;
-    R.a = R.d;
-    R.d = Loc{};
   }
 }
 
