@@ -67,7 +67,7 @@ def parse():
 
 def source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("executor.hip", "executor_device.h", "device_abi.h", "specialize.cpp"):
+    for f in ("executor.hip", "executor_device.h", "device_abi.h", "specialize.cpp", "compiler.cpp"):
         with open(os.path.join(ROOT, "chunk_schedule_execution_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -361,7 +361,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
                 row[name]["oracle_spot_check"] = bool(np.array_equal(oo[R - 1].cpu().numpy()[idx], want[idx]))
             release(p)
         c, ev = tune(None, N, variants=[ring, tree])
-        row["tuner_picks"] = ("ring", "tree")[c[4]]
+        row["tuner_picks"] = ("ring", "tree")[c[5]]
         row["tuner_evaluations"] = ev
         trees.append(row)
         progress(f"tree vs ring {R} ranks {S >> 10} KiB: {row['tree']['us']} vs {row['ring']['us']} us")
