@@ -132,10 +132,11 @@ void setup_device(ccl_plan* p) {
   size_t nx = std::max<size_t>(1, hp.dxf.size());
   int nd = 0;
   for (const auto& D : hp.dins) nd = std::max(nd, D.done_flag + 1);
-  p->d_xflags = static_cast<unsigned long long*>(p->dev_alloc(nx * 8));
-  HIP_TRY(hipMemset(p->d_xflags, 0, nx * 8));
-  p->d_dflags = static_cast<unsigned long long*>(p->dev_alloc(std::max(1, nd) * 8));
-  HIP_TRY(hipMemset(p->d_dflags, 0, std::max(1, nd) * 8));
+  const size_t xbytes = nx * 8 * kFlagStride, dbytes = size_t(std::max(1, nd)) * 8 * kFlagStride;
+  p->d_xflags = static_cast<unsigned long long*>(p->dev_alloc(xbytes));
+  HIP_TRY(hipMemset(p->d_xflags, 0, xbytes));
+  p->d_dflags = static_cast<unsigned long long*>(p->dev_alloc(dbytes));
+  HIP_TRY(hipMemset(p->d_dflags, 0, dbytes));
   p->d_staging = static_cast<unsigned char*>(p->dev_alloc(size_t(hp.staging_bytes)));
   HIP_TRY(hipMemset(p->d_staging, 0, size_t(hp.staging_bytes)));  // LL flags start at 0, never a launch's flag
   p->scratch_stride = ((hp.scratch_elems_per_rank * hp.esz) + 255) / 256 * 256;

@@ -72,13 +72,18 @@ struct DevExec {  // 80 bytes
 };
 static_assert(sizeof(DevExec) == 80, "DevExec layout");
 
+// Transfer and completion flags each own a 128-byte cache line (this many 8-byte
+// words apart): flags packed into shared lines put every writer and poller of a line
+// in one queue of one L2 channel.
+constexpr int kFlagStride = 16;
+
 // Kernel arguments, passed by value.
 struct ExecArgs {
   const DevWG* wgs;
   const DevExec* recs;
   const int32_t* waits;
-  unsigned long long* xflags;  // per transfer: epoch << 24 | slices completed
-  unsigned long long* dflags;  // per completion flag: epoch when done
+  unsigned long long* xflags;  // per transfer (kFlagStride apart): epoch << 24 | slices completed
+  unsigned long long* dflags;  // per completion flag (kFlagStride apart): epoch when done
   unsigned char* staging;
   unsigned int* err;           // [code, wg, instr, epoch_lo]
   unsigned long long* abort_word;  // epoch of an aborted launch

@@ -672,7 +672,7 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
     if (tid == 0) {
       int ok = 1;
       for (int w = 0; w < nwaits && ok; ++w)
-        ok = wait_geq<true>(&A.dflags[A.waits[wait_begin + w]], A.epoch, A, gi, S.wait_ticks) ? 1 : 0;
+        ok = wait_geq<true>(&A.dflags[size_t(A.waits[wait_begin + w]) * kFlagStride], A.epoch, A, gi, S.wait_ticks) ? 1 : 0;
       if (!ok) *S.s_abort = 1;
     }
     __syncthreads();
@@ -723,7 +723,7 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
       const int64_t bo = o * esz;
       const long long waited =
           dispatch_slice<DT, XL, NT>(op, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr,
-                                     pt ? pt + bo : nullptr, n, tid, nthr, (op & OPB_RECV) ? &A.xflags[xin] : nullptr,
+                                     pt ? pt + bo : nullptr, n, tid, nthr, (op & OPB_RECV) ? &A.xflags[size_t(xin) * kFlagStride] : nullptr,
                                      S.E + (unsigned long long)(s + 1), A, gi);
       if (waited < 0) return false;  // the wait gave up: uniform across the workgroup
       S.wait_ticks += (unsigned long long)waited;
@@ -731,7 +731,7 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
       if (op & OPB_SEND) wait_vm_stores();
       __syncthreads();
       if ((op & OPB_SEND) && tid == 0)
-        slot_flag_store<XL>(&A.xflags[xout], S.E + (unsigned long long)(s + 1), XL && use_here(peer_tag) == S.my_tag);
+        slot_flag_store<XL>(&A.xflags[size_t(xout) * kFlagStride], S.E + (unsigned long long)(s + 1), XL && use_here(peer_tag) == S.my_tag);
     }
   }
   if (last) {
@@ -740,9 +740,9 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
       // every wave's stores complete, then a plain flag store (no L2 writeback).
       wait_vm_stores();
       __syncthreads();
-      if (tid == 0) __hip_atomic_store(&A.dflags[done_flag], A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (tid == 0) __hip_atomic_store(&A.dflags[size_t(done_flag) * kFlagStride], A.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     } else if (done_flag >= 0 && tid == 0) {
-      release_store(&A.dflags[done_flag], A.epoch);
+      release_store(&A.dflags[size_t(done_flag) * kFlagStride], A.epoch);
     }
     if (S.itrace && tid == 0) S.itrace[4 * size_t(gi) + 2] = (unsigned long long)wall_clock64();
   }
