@@ -99,6 +99,26 @@ def test_hierarchical_bytes_and_phase_fusion():
             assert host_plan(programs.hierarchical_allreduce(G, L), k, dtype="bf16").bytes(N) == S * (6 * P + 4 * G - 8)
 
 
+@pytest.mark.parametrize("name,args", [("ring_allreduce", (5,)), ("tree_allreduce", (7,)), ("ring_reducescatter", (6,)),
+                                       ("hierarchical_allreduce", (2, 4)), ("two_phase_alltoall", (2, 4)),
+                                       ("alltonext", (3, 4, True)), ("reducescatter_2d", (2, 3)),
+                                       ("hier_stage_reducescatter_intra", (2, 4))])
+@pytest.mark.parametrize("kernel", ["interpreter", "lazy"])
+def test_direct_landings_survive_random_interleavings(name, args, kernel):
+    """Every transfer the direct pass rewrites (copies into the destination, reducing
+    receives into their output chunk) keeps the collective's postcondition in random
+    interleavings of the lowered plan, in task order and in the lazy slice order, at
+    several parallel factors (fused, multi-chunk instructions)."""
+    for k in (1, 2, 3):
+        try:
+            plan = host_plan(programs.REGISTRY[name](*args), k, max_count=1 << 12, transport="direct", nthreads=128,
+                             kernel=kernel)
+        except capi.CCLError as e:
+            assert kernel == "lazy" and e.status == capi.CCL_ERR_UNSUPPORTED  # plans with completion waits
+            continue
+        plan.check(seed=11 + k, nsims=4)
+
+
 def test_ll_protocol_doubles_slot_traffic():
     P, N = 8, 8000
     S = N * 4

@@ -104,17 +104,22 @@ def test_ring_subnormals_are_kept():
     assert_all_equal(ys, want)
 
 
-def test_repeated_launches_and_counts():
+@pytest.mark.parametrize("algo", ["ring", "tree"])
+@pytest.mark.parametrize("transport,kernel", [("staged", "interpreter"), ("direct", "interpreter"),
+                                              ("direct", "specialized")])
+def test_repeated_launches_and_counts(algo, transport, kernel):
     """Epoch-valued flags: back-to-back launches need no reset; one plan serves several
-    counts up to max_count."""
+    counts up to max_count (direct transport: the landings move with the count)."""
     P = 8
-    prog = programs.ring_allreduce(P)
+    prog = programs.ring_allreduce(P) if algo == "ring" else programs.tree_allreduce(P)
+    oracle = O2.ring_allreduce if algo == "ring" else O2.tree_allreduce
     from gpu_util import to_dev, to_host
     import torch
     from chunk_schedule_execution_amd import Plan, PlanConfig
-    plan = Plan(prog, 4, PlanConfig(dtype="f32", max_count=50_000, slice_bytes=8192))
+    plan = Plan(prog, 4, PlanConfig(dtype="f32", max_count=50_000, slice_bytes=8192, transport=transport,
+                                    kernel=kernel))
     for N in (50_000, 777, 50_000, 12_345, 1):
-        case(f"ring AR repeated N={N}")
+        case(f"{algo} AR {transport} {kernel} repeated N={N}")
         xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 7)
         ins = [to_dev(x, "f32") for x in xs]
         outs = [torch.empty(50_000, dtype=torch.float32, device="cuda:0") for _ in range(P)]
@@ -122,7 +127,7 @@ def test_repeated_launches_and_counts():
             plan.execute(ins, outs, N)
         torch.cuda.synchronize()
         plan.status()
-        assert_all_equal([to_host(o, "f32")[:N] for o in outs], O2.ring_allreduce(xs, P, "f32")[0])
+        assert_all_equal([to_host(o, "f32")[:N] for o in outs], oracle(xs, P, "f32")[0])
     plan.destroy()
 
 
