@@ -126,13 +126,16 @@ typedef struct {
                                     are no per-slice flags (twice the slot traffic, far fewer round trips;
                                     the protocol choice of the MSCCLang report, section 3.1 runtime, and the
                                     AutoCCL report's Protocol parameter) */
-#define CCL_FLAG_DIRECT 0x40u     /* direct transport (simple protocol only): when a receive only copies the
-                                    incoming data into a local buffer (and perhaps forwards it), and no
-                                    other instruction touches that location before it, the sender writes
-                                    the location itself and the receive just waits for the transfer's flag
-                                    and forwards from there; such transfers use no staging slot. The
-                                    AutoCCL report's transport parameter; ring AllReduce moves S(5P-4)
-                                    bytes instead of S(6P-4) */
+#define CCL_FLAG_DIRECT 0x40u     /* direct transport (simple protocol only): the sender writes a transfer
+                                    into the receiving rank's own memory instead of a staging slot. A
+                                    receive that copies the data into a local location has it written there
+                                    and only waits for the transfer's flag (forwarding from its own buffer);
+                                    a reducing receive that only forwards its sum has it written into the
+                                    same chunk of the receiver's output (else scratch) buffer and adds its
+                                    local operand there. Applied to a transfer when every other instruction
+                                    of the receiving rank that touches that location runs after the receive
+                                    or before the sender. The AutoCCL report's transport parameter; ring
+                                    AllReduce moves S(5P-4) bytes instead of S(6P-4), with no slots */
 #define CCL_FLAG_STREAMING 0x80u  /* non-temporal hint on local-buffer loads and stores (simple protocol):
                                     streamed lines are not kept in the caches. Helps when the working set is
                                     far larger than the caches, costs when it fits */
