@@ -57,6 +57,9 @@ def parse():
                     help="k,nthreads,slice_bytes,protocol(0 simple, 1 LL, 2 simple+direct, 3 simple+direct+streaming)"
                          "[,kernel(0 interpreter, 1 specialized, 2 lazy; default 1)]: skip tuning (profiling runs)")
     ap.add_argument("--no-extras", action="store_true", help="headline only (profiling runs)")
+    ap.add_argument("--bytes", type=int, default=0,
+                    help="per-rank size of the timed ring AllReduce instead of 3 MiB (profiling runs of other "
+                         "sizes; implies --no-extras)")
     ap.add_argument("--section", choices=["interference", "kernels"], default="",
                     help="after the headline run only this part of the extras")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
@@ -89,6 +92,8 @@ def progress(msg):
 
 def main():
     args = parse()
+    if args.bytes:
+        args.no_extras = True
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the P ranks are "
               "virtual ranks on that GPU, no multi-GPU run exists", file=sys.stderr)
@@ -183,7 +188,7 @@ def main():
 
     # ---- headline: tune, then warmup + timed steps ----------------------------------
     prog = programs.ring_allreduce(P)
-    S = HEADLINE_BYTES
+    S = args.bytes or HEADLINE_BYTES
     N, ins, outs = ring_inputs(S)
     t0 = time.perf_counter()
     if args.fixed:
@@ -223,8 +228,8 @@ def main():
 
     achieved = plan_bytes / t_step / 1e9
     traffic = None
-    tpath = os.path.join(ROOT, "profiles", "executor_ring_ar_8r_3mib_traffic.json")
-    if os.path.exists(tpath):
+    tpath = os.path.join(ROOT, "profiles", f"executor_ring_ar_8r_{S >> 20}mib_traffic.json")
+    if S % (1 << 20) == 0 and os.path.exists(tpath):
         with open(tpath) as fh:
             tj = json.load(fh)
         if tj.get("source_digest") == source_digest() and same_launch(tj.get("config", []), cfg, S // P // cfg[0]):
@@ -244,8 +249,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic: seeded fp32 N(0,1) per virtual rank",
-        "config": {"workload": "ring AllReduce, 8 virtual ranks on one MI355X, fp32, 3 MiB per rank "
-                               "(top of the 32 KiB-3 MiB sweep), one kernel launch per collective",
+        "config": {"workload": f"ring AllReduce, 8 virtual ranks on one MI355X, fp32, {size_text(S)} per rank "
+                               + ("(top of the 32 KiB-3 MiB sweep), " if S == HEADLINE_BYTES else "")
+                               + "one kernel launch per collective",
                    "ranks": P, "bytes_per_rank": S, "elements_per_rank": N,
                    "parallel_factor": cfg[0], "nthreads": cfg[1], "slice_bytes": cfg[2],
                    "protocol": PROTOCOLS[cfg[3]][0], "transport": PROTOCOLS[cfg[3]][1],
@@ -306,7 +312,7 @@ def main():
         out["copy_probe_bytes_per_launch"] = 2 * nb
 
     # ---- CPU baseline: the oracle on the host, same workload, bounded time --------
-    out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    out["cpu_baseline"] = cpu_baseline(args.cpu_seconds, S)
     out["source_digest"] = source_digest()
     print(json.dumps(out), flush=True)
 
@@ -711,15 +717,18 @@ def kernels_other(programs, device_inputs, make_plan, time_launches, release, st
     return rows
 
 
-def cpu_baseline(budget_s: float):
-    """The chain-order oracle (numpy, one thread for elementwise adds) on the 3 MiB x 8
-    rank input, repeated until the budget is spent."""
+def size_text(S: int) -> str:
+    return f"{S >> 20} MiB" if S % (1 << 20) == 0 else f"{S >> 10} KiB" if S % 1024 == 0 else f"{S} B"
+
+
+def cpu_baseline(budget_s: float, S: int = HEADLINE_BYTES):
+    """The chain-order oracle (numpy, one thread for elementwise adds) on the 8-rank input
+    of S bytes per rank (3 MiB by default), repeated until the budget is spent."""
     import numpy as np
 
     import workloads as W
     from oracle import schedule_order as O2
 
-    S = HEADLINE_BYTES
     N = S // 4
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=S)
     reps = 0
@@ -742,7 +751,7 @@ def cpu_baseline(budget_s: float):
         pass
     return {"value": round(S / t * 2 * (P - 1) / P / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"schedule-order oracle, ring AllReduce 8 ranks x 3 MiB fp32, {reps} repetitions "
+            "sample": f"schedule-order oracle, ring AllReduce 8 ranks x {size_text(S)} fp32, {reps} repetitions "
                       f"({t * 1e3:.1f} ms each); numpy elementwise adds run on one thread; host has {cores} "
                       f"cores available ({cpu})"}
 
