@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--bytes", type=int, default=0,
                     help="per-rank size of the timed ring AllReduce instead of 3 MiB (profiling runs of other "
                          "sizes; implies --no-extras)")
-    ap.add_argument("--section", choices=["interference", "kernels"], default="",
+    ap.add_argument("--section", choices=["interference", "kernels", "ranks"], default="",
                     help="after the headline run only this part of the extras")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
     ap.add_argument("--copy-probe", type=int, default=0,
@@ -126,14 +126,14 @@ def main():
         xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=S)
         return N, [torch.from_numpy(x).to(dev) for x in xs], outs
 
-    def tune(prog, N, dtype="f32", protocols=15, variants=None, kernel=KERNEL):
+    def tune(prog, N, dtype="f32", protocols=15, variants=None, kernel=KERNEL, factors=TUNE_FACTORS):
         """Tuned (k, nthreads, slice_bytes, protocol, kernel) of prog with the given
         executor kernel, or, given a list of programs as `variants`, the best over those
         algorithm subspaces with (..., variant index) appended."""
         progs = variants if variants is not None else [prog]
         base = PlanConfig(dtype=dtype, max_count=N, kernel=KERNELS[kernel]).to_c()
-        arrs = [(capi.C.c_int32 * len(v))(*v) for v in (TUNE_FACTORS, TUNE_THREADS, TUNE_SLICES)]
-        space = capi.ccl_tune_space(capi.C.cast(arrs[0], capi.C.POINTER(capi.C.c_int32)), len(TUNE_FACTORS),
+        arrs = [(capi.C.c_int32 * len(v))(*v) for v in (factors, TUNE_THREADS, TUNE_SLICES)]
+        space = capi.ccl_tune_space(capi.C.cast(arrs[0], capi.C.POINTER(capi.C.c_int32)), len(factors),
                                     capi.C.cast(arrs[1], capi.C.POINTER(capi.C.c_int32)), len(TUNE_THREADS),
                                     capi.C.cast(arrs[2], capi.C.POINTER(capi.C.c_int32)), len(TUNE_SLICES),
                                     len(progs), 3, 10, protocols)
@@ -290,6 +290,9 @@ def main():
 
     if args.section == "interference":
         out["interference"] = interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release)
+    elif args.section == "ranks":
+        out["ring_ar_rank_counts"] = rank_counts(np, torch, programs, dev, stream, device_inputs, tune, make_plan,
+                                                 time_launches, busbw_ar, stats, release)
     elif args.section == "kernels":
         out["kernels"] = kernels(prog, ring_inputs, make_plan, time_launches, release, stream)
         out["kernels_other"] = kernels_other(programs, device_inputs, make_plan, time_launches, release, stream,
@@ -344,6 +347,9 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         release(p)
         del ii, oo
     res["sweep"] = sweep
+
+    res["ring_ar_rank_counts"] = rank_counts(np, torch, programs, dev, stream, device_inputs, tune, make_plan,
+                                             time_launches, busbw_ar, stats, release)
 
     # ---- tree versus ring AllReduce at small sizes, and the tuner choosing -----------
     from oracle import schedule_order as O2
@@ -559,6 +565,37 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
     del a, b
     release()
     return res
+
+
+def rank_counts(np, torch, programs, dev, stream, device_inputs, tune, make_plan, time_launches, busbw_ar, stats,
+                release):
+    """Ring AllReduce at 4, 16 and 32 virtual ranks, 1 and 32 MiB per rank, each tuned."""
+    from oracle import schedule_order as O2r
+    ranks = []
+    for R in (4, 16, 32):
+        pr = programs.ring_allreduce(R)
+        for S in (1 << 20, 32 << 20):
+            N = S // 4
+            ii = device_inputs("f32", N, R, 91000 + R * 64 + S // (1 << 20))
+            oo = [torch.empty(N, device=dev) for _ in range(R)]
+            # candidates interpreted (no kernel generation per point); where 32 channels leave
+            # compute units without a workgroup, larger factors are candidates too
+            c, ev = tune(pr, N, kernel=0, factors=TUNE_FACTORS + ([48, 64] if R * 32 < 256 else []))
+            p = make_plan(pr, N, *c[:4], KERNEL)  # the chosen point timed on its generated kernel
+            t = time_launches(lambda: p.execute(ii, oo, N, stream), 20 if S >= DEVICE_INPUT_BYTES else 50)
+            idx = np.random.default_rng(R).integers(0, N, 256)
+            xs = [x.cpu().numpy() for x in ii]
+            ok = bool(np.array_equal(oo[R - 1].cpu().numpy()[idx], O2r.ring_allreduce_at(xs, R, idx, "f32")))
+            ranks.append({"ranks": R, "bytes_per_rank": S, "k": c[0], "nthreads": c[1], "slice_bytes": c[2],
+                          "protocol": PROTOCOLS[c[3]][0], "transport": PROTOCOLS[c[3]][1],
+                          "streaming": PROTOCOLS[c[3]][2], "kernel": KERNELS[KERNEL],
+                          "workgroups": p.info()["num_workgroups"], "busbw": round(busbw_ar(S, t, R), 2),
+                          "tuner_evaluations": ev, "oracle_spot_check": ok, **stats(p, N, t)})
+            progress(f"ring AR {R} ranks {S >> 10} KiB: {ranks[-1]['us']} us")
+            release(p)
+            del ii, oo, xs
+            release()
+    return ranks
 
 
 def interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release):

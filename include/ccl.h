@@ -145,7 +145,7 @@ typedef struct {
 #define CCL_FLAG_SPECIALIZE 0x200u /* run a kernel generated for this plan instead of the interpreting one
                                     (ReSCCL report, section 2.2, lightweight kernel generation), compiled with
                                     hiprtc at create (code objects cached per process). When the plan's
-                                    distinct workgroup programs hold at most 32 instructions in all, each
+                                    distinct workgroup programs hold at most 24 instructions in all, each
                                     becomes straight-line code with the operations and buffers as constants;
                                     longer plans get the loop form (CCL_FLAG_SPECIALIZE_LOOP), whose code stays
                                     within the instruction cache. Same records, flags and results; with

@@ -41,7 +41,7 @@ def test_lazy_order_refuses_completion_waits():
                                              ("hierarchical_allreduce", (2, 8), "bf16"), ("tree_allreduce", (8,), "f32")])
 def test_long_programs_get_the_loop_form(name, args, dtype):
     """Straight-line code inlines one step per instruction of every distinct workgroup
-    program; past 32 instructions it would outgrow the instruction cache, so long plans
+    program; past 24 instructions it would outgrow the instruction cache, so long plans
     get the loop form: one step per distinct operation word, selected per record."""
     prog = programs.REGISTRY[name](*args)
     loop = host_plan(prog, 2, dtype=dtype, nthreads=256, kernel="specialized").info()
@@ -49,6 +49,10 @@ def test_long_programs_get_the_loop_form(name, args, dtype):
     assert loop["specialized_code_bytes"] < 64 << 10
     short = host_plan(programs.ring_allreduce(8), 2, kernel="specialized").info()
     assert short["specialized_instructions"] == 15  # straight-line: every instruction
+    edge = host_plan(programs.ring_allreduce(12), 2, kernel="specialized").info()
+    assert edge["specialized_instructions"] == 23  # 2P - 1: still straight-line
+    long_ring = host_plan(programs.ring_allreduce(16), 2, kernel="specialized").info()
+    assert long_ring["specialized_instructions"] < 31  # 31 would not fit the instruction cache
     forced = host_plan(programs.ring_allreduce(8), 2, kernel="specialized_loop").info()
     assert forced["specialized_instructions"] == len({e.opcode for e in host_plan(programs.ring_allreduce(8), 2).export()})
 
