@@ -136,3 +136,21 @@ def test_plan_bytes_rejects_bad_counts():
     with pytest.raises(capi.CCLError):
         p.bytes(101)
     assert p.bytes(0) == 0
+
+
+def test_build_script_loads_without_the_library():
+    # The build entry point must work on a fresh checkout, where libccl.so does not exist
+    # yet: loading the build script may not import the package (whose __init__ loads it).
+    import subprocess
+    import sys
+
+    code = ("import importlib.util, os, sys\n"
+            f"spec = importlib.util.spec_from_file_location('b', os.path.join({ROOT!r}, "
+            "'chunk_schedule_execution_amd', 'build.py'))\n"
+            "m = importlib.util.module_from_spec(spec); spec.loader.exec_module(m)\n"
+            "assert callable(m.build)\n"
+            "assert 'chunk_schedule_execution_amd.capi' not in sys.modules\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    src = open(os.path.join(ROOT, "__graft_entry__.py")).read()
+    assert "from chunk_schedule_execution_amd.build import" not in src
