@@ -6,7 +6,9 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
+#include <map>
 #include <string>
 #include <vector>
 
@@ -23,6 +25,9 @@ int index_of(const int32_t* v, int n, int32_t x) {
     if (v[i] == x) return i;
   return 0;
 }
+
+// Passes of coordinate descent per subspace at most (each pass visits nc, nt, c once).
+constexpr int kMaxPasses = 4;
 
 struct Coord {
   const int32_t* vals;
@@ -59,38 +64,58 @@ int ccl_tune_coordinate_descent(const ccl_tune_space* space, const ccl_tune_poin
         idx[c] = start ? index_of(coords[c].vals, coords[c].n, start->*(coords[c].field)) : 0;
         pt.*(coords[c].field) = coords[c].vals[idx[c]];
       }
-      double score = objective(&pt, user);
-      ++evals;
+      // objective values of this subspace by candidate indices: a point is timed once
+      std::map<std::array<int, 3>, double> seen;
+      auto eval = [&](const int* ix) {
+        const std::array<int, 3> key{ix[0], ix[1], ix[2]};
+        auto it = seen.find(key);
+        if (it != seen.end()) return it->second;
+        ccl_tune_point q = pt;
+        for (int c = 0; c < 3; ++c) q.*(coords[c].field) = coords[c].vals[ix[c]];
+        const double v = objective(&q, user);
+        ++evals;
+        seen.emplace(key, v);
+        return v;
+      };
+      double score = eval(idx);
       if (first) start_score = score;
       first = false;
-      for (int c = 0; c < 3; ++c) {
-        // step this coordinate up while the objective improves; one look-ahead step
-        // past a candidate that does not improve (resource counts that leave part of
-        // the machine idle can dip between two better values)
-        int i = idx[c];
-        while (i + 1 < coords[c].n) {
-          ccl_tune_point cand = pt;
-          cand.*(coords[c].field) = coords[c].vals[i + 1];
-          double s = objective(&cand, user);
-          ++evals;
-          if (s > score) {
-            pt = cand;
-            score = s;
-            i += 1;
-            continue;
+      // Moves coordinate c from idx[c] in direction dir (+1 / -1) while the objective
+      // improves, looking one candidate past a step that does not improve (resource
+      // counts that leave part of the machine idle can dip between two better values).
+      auto climb = [&](int c, int dir) {
+        bool moved = false;
+        for (;;) {
+          int ix[3] = {idx[0], idx[1], idx[2]};
+          ix[c] = idx[c] + dir;
+          if (ix[c] < 0 || ix[c] >= coords[c].n) break;
+          double s = eval(ix);
+          if (!(s > score)) {
+            ix[c] += dir;
+            if (ix[c] < 0 || ix[c] >= coords[c].n) break;
+            s = eval(ix);
+            if (!(s > score)) break;
           }
-          if (i + 2 >= coords[c].n) break;
-          ccl_tune_point next = pt;
-          next.*(coords[c].field) = coords[c].vals[i + 2];
-          double s2 = objective(&next, user);
-          ++evals;
-          if (!(s2 > score)) break;
-          pt = next;
-          score = s2;
-          i += 2;
+          idx[c] = ix[c];
+          score = s;
+          moved = true;
         }
-        idx[c] = i;
+        return moved;
+      };
+      // First pass: each coordinate raised from its start. Later passes (coordinate
+      // descent repeated until a whole pass changes nothing) move each coordinate up or,
+      // failing that, down from where the others now are: the best thread count can
+      // depend on the slice size chosen after it.
+      for (int pass = 0; pass < kMaxPasses; ++pass) {
+        bool changed = false;
+        for (int c = 0; c < 3; ++c) {
+          bool m = climb(c, +1);
+          if (!m && pass > 0) m = climb(c, -1);
+          changed |= m;
+        }
+        if (!changed) break;
       }
+      for (int c = 0; c < 3; ++c) pt.*(coords[c].field) = coords[c].vals[idx[c]];
       if (score >= 0 && (!have_best || score > best_score)) {
         have_best = true;
         best_score = score;

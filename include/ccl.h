@@ -333,12 +333,15 @@ typedef struct {
 typedef double (*ccl_tune_objective)(const ccl_tune_point* point, void* user);
 
 /*
- * Subspace coordinate descent: for every (variant, protocol) subspace, starting
- * from the smallest candidate of each coordinate (or from `start` where it lies in
- * the space), optimize parallel_factor, then nthreads, then slice_bytes; each
- * coordinate is stepped up through its ascending candidates while the objective
- * improves, looking one candidate past a step that does not improve before
- * stopping. The best point over all subspaces is returned. Pure host logic.
+ * Subspace coordinate descent (AutoCCL report, methods 1-2): for every (variant,
+ * protocol) subspace, starting from the smallest candidate of each coordinate (or
+ * from `start` where it lies in the space), optimize parallel_factor, then
+ * nthreads, then slice_bytes; each coordinate is stepped up through its ascending
+ * candidates while the objective improves, looking one candidate past a step that
+ * does not improve before stopping. Passes repeat (at most four per subspace) until
+ * one moves no coordinate; after the first, a coordinate that cannot rise is
+ * stepped down the same way. Each point is evaluated at most once per subspace.
+ * The best point over all subspaces is returned. Pure host logic.
  */
 int ccl_tune_coordinate_descent(const ccl_tune_space* space, const ccl_tune_point* start,
                                 ccl_tune_objective objective, void* user, ccl_tune_point* best,

@@ -401,7 +401,40 @@ def test_coordinate_descent_finds_the_peak_of_a_unimodal_objective():
     best, rep = capi.ccl_tune_coordinate_descent(_space(F, T, S), f)
     assert (best.parallel_factor, best.nthreads, best.slice_bytes) == peak
     assert rep.best_score == pytest.approx(100)
-    assert rep.evaluations <= 1 + len(F) + len(T) + len(S) + 3
+    # one rising pass, then one confirming pass over the neighbours of the peak
+    assert rep.evaluations <= 1 + len(F) + len(T) + len(S) + 3 + 12
+
+
+def test_coordinate_descent_repeats_passes_when_coordinates_interact():
+    """Coordinate descent repeats its passes until none moves: here the best thread
+    count depends on the slice size (as measured for large ring AllReduces, where
+    1024 threads win only with larger slices), so one rising pass stops at 512
+    threads and a second pass raises it."""
+    F, T, S = [32], [64, 128, 256, 512, 1024], [16384 << i for i in range(6)]
+
+    def f(p):
+        big = p.slice_bytes >= 262144
+        t = {64: 1, 128: 2, 256: 3, 512: 5, 1024: 7 if big else 4}[p.nthreads]
+        c = {16384: 0, 32768: 1, 65536: 2, 131072: 3, 262144: 4, 524288: 2}[p.slice_bytes]
+        return 10.0 * t + c
+    one_pass = max(f(type("P", (), dict(parallel_factor=32, nthreads=512, slice_bytes=sl))) for sl in S)
+    best, rep = capi.ccl_tune_coordinate_descent(_space(F, T, S), f)
+    assert (best.nthreads, best.slice_bytes) == (1024, 262144)
+    assert rep.best_score == 74 > one_pass
+    # an exhaustive search agrees
+    pts = [(f(type("P", (), dict(parallel_factor=32, nthreads=t, slice_bytes=sl))), t, sl) for t in T for sl in S]
+    assert max(pts)[0] == rep.best_score
+
+
+def test_coordinate_descent_evaluates_each_point_once():
+    seen = []
+
+    def f(p):
+        seen.append((p.parallel_factor, p.nthreads, p.slice_bytes, p.protocol, p.variant))
+        return float(p.parallel_factor % 7 + p.nthreads // 64 + p.slice_bytes // 4096)
+    best, rep = capi.ccl_tune_coordinate_descent(_space([1, 2, 4, 8, 16], [64, 128, 256], [4096, 8192, 16384],
+                                                        nvariants=2, protocols=3), f)
+    assert len(seen) == len(set(seen)) == rep.evaluations
 
 
 def test_coordinate_descent_looks_past_one_dip_and_picks_the_subspace():
