@@ -509,7 +509,9 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
             ii = device_inputs("f32", count, Pn, 6000 + len(coll))
             oo = [torch.empty(nout, device=dev) for _ in range(Pn)]
             modes = (("hpds", "state"), ("rr", "connection"))
-            k, pls = fitting([lambda k, sc=sc, al=al: make_plan(pr, count, k, 512, 256 << 10, 2, scheduler=sc,
+            # one launch configuration for both modes (512 threads, 64 KiB slices, direct
+            # transport with streaming hints: the best of a sweep of the ring at this size)
+            k, pls = fitting([lambda k, sc=sc, al=al: make_plan(pr, count, k, 512, 64 << 10, 3, scheduler=sc,
                                                                   wg_alloc=al) for sc, al in modes],
                              ks=(32, 16, 8, 4, 2, 1))
             for (sched, alloc), pl in zip(modes, pls):

@@ -119,7 +119,9 @@ void setup_device(ccl_plan* p) {
   int rc = executor_max_blocks_per_cu(hp.cfg.dtype, hp.cfg.nthreads, &blocks, &err);
   if (rc) fail(rc, err);
   hp.max_resident_wgs = blocks * cus;
-  if (int(hp.dwg.size()) > hp.max_resident_wgs)
+  // a plan that runs a generated kernel is checked against that kernel's occupancy below
+  const bool generated = (hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY | CCL_FLAG_SPECIALIZE_LOOP)) != 0;
+  if (!generated && int(hp.dwg.size()) > hp.max_resident_wgs)
     fail(CCL_ERR_OUT_OF_RESOURCES, "plan needs " + std::to_string(hp.dwg.size()) + " co-resident workgroups, the device holds " +
                                        std::to_string(hp.max_resident_wgs) + " at " + std::to_string(hp.cfg.nthreads) +
                                        " threads");
@@ -160,11 +162,11 @@ void setup_device(ccl_plan* p) {
   }
   if (hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY | CCL_FLAG_SPECIALIZE_LOOP)) {
     const std::string src = specialized_source(hp, local, (hp.cfg.flags & CCL_FLAG_LAZY) != 0,
-                                               (hp.cfg.flags & CCL_FLAG_SPECIALIZE_LOOP) != 0, &p->spec_shapes,
+                                               (hp.cfg.flags & CCL_FLAG_SPECIALIZE_LOOP) != 0, cus, &p->spec_shapes,
                                                &p->spec_instructions);
     int spec_blocks = 0;
     p->spec_fn = load_specialized(src, p->device_id, hp.cfg.nthreads, &spec_blocks, &p->spec_code_bytes);
-    hp.max_resident_wgs = std::min(hp.max_resident_wgs, spec_blocks * cus);
+    hp.max_resident_wgs = spec_blocks * cus;
     if (int(hp.dwg.size()) > spec_blocks * cus)
       fail(CCL_ERR_OUT_OF_RESOURCES, "plan needs " + std::to_string(hp.dwg.size()) +
                                          " co-resident workgroups, the device holds " + std::to_string(spec_blocks * cus) +
@@ -222,7 +224,7 @@ int ccl_plan_create(const ccl_program_desc* prog, int nranks, int nchunks, int p
           bool local = !(p->hp.cfg.flags & CCL_FLAG_COHERENT_ONLY);
           p->spec_code_bytes = compile_specialized(specialized_source(
               p->hp, local, (p->hp.cfg.flags & CCL_FLAG_LAZY) != 0, (p->hp.cfg.flags & CCL_FLAG_SPECIALIZE_LOOP) != 0,
-              &p->spec_shapes, &p->spec_instructions));
+              p->hp.cfg.num_cus, &p->spec_shapes, &p->spec_instructions));
         }
       }
     } catch (...) {

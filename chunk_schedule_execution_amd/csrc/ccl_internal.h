@@ -130,9 +130,11 @@ int executor_max_blocks_per_cu(int dtype, int nthreads, int* blocks, std::string
 int launch_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int nthreads,
                       void* stream, std::string* err);
 
-// specialize.cpp: plan-specialized kernels (CCL_FLAG_SPECIALIZE / CCL_FLAG_LAZY)
-std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bool force_loop, int* num_shapes,
-                               int* num_instructions);
+// specialize.cpp: plan-specialized kernels (CCL_FLAG_SPECIALIZE / CCL_FLAG_LAZY).
+// cus: compute units of the target device; the kernel is compiled for the waves per
+// SIMD that the plan's grid needs to be co-resident on them.
+std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bool force_loop, int cus,
+                               int* num_shapes, int* num_instructions);
 int64_t compile_specialized(const std::string& src);  // compile only (no device needed); code bytes
 void* load_specialized(const std::string& src, int device, int nthreads, int* blocks_per_cu, int64_t* code_bytes);
 int launch_specialized(void* fn, const ExecArgs& args, int nwg, int nthreads, void* stream, std::string* err);

@@ -90,8 +90,8 @@ const std::vector<char>& compile_cached(const std::string& src) {
 
 }  // namespace
 
-std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bool force_loop, int* num_shapes,
-                               int* num_instructions) {
+std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bool force_loop, int cus,
+                               int* num_shapes, int* num_instructions) {
   const bool ll = hp.cfg.flags & CCL_FLAG_LL;
   const bool nt = hp.cfg.flags & CCL_FLAG_STREAMING;
   // operation words (operation and buffers, not the peer rank) are count-independent
@@ -223,8 +223,16 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bo
     }
   }
   s += "}  // namespace\n}  // namespace ccl\n\n";
-  s += "extern \"C\" __global__ __launch_bounds__(" + std::to_string(hp.cfg.nthreads) +
-       ") void ccl_spec_kernel(ccl::ExecArgs A) {\n";
+  // Every workgroup of the grid must be resident at once (they wait for each other's
+  // flags). A grid of more than one workgroup's worth of waves per SIMD asks the
+  // compiler for that occupancy (fewer registers per thread) instead of leaving it to
+  // the launch bound alone, which lets the register count halve the resident waves.
+  const int waves_per_wg = (hp.cfg.nthreads + 63) / 64;
+  const int wgs_per_cu = (ngrid + std::max(1, cus) - 1) / std::max(1, cus);
+  const int waves_per_simd = std::min(8, (wgs_per_cu * waves_per_wg + 3) / 4);
+  s += "extern \"C\" __global__ __launch_bounds__(" + std::to_string(hp.cfg.nthreads) + ")";
+  if (waves_per_simd > 1) s += " __attribute__((amdgpu_waves_per_eu(" + std::to_string(waves_per_simd) + ")))";
+  s += " void ccl_spec_kernel(ccl::ExecArgs A) {\n";
   s += "  using namespace ccl;\n";
   s += "  __shared__ int s_abort;\n";
   s += "  __shared__ DevExec s_rec[" + std::to_string(max_n) + "];\n";

@@ -277,6 +277,34 @@ def test_reducescatter_24r(variant, sched, alloc):
         assert nm.scaled_error(ys[r], ref[r].exact, ref[r].abs_sum, "f32") <= F32_TOL(P)
 
 
+@pytest.mark.parametrize("coll", ["allgather", "reducescatter"])
+def test_24r_ring_at_three_workgroups_per_cu(coll):
+    """k=32 x 512 threads on 24 ranks: 768 workgroups, three per compute unit. Only the
+    generated kernel compiled for that occupancy holds them all; the outputs keep the
+    bits of the oracle (provenance copies for AllGather, chain order for ReduceScatter)."""
+    P = 24
+    case(f"{coll} 24 ranks k=32 nt=512 generated, 3 workgroups per CU")
+    if coll == "allgather":
+        n = 32 * 1001 + 5
+        xs = W.make_inputs("prov_i32", n, P, W.CFG_A2NEXT_AGRS_24R, size_bytes=n * 4)
+        ys, plan = _run(programs.ring_allgather(P), xs, "i32", k=32, nthreads=512, slice_bytes=4096,
+                        transport="direct", streaming=True, kernel="specialized")
+        want = O1.allgather(xs)
+        for r in range(P):
+            assert np.array_equal(ys[r], want), r
+    else:
+        N = P * (32 * 301 + 3)
+        xs = W.make_inputs("normal_f32", N, P, W.CFG_A2NEXT_AGRS_24R, size_bytes=N * 4)
+        ys, plan = _run(programs.ring_reducescatter(P), xs, "f32", k=32, nthreads=512, slice_bytes=4096,
+                        transport="direct", streaming=True, kernel="specialized")
+        want = O2.ring_reducescatter(xs, P, "f32")
+        for r in range(P):
+            assert np.array_equal(ys[r], want[r]), r
+    info = plan.info()
+    assert info["num_workgroups"] == 768 and info["max_resident_wgs"] >= 768
+    plan.destroy()
+
+
 def test_int32_reduction_wraps():
     P, N = 4, 1000
     case("ring AR int32 wrap")
