@@ -74,7 +74,7 @@ class ccl_plan_info_t(C.Structure):
                 ("xcd_local", C.c_int32), ("specialized_shapes", C.c_int32),
                 ("staging_bytes", C.c_int64), ("scratch_bytes", C.c_int64), ("flag_bytes", C.c_int64),
                 ("table_bytes", C.c_int64), ("compile_ms", C.c_double * 6), ("opcode_hist", C.c_int32 * 16),
-                ("specialized_instructions", C.c_int32), ("reserved1", C.c_int32),
+                ("specialized_instructions", C.c_int32), ("specialized_waves_per_simd", C.c_int32),
                 ("specialized_code_bytes", C.c_int64)]
 
 

@@ -60,7 +60,7 @@ struct ccl_plan {
   unsigned long long* d_trace = nullptr;
   unsigned long long* d_xcd = nullptr;  // per launch-grid workgroup: XCD tag of the latest launch
   void* spec_fn = nullptr;              // generated kernel (CCL_FLAG_SPECIALIZE / LAZY), or the interpreter
-  int spec_shapes = 0, spec_instructions = 0;
+  int spec_shapes = 0, spec_instructions = 0, spec_waves = 0;
   int64_t spec_code_bytes = 0;
   hipEvent_t last = nullptr;    // recorded on last_stream when another stream needs ordering
   hipStream_t last_stream = nullptr;
@@ -163,7 +163,7 @@ void setup_device(ccl_plan* p) {
   if (hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY | CCL_FLAG_SPECIALIZE_LOOP)) {
     const std::string src = specialized_source(hp, local, (hp.cfg.flags & CCL_FLAG_LAZY) != 0,
                                                (hp.cfg.flags & CCL_FLAG_SPECIALIZE_LOOP) != 0, cus, &p->spec_shapes,
-                                               &p->spec_instructions);
+                                               &p->spec_instructions, &p->spec_waves);
     int spec_blocks = 0;
     p->spec_fn = load_specialized(src, p->device_id, hp.cfg.nthreads, &spec_blocks, &p->spec_code_bytes);
     hp.max_resident_wgs = spec_blocks * cus;
@@ -224,7 +224,7 @@ int ccl_plan_create(const ccl_program_desc* prog, int nranks, int nchunks, int p
           bool local = !(p->hp.cfg.flags & CCL_FLAG_COHERENT_ONLY);
           p->spec_code_bytes = compile_specialized(specialized_source(
               p->hp, local, (p->hp.cfg.flags & CCL_FLAG_LAZY) != 0, (p->hp.cfg.flags & CCL_FLAG_SPECIALIZE_LOOP) != 0,
-              p->hp.cfg.num_cus, &p->spec_shapes, &p->spec_instructions));
+              p->hp.cfg.num_cus, &p->spec_shapes, &p->spec_instructions, &p->spec_waves));
         }
       }
     } catch (...) {
@@ -342,6 +342,7 @@ int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info) {
     info->xcd_local = plan->d_xcd ? 1 : 0;
     info->specialized_shapes = plan->spec_shapes;
     info->specialized_instructions = plan->spec_instructions;
+    info->specialized_waves_per_simd = plan->spec_waves;
     info->specialized_code_bytes = plan->spec_code_bytes;
     info->max_wg_per_rank = hp.max_wg_per_rank;
     info->num_instructions = int(hp.dins.size());
@@ -357,7 +358,7 @@ int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info) {
     info->scratch_bytes = hp.scratch_elems_per_rank * hp.esz * hp.P;
     int nd = 0;
     for (const auto& D : hp.dins) nd = std::max(nd, D.done_flag + 1);
-    info->flag_bytes = int64_t(hp.dxf.size() + nd) * 8;
+    info->flag_bytes = int64_t(hp.dxf.size() + nd) * 8 * kFlagStride;
     info->table_bytes = int64_t(hp.dwg.size() * sizeof(DevWG) + hp.dins.size() * sizeof(DevExec) * 4 +
                                 hp.dwaits.size() * 4);
     for (int i = 0; i < 6; ++i) info->compile_ms[i] = hp.ms[i];

@@ -134,7 +134,7 @@ int launch_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int
 // cus: compute units of the target device; the kernel is compiled for the waves per
 // SIMD that the plan's grid needs to be co-resident on them.
 std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bool force_loop, int cus,
-                               int* num_shapes, int* num_instructions);
+                               int* num_shapes, int* num_instructions, int* waves_per_simd);
 int64_t compile_specialized(const std::string& src);  // compile only (no device needed); code bytes
 void* load_specialized(const std::string& src, int device, int nthreads, int* blocks_per_cu, int64_t* code_bytes);
 int launch_specialized(void* fn, const ExecArgs& args, int nwg, int nthreads, void* stream, std::string* err);

@@ -91,7 +91,7 @@ const std::vector<char>& compile_cached(const std::string& src) {
 }  // namespace
 
 std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bool force_loop, int cus,
-                               int* num_shapes, int* num_instructions) {
+                               int* num_shapes, int* num_instructions, int* waves_per_simd_out) {
   const bool ll = hp.cfg.flags & CCL_FLAG_LL;
   const bool nt = hp.cfg.flags & CCL_FLAG_STREAMING;
   // operation words (operation and buffers, not the peer rank) are count-independent
@@ -230,6 +230,7 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bo
   const int waves_per_wg = (hp.cfg.nthreads + 63) / 64;
   const int wgs_per_cu = (ngrid + std::max(1, cus) - 1) / std::max(1, cus);
   const int waves_per_simd = std::min(8, (wgs_per_cu * waves_per_wg + 3) / 4);
+  if (waves_per_simd_out) *waves_per_simd_out = std::max(1, waves_per_simd);
   s += "extern \"C\" __global__ __launch_bounds__(" + std::to_string(hp.cfg.nthreads) + ")";
   if (waves_per_simd > 1) s += " __attribute__((amdgpu_waves_per_eu(" + std::to_string(waves_per_simd) + ")))";
   s += " void ccl_spec_kernel(ccl::ExecArgs A) {\n";

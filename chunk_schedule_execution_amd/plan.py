@@ -89,7 +89,7 @@ class Plan:
     def info(self) -> dict:
         i = capi.ccl_plan_info(self.handle)
         d = {name: getattr(i, name) for name, _ in capi.ccl_plan_info_t._fields_
-             if name not in ("compile_ms", "opcode_hist", "reserved", "reserved0", "reserved1")}
+             if name not in ("compile_ms", "opcode_hist", "reserved", "reserved0")}
         d["compile_ms"] = list(i.compile_ms)
         d["opcode_hist"] = list(i.opcode_hist)
         return d

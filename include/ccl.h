@@ -233,11 +233,14 @@ typedef struct {
   int32_t xcd_local;          /* 1: XCD-local layout, plain transfer stores (see CCL_FLAG_COHERENT_ONLY) */
   int32_t specialized_shapes; /* generated kernel (CCL_FLAG_SPECIALIZE / LAZY): distinct instruction
                                  sequences in it; 0 for the interpreting kernel */
-  int64_t staging_bytes, scratch_bytes, flag_bytes, table_bytes;
+  int64_t staging_bytes, scratch_bytes;
+  int64_t flag_bytes;         /* transfer and completion flags, one 128-byte line each */
+  int64_t table_bytes;
   double compile_ms[6];       /* verify, DAG, fusion, schedule, workgroup allocation, lowering */
   int32_t opcode_hist[16];    /* lowered instructions by opcode bits (see ccl_instr_info.opcode) */
   int32_t specialized_instructions; /* generated kernel: instructions over its distinct sequences */
-  int32_t reserved1;
+  int32_t specialized_waves_per_simd; /* generated kernel: minimum waves per SIMD it was compiled for
+                                         (what its grid needs to be co-resident; 1 = no request) */
   int64_t specialized_code_bytes;   /* generated kernel: size of its code object */
 } ccl_plan_info_t;
 

@@ -28,6 +28,21 @@ def test_other_dtypes_and_protocols_compile():
     assert host_plan(programs.direct_alltoall(4), 1, dtype="i32", kernel="specialized").info()["specialized_shapes"] >= 1
 
 
+def test_generated_kernel_asks_for_the_occupancy_its_grid_needs():
+    """All workgroups of a launch wait on each other's flags, so all must be resident:
+    a grid of more than one 4-wave workgroup per compute unit is compiled for that many
+    waves per SIMD, one that fits in fewer is compiled without a request."""
+    def waves(prog, k, nt, **kw):
+        return host_plan(prog, k, nthreads=nt, kernel="specialized", num_cus=256, **kw).info()
+    one = waves(programs.ring_allreduce(8), 32, 256, transport="direct")  # 256 x 4 waves: one per CU
+    assert one["grid_workgroups"] == 256 and one["specialized_waves_per_simd"] == 1
+    assert waves(programs.ring_allreduce(8), 32, 1024)["specialized_waves_per_simd"] == 4  # 16 waves per CU
+    ag = waves(programs.ring_allgather(24), 32, 512, transport="direct")  # 768 x 8 waves over 256 CUs
+    assert ag["grid_workgroups"] == 768 and ag["specialized_waves_per_simd"] == 6
+    assert waves(programs.ring_allreduce(8), 64, 1024)["specialized_waves_per_simd"] == 8  # the most a SIMD holds
+    assert host_plan(programs.ring_allreduce(8), 32, nthreads=1024).info()["specialized_waves_per_simd"] == 0
+
+
 def test_lazy_order_refuses_completion_waits():
     """A completion wait covers a whole instruction; in the lazy order its workgroup may
     still be at an earlier slice of others, so such plans are refused."""
