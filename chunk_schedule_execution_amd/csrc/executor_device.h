@@ -161,8 +161,10 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
     base = head * esz;
   }
   // Vectors per thread per pass: all issued before any is consumed. bf16 needs more
-  // registers per vector for its widening adds, so it takes two per pass.
-  constexpr int U = (DT == CCL_BF16) ? 2 : 4;
+  // registers per vector for its widening adds and takes two, except in the streaming
+  // variant (long transfers), where two kept half the loads in flight and streamed
+  // 8-12 % slower at 64-256 MiB per rank; at latency-bound sizes four cost 10-17 %.
+  constexpr int U = (DT == CCL_BF16 && !NT) ? 2 : 4;
   const uint4 zero = {0, 0, 0, 0};
   // First pass of the second operand, loaded before the wait only in the streaming
   // variant (large transfers): a wave's loads complete in order, so the polling wave's

@@ -648,6 +648,14 @@ def test_streaming_hints_keep_the_bits(transport):
     xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 31)
     ys, _ = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, transport=transport, streaming=True)
     assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
+    # bf16 in the streaming variant moves four vectors per thread per pass: several full
+    # passes per instruction, odd chunk lengths (unaligned heads) and ragged tails
+    P, N = 8, 3 * 262144 + 40
+    case(f"streaming ring AR bf16 {transport}")
+    xs = W.make_inputs("normal_bf16", N, P, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 7)
+    ys, _ = _run(programs.ring_allreduce(P), xs, "bf16", k=4, nthreads=256, transport=transport, streaming=True,
+                 slice_bytes=64 << 10, repeat=2)
+    assert_all_equal(ys, O2.ring_allreduce(xs, P, "bf16")[0])
 
 
 def test_execute_refuses_graph_capture():
