@@ -164,7 +164,10 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
   // registers per vector for its widening adds and takes two, except in the streaming
   // variant (long transfers), where two kept half the loads in flight and streamed
   // 8-12 % slower at 64-256 MiB per rank; at latency-bound sizes four cost 10-17 %.
-  constexpr int U = (DT == CCL_BF16 && !NT) ? 2 : 4;
+  // Streaming copies and forwards of 32-bit data (one operand) take eight: a 24-rank
+  // ring AllGather at 128 MiB went from 68 to 77 % of HBM peak, while eight for two
+  // operands ran out of registers (ReduceScatter 69 -> 31 %).
+  constexpr int U = (NT && !SRCB && DT != CCL_BF16) ? 8 : (DT == CCL_BF16 && !NT) ? 2 : 4;
   const uint4 zero = {0, 0, 0, 0};
   // First pass of the second operand, loaded before the wait only in the streaming
   // variant (large transfers): a wave's loads complete in order, so the polling wave's

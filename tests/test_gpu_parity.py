@@ -658,6 +658,21 @@ def test_streaming_hints_keep_the_bits(transport):
     assert_all_equal(ys, O2.ring_allreduce(xs, P, "bf16")[0])
 
 
+@pytest.mark.parametrize("transport", ["staged", "direct"])
+def test_streaming_copies_several_passes(transport):
+    """Streaming copies and forwards of 32-bit data move eight vectors per thread per
+    pass: pieces of several passes and slices, odd lengths (unaligned heads, ragged
+    tails), int32 provenance values that must all land in rank order."""
+    P, n = 8, 3 * 65536 + 13
+    case(f"streaming ring AllGather {transport}")
+    xs = W.make_inputs("prov_i32", n, P, W.CFG_A2NEXT_AGRS_24R, size_bytes=n * 4)
+    ys, _ = _run(programs.ring_allgather(P), xs, "i32", k=2, nthreads=256, slice_bytes=64 << 10,
+                 transport=transport, streaming=True, kernel="specialized", repeat=2)
+    want = O1.allgather(xs)
+    for r in range(P):
+        assert np.array_equal(ys[r], want), r
+
+
 def test_execute_refuses_graph_capture():
     """Each launch carries a fresh epoch: a graph would replay a stale one."""
     import torch
