@@ -95,8 +95,8 @@ def main():
     if args.bytes:
         args.no_extras = True
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); the P ranks are "
-              "virtual ranks on that GPU, no multi-GPU run exists", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the P ranks are virtual ranks "
+              "sharing that GPU's memory, and there is no multi-GPU run", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
