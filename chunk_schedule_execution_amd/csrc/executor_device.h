@@ -656,13 +656,13 @@ __device__ __forceinline__ unsigned char* buf_of(const WgState& S, uint32_t b) {
 
 // One instruction: slices [s_begin, s_end) of it (s_end < 0: all of them). `first`
 // runs its completion waits, `last` sets its completion flag, so an instruction can
-// also be run one slice per call (the lazy loop order). OPW >= 0 fixes the low 24 bits
-// of the op word (operation and buffers; plan-specialized code), LLK fixes the
-// protocol (-1: the launch's). Returns false when the workgroup must leave because a
-// wait gave up.
+// also be run one slice per call (the lazy loop order); `wg_last` marks the
+// workgroup's final instruction. OPW >= 0 fixes the low 24 bits of the op word
+// (operation and buffers; plan-specialized code), LLK fixes the protocol (-1: the
+// launch's). Returns false when the workgroup must leave because a wait gave up.
 template <int DT, bool XL, bool NT, long long OPW, int LLK>
 __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const DevExec& R, int gi, int s_begin,
-                                          int s_end, bool first, bool last) {
+                                          int s_end, bool first, bool last, bool wg_last) {
   constexpr int esz = Arith<DT>::esz;
   const int tid = S.tid, nthr = S.nthr;
   if (first && S.itrace && tid == 0) S.itrace[4 * size_t(gi)] = (unsigned long long)wall_clock64();
@@ -672,6 +672,20 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
   const int xin = uni(R.xin), xout = uni(R.xout), done_flag = uni(R.done_flag);
   const int nwaits = uni(R.nwaits);
   const int64_t len = uni64(R.len);
+  const bool ll = LLK < 0 ? A.ll != 0 : LLK == 1;
+  // A receive whose data the sender already placed (direct transport) only waits for
+  // the transfer's flag. As the workgroup's final instruction, with no completion flag
+  // of its own, nothing depends on that wait: the launch ends only once the sending
+  // workgroup has, and the end of the launch makes the sender's stores visible. Its
+  // flag round trip would only lengthen the chain, so it is not taken.
+  if (wg_last && done_flag < 0 && !ll && (op & OPB_RECV) && !(op & (OPB_DSTA | OPB_SEND))) {
+    if (S.itrace && tid == 0 && last) {
+      const unsigned long long now = (unsigned long long)wall_clock64();
+      S.itrace[4 * size_t(gi) + 1] = now;
+      S.itrace[4 * size_t(gi) + 2] = now;
+    }
+    return true;
+  }
   if (first && nwaits > 0) {
     const int wait_begin = uni(R.wait_begin);
     if (tid == 0) {
@@ -704,7 +718,6 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
   unsigned long long done_tag = 0;
   const int done_peer = (XL && last && done_flag >= 0 && A.xcd_tags) ? uni(R.done_peer) : -1;
   if (done_peer >= 0) done_tag = __hip_atomic_load(&A.xcd_tags[done_peer], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const bool ll = LLK < 0 ? A.ll != 0 : LLK == 1;
   if (ll) {
     // one pass over the whole range (at s_begin 0); receivers poll the units they consume
     if (s_begin == 0) {
@@ -775,7 +788,8 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
     stage_records(A, W.first + c0, cnt, s_rec, S.tid, S.nthr);
     __syncthreads();
     for (int j = 0; j < cnt; ++j) {
-      if (!run_instr<DT, XL, NT, -1, -1>(A, S, s_rec[j], W.first + c0 + j, 0, -1, true, true)) return;
+      if (!run_instr<DT, XL, NT, -1, -1>(A, S, s_rec[j], W.first + c0 + j, 0, -1, true, true, c0 + j + 1 == W.n))
+        return;
       ++ran;
     }
     if (c0 + kLdsRecs < W.n) __syncthreads();  // all reads of this block done before it is overwritten

@@ -162,15 +162,15 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bo
   if (loop_form) {
     // one step per distinct operation word; j-th record's word selects it
     s += "__device__ __forceinline__ bool spec_step(const ExecArgs& A, WgState& S, const DevExec& R, int gi, int s0, "
-         "int s1, bool first, bool last) {\n";
+         "int s1, bool first, bool last, bool wl) {\n";
     s += "  switch (uint32_t(uni(int32_t(R.op))) & 0xffffffu) {\n";
     for (uint32_t o : ops)
-      s += "    case " + hex32(o).substr(0, 8) + "u: return " + step(o, "R", "gi", "s0, s1, first, last") + ";\n";
+      s += "    case " + hex32(o).substr(0, 8) + "u: return " + step(o, "R", "gi", "s0, s1, first, last, wl") + ";\n";
     s += "    default: return false;  // every word of the plan has a case\n  }\n}\n";
     s += "__device__ __forceinline__ int spec_loop(const ExecArgs& A, WgState& S, const DevExec* r, int g, int n) {\n";
     if (!lazy) {
       s += "  for (int j = 0; j < n; ++j)\n";
-      s += "    if (!spec_step(A, S, r[j], g + j, 0, -1, true, true)) return -1;\n";
+      s += "    if (!spec_step(A, S, r[j], g + j, 0, -1, true, true, j + 1 == n)) return -1;\n";
     } else {
       s += "  int iters = 1;\n";
       s += "  for (int j = 0; j < n; ++j) {\n";
@@ -179,7 +179,7 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bo
       s += "  for (int it = 0; it < iters; ++it)\n";
       s += "    for (int j = 0; j < n; ++j) {\n";
       s += std::string("      const int e = ") + (ll ? "1" : "uni(r[j].nsl) > 1 ? uni(r[j].nsl) : 1") + ";\n";
-      s += "      if (it < e && !spec_step(A, S, r[j], g + j, it, it + 1, it == 0, it == e - 1)) return -1;\n";
+      s += "      if (it < e && !spec_step(A, S, r[j], g + j, it, it + 1, it == 0, it == e - 1, j + 1 == n)) return -1;\n";
       s += "    }\n";
     }
     s += "  return n;\n}\n";
@@ -195,7 +195,9 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bo
            "(const ExecArgs& A, WgState& S, const DevExec* r, int g) {\n";
       if (!lazy) {
         for (int j = 0; j < n; ++j)
-          s += "  if (!" + step(seq[j], "r[" + std::to_string(j) + "]", "g + " + std::to_string(j), "0, -1, true, true") +
+          s += "  if (!" +
+               step(seq[j], "r[" + std::to_string(j) + "]", "g + " + std::to_string(j),
+                    std::string("0, -1, true, true, ") + (j + 1 == n ? "true" : "false")) +
                ") return -1;\n";
       } else {
         // one slice of every instruction per iteration; an LL instruction is one pass
@@ -214,7 +216,7 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bo
           const std::string e = "e" + std::to_string(j);
           s += "    if (it < " + e + " && !" +
                step(seq[j], "r[" + std::to_string(j) + "]", "g + " + std::to_string(j),
-                    "it, it + 1, it == 0, it == " + e + " - 1") +
+                    "it, it + 1, it == 0, it == " + e + " - 1, " + (j + 1 == n ? "true" : "false")) +
                ") return -1;\n";
         }
         s += "  }\n";
