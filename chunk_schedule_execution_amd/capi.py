@@ -40,6 +40,7 @@ CCL_FLAG_FORCE_XCD_LOCAL = 0x100
 CCL_FLAG_SPECIALIZE = 0x200
 CCL_FLAG_LAZY = 0x400
 CCL_FLAG_SPECIALIZE_LOOP = 0x800
+CCL_FLAG_DEBUG_DROP_FLAG = 0x1000
 CCL_I_RECV, CCL_I_SRCB, CCL_I_DSTA, CCL_I_SEND, CCL_I_LOCAL_IN = 0x1, 0x2, 0x4, 0x8, 0x10
 
 

@@ -303,6 +303,7 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
     A.timeout_ticks = plan->timeout_ticks;
     A.ll = (hp.cfg.flags & CCL_FLAG_LL) ? 1 : 0;
     A.ll_flag = uint32_t(epoch);
+    A.drop_xfer = (hp.cfg.flags & CCL_FLAG_DEBUG_DROP_FLAG) ? 0 : -1;
     for (int r = 0; r < hp.P; ++r) {
       A.base[CCL_BUF_INPUT][r] = const_cast<unsigned char*>(static_cast<const unsigned char*>(sendbufs[r]));
       A.base[CCL_BUF_OUTPUT][r] = static_cast<unsigned char*>(recvbufs[r]);

@@ -168,6 +168,9 @@ void validate(HostPlan& hp, const ccl_program_desc* prog, int nranks, int nchunk
   if (cfg->slice_bytes < 0) fail(CCL_ERR_INVALID_ARGUMENT, "slice_bytes must be >= 0");
   if (cfg->scheduler < 0 || cfg->scheduler > 2) fail(CCL_ERR_INVALID_ARGUMENT, "scheduler");
   if (cfg->wg_alloc < 0 || cfg->wg_alloc > 1) fail(CCL_ERR_INVALID_ARGUMENT, "wg_alloc");
+  if ((cfg->flags & CCL_FLAG_DEBUG_DROP_FLAG) && (cfg->flags & (CCL_FLAG_LL | CCL_FLAG_DIRECT)))
+    fail(CCL_ERR_UNSUPPORTED, "flag dropping needs the staged slice-flag protocol (LL flags travel in the data; a "
+                              "direct receive at the end of a workgroup is not waited for)");
 
   hp.desc = d;
   hp.desc.ops = nullptr;

@@ -35,6 +35,8 @@ class PlanConfig:
     force_xcd_local: bool = False  # that variant even for spread layouts (tests its release path)
     num_cus: int = 0
     timeout_us: int = 0
+    # failure injection for watchdog tests: transfer 0's flag is never set
+    debug_drop_flag: bool = False
     # "interpreter" (one kernel for every plan), "specialized" (a kernel generated for
     # this plan: straight-line code for short plans, the loop form for long ones),
     # "specialized_loop" (the loop form always) or "lazy" (a generated kernel in the
@@ -67,6 +69,8 @@ class PlanConfig:
             flags |= capi.CCL_FLAG_SPECIALIZE | capi.CCL_FLAG_LAZY
         elif self.kernel != "interpreter":
             raise ValueError(f"unknown kernel {self.kernel!r}")
+        if self.debug_drop_flag:
+            flags |= capi.CCL_FLAG_DEBUG_DROP_FLAG
         if self.protocol == "ll":
             flags |= capi.CCL_FLAG_LL
         elif self.protocol != "simple":

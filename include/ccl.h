@@ -159,6 +159,13 @@ typedef struct {
                                     any (the algorithm once per slice; ReSCCL report, section 2.1), instead of
                                     every slice of an instruction before the next. CCL_ERR_UNSUPPORTED for
                                     plans with cross-workgroup completion waits */
+#define CCL_FLAG_DEBUG_DROP_FLAG 0x1000u /* failure injection for tests of the watchdog (simple protocol): the
+                                    sender of transfer 0 never sets its flag, so its receiver waits out the
+                                    watchdog budget (timeout_us) and every launch of the plan ends with
+                                    CCL_ERR_TIMEOUT from ccl_plan_status; every workgroup still leaves.
+                                    Refused (CCL_ERR_UNSUPPORTED) with CCL_FLAG_LL, whose flags travel inside
+                                    the data, and with CCL_FLAG_DIRECT, where a receive that ends its
+                                    workgroup is not waited for */
 #define CCL_FLAG_COHERENT_ONLY 0x20u /* write transfers and their flags with agent-coherent stores. By default a
                                     plan whose lowered layout keeps every transfer on one XCD (workgroup ids
                                     congruent mod 8, which the round-robin dispatch places together) writes

@@ -154,3 +154,15 @@ def test_build_script_loads_without_the_library():
     assert r.returncode == 0, r.stderr
     src = open(os.path.join(ROOT, "__graft_entry__.py")).read()
     assert "from chunk_schedule_execution_amd.build import" not in src
+
+
+def test_flag_dropping_needs_the_staged_slice_flag_protocol():
+    """The watchdog's failure injection (transfer 0's flag is never set) is refused where
+    a missing flag would go unnoticed: LL flags travel inside the data, and a direct
+    receive that ends its workgroup is not waited for."""
+    prog = programs.ring_allreduce(4)
+    assert host_plan(prog, debug_drop_flag=True).info()["num_transfers"] > 0
+    for knobs in (dict(protocol="ll"), dict(transport="direct")):
+        with pytest.raises(capi.CCLError) as e:
+            host_plan(prog, debug_drop_flag=True, **knobs)
+        assert e.value.status == capi.CCL_ERR_UNSUPPORTED

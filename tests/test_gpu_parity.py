@@ -673,6 +673,39 @@ def test_streaming_copies_several_passes(transport):
         assert np.array_equal(ys[r], want), r
 
 
+@pytest.mark.parametrize("kernel", ["interpreter", "specialized"])
+def test_watchdog_ends_a_launch_whose_flag_never_comes(kernel):
+    """Failure detection: transfer 0's sender never sets its flag (failure injection),
+    so its receiver waits out a 20 ms watchdog budget, records CCL_ERR_TIMEOUT and
+    aborts the launch; every other waiter leaves, the launch ends, and the status call
+    reports the timeout. Later launches of the same plan fail the same way, and a
+    healthy plan afterwards still matches the oracle."""
+    import time
+
+    import torch
+
+    from chunk_schedule_execution_amd import Plan, PlanConfig, capi
+    from gpu_util import to_dev
+
+    P, N = 4, 4 * 4096
+    case(f"watchdog, dropped flag, {kernel} kernel")
+    xs = W.make_inputs("int_f32", N, P, W.CFG_RING_AR_4R_INT, size_bytes=N * 4)
+    ins = [to_dev(x, "f32") for x in xs]
+    outs = [torch.empty(N, device="cuda:0") for _ in range(P)]
+    bad = Plan(programs.ring_allreduce(P), 2, PlanConfig(dtype="f32", max_count=N, nthreads=256, timeout_us=20000,
+                                                         debug_drop_flag=True, kernel=kernel))
+    for launch in range(2):
+        t0 = time.perf_counter()
+        bad.execute(ins, outs, N)
+        with pytest.raises(capi.CCLError) as e:
+            bad.status()
+        assert e.value.status == capi.CCL_ERR_TIMEOUT, str(e.value)
+        assert time.perf_counter() - t0 < 5.0
+    bad.destroy()
+    ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=2, nthreads=256, kernel=kernel)
+    assert_all_equal(ys, O1.allreduce(xs, "f32").exact.astype(np.float32))
+
+
 def test_execute_refuses_graph_capture():
     """Each launch carries a fresh epoch: a graph would replay a stale one."""
     import torch
