@@ -131,7 +131,8 @@ void setup_device(ccl_plan* p) {
   p->d_waits = upload(p, hp.dwaits);
   p->geo.resize(4);
   for (auto& g : p->geo) g.d = static_cast<DevExec*>(p->dev_alloc(std::max<size_t>(1, hp.dins.size()) * sizeof(DevExec)));
-  size_t nx = std::max<size_t>(1, hp.dxf.size());
+  // one spare transfer flag for failure injection (CCL_FLAG_DEBUG_DROP_FLAG)
+  size_t nx = hp.dxf.size() + 1;
   int nd = 0;
   for (const auto& D : hp.dins) nd = std::max(nd, D.done_flag + 1);
   const size_t xbytes = nx * 8 * kFlagStride, dbytes = size_t(std::max(1, nd)) * 8 * kFlagStride;
@@ -303,7 +304,6 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
     A.timeout_ticks = plan->timeout_ticks;
     A.ll = (hp.cfg.flags & CCL_FLAG_LL) ? 1 : 0;
     A.ll_flag = uint32_t(epoch);
-    A.drop_xfer = (hp.cfg.flags & CCL_FLAG_DEBUG_DROP_FLAG) ? 0 : -1;
     for (int r = 0; r < hp.P; ++r) {
       A.base[CCL_BUF_INPUT][r] = const_cast<unsigned char*>(static_cast<const unsigned char*>(sendbufs[r]));
       A.base[CCL_BUF_OUTPUT][r] = static_cast<unsigned char*>(recvbufs[r]);

@@ -1080,6 +1080,9 @@ void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec
            (uint32_t(D.t_rank < 0 ? 0 : D.t_rank) << 24);
     E.xin = D.xin;
     E.xout = D.xout;
+    // failure injection: the sender of transfer 0 sets a spare flag (one past the last
+    // transfer's) that no receiver waits for, so transfer 0's receiver never sees one
+    if ((hp.cfg.flags & CCL_FLAG_DEBUG_DROP_FLAG) && D.xout == 0) E.xout = int32_t(hp.dxf.size());
     E.done_flag = D.done_flag;
     E.wait_begin = D.wait_begin;
     E.nwaits = D.nwaits;

@@ -748,7 +748,7 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
       if (S.itrace && tid == 0 && s == 0) S.itrace[4 * size_t(gi) + 1] = (unsigned long long)wall_clock64();
       if (op & OPB_SEND) wait_vm_stores();
       __syncthreads();
-      if ((op & OPB_SEND) && tid == 0 && xout != A.drop_xfer)
+      if ((op & OPB_SEND) && tid == 0)
         slot_flag_store<XL>(&A.xflags[size_t(xout) * kFlagStride], S.E + (unsigned long long)(s + 1), XL && use_here(peer_tag) == S.my_tag);
     }
   }
