@@ -450,19 +450,21 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         row = {"bytes_per_rank": S}
         for name, pr in (("two_phase", programs.two_phase_alltoall(G, L)), ("direct", programs.direct_alltoall(Pa))):
             best = None
-            for k, nt in ((1, 256), (2, 256), (2, 128), (4, 128)):
+            # direct transport, with and without the streaming variant (whose copies keep
+            # eight vectors per thread in flight)
+            for k, nt, proto in ((1, 256, 2), (2, 256, 2), (2, 128, 2), (4, 128, 2), (1, 256, 3), (2, 256, 3)):
                 try:
-                    pl = make_plan(pr, N, k, nt, 256 << 10, 2, dtype="i32")
+                    pl = make_plan(pr, N, k, nt, 256 << 10, proto, dtype="i32")
                 except capi.CCLError:
                     continue  # more workgroups than fit at once
                 t = time_launches(lambda: pl.execute(ii, oo, N, stream), 10)
                 if best is None or t < best[0]:
-                    best = (t, k, pl.info()["num_workgroups"], stats(pl, N, t)["hbm_frac"])
+                    best = (t, k, nt, PROTOCOLS[proto][2], pl.info()["num_workgroups"], stats(pl, N, t)["hbm_frac"])
                 release(pl)
             if best:
-                t, k, nwg, hf = best
-                row[name] = {"us": round(t * 1e6, 2), "k": k, "workgroups": nwg, "hbm_frac": hf,
-                             "busbw": round(S / t * (Pa - 1) / Pa / 1e9, 2)}
+                t, k, nt, streaming, nwg, hf = best
+                row[name] = {"us": round(t * 1e6, 2), "k": k, "nthreads": nt, "streaming": streaming,
+                             "workgroups": nwg, "hbm_frac": hf, "busbw": round(S / t * (Pa - 1) / Pa / 1e9, 2)}
         a2a.append(row)
         del ii, oo
         release()
@@ -480,9 +482,12 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         row = {"bytes_per_rank": S}
         for split in (True, False):
             modes = (("hpds", "state"), ("rr", "connection"))
-            k, pls = fitting([lambda k, sc=sc, al=al: make_plan(programs.alltonext(G, L, split=split), N, k, 512,
-                                                                  256 << 10, 2, scheduler=sc, wg_alloc=al)
-                              for sc, al in modes])
+            # one launch configuration for both modes (256 threads, 128 KiB slices, direct
+            # transport with streaming hints: the best of a sweep at 64 MiB, where 256
+            # threads let the split program's 1120-1248 workgroups of k = 16 fit at once)
+            k, pls = fitting([lambda k, sc=sc, al=al: make_plan(programs.alltonext(G, L, split=split), N, k, 256,
+                                                                  128 << 10, 3, scheduler=sc, wg_alloc=al)
+                              for sc, al in modes], ks=(16, 8, 4, 2, 1))
             for (sched, alloc), pl in zip(modes, pls):
                 t = time_launches(lambda: pl.execute(ii, oo, N, stream), 10)
                 row[f"{'split' if split else 'unsplit'}_{sched}_{alloc}"] = {
