@@ -514,18 +514,38 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
             ii = device_inputs("f32", count, Pn, 6000 + len(coll))
             oo = [torch.empty(nout, device=dev) for _ in range(Pn)]
             modes = (("hpds", "state"), ("rr", "connection"))
-            # one launch configuration for both modes (512 threads, 64 KiB slices, direct
-            # transport with streaming hints: the best of a sweep of the ring at this size)
-            k, pls = fitting([lambda k, sc=sc, al=al: make_plan(pr, count, k, 512, 64 << 10, 3, scheduler=sc,
-                                                                  wg_alloc=al) for sc, al in modes],
-                             ks=(32, 16, 8, 4, 2, 1))
-            for (sched, alloc), pl in zip(modes, pls):
-                t = time_launches(lambda: pl.execute(ii, oo, count, stream), 5)
-                Sb = n_big * 4
-                agrs[f"{coll}_{variant}_{sched}_{alloc}"] = {
-                    "us": round(t * 1e6, 2), "busbw": round(Sb / t * (Pn - 1) / Pn / 1e9, 2), "k": k,
-                    "workgroups": pl.info()["num_workgroups"], "hbm_frac": stats(pl, count, t)["hbm_frac"]}
-            release(*pls)
+            Sb = n_big * 4
+            if variant == "ring":
+                # one launch configuration for both modes (512 threads, 64 KiB slices, direct
+                # transport with streaming hints: the best of a sweep of the ring at this size)
+                k, pls = fitting([lambda k, sc=sc, al=al: make_plan(pr, count, k, 512, 64 << 10, 3, scheduler=sc,
+                                                                      wg_alloc=al) for sc, al in modes],
+                                 ks=(32, 16, 8, 4, 2, 1))
+                for (sched, alloc), pl in zip(modes, pls):
+                    t = time_launches(lambda: pl.execute(ii, oo, count, stream), 5)
+                    agrs[f"{coll}_{variant}_{sched}_{alloc}"] = {
+                        "us": round(t * 1e6, 2), "busbw": round(Sb / t * (Pn - 1) / Pn / 1e9, 2), "k": k,
+                        "workgroups": pl.info()["num_workgroups"], "hbm_frac": stats(pl, count, t)["hbm_frac"]}
+                release(*pls)
+            else:
+                # each mode at its best point of one small sweep: state-based allocation needs
+                # half the workgroups, so it reaches channel counts whose connection-based
+                # grid would not fit on the device at once
+                for sched, alloc in modes:
+                    best = None
+                    for k, nt in ((4, 512), (8, 512), (8, 256), (16, 256), (16, 128)):
+                        try:
+                            pl = make_plan(pr, count, k, nt, 64 << 10, 3, scheduler=sched, wg_alloc=alloc)
+                        except capi.CCLError:
+                            continue  # more workgroups than fit at once
+                        t = time_launches(lambda: pl.execute(ii, oo, count, stream), 5)
+                        if best is None or t < best[0]:
+                            best = (t, k, nt, pl.info()["num_workgroups"], stats(pl, count, t)["hbm_frac"])
+                        release(pl)
+                    t, k, nt, nwg, hf = best
+                    agrs[f"{coll}_{variant}_{sched}_{alloc}"] = {
+                        "us": round(t * 1e6, 2), "busbw": round(Sb / t * (Pn - 1) / Pn / 1e9, 2), "k": k,
+                        "nthreads": nt, "workgroups": nwg, "hbm_frac": hf}
             del ii, oo
             release()
     res["allgather_reducescatter_24r_128mib"] = agrs
