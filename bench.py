@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also run the plain copy kernel this many times on 256 MiB (counter calibration)")
+    ap.add_argument("--workload", choices=["ring_allreduce_8r", "allgather_24r", "reducescatter_24r"],
+                    default="ring_allreduce_8r",
+                    help="profiling runs of another collective instead of the headline: the 24-rank ring AllGather "
+                         "or ReduceScatter at 128 MiB (the larger buffer), with --fixed (default 32,512,65536,3)")
     return ap.parse_args()
 
 
@@ -90,8 +94,65 @@ def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def profile_collective(args) -> None:
+    """One JSON line for a 24-rank ring AllGather or ReduceScatter at 128 MiB, timed with
+    HIP events on the launch stream in a fixed configuration (profiling runs)."""
+    import torch
+
+    from chunk_schedule_execution_amd import Plan, PlanConfig, capi, programs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    Pn = 24
+    n_big = Pn * ((32 << 20) // Pn)  # 33,554,424 fp32: the AllGather output, the ReduceScatter input
+    ag = args.workload == "allgather_24r"
+    prog = programs.ring_allgather(Pn) if ag else programs.ring_reducescatter(Pn)
+    count, nout = (n_big // Pn, n_big) if ag else (n_big, n_big // Pn)
+    cfg = tuple(int(v) for v in (args.fixed or "32,512,65536,3").split(","))[:4]
+    k, nt, sl, proto = cfg
+    g = torch.Generator(device=dev)
+    g.manual_seed(6000 + len(args.workload))
+    ii = [torch.randn(count, generator=g, device=dev) for _ in range(Pn)]
+    oo = [torch.empty(nout, device=dev) for _ in range(Pn)]
+    plan = Plan(prog, k, PlanConfig(dtype="f32", max_count=count, nthreads=nt, slice_bytes=sl,
+                                    protocol=PROTOCOLS[proto][0], transport=PROTOCOLS[proto][1],
+                                    streaming=PROTOCOLS[proto][2], kernel=KERNELS[KERNEL]))
+    for _ in range(args.warmup):
+        plan.execute(ii, oo, count, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.execute(ii, oo, count, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    plan.status()
+    t = e0.elapsed_time(e1) * 1e-3 / args.steps
+    pb = plan.bytes(count)
+    Sb = n_big * 4
+    if args.copy_probe:
+        nb = 1 << 28
+        a = torch.zeros(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty(nb, dtype=torch.uint8, device=dev)
+        for _ in range(args.copy_probe):
+            capi.ccl_copy_probe(b.data_ptr(), a.data_ptr(), nb, 256, 256, stream.cuda_stream)
+        torch.cuda.synchronize()
+    print(json.dumps({"workload": f"ring {'AllGather' if ag else 'ReduceScatter'}, 24 virtual ranks, fp32, 128 MiB",
+                      "config": list(cfg), "workgroups": plan.info()["num_workgroups"], "steps": args.steps,
+                      "us_per_launch": round(t * 1e6, 2), "busbw": round(Sb / t * (Pn - 1) / Pn / 1e9, 2),
+                      "plan_bytes_per_launch": pb, "hbm_frac": round(pb / t / 1e9 / HBM_PEAK_GBS, 4),
+                      "source_digest": source_digest()}), flush=True)
+    plan.destroy()
+
+
 def main():
     args = parse()
+    if args.workload != "ring_allreduce_8r":
+        if args.gpus != 1:
+            print("bench.py runs on one GPU only", file=sys.stderr)
+            sys.exit(2)
+        profile_collective(args)
+        return
     if args.bytes:
         args.no_extras = True
     if args.gpus != 1:
