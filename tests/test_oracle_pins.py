@@ -329,6 +329,45 @@ def test_o2_rs2d_integer_exact():
         assert np.array_equal(got[r].astype(np.float64), ref[r].exact)
 
 
+def _rs2d_on_golden(golden, name, fn):
+    d = _fixture(golden, name)
+    G, L = int(d["G"][0]), int(d["L"][0])
+    xs = [np.array(ints(d[f"x{r}"]), np.float32) for r in range(G * L)]
+    got = fn(xs, G, L, "f32")
+    return [int(np.asarray(y).astype(np.int64)[0]) for y in got], d
+
+
+@pytest.mark.parametrize("name", ["reducescatter_2d_g2l2_order.txt", "reducescatter_2d_g2l3_chain.txt"])
+def test_o2_rs2d_golden(golden, name):
+    """Hand-worked fixtures fix the 2-D ReduceScatter's association: inside the group
+    first (chain from lane l+1 to the owning lane l), then across the groups."""
+    got, d = _rs2d_on_golden(golden, name, O2.reducescatter_2d)
+    assert got == ints(d["y"])
+
+
+def _rs2d_variant(xs, G, L, dtype, cross_first=False, owner_first=False, wrong_map=False):
+    """Plausible slips in a 2-D ReduceScatter, for the planted-mistake test below."""
+    n = len(xs[0]) // (G * L)
+    out = []
+    for b in range(G * L):
+        l, h = divmod(b, G) if wrong_map else (b % L, b // L)
+        lo, hi = b * n, (b + 1) * n
+        lane_order = [(l + t) % L for t in range(L)] if owner_first else [(l + 1 + t) % L for t in range(L)]
+        group_order = [(h + 1 + t) % G for t in range(G)]
+        if cross_first:
+            parts = [O2.fold([np.asarray(xs[g * L + ln][lo:hi]) for g in group_order], dtype) for ln in lane_order]
+        else:
+            parts = [O2.fold([np.asarray(xs[g * L + ln][lo:hi]) for ln in lane_order], dtype) for g in group_order]
+        out.append(O2.fold(parts, dtype))
+    return out
+
+
+def test_rs2d_variant_harness_is_the_oracle_when_unplanted(golden):
+    for name in ("reducescatter_2d_g2l2_order.txt", "reducescatter_2d_g2l3_chain.txt"):
+        got, d = _rs2d_on_golden(golden, name, _rs2d_variant)
+        assert got == ints(d["y"])
+
+
 # ---------------------------------------------------------------- program interpreter
 
 # A 2-rank AllReduce written out by hand: rank 1 sends its chunk 0 to rank 0, which
@@ -394,6 +433,35 @@ def test_scaled_error_cases():
     assert nm.scaled_error(np.array([1.0, 0.0, -3.0], np.float32), exact, abs_sum, "f32") == 0.0
     assert nm.scaled_error(np.array([1.5, 0.0, -3.0], np.float32), exact, abs_sum, "f32") == 0.5 / 3
     assert nm.scaled_error(np.array([1.0, 1e-30, -3.0], np.float32), exact, abs_sum, "f32") == float("inf")
+
+
+def test_elementwise_rel_error_cases():
+    """Hand-worked: only elements whose exact sum is at least 1e-3 of their magnitude
+    sum count; all-zero columns never do."""
+    exact = np.array([1.0, 0.0, -3.0, 1e-4])
+    abs_sum = np.array([3.0, 0.0, 3.0, 2.0])
+    y = np.array([1.5, 0.0, -2.7, 5.0], np.float32)
+    # kept: elements 0 (|1| >= 0.003) and 2 (|-3| >= 0.003); element 3 (1e-4 < 0.002) is not
+    assert nm.elementwise_rel_error(y, exact, abs_sum, "f32") == pytest.approx(0.5)
+    y2 = np.array([1.0, 0.0, -2.7, 5.0], np.float32)
+    assert nm.elementwise_rel_error(y2, exact, abs_sum, "f32") == pytest.approx(0.3 / 3.0, rel=1e-6)
+    assert nm.elementwise_rel_error(y2, exact, abs_sum, "f32", floor=1e-5) == pytest.approx((5.0 - 1e-4) / 1e-4, rel=1e-6)
+    assert nm.elementwise_rel_error(np.zeros(2, np.float32), np.zeros(2), np.zeros(2), "f32") == 0.0
+
+
+@pytest.mark.parametrize("P", [4, 8, 24])
+def test_elementwise_rel_error_within_derived_bound(P):
+    """Recursive summation: |y - s| <= (P-1) u sum|x| (u = 2^-24, up to O(u^2)); on the
+    kept elements |s| >= 1e-3 sum|x|, so the plain relative error is at most
+    (P-1) u 1e3 there. The chain-order oracle stays inside it; adding one input twice
+    (a planted duplicate addend) does not."""
+    xs = W.make_inputs("normal_f32", 20000, P, cfg_id=84)
+    ref = O1.allreduce(xs, "f32")
+    y = O2.ring_allreduce(xs, P, "f32")[0]
+    bound = (P - 1) * 2.0**-24 * 1e3 * (1 + 1e-6)
+    assert nm.elementwise_rel_error(y, ref.exact, ref.abs_sum, "f32") <= bound
+    bad = O2.add_stored(y, xs[0], "f32")
+    assert nm.elementwise_rel_error(bad, ref.exact, ref.abs_sum, "f32") > bound
 
 
 # ---------------------------------------------------------------- O2 tree
@@ -500,6 +568,17 @@ def test_planted_mistakes_fail_the_pins(golden, monkeypatch):
         # own chunk j by j mod P instead of by block
         m.setattr(O2, "_ring_chunk", lambda xs, lo, hi, owner, dtype: real(xs, lo, hi, lo % len(xs), dtype))
         assert not _golden_ring_ok(golden, "ring_allreduce_p3_blocks.txt")
+
+    # the 2-D ReduceScatter: stages swapped, chain starting at the owning lane, blocks
+    # mapped to (group, lane) the wrong way round; each fails a fixture and lands where
+    # the fixture works it out by hand
+    for kw, row, name in ((dict(cross_first=True), "swapped", "reducescatter_2d_g2l2_order.txt"),
+                          (dict(owner_first=True), "owner_first", "reducescatter_2d_g2l3_chain.txt"),
+                          (dict(wrong_map=True), "wrong_map", "reducescatter_2d_g2l3_chain.txt")):
+        with monkeypatch.context() as m:
+            m.setattr(O2, "reducescatter_2d", lambda xs, G, L, dtype, kw=kw: _rs2d_variant(xs, G, L, dtype, **kw))
+            got, d = _rs2d_on_golden(golden, name, O2.reducescatter_2d)
+            assert got != ints(d["y"]) and got == ints(d[row]), kw
 
     with monkeypatch.context() as m:
         m.setattr(nm, "f32_to_bf16_rne", lambda x: (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16))
