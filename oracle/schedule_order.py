@@ -197,34 +197,45 @@ def chunk_of(idx, N: int, C: int):
 
 def ring_allreduce_at(xs, nchunks, idx, dtype):
     """Ring AllReduce output at element indices ``idx`` (same for every rank)."""
-    P = len(xs)
-    N = len(xs[0])
+    idx = np.asarray(idx, dtype=np.int64)
+    return ring_allreduce_columns([np.asarray(x)[idx] for x in xs], len(xs[0]), nchunks, idx, dtype)
+
+
+def ring_allreduce_columns(cols, N, nchunks, idx, dtype):
+    """The same, given only each rank's values at ``idx`` (cols[r] = x_r[idx]) and the
+    per-rank length N: full-size inputs never need to be on the host."""
+    P = len(cols)
     c = nchunks // P
     idx = np.asarray(idx, dtype=np.int64)
     owner = chunk_of(idx, N, nchunks) // c
-    out = np.empty(len(idx), dtype=np.asarray(xs[0]).dtype)
+    out = np.empty(len(idx), dtype=np.asarray(cols[0]).dtype)
     for o in range(P):
         sel = np.nonzero(owner == o)[0]
         if sel.size == 0:
             continue
         order = [(o + 1 + t) % P for t in range(P)]
-        out[sel] = fold([np.asarray(xs[r])[idx[sel]] for r in order], dtype)
+        out[sel] = fold([np.asarray(cols[r])[sel] for r in order], dtype)
     return out
 
 
 def hierarchical_allreduce_at(xs, G, L, idx, dtype):
-    N = len(xs[0])
+    idx = np.asarray(idx, dtype=np.int64)
+    return hierarchical_allreduce_columns([np.asarray(x)[idx] for x in xs], len(xs[0]), G, L, idx, dtype)
+
+
+def hierarchical_allreduce_columns(cols, N, G, L, idx, dtype):
+    """Hierarchical AllReduce at ``idx`` given only each rank's values there."""
     C = L * G
     idx = np.asarray(idx, dtype=np.int64)
     j = chunk_of(idx, N, C)
-    out = np.empty(len(idx), dtype=np.asarray(xs[0]).dtype)
+    out = np.empty(len(idx), dtype=np.asarray(cols[0]).dtype)
     for jj in np.unique(j):
         sel = np.nonzero(j == jj)[0]
         l, gp = divmod(int(jj), G)
         partial = []
         for g in range(G):
             lanes = [(l + 1 + t) % L for t in range(L)]
-            partial.append(fold([np.asarray(xs[g * L + ln])[idx[sel]] for ln in lanes], dtype))
+            partial.append(fold([np.asarray(cols[g * L + ln])[sel] for ln in lanes], dtype))
         groups = [(gp + 1 + t) % G for t in range(G)]
         out[sel] = fold([partial[g] for g in groups], dtype)
     return out

@@ -37,6 +37,36 @@ def assert_all_equal(ys, want):
             raise AssertionError(f"rank {r}: {bad.size} elements differ, first at {bad[:5]}: {y[bad[:5]]} vs {want[bad[:5]]}")
 
 
+def chk_ring(P, dtype="f32"):
+    """Check of one launch of a repeated run: the ring's chain order on that launch's inputs."""
+    return lambda ys, xs, prior: assert_all_equal(ys, O2.ring_allreduce(xs, P, dtype)[0])
+
+
+def chk_tree(nchunks, dtype="f32"):
+    return lambda ys, xs, prior: assert_all_equal(ys, O2.tree_allreduce(xs, nchunks, dtype)[0])
+
+
+def chk_hier(G, L, dtype="bf16"):
+    return lambda ys, xs, prior: assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, dtype)[0])
+
+
+def chk_per_rank(want_of):
+    """want_of(xs, prior) gives every rank's expected output."""
+    def check(ys, xs, prior):
+        want = want_of(xs, prior)
+        for r in range(len(ys)):
+            assert np.array_equal(ys[r], want[r]), r
+    return check
+
+
+def chk_alltoall():
+    return chk_per_rank(lambda xs, prior: O1.alltoall(xs))
+
+
+def chk_allgather():
+    return chk_per_rank(lambda xs, prior: [O1.allgather(xs)] * len(xs))
+
+
 # ------------------------------------------------------------------ ring AllReduce
 
 def test_ring_allreduce_4r_1mib_integer_exact():
@@ -113,21 +143,15 @@ def test_repeated_launches_and_counts(algo, transport, kernel):
     P = 8
     prog = programs.ring_allreduce(P) if algo == "ring" else programs.tree_allreduce(P)
     oracle = O2.ring_allreduce if algo == "ring" else O2.tree_allreduce
-    from gpu_util import to_dev, to_host
-    import torch
     from chunk_schedule_execution_amd import Plan, PlanConfig
     plan = Plan(prog, 4, PlanConfig(dtype="f32", max_count=50_000, slice_bytes=8192, transport=transport,
                                     kernel=kernel))
+    check = chk_ring(P) if algo == "ring" else chk_tree(P)
     for N in (50_000, 777, 50_000, 12_345, 1):
         case(f"{algo} AR {transport} {kernel} repeated N={N}")
         xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 7)
-        ins = [to_dev(x, "f32") for x in xs]
-        outs = [torch.empty(50_000, dtype=torch.float32, device="cuda:0") for _ in range(P)]
-        for _ in range(3):
-            plan.execute(ins, outs, N)
-        torch.cuda.synchronize()
-        plan.status()
-        assert_all_equal([to_host(o, "f32")[:N] for o in outs], oracle(xs, P, "f32")[0])
+        ys, _ = _run(prog, xs, "f32", plan=plan, repeat=3, check=check)
+        assert_all_equal(ys, oracle(xs, P, "f32")[0])
     plan.destroy()
 
 
@@ -143,11 +167,17 @@ def test_ring_allreduce_8r_full_size_sampled(S, k, nt, sl, knobs):
     P, N = 8, S // 4
     case(f"ring AR full size S={S} k={k} nt={nt} {knobs}")
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=S)
-    ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=k, nthreads=nt, slice_bytes=sl, repeat=2, **knobs)
-    for r in range(1, P):
-        assert np.array_equal(ys[r], ys[0])
     rng = np.random.default_rng(1)
     idx = np.unique(np.concatenate([rng.integers(0, N, 4000), [0, N - 1], np.arange(N // P - 3, N // P + 3)]))
+
+    def sampled(ys, xj, prior):
+        for r in range(1, P):
+            assert np.array_equal(ys[r], ys[0])
+        assert np.array_equal(ys[0][idx], O2.ring_allreduce_at(xj, P, idx, "f32"))
+    ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=k, nthreads=nt, slice_bytes=sl, repeat=2, check=sampled,
+                 **knobs)
+    for r in range(1, P):
+        assert np.array_equal(ys[r], ys[0])
     assert np.array_equal(ys[0][idx], O2.ring_allreduce_at(xs, P, idx, "f32"))
     ref = O1.allreduce_at(xs, idx, "f32")
     assert nm.scaled_error(ys[0][idx], ref.exact, ref.abs_sum, "f32") <= F32_TOL(P)
@@ -358,7 +388,7 @@ def test_ll_repeated_launches():
     P, N = 8, 50_000
     case("LL ring AR repeated")
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 11)
-    ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=4, protocol="ll", repeat=5)
+    ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=4, protocol="ll", repeat=5, check=chk_ring(P))
     assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
 
 
@@ -382,7 +412,7 @@ def test_xcd_local_and_coherent_stores_agree(protocol, k, nt, num_cus):
         modes.append(dict(xcd_local=True, force_xcd_local=True))
     for mode in modes:
         ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=k, protocol=protocol, nthreads=nt,
-                        slice_bytes=16 << 10, repeat=4, num_cus=num_cus, **mode)
+                        slice_bytes=16 << 10, repeat=4, check=chk_ring(P), num_cus=num_cus, **mode)
         info = plan.info()
         aligned = num_cus != 8
         assert info["xcd_local"] == (1 if mode["xcd_local"] and (aligned or mode.get("force_xcd_local")) else 0)
@@ -398,6 +428,7 @@ def test_xcd_local_hierarchical_and_alltoall():
     want = O2.hierarchical_allreduce(xs, G, L, "bf16")[0]
     for xcd_local in (True, False):
         ys, _ = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, xcd_local=xcd_local, repeat=3,
+                     check=chk_hier(G, L),
                      slice_bytes=8192)
         assert_all_equal(ys, want)
     G, L, b = 4, 8, 513
@@ -405,7 +436,8 @@ def test_xcd_local_hierarchical_and_alltoall():
     xs = W.make_inputs("uniform_i32", P * b, P, W.CFG_A2A_32R_INT32, size_bytes=P * b * 4 + 17)
     want = O1.alltoall(xs)
     for xcd_local in (True, False):
-        ys, _ = _run(programs.two_phase_alltoall(G, L), xs, "i32", k=1, xcd_local=xcd_local, repeat=3, nthreads=256)
+        ys, _ = _run(programs.two_phase_alltoall(G, L), xs, "i32", k=1, xcd_local=xcd_local, repeat=3, check=chk_alltoall(),
+                     nthreads=256)
         for r in range(P):
             assert np.array_equal(ys[r], want[r]), r
 
@@ -423,7 +455,8 @@ def test_tree_allreduce(P, c, N, k, dtype, mode):
     kind = "normal_bf16" if dtype == "bf16" else "normal_f32"
     xs = W.make_inputs(kind, N, P, W.CFG_TREE_AR, size_bytes=N * 4 + P)
     knobs = dict(protocol="ll") if mode == "ll" else dict(transport=mode)
-    ys, _ = _run(programs.tree_allreduce(P, c), xs, dtype, k=k, slice_bytes=8192, repeat=2, **knobs)
+    ys, _ = _run(programs.tree_allreduce(P, c), xs, dtype, k=k, slice_bytes=8192, repeat=2,
+                 check=chk_tree(P * c, dtype), **knobs)
     assert_all_equal(ys, O2.tree_allreduce(xs, P * c, dtype)[0])
 
 
@@ -447,7 +480,8 @@ def test_specialized_ring_allreduce(kernel, P, N, k, sl, knobs):
     to dozens of slices per instruction) give the chain-order bits."""
     case(f"{kernel} ring AR P={P} N={N} k={k} slice={sl} {knobs}")
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 37)
-    ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=k, slice_bytes=sl, kernel=kernel, repeat=3, **knobs)
+    ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=k, slice_bytes=sl, kernel=kernel, repeat=3,
+                    check=chk_ring(P), **knobs)
     assert plan.info()["specialized_shapes"] == 1
     assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
 
@@ -507,7 +541,7 @@ def test_generated_loop_form_long_programs(kernel):
         case(f"{kernel} fused hierarchical bf16")
         xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 53)
         ys, plan = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, slice_bytes=4096, kernel=kernel,
-                        repeat=2)
+                        repeat=2, check=chk_hier(G, L))
         assert 0 < plan.info()["specialized_instructions"] <= 12
         assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
     G, L, N = 3, 8, 8 * 777
@@ -530,7 +564,7 @@ def test_generated_loop_form_long_programs(kernel):
     P, N = 8, 8 * 3001
     case(f"{kernel} tree AR")
     xs = W.make_inputs("normal_f32", N, P, W.CFG_TREE_AR, size_bytes=N * 4 + 53)
-    ys, _ = _run(programs.tree_allreduce(P), xs, "f32", k=4, kernel=kernel, repeat=2)
+    ys, _ = _run(programs.tree_allreduce(P), xs, "f32", k=4, kernel=kernel, repeat=2, check=chk_tree(P))
     assert_all_equal(ys, O2.tree_allreduce(xs, P, "f32")[0])
     G, L, b = 4, 8, 257
     P = G * L
@@ -569,14 +603,17 @@ def test_collectives_under_concurrent_gemms():
     torch.cuda.synchronize()
     P, N = 8, 3 * 65536 + 24
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 31)
-    for prog, want, knobs in ((programs.ring_allreduce(P), O2.ring_allreduce(xs, P, "f32")[0], dict(k=32, transport="direct")),
-                              (programs.tree_allreduce(P), O2.tree_allreduce(xs, P, "f32")[0], dict(k=8)),
-                              (programs.ring_allreduce(P), O2.ring_allreduce(xs, P, "f32")[0], dict(k=8, protocol="ll"))):
+    for prog, want, chk, knobs in ((programs.ring_allreduce(P), O2.ring_allreduce(xs, P, "f32")[0], chk_ring(P),
+                                    dict(k=32, transport="direct")),
+                                   (programs.tree_allreduce(P), O2.tree_allreduce(xs, P, "f32")[0], chk_tree(P),
+                                    dict(k=8)),
+                                   (programs.ring_allreduce(P), O2.ring_allreduce(xs, P, "f32")[0], chk_ring(P),
+                                    dict(k=8, protocol="ll"))):
         case(f"{prog.name} {knobs} under GEMMs")
         with torch.cuda.stream(side):
             for _ in range(40):
                 torch.matmul(a, b, out=c)
-        ys, _ = _run(prog, xs, "f32", repeat=4, **knobs)
+        ys, _ = _run(prog, xs, "f32", repeat=4, check=chk, **knobs)
         assert_all_equal(ys, want)
 
 
@@ -590,7 +627,7 @@ def test_direct_ring_allreduce(P, N, k, xcd_local):
     case(f"direct ring AR P={P} N={N} k={k} xcd_local={xcd_local}")
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 19)
     ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=k, transport="direct", xcd_local=xcd_local,
-                    slice_bytes=8192, repeat=3)
+                    slice_bytes=8192, repeat=3, check=chk_ring(P))
     assert any(e.opcode & 0x10 for e in plan.export())
     assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
 
@@ -601,7 +638,8 @@ def test_direct_other_collectives():
     G, L, N = 2, 8, 8 * 4099
     case("direct hierarchical bf16")
     xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 23)
-    ys, _ = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, transport="direct", repeat=2)
+    ys, _ = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, transport="direct", repeat=2,
+                 check=chk_hier(G, L))
     assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
     G, L, b = 4, 8, 257
     P = G * L
@@ -609,7 +647,7 @@ def test_direct_other_collectives():
     want = O1.alltoall(xs)
     for prog in (programs.two_phase_alltoall(G, L), programs.direct_alltoall(P)):
         case(f"direct {prog.name}")
-        ys, _ = _run(prog, xs, "i32", k=1, transport="direct", nthreads=256, repeat=2)
+        ys, _ = _run(prog, xs, "i32", k=1, transport="direct", nthreads=256, repeat=2, check=chk_alltoall())
         for r in range(P):
             assert np.array_equal(ys[r], want[r]), r
     G, L, N = 3, 8, 8 * 777
@@ -641,6 +679,7 @@ def test_streaming_hints_keep_the_bits(transport):
     case(f"streaming ring AR {transport}")
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 31)
     ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=8, transport=transport, streaming=True, repeat=2,
+                 check=chk_ring(P),
                  slice_bytes=16 << 10)
     assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
     G, L, N = 2, 8, 8 * 2051
@@ -654,7 +693,7 @@ def test_streaming_hints_keep_the_bits(transport):
     case(f"streaming ring AR bf16 {transport}")
     xs = W.make_inputs("normal_bf16", N, P, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 7)
     ys, _ = _run(programs.ring_allreduce(P), xs, "bf16", k=4, nthreads=256, transport=transport, streaming=True,
-                 slice_bytes=64 << 10, repeat=2)
+                 slice_bytes=64 << 10, repeat=2, check=chk_ring(P, "bf16"))
     assert_all_equal(ys, O2.ring_allreduce(xs, P, "bf16")[0])
 
 
@@ -667,7 +706,8 @@ def test_streaming_copies_several_passes(transport):
     case(f"streaming ring AllGather {transport}")
     xs = W.make_inputs("prov_i32", n, P, W.CFG_A2NEXT_AGRS_24R, size_bytes=n * 4)
     ys, _ = _run(programs.ring_allgather(P), xs, "i32", k=2, nthreads=256, slice_bytes=64 << 10,
-                 transport=transport, streaming=True, kernel="specialized", repeat=2)
+                 transport=transport, streaming=True, kernel="specialized", repeat=2,
+                 check=chk_allgather())
     want = O1.allgather(xs)
     for r in range(P):
         assert np.array_equal(ys[r], want), r
@@ -732,3 +772,80 @@ def test_execute_refuses_graph_capture():
     torch.cuda.synchronize()
     plan.status()
     plan.destroy()
+
+
+# ------------------------------------------------------------------ debug poison, link utilisation, CU budget
+
+@pytest.mark.parametrize("what", ["ring_staged", "ring_ll", "ring_direct", "tree_scratch", "hier_bf16", "a2a_two_phase"])
+def test_debug_poison_changes_no_bits(what):
+    """CCL_FLAG_DEBUG_POISON fills the staging slots and scratch with 0xFA bytes before
+    every launch: a read of a slot or a scratch partial before its producer wrote it in
+    this launch would carry the sentinel into the outputs. Launch after launch on fresh
+    inputs the bits stay the oracle's."""
+    P, N = 8, 3 * 65536 + 24
+    case(f"debug poison {what}")
+    if what.startswith("ring"):
+        xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 61)
+        knobs = {"ring_staged": dict(), "ring_ll": dict(protocol="ll"), "ring_direct": dict(transport="direct")}[what]
+        ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=8, slice_bytes=16 << 10, debug_poison=True, repeat=3,
+                        check=chk_ring(P), **knobs)
+        assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
+        assert plan.info()["staging_bytes"] > 0 or what == "ring_direct"
+    elif what == "tree_scratch":
+        xs = W.make_inputs("normal_f32", N, P, W.CFG_TREE_AR, size_bytes=N * 4 + 61)
+        ys, plan = _run(programs.tree_allreduce(P), xs, "f32", k=4, slice_bytes=16 << 10, debug_poison=True, repeat=3,
+                        check=chk_tree(P), kernel="specialized")
+        assert plan.info()["scratch_bytes"] > 0
+        assert_all_equal(ys, O2.tree_allreduce(xs, P, "f32")[0])
+    elif what == "hier_bf16":
+        G, L, N = 2, 8, 8 * 4099
+        xs = W.make_inputs("normal_bf16", N, G * L, W.CFG_HIER_AR_16R_BF16, size_bytes=N * 2 + 61)
+        ys, _ = _run(programs.hierarchical_allreduce(G, L), xs, "bf16", k=2, slice_bytes=4096, debug_poison=True,
+                     repeat=2, check=chk_hier(G, L))
+        assert_all_equal(ys, O2.hierarchical_allreduce(xs, G, L, "bf16")[0])
+    else:
+        G, L, b = 4, 8, 517
+        P = G * L
+        xs = W.make_inputs("uniform_i32", P * b, P, W.CFG_A2A_32R_INT32, size_bytes=P * b * 4 + 61)
+        ys, _ = _run(programs.two_phase_alltoall(G, L), xs, "i32", k=1, nthreads=256, debug_poison=True, repeat=2,
+                     check=chk_alltoall())
+        want = O1.alltoall(xs)
+        for r in range(P):
+            assert np.array_equal(ys[r], want[r]), r
+
+
+def test_link_busy_fractions_of_a_traced_ring():
+    """Link utilisation from the device trace: one record per (src, dst, channel,
+    instance) connection of the 8-rank ring (P * k of them), every fraction in (0, 1]."""
+    P, N, k = 8, 8 * 65536, 4
+    case("link busy fractions, ring AR traced")
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 67)
+    ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=k, slice_bytes=32 << 10, trace=True,
+                    kernel="specialized")
+    assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
+    links = plan.link_busy()
+    assert len(links) == P * k
+    assert {(s, d) for s, d, _, _, _ in links} == {(r, (r + 1) % P) for r in range(P)}
+    assert all(0.0 < f <= 1.0 for *_, f in links), links
+    plan.destroy()
+
+
+def test_cu_budget_bounds_the_grid():
+    """A plan created for a budget of 16 compute units is checked against 16 CUs'
+    occupancy: a grid larger than that is refused, one within it runs and keeps the
+    oracle's bits (the budget only shrinks the bound; it reserves nothing)."""
+    from chunk_schedule_execution_amd import Plan, PlanConfig, capi
+    P, N = 8, 8 * 4096
+    case("CU budget 16")
+    full = Plan(programs.ring_allreduce(P), 4, PlanConfig(max_count=N, nthreads=1024))
+    budget = Plan(programs.ring_allreduce(P), 4, PlanConfig(max_count=N, nthreads=1024, num_cus=16))
+    per_cu = full.info()["max_resident_wgs"] // 256
+    assert budget.info()["max_resident_wgs"] == per_cu * 16
+    full.destroy()
+    budget.destroy()
+    with pytest.raises(capi.CCLError) as e:
+        Plan(programs.ring_allreduce(P), 32, PlanConfig(max_count=N, nthreads=1024, num_cus=16))
+    assert e.value.status == capi.CCL_ERR_OUT_OF_RESOURCES
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 71)
+    ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=2, nthreads=256, num_cus=16, kernel="specialized")
+    assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])

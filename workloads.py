@@ -104,6 +104,26 @@ def make_inputs(kind: str, n: int, nranks: int, cfg_id: int, size_bytes: int | N
     return [make_rank_input(kind, n, cfg_id, size_bytes, r) for r in range(nranks)]
 
 
+def device_inputs(kind: str, n: int, nranks: int, seed: int, device="cuda:0"):
+    """Inputs of all ranks drawn on the GPU by torch's seeded generator (large sizes,
+    where drawing on the host would dominate): one generator seeded with ``seed``, ranks
+    drawn in order. ``kind``: normal_f32, normal_bf16 (N(0,1) cast by torch; returned as
+    torch.bfloat16), uniform_i32 (the whole int32 range). Both sides read the same bits:
+    the oracle gets them through a device-to-host copy."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    if kind == "uniform_i32":
+        return [torch.randint(-2**31, 2**31 - 1, (n,), generator=g, device=device, dtype=torch.int32)
+                for _ in range(nranks)]
+    if kind == "normal_f32":
+        return [torch.randn(n, generator=g, device=device) for _ in range(nranks)]
+    if kind == "normal_bf16":
+        return [torch.randn(n, generator=g, device=device).to(torch.bfloat16) for _ in range(nranks)]
+    raise ValueError(f"unknown device input kind {kind!r}")
+
+
 def dtype_of_kind(kind: str) -> str:
     return {"int_f32": "f32", "normal_f32": "f32", "normal_bf16": "bf16", "uniform_i32": "i32",
             "prov_i32": "i32", "prov_f32": "f32", "normal_f32_denorm": "f32"}[kind]
