@@ -90,6 +90,44 @@ const std::vector<char>& compile_cached(const std::string& src) {
 
 }  // namespace
 
+// Under the lazy loop order two instructions of one workgroup are ordered slice by
+// slice only: slice s of the later one may run before slice s + 1 of the earlier one.
+// That keeps their data dependencies only when every local location both touch (one
+// of them writing it) is the same chunk range in both, so that their slices cover the
+// same elements. Plans where a workgroup writes one range and touches an overlapping
+// but different range of the same buffer are refused. (Slots are per transfer and
+// direct landings are checked when direct transport is chosen.)
+static void check_lazy_local_ranges(const HostPlan& hp) {
+  struct Acc {
+    int buf, idx, cnt;
+    bool write;
+  };
+  for (const DevWG& G : hp.dwg) {
+    std::vector<Acc> seen;
+    for (int t = 0; t < G.n; ++t) {
+      const DevInstr& D = hp.dins[G.first + t];
+      Acc mine[3];
+      int n = 0;
+      if (!(D.op & OPB_RECV) || (D.op & OPB_LOCAL_IN)) mine[n++] = {D.a_buf, D.a_idx, D.cnt, false};
+      if (D.op & OPB_SRCB) mine[n++] = {D.b_buf, D.b_idx, D.cnt, false};
+      if (D.op & OPB_DSTA) mine[n++] = {D.d_buf, D.d_idx, D.cnt, true};
+      for (int i = 0; i < n; ++i)
+        for (const Acc& o : seen) {
+          if (o.buf != mine[i].buf || !(o.write || mine[i].write)) continue;
+          const bool overlap = o.idx < mine[i].idx + mine[i].cnt && mine[i].idx < o.idx + o.cnt;
+          if (overlap && (o.idx != mine[i].idx || o.cnt != mine[i].cnt))
+            fail(CCL_ERR_UNSUPPORTED,
+                 "the lazy loop order needs the instructions of a workgroup to touch overlapping local ranges only "
+                 "as identical chunk ranges (rank " + std::to_string(G.rank) + ", buffer " +
+                     std::to_string(o.buf) + ", chunks [" + std::to_string(o.idx) + ", " +
+                     std::to_string(o.idx + o.cnt) + ") and [" + std::to_string(mine[i].idx) + ", " +
+                     std::to_string(mine[i].idx + mine[i].cnt) + "))");
+        }
+      for (int i = 0; i < n; ++i) seen.push_back(mine[i]);
+    }
+  }
+}
+
 std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bool force_loop, int cus,
                                int* num_shapes, int* num_instructions, int* waves_per_simd_out) {
   const bool ll = hp.cfg.flags & CCL_FLAG_LL;
@@ -140,12 +178,14 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bo
     for (uint32_t o : sh)
       if (std::find(ops.begin(), ops.end(), o) == ops.end()) ops.push_back(o);
   const bool loop_form = force_loop || total > size_t(kMaxStraightInstructions);
-  if (lazy)
+  if (lazy) {
     for (const auto& D : hp.dins)
       if (D.nwaits > 0)
         fail(CCL_ERR_UNSUPPORTED,
              "the lazy loop order needs a plan without cross-workgroup completion waits (one would wait for a "
              "whole instruction while its workgroup is still at an earlier slice of others)");
+    if (!(hp.cfg.flags & CCL_FLAG_LL)) check_lazy_local_ranges(hp);
+  }
   if (num_shapes) *num_shapes = int(shapes.size());
   if (num_instructions) *num_instructions = int(loop_form ? ops.size() : total);
 
