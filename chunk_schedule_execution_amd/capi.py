@@ -41,6 +41,7 @@ CCL_FLAG_SPECIALIZE = 0x200
 CCL_FLAG_LAZY = 0x400
 CCL_FLAG_SPECIALIZE_LOOP = 0x800
 CCL_FLAG_DEBUG_DROP_FLAG = 0x1000
+CCL_FLAG_DEBUG_POISON = 0x2000
 CCL_I_RECV, CCL_I_SRCB, CCL_I_DSTA, CCL_I_SEND, CCL_I_LOCAL_IN = 0x1, 0x2, 0x4, 0x8, 0x10
 
 
@@ -76,7 +77,7 @@ class ccl_plan_info_t(C.Structure):
                 ("staging_bytes", C.c_int64), ("scratch_bytes", C.c_int64), ("flag_bytes", C.c_int64),
                 ("table_bytes", C.c_int64), ("compile_ms", C.c_double * 6), ("opcode_hist", C.c_int32 * 16),
                 ("specialized_instructions", C.c_int32), ("specialized_waves_per_simd", C.c_int32),
-                ("specialized_code_bytes", C.c_int64)]
+                ("specialized_code_bytes", C.c_int64), ("dag_width", C.c_int32), ("dag_depth", C.c_int32)]
 
 
 class ccl_instr_info(C.Structure):
@@ -84,6 +85,11 @@ class ccl_instr_info(C.Structure):
         "rank", "wg", "subpipe", "channel", "instance", "opcode", "a_buf", "a_idx", "b_buf", "b_idx",
         "d_buf", "d_idx", "count", "recv_peer", "send_peer", "xin", "xout", "nwaits", "chunk_id",
         "done_flag")]
+
+
+class ccl_link_busy(C.Structure):
+    _fields_ = [("src_rank", C.c_int32), ("dst_rank", C.c_int32), ("channel", C.c_int32), ("instance", C.c_int32),
+                ("busy_fraction", C.c_double)]
 
 
 class ccl_tune_point(C.Structure):
@@ -140,6 +146,7 @@ def _load():
         "ccl_plan_check": (C.c_int, [C.c_void_p, C.c_uint64, C.c_int]),
         "ccl_plan_status": (C.c_int, [C.c_void_p]),
         "ccl_plan_read_trace": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t]),
+        "ccl_plan_link_busy": (C.c_int, [C.c_void_p, P(ccl_link_busy), C.c_size_t, P(C.c_size_t)]),
         "ccl_tune_coordinate_descent": (C.c_int, [P(ccl_tune_space), P(ccl_tune_point), ccl_tune_objective,
                                                   C.c_void_p, P(ccl_tune_point), P(ccl_tune_report)]),
         "ccl_tune": (C.c_int, [P(P(ccl_program_desc)), C.c_int, C.c_int64, P(ccl_plan_config),
@@ -156,7 +163,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("ccl_version", "ccl_error_string", "ccl_last_error_detail", "ccl_plan_create", "ccl_execute",
             "ccl_plan_destroy", "ccl_plan_info", "ccl_plan_bytes", "ccl_plan_export", "ccl_plan_check",
-            "ccl_plan_status", "ccl_plan_read_trace", "ccl_tune_coordinate_descent", "ccl_tune",
+            "ccl_plan_status", "ccl_plan_read_trace", "ccl_plan_link_busy", "ccl_tune_coordinate_descent", "ccl_tune",
             "ccl_copy_probe")
 
 
@@ -239,6 +246,16 @@ def ccl_plan_read_trace(plan: int, nwg: int, ninstr: int = 0):
     _check(_lib.ccl_plan_read_trace(C.c_void_p(plan), buf, C.sizeof(buf)), "ccl_plan_read_trace")
     recs = [tuple(buf[4 * w:4 * w + 4]) for w in range(n)]
     return (recs[:nwg], recs[nwg:]) if ninstr else recs
+
+
+def ccl_plan_link_busy(plan: int):
+    """Per-connection busy fractions of the last traced launch: a list of
+    (src_rank, dst_rank, channel, instance, busy_fraction)."""
+    n = C.c_size_t()
+    _check(_lib.ccl_plan_link_busy(C.c_void_p(plan), None, 0, C.byref(n)), "ccl_plan_link_busy")
+    arr = (ccl_link_busy * max(1, n.value))()
+    _check(_lib.ccl_plan_link_busy(C.c_void_p(plan), arr, n.value, C.byref(n)), "ccl_plan_link_busy")
+    return [(a.src_rank, a.dst_rank, a.channel, a.instance, a.busy_fraction) for a in arr[:n.value]]
 
 
 def ccl_tune_coordinate_descent(space: ccl_tune_space, objective, start: ccl_tune_point | None = None):

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <array>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -101,6 +102,11 @@ struct ccl_plan {
 
 namespace {
 
+// CCL_FLAG_DEBUG_POISON fill: every byte of the staging slots and scratch, so every
+// 4-byte word (and an LL unit's flag) reads kPoisonWord.
+constexpr int kPoisonByte = 0xFA;
+constexpr uint32_t kPoisonWord = 0xFAFAFAFAu;
+
 template <typename T>
 T* upload(ccl_plan* p, const std::vector<T>& v) {
   T* d = static_cast<T*>(p->dev_alloc(std::max<size_t>(1, v.size()) * sizeof(T)));
@@ -114,6 +120,9 @@ void setup_device(ccl_plan* p) {
   int cus = 0, rate_khz = 0;
   HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, p->device_id));
   HIP_TRY(hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, p->device_id));
+  // a CU budget bounds the workgroups that must be resident at once (it never raises
+  // the device's own count)
+  if (hp.cu_budget > 0) cus = std::min(cus, hp.cu_budget);
   int blocks = 0;
   std::string err;
   int rc = executor_max_blocks_per_cu(hp.cfg.dtype, hp.cfg.nthreads, &blocks, &err);
@@ -298,7 +307,9 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
     A.trace = plan->d_trace;
     A.xcd_tags = plan->d_xcd;
     unsigned long long epoch = plan->epoch + 1;
-    if (uint32_t(epoch) == 0) ++epoch;  // LL units use the low 32 bits; zero is the slots' initial value
+    // LL units use the low 32 bits: zero is the slots' initial value, kPoisonWord what
+    // CCL_FLAG_DEBUG_POISON leaves in them; neither may ever be a launch's flag
+    while (uint32_t(epoch) == 0 || uint32_t(epoch) == kPoisonWord) ++epoch;
     A.slice_elems = hp.slice_elems;
     A.epoch = epoch;
     A.timeout_ticks = plan->timeout_ticks;
@@ -314,6 +325,11 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
     if (plan->launched && s != plan->last_stream) {
       HIP_TRY(hipEventRecord(plan->last, plan->last_stream));
       HIP_TRY(hipStreamWaitEvent(s, plan->last, 0));
+    }
+    if (hp.cfg.flags & CCL_FLAG_DEBUG_POISON) {  // stream-ordered: after the previous launch, before this one
+      if (hp.staging_bytes) HIP_TRY(hipMemsetAsync(plan->d_staging, kPoisonByte, size_t(hp.staging_bytes), s));
+      if (plan->d_scratch)
+        HIP_TRY(hipMemsetAsync(plan->d_scratch, kPoisonByte, size_t(plan->scratch_stride) * hp.P, s));
     }
     std::string err;
     int rc = plan->spec_fn ? launch_specialized(plan->spec_fn, A, int(hp.dwg.size()), hp.cfg.nthreads, stream, &err)
@@ -364,6 +380,8 @@ int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info) {
                                 hp.dwaits.size() * 4);
     for (int i = 0; i < 6; ++i) info->compile_ms[i] = hp.ms[i];
     for (const auto& D : hp.dins) info->opcode_hist[D.op & 15]++;
+    info->dag_width = hp.dag_width;
+    info->dag_depth = hp.dag_depth;
     return CCL_OK;
   });
 }
@@ -451,6 +469,69 @@ int ccl_plan_read_trace(ccl_plan* plan, void* host, size_t bytes) {
     if (bytes >= full) need = full;
     if (plan->launched) HIP_TRY(hipStreamSynchronize(plan->last_stream));
     HIP_TRY(hipMemcpy(host, plan->d_trace, need, hipMemcpyDeviceToHost));
+    return CCL_OK;
+  });
+}
+
+int ccl_plan_link_busy(ccl_plan* plan, ccl_link_busy* out, size_t cap, size_t* n) {
+  if (!plan || !n || (cap && !out)) return set_error(CCL_ERR_INVALID_ARGUMENT, "null argument");
+  return guarded([&] {
+    std::lock_guard<std::mutex> lk(plan->mu);
+    const HostPlan& hp = plan->hp;
+    if (!plan->d_trace) fail(CCL_ERR_INVALID_ARGUMENT, "plan was not created with CCL_FLAG_TRACE");
+    if (!plan->launched) fail(CCL_ERR_INVALID_ARGUMENT, "the plan has not been launched");
+    const size_t nwg = hp.dwg.size(), nin = hp.dins.size();
+    std::vector<unsigned long long> t((nwg + nin) * 4);
+    HIP_TRY(hipStreamSynchronize(plan->last_stream));
+    HIP_TRY(hipMemcpy(t.data(), plan->d_trace, t.size() * 8, hipMemcpyDeviceToHost));
+    unsigned long long t0 = ~0ull, t1 = 0;
+    for (size_t w = 0; w < nwg; ++w)
+      if (t[4 * w + 3] > 0) {  // workgroups that ran instructions
+        t0 = std::min(t0, t[4 * w]);
+        t1 = std::max(t1, t[4 * w + 1]);
+      }
+    // per connection: the intervals of the instructions that send on it
+    std::map<std::array<int, 4>, std::vector<std::pair<unsigned long long, unsigned long long>>> busy;
+    for (size_t w = 0; w < nwg; ++w) {
+      const DevWG& G = hp.dwg[w];
+      for (int j = 0; j < G.n; ++j) {
+        const size_t gi = size_t(G.first + j);
+        const DevInstr& D = hp.dins[gi];
+        if (D.xout < 0) continue;
+        const Instr& I = hp.ins[hp.dins_base[gi]];
+        const Xfer& X = hp.xf[I.xout];
+        const unsigned long long* r = &t[4 * (nwg + gi)];
+        auto& v = busy[{X.src_rank, X.dst_rank, X.channel, D.instance}];
+        if (r[0] > 0 && r[2] >= r[0]) v.emplace_back(r[0], r[2]);
+      }
+    }
+    *n = busy.size();
+    size_t j = 0;
+    const double span = t1 > t0 ? double(t1 - t0) : 0.0;
+    for (auto& kv : busy) {
+      if (j >= cap) break;
+      auto& v = kv.second;
+      std::sort(v.begin(), v.end());
+      unsigned long long covered = 0, lo = 0, hi = 0;
+      bool open = false;
+      for (const auto& iv : v) {
+        if (!open || iv.first > hi) {
+          if (open) covered += hi - lo;
+          lo = iv.first;
+          hi = iv.second;
+          open = true;
+        } else {
+          hi = std::max(hi, iv.second);
+        }
+      }
+      if (open) covered += hi - lo;
+      out[j].src_rank = kv.first[0];
+      out[j].dst_rank = kv.first[1];
+      out[j].channel = kv.first[2];
+      out[j].instance = kv.first[3];
+      out[j].busy_fraction = span > 0 ? double(covered) / span : 0.0;
+      ++j;
+    }
     return CCL_OK;
   });
 }

@@ -4,6 +4,7 @@
 #include <cstdint>
 #include <stdexcept>
 #include <string>
+#include <set>
 #include <vector>
 
 #include "../../include/ccl.h"
@@ -104,6 +105,8 @@ struct HostPlan {
   int max_wg_per_rank = 0;
   int max_resident_wgs = 0;
   int wg_stride = 1;  // lowered ids per base workgroup (>= k; extra ids are empty)
+  int dag_width = 0, dag_depth = 0;  // base instruction DAG: maximum antichain, longest chain
+  int cu_budget = 0;  // compute units the plan may occupy (0: the whole device)
   double ms[6] = {0, 0, 0, 0, 0, 0};
 };
 
@@ -113,6 +116,7 @@ void compile_plan(HostPlan& hp, const ccl_program_desc* prog, int nranks, int nc
 int64_t output_chunks(const ccl_program_desc& d);
 int64_t plan_bytes(const HostPlan& hp, int64_t count);
 int64_t output_elems(const HostPlan& hp, int64_t count);
+void dag_parallelism(const std::vector<std::set<int>>& succ, int* width, int* depth);
 void group_members(const ccl_program_desc& d, int r, std::vector<int>& members, int& pos);
 int group_count(const ccl_program_desc& d);
 

@@ -11,6 +11,7 @@
 #include <algorithm>
 #include <chrono>
 #include <cstring>
+#include <functional>
 #include <map>
 #include <numeric>
 #include <queue>
@@ -180,6 +181,7 @@ void validate(HostPlan& hp, const ccl_program_desc* prog, int nranks, int nchunk
   hp.cfg = *cfg;
   hp.cfg.nthreads = nt;
   if (hp.cfg.slice_bytes == 0) hp.cfg.slice_bytes = 256 * 1024;
+  hp.cu_budget = cfg->num_cus > 0 ? cfg->num_cus : 0;
   if (hp.cfg.num_cus <= 0) hp.cfg.num_cus = 256;
   if (hp.cfg.timeout_us <= 0) hp.cfg.timeout_us = 2000000;
   hp.esz = cfg->dtype == CCL_BF16 ? 2 : 4;
@@ -1104,6 +1106,91 @@ void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec
   }
 }
 
+// ---------------------------------------------------------------- DAG parallelism
+
+// Parallelism of the instruction DAG (MSCCLang report, section 3.3, which analyses the
+// instruction DAG's parallelism): its depth (instructions on the longest dependency
+// chain) and width, the largest set of instructions no two of which are ordered (a
+// maximum antichain). By Dilworth's theorem the width equals the instruction count
+// minus a maximum matching of the bipartite graph that joins u to every v reachable
+// from u; the matching is found by Hopcroft-Karp over the transitive closure.
+void dag_parallelism(const std::vector<std::set<int>>& succ, int* width, int* depth) {
+  const int n = int(succ.size());
+  *width = 0;
+  *depth = 0;
+  if (n == 0) return;
+  std::vector<int> key(n);
+  std::iota(key.begin(), key.end(), 0);
+  const std::vector<int> order = topo_order(succ, key);
+  std::vector<int> lvl(n, 1);
+  for (int u : order)
+    for (int v : succ[u]) lvl[v] = std::max(lvl[v], lvl[u] + 1);
+  *depth = *std::max_element(lvl.begin(), lvl.end());
+  if (n > 8192) {  // closure would need n^2 bits; report the width as unknown
+    *width = -1;
+    return;
+  }
+  const int words = (n + 63) / 64;
+  std::vector<uint64_t> reach(size_t(n) * words, 0);
+  for (int i = n - 1; i >= 0; --i) {
+    const int u = order[i];
+    uint64_t* ru = &reach[size_t(u) * words];
+    for (int v : succ[u]) {
+      ru[v / 64] |= 1ull << (v % 64);
+      const uint64_t* rv = &reach[size_t(v) * words];
+      for (int w = 0; w < words; ++w) ru[w] |= rv[w];
+    }
+  }
+  std::vector<std::vector<int>> adj(n);
+  for (int u = 0; u < n; ++u)
+    for (int w = 0; w < words; ++w)
+      for (uint64_t b = reach[size_t(u) * words + w]; b; b &= b - 1) adj[u].push_back(w * 64 + __builtin_ctzll(b));
+  // Hopcroft-Karp: left copy u -> right copy v for every v reachable from u
+  std::vector<int> match_l(n, -1), match_r(n, -1), dist(n);
+  auto bfs = [&]() {
+    std::queue<int> q;
+    bool found = false;
+    for (int u = 0; u < n; ++u) {
+      dist[u] = match_l[u] < 0 ? 0 : -1;
+      if (match_l[u] < 0) q.push(u);
+    }
+    while (!q.empty()) {
+      const int u = q.front();
+      q.pop();
+      for (int v : adj[u]) {
+        const int w = match_r[v];
+        if (w < 0) {
+          found = true;
+        } else if (dist[w] < 0) {
+          dist[w] = dist[u] + 1;
+          q.push(w);
+        }
+      }
+    }
+    return found;
+  };
+  std::vector<size_t> it(n);
+  std::function<bool(int)> dfs = [&](int u) -> bool {
+    for (; it[u] < adj[u].size(); ++it[u]) {
+      const int v = adj[u][it[u]], w = match_r[v];
+      if (w < 0 || (dist[w] == dist[u] + 1 && dfs(w))) {
+        match_l[u] = v;
+        match_r[v] = u;
+        return true;
+      }
+    }
+    dist[u] = -1;
+    return false;
+  };
+  int matching = 0;
+  while (bfs()) {
+    std::fill(it.begin(), it.end(), 0);
+    for (int u = 0; u < n; ++u)
+      if (match_l[u] < 0 && dfs(u)) ++matching;
+  }
+  *width = n - matching;
+}
+
 void compile_plan(HostPlan& hp, const ccl_program_desc* prog, int nranks, int nchunks, int k,
                   const ccl_plan_config* cfg) {
   auto t0 = Clock::now();
@@ -1118,6 +1205,7 @@ void compile_plan(HostPlan& hp, const ccl_program_desc* prog, int nranks, int nc
   hp.ms[2] = ms_since(t0);
   t0 = Clock::now();
   schedule(hp, dag);
+  dag_parallelism(dag, &hp.dag_width, &hp.dag_depth);
   hp.ms[3] = ms_since(t0);
   t0 = Clock::now();
   allocate_workgroups(hp);

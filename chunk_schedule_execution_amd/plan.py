@@ -37,6 +37,8 @@ class PlanConfig:
     timeout_us: int = 0
     # failure injection for watchdog tests: transfer 0's flag is never set
     debug_drop_flag: bool = False
+    # debug mode: staging slots and scratch filled with a sentinel before every launch
+    debug_poison: bool = False
     # "interpreter" (one kernel for every plan), "specialized" (a kernel generated for
     # this plan: straight-line code for short plans, the loop form for long ones),
     # "specialized_loop" (the loop form always) or "lazy" (a generated kernel in the
@@ -71,6 +73,8 @@ class PlanConfig:
             raise ValueError(f"unknown kernel {self.kernel!r}")
         if self.debug_drop_flag:
             flags |= capi.CCL_FLAG_DEBUG_DROP_FLAG
+        if self.debug_poison:
+            flags |= capi.CCL_FLAG_DEBUG_POISON
         if self.protocol == "ll":
             flags |= capi.CCL_FLAG_LL
         elif self.protocol != "simple":
@@ -118,6 +122,11 @@ class Plan:
         if instructions:
             return capi.ccl_plan_read_trace(self.handle, i["grid_workgroups"], i["num_instructions"])
         return capi.ccl_plan_read_trace(self.handle, i["grid_workgroups"])
+
+    def link_busy(self):
+        """Per-connection busy fractions of the last launch (plans built with trace=True):
+        (src_rank, dst_rank, channel, instance, busy_fraction) per connection."""
+        return capi.ccl_plan_link_busy(self.handle)
 
     def output_len(self, count: int) -> int:
         return (self.program.out_chunks * count) // self.program.in_chunks

@@ -166,6 +166,12 @@ typedef struct {
                                     Refused (CCL_ERR_UNSUPPORTED) with CCL_FLAG_LL, whose flags travel inside
                                     the data, and with CCL_FLAG_DIRECT, where a receive that ends its
                                     workgroup is not waited for */
+#define CCL_FLAG_DEBUG_POISON 0x2000u /* debug mode: before every launch, on the launch's stream, fill the plan's
+                                    staging slots and scratch with the byte 0xFA (fp32 -6.5e35, bf16 -6.5e35,
+                                    int32 -84215046; as a low-latency unit its flag word is never a launch's),
+                                    so that a read of a slot or scratch location before its producer wrote
+                                    it in this launch shows up in the outputs. Results are unchanged
+                                    otherwise; costs one fill per launch */
 #define CCL_FLAG_COHERENT_ONLY 0x20u /* write transfers and their flags with agent-coherent stores. By default a
                                     plan whose lowered layout keeps every transfer on one XCD (workgroup ids
                                     congruent mod 8, which the round-robin dispatch places together) writes
@@ -183,7 +189,12 @@ typedef struct {
   int32_t scheduler;   /* CCL_SCHED_* */
   int32_t wg_alloc;    /* CCL_WG_* */
   uint32_t flags;      /* CCL_FLAG_* */
-  int32_t num_cus;     /* CUs assumed by the co-residency check for HOST_ONLY plans (0 = 256) */
+  int32_t num_cus;     /* compute-unit budget (0 = the whole device). The co-residency check bounds the
+                          grid by occupancy x min(num_cus, the device's CUs), so a plan sized for a budget
+                          leaves the other CUs to concurrent work (AutoCCL report, method 3: tuning while
+                          computation holds part of the GPU; ReSCCL report, section 1: thread blocks taken
+                          from computation). HOST_ONLY plans assume num_cus CUs (0 = 256). The layout keeps
+                          every instance on one XCD only when the padded grid fits num_cus (0 = 256) */
   int64_t timeout_us;  /* watchdog budget of one device spin-wait, microseconds (0 = 2,000,000) */
 } ccl_plan_config;
 
@@ -249,6 +260,13 @@ typedef struct {
   int32_t specialized_waves_per_simd; /* generated kernel: minimum waves per SIMD it was compiled for
                                          (what its grid needs to be co-resident; 1 = no request) */
   int64_t specialized_code_bytes;   /* generated kernel: size of its code object */
+  /* Parallelism of the fused instruction DAG of the base program (instance 0, all ranks;
+     MSCCLang report, section 3.3: the analysis reports the instruction DAG's parallelism):
+     dag_width = the most instructions no two of which are ordered by a dependency (a
+     maximum antichain; -1 if the DAG is too large to compute it), dag_depth = the
+     instructions on its longest dependency chain. */
+  int32_t dag_width;
+  int32_t dag_depth;
 } ccl_plan_info_t;
 
 int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info);
@@ -310,8 +328,34 @@ int ccl_plan_status(ccl_plan* plan);
  * end, 0}. */
 int ccl_plan_read_trace(ccl_plan* plan, void* host, size_t bytes);
 
+/*
+ * Communication-link utilisation of the last launch of a CCL_FLAG_TRACE plan (MSCCLang
+ * report, section 3.3: the analysis reports how busy the communication links are). A
+ * connection is one (sending rank, receiving rank, channel, instance); it is busy while
+ * an instruction that sends on it runs (from its start to its end in the device trace).
+ * busy_fraction = length of the union of those intervals / the launch's span (first
+ * workgroup start to last workgroup end). Fills up to `cap` records, ordered by
+ * (src_rank, dst_rank, channel, instance); *n receives the number of connections.
+ * Synchronizes with the plan's last launch. Errors: INVALID_ARGUMENT (no trace, null
+ * pointers, no launch yet), HIP.
+ */
+typedef struct {
+  int32_t src_rank, dst_rank, channel, instance;
+  double busy_fraction;
+} ccl_link_busy;
+
+int ccl_plan_link_busy(ccl_plan* plan, ccl_link_busy* out, size_t cap, size_t* n);
+
 /* ---- tuner (AutoCCL report, "Methods" 1-2: resource parameters tuned by
- * coordinate descent inside each implementation subspace) ---------------- */
+ * coordinate descent inside each implementation subspace) ----------------
+ *
+ * Two entry points instead of one: ccl_tune_coordinate_descent is the search alone
+ * over any objective (pure host logic, testable without a GPU), ccl_tune plugs in the
+ * device objective. ccl_tune takes a list of programs, one per algorithm subspace (the
+ * pages' implementation dimension: e.g. ring and tree AllReduce), instead of one
+ * program, so the parallel factor is a coordinate of the returned point rather than a
+ * separate output, and it takes a base configuration whose dtype, max_count, scheduler,
+ * allocation and kernel flags every candidate plan inherits. */
 typedef struct {
   int32_t variant;         /* algorithm subspace (index into the program list) */
   int32_t parallel_factor; /* channels / instances (nc) */

@@ -166,3 +166,23 @@ def test_flag_dropping_needs_the_staged_slice_flag_protocol():
         with pytest.raises(capi.CCLError) as e:
             host_plan(prog, debug_drop_flag=True, **knobs)
         assert e.value.status == capi.CCL_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("P,c", [(4, 1), (8, 1), (8, 2), (3, 2)])
+def test_dag_parallelism_of_the_ring(P, c):
+    """The fused ring is c*P independent chains of 2P-1 instructions (send, P-2 reducing
+    forwards, the final reduce, P-2 forwards, the last receive): depth 2P-1, and the
+    largest set of mutually unordered instructions takes one from each chain."""
+    info = host_plan(programs.ring_allreduce(P, c) if c > 1 else programs.ring_allreduce(P), 2).info()
+    assert info["dag_depth"] == 2 * P - 1
+    assert info["dag_width"] == c * P
+
+
+def test_dag_parallelism_of_the_tree_and_two_phase_alltoall():
+    """The tree's chains are shorter than the ring's (depth below 2P-1), and the two-phase
+    AllToAll's phase-1 copies into distinct gather slots are all unordered, so its width
+    is at least the number of ranks."""
+    tree = host_plan(programs.tree_allreduce(8), 1).info()
+    assert 0 < tree["dag_depth"] < 15 and tree["dag_width"] >= 8
+    a2a = host_plan(programs.two_phase_alltoall(4, 8), 1).info()
+    assert a2a["dag_width"] >= 32 and a2a["dag_depth"] >= 3
