@@ -152,6 +152,7 @@ def _load():
         "ccl_tune": (C.c_int, [P(P(ccl_program_desc)), C.c_int, C.c_int64, P(ccl_plan_config),
                                P(ccl_tune_space), C.c_void_p, P(ccl_tune_point), P(ccl_tune_report)]),
         "ccl_copy_probe": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_int, C.c_void_p]),
+        "ccl_litmus_message_passing": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, P(C.c_int64), C.c_void_p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -164,7 +165,7 @@ _lib = _load()
 EXPORTED = ("ccl_version", "ccl_error_string", "ccl_last_error_detail", "ccl_plan_create", "ccl_execute",
             "ccl_plan_destroy", "ccl_plan_info", "ccl_plan_bytes", "ccl_plan_export", "ccl_plan_check",
             "ccl_plan_status", "ccl_plan_read_trace", "ccl_plan_link_busy", "ccl_tune_coordinate_descent", "ccl_tune",
-            "ccl_copy_probe")
+            "ccl_copy_probe", "ccl_litmus_message_passing")
 
 
 def lib():
@@ -280,3 +281,12 @@ def ccl_tune(descs, count: int, base: ccl_plan_config, space: ccl_tune_space, st
 def ccl_copy_probe(dst: int, src: int, nbytes: int, nblocks: int, nthreads: int, stream: int = 0) -> None:
     _check(_lib.ccl_copy_probe(C.c_void_p(dst), C.c_void_p(src), C.c_size_t(nbytes), nblocks, nthreads,
                                C.c_void_p(stream)), "ccl_copy_probe")
+
+
+def ccl_litmus_message_passing(cross_xcd: bool, rounds: int, words: int, timeout_us: int = 200000, stream: int = 0):
+    """Per pair: (producer XCD, consumer XCD, rounds completed, mismatching words, first bad
+    round, its first word index, plain flag stores, expired waits)."""
+    res = (C.c_int64 * 64)()
+    _check(_lib.ccl_litmus_message_passing(int(bool(cross_xcd)), rounds, words, C.c_int64(timeout_us), res,
+                                           C.c_void_p(stream)), "ccl_litmus_message_passing")
+    return [tuple(res[8 * p:8 * p + 8]) for p in range(8)]

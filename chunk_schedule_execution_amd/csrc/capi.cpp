@@ -536,6 +536,45 @@ int ccl_plan_link_busy(ccl_plan* plan, ccl_link_busy* out, size_t cap, size_t* n
   });
 }
 
+int ccl_litmus_message_passing(int cross_xcd, int rounds, int words, int64_t timeout_us, int64_t* results,
+                               void* stream) {
+  if (!results || rounds < 1 || rounds > 1000000 || words < 4 || words > (1 << 20) || words % 4 || timeout_us < 1)
+    return set_error(CCL_ERR_INVALID_ARGUMENT, "litmus: bad arguments");
+  return guarded([&] {
+    constexpr int npairs = 8;  // producers 0..7; consumers 8..15 (ids congruent mod 8 share an XCD)
+    const size_t region = (size_t(words) * 4 + 255) / 256 * 256;
+    const size_t flag_bytes = size_t(npairs) * kFlagStride * 8;
+    const size_t sizes[6] = {region * npairs, flag_bytes, flag_bytes, 2 * npairs * 8, npairs * 8 * 8, 8};
+    void* bufs[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    struct Free {
+      void** b;
+      ~Free() {
+        for (int i = 0; i < 6; ++i)
+          if (b[i]) (void)hipFree(b[i]);
+      }
+    } guard{bufs};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (int i = 0; i < 6; ++i) {
+      HIP_TRY(hipMalloc(&bufs[i], sizes[i]));
+      HIP_TRY(hipMemsetAsync(bufs[i], 0, sizes[i], s));
+    }
+    int dev = 0, rate_khz = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev));
+    if (rate_khz <= 0) rate_khz = 100000;
+    std::string err;
+    int rc = launch_litmus_mp(static_cast<unsigned char*>(bufs[0]), static_cast<unsigned long long*>(bufs[1]),
+                              static_cast<unsigned long long*>(bufs[2]), static_cast<unsigned long long*>(bufs[3]),
+                              static_cast<long long*>(bufs[4]), static_cast<unsigned long long*>(bufs[5]), npairs,
+                              rounds, words, cross_xcd ? 1 : 0, (long long)(timeout_us * (rate_khz / 1000.0)), stream,
+                              &err);
+    if (rc) fail(rc, err);
+    HIP_TRY(hipStreamSynchronize(s));
+    HIP_TRY(hipMemcpy(results, bufs[4], npairs * 8 * 8, hipMemcpyDeviceToHost));
+    return CCL_OK;
+  });
+}
+
 int ccl_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int nthreads, void* stream) {
   if (!dst || !src || bytes % 16 || nblocks < 1 || nthreads < 64 || nthreads > 1024 || nthreads % 64)
     return set_error(CCL_ERR_INVALID_ARGUMENT, "copy probe: bad arguments");

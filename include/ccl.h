@@ -418,6 +418,25 @@ int ccl_tune(const ccl_program_desc* const* variants, int nvariants, int64_t cou
  * nominal 8 TB/s, and the reference kernel for calibrating traffic counters. */
 int ccl_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int nthreads, void* stream);
 
+/*
+ * Message-passing litmus test of the transfer-store policy across workgroups (a
+ * diagnostic beside the executor, like the copy probe). Eight producer workgroups
+ * (ids 0-7) each hand `rounds` rounds of `words` fresh 32-bit words (a multiple of 4,
+ * at most 2^20) to a consumer workgroup: id p + 8 (ids congruent mod 8: the same XCD
+ * under the round-robin dispatch) or, with cross_xcd, id 8 + (p + 1) mod 8 (another
+ * XCD). Each round uses the executor's own operations: plain data stores, the flag set
+ * with a plain store when the consumer published the producer's XCD and with an
+ * agent-scope release otherwise, agent-scope flag polls and agent-coherent data loads;
+ * the consumer checks every word and acknowledges the round. Every wait is bounded by
+ * timeout_us; a mismatch or an expiry stops every pair. The call allocates its own
+ * device buffers, runs on `stream` and synchronizes with it. results (host, 64 values)
+ * holds per pair p at [8p ...]: producer XCD, consumer XCD, rounds the consumer
+ * completed, mismatching words, first mismatching round (0: none), its first word
+ * index, flags set with a plain store, waits that expired.
+ */
+int ccl_litmus_message_passing(int cross_xcd, int rounds, int words, int64_t timeout_us, int64_t* results,
+                               void* stream);
+
 /* ---- errors --------------------------------------------------------------- */
 const char* ccl_error_string(int status);
 const char* ccl_last_error_detail(void);

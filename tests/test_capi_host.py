@@ -186,3 +186,11 @@ def test_dag_parallelism_of_the_tree_and_two_phase_alltoall():
     assert 0 < tree["dag_depth"] < 15 and tree["dag_width"] >= 8
     a2a = host_plan(programs.two_phase_alltoall(4, 8), 1).info()
     assert a2a["dag_width"] >= 32 and a2a["dag_depth"] >= 3
+
+
+def test_litmus_rejects_bad_arguments_before_touching_the_gpu():
+    """Zero rounds, a word count that is not a multiple of 4, more than 2^20 words."""
+    for args in ((False, 0, 64), (False, 10, 6), (False, 10, 1 << 21)):
+        with pytest.raises(capi.CCLError) as e:
+            capi.ccl_litmus_message_passing(*args)
+        assert e.value.status == capi.CCL_ERR_INVALID_ARGUMENT

@@ -1,0 +1,36 @@
+"""Message-passing litmus test of the executor's transfer-store policy (release /
+acquire across workgroups on the same and on different XCDs), through the C ABI.
+
+Each round a producer workgroup writes fresh words with plain stores and sets a flag
+(plain store when the consumer runs on its XCD, agent-scope release otherwise); the
+consumer polls the flag and reads the words with agent-coherent loads, exactly as the
+executor's receives do. Any stale word would be counted; every wait is bounded."""
+
+import pytest
+
+from chunk_schedule_execution_amd import capi
+
+pytestmark = pytest.mark.gpu
+
+
+def case(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+@pytest.mark.parametrize("cross", [False, True])
+@pytest.mark.parametrize("words", [3072, 65536])
+def test_message_passing_sees_every_round(cross, words):
+    import torch
+    rounds = 2000 if words <= 4096 else 200
+    case(f"litmus message passing cross_xcd={cross} words={words} rounds={rounds}")
+    res = capi.ccl_litmus_message_passing(cross, rounds, words, 200000, torch.cuda.current_stream().cuda_stream)
+    for p, (pxcd, cxcd, done, bad, first_round, first_word, plain_flags, expired) in enumerate(res):
+        assert expired == 0, (p, res[p])
+        assert bad == 0 and first_round == 0, (p, res[p])
+        assert done == rounds, (p, res[p])
+        if cross:
+            assert pxcd != cxcd and plain_flags == 0, (p, res[p])  # every flag is a full release
+        elif pxcd == cxcd:
+            assert plain_flags == rounds, (p, res[p])  # the plain-store path was the one tested
+    if not cross:  # workgroup ids congruent mod 8 land on one XCD under the round-robin dispatch
+        assert sum(1 for r in res if r[0] == r[1]) >= 6, res

@@ -395,11 +395,11 @@ def test_ll_repeated_launches():
 # ------------------------------------------------------------------ slot store policy
 
 @pytest.mark.parametrize("protocol", ["simple", "ll"])
-@pytest.mark.parametrize("k,nt,num_cus", [(8, 256, 0), (3, 512, 0), (32, 1024, 0), (5, 256, 8)])
+@pytest.mark.parametrize("k,nt,num_cus", [(8, 256, 0), (3, 512, 0), (32, 1024, 0), (5, 256, 10)])
 def test_xcd_local_and_coherent_stores_agree(protocol, k, nt, num_cus):
     """An XCD-aligned layout writes transfers with plain stores and sets each flag with a
     plain store when the receiving workgroup published the sender's own XCD, else with a
-    release. With num_cus=8 the layout estimate rejects the aligned grid: the plan keeps
+    release. With a budget of 10 CUs the layout estimate rejects the aligned grid: the plan keeps
     coherent stores, or (forced) runs the XCD-local variant with most receivers on other
     XCDs, so both flag kinds occur. Every way the bits are the chain order, launch after
     launch."""
@@ -408,15 +408,15 @@ def test_xcd_local_and_coherent_stores_agree(protocol, k, nt, num_cus):
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 13)
     want = O2.ring_allreduce(xs, P, "f32")[0]
     modes = [dict(xcd_local=True), dict(xcd_local=False)]
-    if num_cus == 8:
+    if num_cus == 10:
         modes.append(dict(xcd_local=True, force_xcd_local=True))
     for mode in modes:
         ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=k, protocol=protocol, nthreads=nt,
                         slice_bytes=16 << 10, repeat=4, check=chk_ring(P), num_cus=num_cus, **mode)
         info = plan.info()
-        aligned = num_cus != 8
+        aligned = num_cus != 10
         assert info["xcd_local"] == (1 if mode["xcd_local"] and (aligned or mode.get("force_xcd_local")) else 0)
-        if num_cus == 8:
+        if num_cus == 10:
             assert info["grid_workgroups"] == P * k  # no XCD padding
         assert_all_equal(ys, want)
 
@@ -838,7 +838,7 @@ def test_cu_budget_bounds_the_grid():
     P, N = 8, 8 * 4096
     case("CU budget 16")
     full = Plan(programs.ring_allreduce(P), 4, PlanConfig(max_count=N, nthreads=1024))
-    budget = Plan(programs.ring_allreduce(P), 4, PlanConfig(max_count=N, nthreads=1024, num_cus=16))
+    budget = Plan(programs.ring_allreduce(P), 2, PlanConfig(max_count=N, nthreads=1024, num_cus=16))
     per_cu = full.info()["max_resident_wgs"] // 256
     assert budget.info()["max_resident_wgs"] == per_cu * 16
     full.destroy()
