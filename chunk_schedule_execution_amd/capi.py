@@ -139,6 +139,7 @@ def _load():
         "ccl_plan_create": (C.c_int, [P(ccl_program_desc), C.c_int, C.c_int, C.c_int, P(ccl_plan_config),
                                       P(C.c_void_p)]),
         "ccl_execute": (C.c_int, [C.c_void_p, P(C.c_void_p), P(C.c_void_p), C.c_int64, C.c_void_p]),
+        "ccl_execute_static": (C.c_int, [C.c_void_p, P(C.c_void_p), P(C.c_void_p), C.c_int64, C.c_void_p]),
         "ccl_plan_destroy": (C.c_int, [C.c_void_p]),
         "ccl_plan_info": (C.c_int, [C.c_void_p, P(ccl_plan_info_t)]),
         "ccl_plan_bytes": (C.c_int64, [C.c_void_p, C.c_int64]),
@@ -163,6 +164,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("ccl_version", "ccl_error_string", "ccl_last_error_detail", "ccl_plan_create", "ccl_execute",
+            "ccl_execute_static",
             "ccl_plan_destroy", "ccl_plan_info", "ccl_plan_bytes", "ccl_plan_export", "ccl_plan_check",
             "ccl_plan_status", "ccl_plan_read_trace", "ccl_plan_link_busy", "ccl_tune_coordinate_descent", "ccl_tune",
             "ccl_copy_probe", "ccl_litmus_message_passing")
@@ -205,6 +207,15 @@ def ccl_execute(plan: int, sendbufs, recvbufs, count: int, stream: int = 0) -> N
     sb = (C.c_void_p * n)(*sendbufs)
     rb = (C.c_void_p * n)(*recvbufs)
     _check(_lib.ccl_execute(C.c_void_p(plan), sb, rb, C.c_int64(count), C.c_void_p(stream)), "ccl_execute")
+
+
+def ccl_execute_static(plan: int, sendbufs, recvbufs, count: int, stream: int = 0) -> None:
+    """ccl_execute without any device allocation (the library's static device scratch)."""
+    n = len(sendbufs)
+    sb = (C.c_void_p * n)(*sendbufs)
+    rb = (C.c_void_p * n)(*recvbufs)
+    _check(_lib.ccl_execute_static(C.c_void_p(plan), sb, rb, C.c_int64(count), C.c_void_p(stream)),
+           "ccl_execute_static")
 
 
 def ccl_plan_destroy(plan: int) -> None:

@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <array>
+#include <atomic>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -78,6 +79,11 @@ struct ccl_plan {
   unsigned long long epoch = 0;
   long long timeout_ticks = 0;
   int64_t scratch_stride = 0;  // bytes between ranks' scratch
+  uint64_t id = 0;             // unique per plan created in this process
+  // the last ccl_execute_static launch of this plan (its state lives in the static scratch)
+  bool static_launched = false;
+  int static_device = -1;
+  hipStream_t static_stream = nullptr;
   std::mutex mu;
 
   void* dev_alloc(size_t bytes) {
@@ -106,6 +112,66 @@ namespace {
 // 4-byte word (and an LL unit's flag) reads kPoisonWord.
 constexpr int kPoisonByte = 0xFA;
 constexpr uint32_t kPoisonWord = 0xFAFAFAFAu;
+
+// XCD-local layout: every transfer between workgroups whose launch ids are congruent
+// mod 8, which the round-robin dispatch over the eight XCDs places on one XCD (the
+// kernel checks each launch's actual placement through the published tags).
+bool xcd_local_layout(const HostPlan& hp) {
+  bool local = !(hp.cfg.flags & CCL_FLAG_COHERENT_ONLY);
+  for (size_t w = 0; w < hp.dwg.size() && local && !(hp.cfg.flags & CCL_FLAG_FORCE_XCD_LOCAL); ++w)
+    for (int t = 0; t < hp.dwg[w].n && local; ++t) {
+      const DevInstr& D = hp.dins[hp.dwg[w].first + t];
+      if (D.peer_wg >= 0 && int(w) % 8 != D.peer_wg % 8) local = false;
+    }
+  return local;
+}
+
+// Argument checks shared by ccl_execute and ccl_execute_static.
+void check_exec_args(const HostPlan& hp, const void* const* sendbufs, void* const* recvbufs, int64_t count) {
+  if (!sendbufs || !recvbufs) fail(CCL_ERR_INVALID_ARGUMENT, "null buffer table");
+  if (count < 0 || count > hp.cfg.max_count) fail(CCL_ERR_INVALID_ARGUMENT, "count out of range [0, max_count]");
+  if (count % hp.granule)
+    fail(CCL_ERR_INVALID_ARGUMENT, "count must be a multiple of " + std::to_string(hp.granule) + " for this program");
+  for (int r = 0; r < hp.P; ++r) {
+    if (!sendbufs[r] || !recvbufs[r]) fail(CCL_ERR_INVALID_ARGUMENT, "null buffer for rank " + std::to_string(r));
+    if (sendbufs[r] == recvbufs[r]) fail(CCL_ERR_INVALID_ARGUMENT, "in-place execution is not supported");
+  }
+}
+
+// The launch epoch is a kernel argument: a captured launch replayed from a graph would
+// reuse it and find its flags already set by the previous replay. Checked before any
+// other HIP call, so a capture in progress is left untouched.
+void refuse_capture(void* stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  HIP_TRY(hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap));
+  if (cap != hipStreamCaptureStatusNone)
+    fail(CCL_ERR_UNSUPPORTED, "a collective launch cannot be captured into a graph (each launch needs a fresh epoch)");
+}
+
+// Next launch epoch after `e`: its low 32 bits are an LL unit's flag, so never 0 (the
+// slots' initial value) nor what CCL_FLAG_DEBUG_POISON leaves in them.
+unsigned long long next_epoch(unsigned long long e) {
+  ++e;
+  while (uint32_t(e) == 0 || uint32_t(e) == kPoisonWord) ++e;
+  return e;
+}
+
+std::atomic<uint64_t> g_plan_ids{0};
+
+// Host-side state of the static scratch on one device: the launch epoch (shared by every
+// static launch there, so flags a previous launch left are always older), which plan's
+// tables the array holds and for which count, and device facts looked up once.
+struct StaticDevice {
+  std::mutex mu;
+  unsigned long long epoch = 0;
+  uint64_t plan_id = 0;
+  int64_t count = -1;
+  int cus = 0, rate_khz = 0;
+  std::vector<unsigned char> image;  // tables and records as uploaded
+};
+StaticDevice g_static[kMaxDevices];
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
 template <typename T>
 T* upload(ccl_plan* p, const std::vector<T>& v) {
@@ -157,15 +223,7 @@ void setup_device(ccl_plan* p) {
   HIP_TRY(hipMemset(p->d_err, 0, 16));
   p->d_abort = static_cast<unsigned long long*>(p->dev_alloc(8));
   HIP_TRY(hipMemset(p->d_abort, 0, 8));
-  // XCD-local layout: every transfer between workgroups whose launch ids are congruent
-  // mod 8, which the round-robin dispatch over the eight XCDs places on one XCD (the
-  // kernel checks each launch's actual placement through the published tags).
-  bool local = !(hp.cfg.flags & CCL_FLAG_COHERENT_ONLY);
-  for (size_t w = 0; w < hp.dwg.size() && local && !(hp.cfg.flags & CCL_FLAG_FORCE_XCD_LOCAL); ++w)
-    for (int t = 0; t < hp.dwg[w].n && local; ++t) {
-      const DevInstr& D = hp.dins[hp.dwg[w].first + t];
-      if (D.peer_wg >= 0 && int(w) % 8 != D.peer_wg % 8) local = false;
-    }
+  const bool local = xcd_local_layout(hp);
   if (local) {
     p->d_xcd = static_cast<unsigned long long*>(p->dev_alloc(std::max<size_t>(1, hp.dwg.size()) * 8));
     HIP_TRY(hipMemset(p->d_xcd, 0, std::max<size_t>(1, hp.dwg.size()) * 8));  // no tag matches an epoch >= 1
@@ -220,6 +278,7 @@ int ccl_plan_create(const ccl_program_desc* prog, int nranks, int nchunks, int p
   *out = nullptr;
   return guarded([&] {
     ccl_plan* p = new ccl_plan();
+    p->id = ++g_plan_ids;
     try {
       compile_plan(p->hp, prog, nranks, nchunks, parallel_factor, cfg);
       if (!(p->hp.cfg.flags & CCL_FLAG_HOST_ONLY)) {
@@ -260,22 +319,9 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
     std::lock_guard<std::mutex> lk(plan->mu);
     HostPlan& hp = plan->hp;
     if (!plan->device) fail(CCL_ERR_INVALID_ARGUMENT, "plan was created host-only");
-    if (!sendbufs || !recvbufs) fail(CCL_ERR_INVALID_ARGUMENT, "null buffer table");
-    if (count < 0 || count > hp.cfg.max_count) fail(CCL_ERR_INVALID_ARGUMENT, "count out of range [0, max_count]");
-    if (count % hp.granule)
-      fail(CCL_ERR_INVALID_ARGUMENT, "count must be a multiple of " + std::to_string(hp.granule) + " for this program");
-    for (int r = 0; r < hp.P; ++r) {
-      if (!sendbufs[r] || !recvbufs[r]) fail(CCL_ERR_INVALID_ARGUMENT, "null buffer for rank " + std::to_string(r));
-      if (sendbufs[r] == recvbufs[r]) fail(CCL_ERR_INVALID_ARGUMENT, "in-place execution is not supported");
-    }
+    check_exec_args(hp, sendbufs, recvbufs, count);
     if (count == 0) return CCL_OK;
-    // The launch epoch is a kernel argument: a captured launch replayed from a graph
-    // would reuse it and find its flags already set by the previous replay. Checked
-    // before any other HIP call, so a capture in progress is left untouched.
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    HIP_TRY(hipStreamIsCapturing(reinterpret_cast<hipStream_t>(stream), &cap));
-    if (cap != hipStreamCaptureStatusNone)
-      fail(CCL_ERR_UNSUPPORTED, "ccl_execute cannot be captured into a graph (each launch needs a fresh epoch)");
+    refuse_capture(stream);
     int dev = -1;
     HIP_TRY(hipGetDevice(&dev));
     if (dev != plan->device_id) fail(CCL_ERR_INVALID_ARGUMENT, "plan belongs to another device");
@@ -306,10 +352,7 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
     A.abort_word = plan->d_abort;
     A.trace = plan->d_trace;
     A.xcd_tags = plan->d_xcd;
-    unsigned long long epoch = plan->epoch + 1;
-    // LL units use the low 32 bits: zero is the slots' initial value, kPoisonWord what
-    // CCL_FLAG_DEBUG_POISON leaves in them; neither may ever be a launch's flag
-    while (uint32_t(epoch) == 0 || uint32_t(epoch) == kPoisonWord) ++epoch;
+    const unsigned long long epoch = next_epoch(plan->epoch);
     A.slice_elems = hp.slice_elems;
     A.epoch = epoch;
     A.timeout_ticks = plan->timeout_ticks;
@@ -340,6 +383,119 @@ int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbu
     plan->epoch = epoch;
     plan->last_stream = s;
     plan->launched = true;
+    return CCL_OK;
+  });
+}
+
+int ccl_execute_static(ccl_plan* plan, const void* const* sendbufs, void* const* recvbufs, int64_t count,
+                       void* stream) {
+  if (!plan) return set_error(CCL_ERR_INVALID_ARGUMENT, "null plan");
+  return guarded([&] {
+    std::lock_guard<std::mutex> lk(plan->mu);
+    const HostPlan& hp = plan->hp;
+    check_exec_args(hp, sendbufs, recvbufs, count);
+    if (count == 0) return CCL_OK;
+    refuse_capture(stream);
+    int dev = -1;
+    HIP_TRY(hipGetDevice(&dev));
+    if (plan->device && dev != plan->device_id) fail(CCL_ERR_INVALID_ARGUMENT, "plan belongs to another device");
+    if (dev < 0 || dev >= kMaxDevices) fail(CCL_ERR_INVALID_ARGUMENT, "device id out of range");
+    unsigned char* base = nullptr;
+    std::string err;
+    int rc = static_scratch_base(dev, &base, &err);
+    if (rc) fail(rc, err);
+    StaticDevice& st = g_static[dev];
+    std::lock_guard<std::mutex> lk2(st.mu);
+    if (!st.cus) {
+      HIP_TRY(hipDeviceGetAttribute(&st.cus, hipDeviceAttributeMultiprocessorCount, dev));
+      HIP_TRY(hipDeviceGetAttribute(&st.rate_khz, hipDeviceAttributeWallClockRate, dev));
+      if (st.rate_khz <= 0) st.rate_khz = 100000;
+    }
+    // every workgroup of the interpreting kernel must be resident at once (within the
+    // plan's CU budget)
+    int blocks = 0;
+    rc = executor_max_blocks_per_cu(hp.cfg.dtype, hp.cfg.nthreads, &blocks, &err);
+    if (rc) fail(rc, err);
+    const int cus = hp.cu_budget > 0 ? std::min(st.cus, hp.cu_budget) : st.cus;
+    const size_t grid = hp.dwg.size();
+    if (int64_t(grid) > int64_t(blocks) * cus)
+      fail(CCL_ERR_OUT_OF_RESOURCES, "plan needs " + std::to_string(grid) + " co-resident workgroups, the device holds " +
+                                         std::to_string(blocks * cus) + " of the interpreting kernel");
+    // sizes against the fixed regions and the variable one
+    int nd = 0;
+    for (const auto& D : hp.dins) nd = std::max(nd, D.done_flag + 1);
+    const size_t nx = hp.dxf.size() + 1;  // + the spare flag of CCL_FLAG_DEBUG_DROP_FLAG
+    const size_t scr_stride = size_t(align256(size_t(hp.scratch_elems_per_rank * hp.esz)));
+    const size_t off_wgs = kStaticVarOff;
+    const size_t off_waits = align256(off_wgs + grid * sizeof(DevWG));
+    const size_t off_recs = align256(off_waits + hp.dwaits.size() * 4);
+    const size_t off_stage = align256(off_recs + hp.dins.size() * sizeof(DevExec));
+    const size_t off_scr = align256(off_stage + size_t(hp.staging_bytes));
+    const size_t end = off_scr + scr_stride * hp.P;
+    if (nx * 8 * kFlagStride > kStaticXflagBytes || size_t(nd) * 8 * kFlagStride > kStaticDflagBytes ||
+        grid * 8 > kStaticTagBytes || end > kStaticScratchBytes)
+      fail(CCL_ERR_OUT_OF_RESOURCES,
+           "plan needs " + std::to_string(end) + " bytes of the static scratch (at most " +
+               std::to_string(kStaticScratchBytes) + "), " + std::to_string(nx) + " transfer flags (at most " +
+               std::to_string(kStaticXflagBytes / (8 * kFlagStride)) + "), " + std::to_string(nd) +
+               " completion flags (at most " + std::to_string(kStaticDflagBytes / (8 * kFlagStride)) + ") and " +
+               std::to_string(grid) + " workgroups (at most " + std::to_string(kStaticTagBytes / 8) + ")");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // tables and records for this plan and count, unless the array holds them already
+    // (stream-ordered after every earlier launch on this stream; the host image stays
+    // valid until the copy has completed)
+    if (st.plan_id != plan->id || st.count != count) {
+      std::vector<DevExec> recs;
+      compute_exec_records(hp, count, recs);
+      st.image.assign(off_stage - off_wgs, 0);
+      std::memcpy(st.image.data(), hp.dwg.data(), grid * sizeof(DevWG));
+      if (!hp.dwaits.empty()) std::memcpy(st.image.data() + (off_waits - off_wgs), hp.dwaits.data(), hp.dwaits.size() * 4);
+      if (!recs.empty()) std::memcpy(st.image.data() + (off_recs - off_wgs), recs.data(), recs.size() * sizeof(DevExec));
+      HIP_TRY(hipMemcpyAsync(base + off_wgs, st.image.data(), st.image.size(), hipMemcpyHostToDevice, s));
+      HIP_TRY(hipStreamSynchronize(s));
+      st.plan_id = plan->id;
+      st.count = count;
+    }
+    // clear what must start at zero: the error word, and low-latency slots (their flag
+    // words must never hold this launch's flag); poison mode fills slots and scratch
+    HIP_TRY(hipMemsetAsync(base + kStaticErrOff, 0, 16, s));
+    const bool ll = (hp.cfg.flags & CCL_FLAG_LL) != 0;
+    if (hp.cfg.flags & CCL_FLAG_DEBUG_POISON) {
+      if (hp.staging_bytes) HIP_TRY(hipMemsetAsync(base + off_stage, kPoisonByte, size_t(hp.staging_bytes), s));
+      if (scr_stride) HIP_TRY(hipMemsetAsync(base + off_scr, kPoisonByte, scr_stride * hp.P, s));
+    } else if (ll && hp.staging_bytes) {
+      HIP_TRY(hipMemsetAsync(base + off_stage, 0, size_t(hp.staging_bytes), s));
+    }
+    const bool local = xcd_local_layout(hp);
+    const unsigned long long epoch = next_epoch(st.epoch);
+    ExecArgs A{};
+    A.wgs = reinterpret_cast<const DevWG*>(base + off_wgs);
+    A.recs = reinterpret_cast<const DevExec*>(base + off_recs);
+    A.waits = reinterpret_cast<const int32_t*>(base + off_waits);
+    A.xflags = reinterpret_cast<unsigned long long*>(base + kStaticXflagOff);
+    A.dflags = reinterpret_cast<unsigned long long*>(base + kStaticDflagOff);
+    A.staging = base + off_stage;
+    A.err = reinterpret_cast<unsigned int*>(base + kStaticErrOff);
+    A.abort_word = reinterpret_cast<unsigned long long*>(base + kStaticErrOff + 16);
+    A.trace = nullptr;
+    A.xcd_tags = local ? reinterpret_cast<unsigned long long*>(base + kStaticTagOff) : nullptr;
+    A.slice_elems = hp.slice_elems;
+    A.epoch = epoch;
+    A.timeout_ticks = (long long)(hp.cfg.timeout_us * (st.rate_khz / 1000.0));
+    A.ll = ll ? 1 : 0;
+    A.ll_flag = uint32_t(epoch);
+    for (int r = 0; r < hp.P; ++r) {
+      A.base[CCL_BUF_INPUT][r] = const_cast<unsigned char*>(static_cast<const unsigned char*>(sendbufs[r]));
+      A.base[CCL_BUF_OUTPUT][r] = static_cast<unsigned char*>(recvbufs[r]);
+      A.base[CCL_BUF_SCRATCH][r] = scr_stride ? base + off_scr + scr_stride * r : nullptr;
+    }
+    rc = launch_executor(A, hp.cfg.dtype, local, (hp.cfg.flags & CCL_FLAG_STREAMING) != 0, int(grid),
+                         hp.cfg.nthreads, stream, &err);
+    if (rc) fail(rc, err);
+    st.epoch = epoch;
+    plan->static_launched = true;
+    plan->static_device = dev;
+    plan->static_stream = s;
     return CCL_OK;
   });
 }
@@ -447,6 +603,21 @@ int ccl_plan_status(ccl_plan* plan) {
   if (!plan) return set_error(CCL_ERR_INVALID_ARGUMENT, "null plan");
   return guarded([&] {
     std::lock_guard<std::mutex> lk(plan->mu);
+    if (plan->static_launched) {  // the last static launch on its device reported through the static error word
+      plan->static_launched = false;
+      HIP_TRY(hipStreamSynchronize(plan->static_stream));
+      unsigned char* base = nullptr;
+      std::string err;
+      int rc = static_scratch_base(plan->static_device, &base, &err);
+      if (rc) fail(rc, err);
+      unsigned int e[4] = {0, 0, 0, 0};
+      HIP_TRY(hipMemcpy(e, base + kStaticErrOff, sizeof e, hipMemcpyDeviceToHost));
+      if (e[0] != 0) {
+        HIP_TRY(hipMemset(base + kStaticErrOff, 0, sizeof e));
+        fail(-int(e[0]), "static launch " + std::to_string(e[3]) + ": workgroup " + std::to_string(e[1]) +
+                             " timed out at instruction " + std::to_string(e[2]));
+      }
+    }
     if (!plan->device) return CCL_OK;
     if (plan->launched) HIP_TRY(hipStreamSynchronize(plan->last_stream));
     unsigned int e[4] = {0, 0, 0, 0};

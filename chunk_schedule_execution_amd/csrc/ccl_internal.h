@@ -137,6 +137,21 @@ int launch_litmus_mp(unsigned char* data, unsigned long long* flags, unsigned lo
                      unsigned long long* tags, long long* results, unsigned long long* stop, int npairs, int rounds,
                      int words, int cross, long long timeout_ticks, void* stream, std::string* err);
 
+// static_scratch.hip: the device array behind ccl_execute_static (the entry point that
+// allocates nothing). Fixed regions, so that a location only ever holds one kind of
+// epoch-valued word whatever plan last used it:
+constexpr size_t kStaticScratchBytes = size_t(64) << 20;
+constexpr size_t kStaticXflagOff = 0, kStaticXflagBytes = size_t(4) << 20;   // 32768 transfer flags
+constexpr size_t kStaticDflagOff = kStaticXflagOff + kStaticXflagBytes;
+constexpr size_t kStaticDflagBytes = size_t(2) << 20;                        // 16384 completion flags
+constexpr size_t kStaticTagOff = kStaticDflagOff + kStaticDflagBytes;
+constexpr size_t kStaticTagBytes = size_t(64) << 10;                         // 8192 workgroup XCD tags
+constexpr size_t kStaticErrOff = kStaticTagOff + kStaticTagBytes;            // error word (16 B), abort word (8 B)
+constexpr size_t kStaticVarOff = kStaticErrOff + 256;                        // tables, records, slots, scratch
+constexpr int kMaxDevices = 64;
+// Device address of the array on `device` (which must be current on the first call).
+int static_scratch_base(int device, unsigned char** base, std::string* err);
+
 // specialize.cpp: plan-specialized kernels (CCL_FLAG_SPECIALIZE / CCL_FLAG_LAZY).
 // cus: compute units of the target device; the kernel is compiled for the waves per
 // SIMD that the plan's grid needs to be co-resident on them.

@@ -144,6 +144,19 @@ class Plan:
             s = torch.cuda.current_stream().cuda_stream
         capi.ccl_execute(self.handle, [t.data_ptr() for t in inputs], [t.data_ptr() for t in outputs], count, s)
 
+    def execute_static(self, inputs, outputs, count: int | None = None, stream=None) -> None:
+        """Like execute, allocating nothing: the plan (host-only plans included) runs on the
+        library's static device scratch."""
+        if count is None:
+            count = inputs[0].numel()
+        if stream is not None:
+            s = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        else:
+            import torch
+            s = torch.cuda.current_stream().cuda_stream
+        capi.ccl_execute_static(self.handle, [t.data_ptr() for t in inputs], [t.data_ptr() for t in outputs], count,
+                                s)
+
     def destroy(self) -> None:
         if self.handle:
             capi.ccl_plan_destroy(self.handle)

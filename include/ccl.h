@@ -232,6 +232,33 @@ int ccl_plan_create(const ccl_program_desc* prog, int nranks, int nchunks, int p
 int ccl_execute(ccl_plan* plan, const void* const* sendbufs, void* const* recvbufs, int64_t count,
                 void* stream);
 
+/*
+ * For callers that cannot allocate device memory: code under HIP graph capture set-up,
+ * tight serving loops, harnesses that forbid hipMalloc. Runs the collective of `plan`
+ * like ccl_execute (same arguments, same results bit for bit) but allocates nothing:
+ * no hipMalloc, hipFree or allocating library call. `plan` may be a CCL_FLAG_HOST_ONLY
+ * plan, which owns no device memory at all; a device plan's own memory is not used.
+ * Every device-side word of the launch -- transfer and completion flags, workgroup XCD
+ * tags, the error word, the workgroup table, the instruction records, staging slots
+ * and scratch -- lives in the library's static device scratch, one 64 MiB array per GPU,
+ * held from the first such call on that GPU until the process ends. The interpreting
+ * kernel runs (a plan's generated kernel is not loaded; trace recording is off).
+ * Per GPU the array keeps the last call's contents: tables are uploaded only when the
+ * plan or count differs from that call (a synchronous copy on `stream`), launch epochs
+ * rise across all calls on the GPU so flags left by earlier calls never satisfy a wait,
+ * and the error word (plus, for CCL_FLAG_LL, the slots) is cleared on `stream` before
+ * the launch. Calls on one GPU share the array: calls that overlap in time (on
+ * different streams, or from several threads) race and give undefined results; keep
+ * them on one stream. ccl_plan_status(plan) reports a watchdog expiry of the plan's
+ * last call here (the error word is shared, so only until the next call on that GPU).
+ * Errors: as ccl_execute, and OUT_OF_RESOURCES when the plan needs more than the array
+ * holds (64 MiB in all, of which 57.7 MiB for tables, records, slots and scratch;
+ * 32,768 transfer flags, 16,384 completion flags, 8,192 workgroups) or more co-resident
+ * workgroups of the interpreting kernel than the device (or the plan's CU budget) holds.
+ */
+int ccl_execute_static(ccl_plan* plan, const void* const* sendbufs, void* const* recvbufs, int64_t count,
+                       void* stream);
+
 /* Wait for the plan's last launch and free everything it owns. NULL is a no-op. */
 int ccl_plan_destroy(ccl_plan* plan);
 
