@@ -189,18 +189,20 @@ def main():
         xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=S)
         return N, [torch.from_numpy(x).to(dev) for x in xs], outs
 
-    def tune(prog, N, dtype="f32", protocols=15, variants=None, kernel=KERNEL, factors=TUNE_FACTORS):
+    def tune(prog, N, dtype="f32", protocols=15, variants=None, kernel=KERNEL, factors=TUNE_FACTORS, num_cus=0,
+             on=None):
         """Tuned (k, nthreads, slice_bytes, protocol, kernel) of prog with the given
         executor kernel, or, given a list of programs as `variants`, the best over those
-        algorithm subspaces with (..., variant index) appended."""
+        algorithm subspaces with (..., variant index) appended. num_cus: a CU budget every
+        candidate plan is sized to; on: the stream the candidates are timed on."""
         progs = variants if variants is not None else [prog]
-        base = PlanConfig(dtype=dtype, max_count=N, kernel=KERNELS[kernel]).to_c()
+        base = PlanConfig(dtype=dtype, max_count=N, kernel=KERNELS[kernel], num_cus=num_cus).to_c()
         arrs = [(capi.C.c_int32 * len(v))(*v) for v in (factors, TUNE_THREADS, TUNE_SLICES)]
         space = capi.ccl_tune_space(capi.C.cast(arrs[0], capi.C.POINTER(capi.C.c_int32)), len(factors),
                                     capi.C.cast(arrs[1], capi.C.POINTER(capi.C.c_int32)), len(TUNE_THREADS),
                                     capi.C.cast(arrs[2], capi.C.POINTER(capi.C.c_int32)), len(TUNE_SLICES),
                                     len(progs), 3, 10, protocols)
-        best, rep = capi.ccl_tune([p.to_desc() for p in progs], N, base, space, stream.cuda_stream)
+        best, rep = capi.ccl_tune([p.to_desc() for p in progs], N, base, space, (on or stream).cuda_stream)
         c = (best.parallel_factor, best.nthreads, best.slice_bytes, best.protocol, kernel)
         return (c + (best.variant,) if variants is not None else c), rep.evaluations
 
@@ -758,88 +760,155 @@ def rank_counts(np, torch, programs, dev, stream, device_inputs, tune, make_plan
     return ranks
 
 
+class GemmLoad:
+    """Keeps `stream` busy with 8192^3 bf16 GEMMs while the `with` block runs: a thread
+    enqueues batches of GEMMs, keeping two batches in flight, and stops when the block
+    ends; the GEMM rate over the block is measured with events on that stream."""
+
+    def __init__(self, torch, stream, a, b, c, batch=4):
+        import threading
+        self.torch, self.stream, self.a, self.b, self.c, self.batch = torch, stream, a, b, c, batch
+        self.stop = threading.Event()
+        self.thread = threading.Thread(target=self._run, daemon=True)
+        self.count = 0
+
+    def _run(self):
+        torch = self.torch
+        pending = []
+        with torch.cuda.stream(self.stream):
+            while not self.stop.is_set():
+                for _ in range(self.batch):
+                    torch.matmul(self.a, self.b, out=self.c)
+                self.count += self.batch
+                e = torch.cuda.Event()
+                e.record(self.stream)
+                pending.append(e)
+                if len(pending) > 2:
+                    pending.pop(0).synchronize()
+
+    def __enter__(self):
+        torch = self.torch
+        self.e0, self.e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(self.stream):
+            for _ in range(2):  # running before the measured work starts
+                torch.matmul(self.a, self.b, out=self.c)
+        self.e0.record(self.stream)
+        self.thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop.set()
+        self.thread.join()
+        self.e1.record(self.stream)
+        self.torch.cuda.synchronize()
+        n = self.a.shape[0]
+        t = self.e0.elapsed_time(self.e1) * 1e-3
+        self.tflops = 2 * n ** 3 * self.count / t / 1e12 if self.count and t > 0 else 0.0
+        return False
+
+
 def interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release):
-    """AutoCCL tunes inside the running job, where computation competes for the GPU.
-    Here a loop of 8192^3 bf16 GEMMs (hipBLASLt through torch) runs on a second stream
-    (default priority) while the ring AllReduce is tuned and timed; the config tuned in
-    isolation and the one tuned under the GEMMs are both timed under the GEMMs."""
-    side = torch.cuda.Stream(device=dev)
+    """AutoCCL tunes inside the running job, where computation competes for the GPU;
+    ReSCCL frees compute for it by taking fewer thread blocks. Here 8192^3 bf16 GEMMs
+    (hipBLASLt through torch) run beside the 8-rank ring AllReduce:
+
+    * shared: GEMMs on a second stream over the whole GPU; the collective tuned alone
+      and tuned while the GEMMs run, both timed under the GEMMs;
+    * reserved: for budgets of B = 32 / 64 / 128 compute units, the collective runs on a
+      stream masked to B CUs (mask bits 0..B-1: B/8 CUs on each XCD) with plans sized
+      to B CUs, the GEMMs on a stream masked to the other 256 - B; the tuner runs there
+      while the GEMMs run, and its pick is compared with the one it makes within the
+      same budget alone.
+    Candidates are timed on the interpreting kernel (no kernel generation inside the
+    tuning); the chosen points are timed on their generated kernels. Reported: chosen
+    points, workgroups, collective time alone and under the GEMMs, and the GEMM rate
+    (alone on its CUs, and meanwhile). Masked streams each hold a hardware queue of their
+    own, so one pair per budget is created and kept for both sizes."""
+    from chunk_schedule_execution_amd import capi
+
     n = 8192
     a = torch.randn(n, n, device=dev).to(torch.bfloat16)
     b = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
     c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    side = torch.cuda.Stream(device=dev)
 
-    def gemms(count):
-        with torch.cuda.stream(side):
+    def gemm_tflops(on, count=20):
+        with torch.cuda.stream(on):
+            for _ in range(3):
+                torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(on)
+        with torch.cuda.stream(on):
             for _ in range(count):
                 torch.matmul(a, b, out=c)
+        e1.record(on)
+        torch.cuda.synchronize()
+        return round(2 * n ** 3 / (e0.elapsed_time(e1) * 1e-3 / count) / 1e12, 1)
 
-    def on_side(count):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(side)
-        gemms(count)
-        e1.record(side)
-        return e0, e1
-
-    gemms(3)
-    torch.cuda.synchronize()
-    g0, g1 = on_side(20)
-    torch.cuda.synchronize()
-    t_gemm = g0.elapsed_time(g1) * 1e-3 / 20
-    out = {"gemm": "bf16 8192x8192x8192, torch.matmul on a second stream",
-           "gemm_alone_tflops": round(2 * n ** 3 / t_gemm / 1e12, 1), "sizes": []}
-
-    def timed_under_gemms(fn, iters):
-        """Mean seconds per fn() on `stream` while GEMMs keep the second stream busy;
-        also the GEMM rate over the same span."""
+    def launches(fn, iters, comm):
         for _ in range(3):
             fn()
-        stream.synchronize()
-        # enough GEMMs to outlast the timed launches (estimated from an isolated run)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        e0.record(comm)
         for _ in range(iters):
             fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        alone = e0.elapsed_time(e1) * 1e-3 / iters
-        cover = int(3 * alone * iters / t_gemm) + 8
-        gemms(2)  # the GEMMs are running when the timed launches start
-        g0, g1 = on_side(cover)
-        e0.record(stream)
-        for _ in range(iters):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        t = e0.elapsed_time(e1) * 1e-3 / iters
-        tg = g0.elapsed_time(g1) * 1e-3 / cover
-        return alone, t, 2 * n ** 3 / tg / 1e12
+        e1.record(comm)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / iters
 
-    for S in (3 << 20, 32 << 20):
-        N, ii, oo = ring_inputs(S)
-        t0 = time.perf_counter()
-        c_pure, _ = tune(prog, N, kernel=KERNEL)
+    def measure(cfg, N, ii, oo, comm, gstream, iters, **kw):
+        p = make_plan(prog, N, *cfg, **kw)
+        alone = launches(lambda: p.execute(ii, oo, N, comm), iters, comm)
+        with GemmLoad(torch, gstream, a, b, c) as g:
+            t = launches(lambda: p.execute(ii, oo, N, comm), iters, comm)
+        r = {"k": cfg[0], "nthreads": cfg[1], "slice_bytes": cfg[2], "protocol": cfg[3],
+             "workgroups": p.info()["num_workgroups"], "us_alone": round(alone * 1e6, 2),
+             "us_under_gemms": round(t * 1e6, 2), "gemm_tflops_meanwhile": round(g.tflops, 1)}
+        release(p)
+        return r
+
+    out = {"gemm": "bf16 8192x8192x8192, torch.matmul", "gemm_alone_tflops": gemm_tflops(side), "sizes": []}
+    budgets = (32, 64, 128)
+    masked = {B: (capi.ccl_stream_create_cu_masked(capi.cu_mask_words(range(B))),
+                  capi.ccl_stream_create_cu_masked(capi.cu_mask_words(range(B, 256)))) for B in budgets}
+    try:
+        out["gemm_tflops_on_the_other_cus"] = {B: gemm_tflops(torch.cuda.ExternalStream(masked[B][1]))
+                                               for B in budgets}
+        progress(f"interference: GEMM alone {out['gemm_alone_tflops']} TFLOP/s, on 256-B CUs "
+                 f"{out['gemm_tflops_on_the_other_cus']}")
+        for S in (3 << 20, 32 << 20):
+            N, ii, oo = ring_inputs(S)
+            iters = 50 if S < (32 << 20) else 20
+            row = {"bytes_per_rank": S}
+            c_pure, _ = tune(prog, N, kernel=0)
+            with GemmLoad(torch, side, a, b, c):
+                c_int, ev = tune(prog, N, kernel=0)
+            row["shared_tuned_alone"] = measure(c_pure[:4] + (KERNEL,), N, ii, oo, stream, side, iters)
+            row["shared_tuned_under_gemms"] = measure(c_int[:4] + (KERNEL,), N, ii, oo, stream, side, iters)
+            row["shared_tuner_evaluations_under_gemms"] = ev
+            progress(f"interference {S >> 20} MiB shared: tuned alone {row['shared_tuned_alone']['us_under_gemms']} "
+                     f"us under GEMMs, tuned under GEMMs {row['shared_tuned_under_gemms']['us_under_gemms']} us")
+            for B in budgets:
+                comm = torch.cuda.ExternalStream(masked[B][0])
+                gst = torch.cuda.ExternalStream(masked[B][1])
+                c_alone_b, _ = tune(prog, N, kernel=0, num_cus=B, on=comm)
+                with GemmLoad(torch, gst, a, b, c):
+                    c_b, ev_b = tune(prog, N, kernel=0, num_cus=B, on=comm)
+                entry = {"tuner_evaluations_under_gemms": ev_b,
+                         "tuned_alone": measure(c_alone_b[:4] + (KERNEL,), N, ii, oo, comm, gst, iters, num_cus=B),
+                         "tuned_under_gemms": measure(c_b[:4] + (KERNEL,), N, ii, oo, comm, gst, iters, num_cus=B)}
+                row[f"reserved_{B}_cus"] = entry
+                progress(f"interference {S >> 20} MiB, {B} CUs: alone {entry['tuned_under_gemms']['us_alone']} us, "
+                         f"under GEMMs {entry['tuned_under_gemms']['us_under_gemms']} us, GEMMs meanwhile "
+                         f"{entry['tuned_under_gemms']['gemm_tflops_meanwhile']} TFLOP/s")
+            out["sizes"].append(row)
+            del ii, oo
+    finally:
         torch.cuda.synchronize()
-        tune_s = time.perf_counter() - t0
-        # a GEMM backlog that outlasts the tuning under interference (slower than alone)
-        gemms(int(6 * tune_s / t_gemm) + 16)
-        t0 = time.perf_counter()
-        c_int, ev = tune(prog, N, kernel=KERNEL)
-        tune_int_s = time.perf_counter() - t0
-        torch.cuda.synchronize()
-        row = {"bytes_per_rank": S, "tuner_evaluations_under_gemms": ev, "tune_seconds_alone": round(tune_s, 2),
-               "tune_seconds_under_gemms": round(tune_int_s, 2)}
-        for name, cfg in (("tuned_alone", c_pure), ("tuned_under_gemms", c_int)):
-            p = make_plan(prog, N, *cfg)
-            alone, t, tf = timed_under_gemms(lambda: p.execute(ii, oo, N, stream), 50 if S < (32 << 20) else 20)
-            row[name] = {"k": cfg[0], "nthreads": cfg[1], "slice_bytes": cfg[2], "protocol": cfg[3],
-                         "kernel": KERNELS[cfg[4]],
-                         "workgroups": p.info()["num_workgroups"],
-                         "us_alone": round(alone * 1e6, 2), "us_under_gemms": round(t * 1e6, 2),
-                         "busbw_under_gemms": round(busbw_ar(S, t), 2), "gemm_tflops_meanwhile": round(tf, 1)}
-            release(p)
-        out["sizes"].append(row)
-        del ii, oo
+        for pair in masked.values():
+            for s_ in pair:
+                capi.ccl_stream_destroy(s_)
     del a, b, c
     release()
     return out

@@ -154,6 +154,9 @@ def _load():
                                P(ccl_tune_space), C.c_void_p, P(ccl_tune_point), P(ccl_tune_report)]),
         "ccl_copy_probe": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_int, C.c_void_p]),
         "ccl_litmus_message_passing": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, P(C.c_int64), C.c_void_p]),
+        "ccl_stream_create_cu_masked": (C.c_int, [P(C.c_uint32), C.c_int, P(C.c_void_p)]),
+        "ccl_stream_destroy": (C.c_int, [C.c_void_p]),
+        "ccl_cu_probe": (C.c_int, [C.c_void_p, C.c_int, C.c_int, P(C.c_uint32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -167,7 +170,8 @@ EXPORTED = ("ccl_version", "ccl_error_string", "ccl_last_error_detail", "ccl_pla
             "ccl_execute_static",
             "ccl_plan_destroy", "ccl_plan_info", "ccl_plan_bytes", "ccl_plan_export", "ccl_plan_check",
             "ccl_plan_status", "ccl_plan_read_trace", "ccl_plan_link_busy", "ccl_tune_coordinate_descent", "ccl_tune",
-            "ccl_copy_probe", "ccl_litmus_message_passing")
+            "ccl_copy_probe", "ccl_litmus_message_passing", "ccl_stream_create_cu_masked", "ccl_stream_destroy",
+            "ccl_cu_probe")
 
 
 def lib():
@@ -301,3 +305,35 @@ def ccl_litmus_message_passing(cross_xcd: bool, rounds: int, words: int, timeout
     _check(_lib.ccl_litmus_message_passing(int(bool(cross_xcd)), rounds, words, C.c_int64(timeout_us), res,
                                            C.c_void_p(stream)), "ccl_litmus_message_passing")
     return [tuple(res[8 * p:8 * p + 8]) for p in range(8)]
+
+
+def cu_mask_words(cus, nwords: int = 8):
+    """32-bit mask words enabling the given compute-unit indices."""
+    m = [0] * nwords
+    for c in cus:
+        m[c // 32] |= 1 << (c % 32)
+    return m
+
+
+def ccl_stream_create_cu_masked(mask_words) -> int:
+    """A stream restricted to the CUs whose bits are set; returns its handle (hipStream_t)."""
+    n = len(mask_words)
+    arr = (C.c_uint32 * n)(*[int(w) & 0xFFFFFFFF for w in mask_words])
+    s = C.c_void_p()
+    _check(_lib.ccl_stream_create_cu_masked(arr, n, C.byref(s)), "ccl_stream_create_cu_masked")
+    return s.value
+
+
+def ccl_stream_destroy(stream: int) -> None:
+    _check(_lib.ccl_stream_destroy(C.c_void_p(stream)), "ccl_stream_destroy")
+
+
+def ccl_cu_probe(stream: int, nblocks: int, hold_us: int = 50):
+    """Per block (XCD, shader engine, shader array, CU id) where it ran."""
+    out = (C.c_uint32 * (2 * nblocks))()
+    _check(_lib.ccl_cu_probe(C.c_void_p(stream), nblocks, hold_us, out), "ccl_cu_probe")
+    res = []
+    for b in range(nblocks):
+        x, hw = out[2 * b], out[2 * b + 1]
+        res.append((x, (hw >> 13) & 7, (hw >> 12) & 1, (hw >> 8) & 15))
+    return res

@@ -1,5 +1,6 @@
 // C ABI entry points and the device runtime of a plan: upload of the lowered
 // tables, plan-owned staging / scratch / flag memory, epochs, launch, status, trace.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -742,6 +743,61 @@ int ccl_litmus_message_passing(int cross_xcd, int rounds, int words, int64_t tim
     if (rc) fail(rc, err);
     HIP_TRY(hipStreamSynchronize(s));
     HIP_TRY(hipMemcpy(results, bufs[4], npairs * 8 * 8, hipMemcpyDeviceToHost));
+    return CCL_OK;
+  });
+}
+
+int ccl_stream_create_cu_masked(const uint32_t* mask, int nwords, void** stream) {
+  if (!stream) return set_error(CCL_ERR_INVALID_ARGUMENT, "null stream pointer");
+  *stream = nullptr;
+  if (!mask || nwords < 1 || nwords > 64) return set_error(CCL_ERR_INVALID_ARGUMENT, "mask: 1..64 32-bit words");
+  return guarded([&] {
+    int dev = 0, cus = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    // the runtime is handed exactly the words that cover the device's CUs (a copy the
+    // size of its argument), so it never reads past the caller's array
+    std::vector<uint32_t> m(mask, mask + std::min(nwords, (cus + 31) / 32));
+    int set = 0;
+    for (int i = 0; i < nwords * 32 && i < cus; ++i) set += (m[i / 32] >> (i % 32)) & 1u;
+    if (set == 0) fail(CCL_ERR_INVALID_ARGUMENT, "the mask enables no compute unit of the device");
+    hipStream_t s = nullptr;
+    HIP_TRY(hipExtStreamCreateWithCUMask(&s, uint32_t(m.size()), m.data()));
+    *stream = s;
+    return CCL_OK;
+  });
+}
+
+int ccl_stream_destroy(void* stream) {
+  if (!stream) return CCL_OK;
+  return guarded([&] {
+    HIP_TRY(hipStreamDestroy(reinterpret_cast<hipStream_t>(stream)));
+    return CCL_OK;
+  });
+}
+
+int ccl_cu_probe(void* stream, int nblocks, int hold_us, uint32_t* out) {
+  if (!out || nblocks < 1 || nblocks > 65536 || hold_us < 0 || hold_us > 100000)
+    return set_error(CCL_ERR_INVALID_ARGUMENT, "placement probe: bad arguments");
+  return guarded([&] {
+    int dev = 0, rate_khz = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev));
+    if (rate_khz <= 0) rate_khz = 100000;
+    unsigned* d = nullptr;
+    const size_t bytes = size_t(nblocks) * 2 * sizeof(unsigned);
+    HIP_TRY(hipMalloc(&d, bytes));
+    struct Free {
+      unsigned* p;
+      ~Free() { (void)hipFree(p); }
+    } guard{d};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    HIP_TRY(hipMemsetAsync(d, 0xFF, bytes, s));
+    std::string err;
+    const int rc = launch_cu_probe(d, nblocks, (long long)hold_us * (rate_khz / 1000), stream, &err);
+    if (rc) fail(rc, err);
+    HIP_TRY(hipStreamSynchronize(s));
+    HIP_TRY(hipMemcpy(out, d, bytes, hipMemcpyDeviceToHost));
     return CCL_OK;
   });
 }

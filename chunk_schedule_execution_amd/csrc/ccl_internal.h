@@ -133,6 +133,7 @@ int launch_executor(const ExecArgs& args, int dtype, bool xcd_local, bool stream
 int executor_max_blocks_per_cu(int dtype, int nthreads, int* blocks, std::string* err);
 int launch_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int nthreads,
                       void* stream, std::string* err);
+int launch_cu_probe(unsigned* out, int nblocks, long long hold_ticks, void* stream, std::string* err);
 int launch_litmus_mp(unsigned char* data, unsigned long long* flags, unsigned long long* acks,
                      unsigned long long* tags, long long* results, unsigned long long* stop, int npairs, int rounds,
                      int words, int cross, long long timeout_ticks, void* stream, std::string* err);

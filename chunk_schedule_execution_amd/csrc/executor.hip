@@ -167,6 +167,18 @@ __global__ __launch_bounds__(256) void litmus_mp_kernel(LitmusArgs A) {
   }
 }
 
+// Placement probe: each workgroup records the XCD it runs on (XCC_ID) and its hardware
+// id word (HW_ID: CU, shader array and engine), then stays for `hold_ticks` of the wall
+// clock so that later workgroups spread over other compute units.
+__global__ __launch_bounds__(64) void cu_probe_kernel(unsigned* out, long long hold_ticks) {
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = xcd_id();
+    out[2 * blockIdx.x + 1] = __builtin_amdgcn_s_getreg((4) | (0 << 6) | ((32 - 1) << 11));
+    const long long t0 = wall_clock64();
+    while (wall_clock64() - t0 < hold_ticks) __builtin_amdgcn_s_sleep(8);
+  }
+}
+
 }  // namespace
 
 template <int DT>
@@ -235,6 +247,17 @@ int launch_litmus_mp(unsigned char* data, unsigned long long* flags, unsigned lo
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     *err = std::string("litmus launch: ") + hipGetErrorString(e);
+    return CCL_ERR_HIP;
+  }
+  return CCL_OK;
+}
+
+int launch_cu_probe(unsigned* out, int nblocks, long long hold_ticks, void* stream, std::string* err) {
+  hipLaunchKernelGGL(cu_probe_kernel, dim3(nblocks), dim3(64), 0, reinterpret_cast<hipStream_t>(stream), out,
+                     hold_ticks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    *err = std::string("placement probe launch: ") + hipGetErrorString(e);
     return CCL_ERR_HIP;
   }
   return CCL_OK;

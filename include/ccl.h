@@ -464,6 +464,32 @@ int ccl_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int nt
 int ccl_litmus_message_passing(int cross_xcd, int rounds, int words, int64_t timeout_us, int64_t* results,
                                void* stream);
 
+/* ---- compute-unit reservation (AutoCCL report, method 3 and its interference
+ * results: communication tuned while computation runs beside it; ReSCCL report,
+ * section 1: thread blocks the collective takes from computation) -------------- */
+
+/*
+ * Create a stream whose kernels run only on the compute units enabled in `mask`
+ * (nwords 32-bit words, bit i = compute unit i of the device's numbering, 1..64 words;
+ * bits beyond the device's CU count are ignored). Default priority. A plan created with
+ * num_cus = the number of enabled CUs is checked for co-residency against them, so its
+ * launches on this stream never wait for workgroups that cannot be placed; work on a
+ * stream with the complementary mask never takes those CUs. The caller destroys the
+ * stream with ccl_stream_destroy. Errors: INVALID_ARGUMENT (null pointers, bad length,
+ * a mask that enables none of the device's CUs), HIP.
+ */
+int ccl_stream_create_cu_masked(const uint32_t* mask, int nwords, void** stream);
+int ccl_stream_destroy(void* stream);
+
+/*
+ * Placement probe: launches `nblocks` one-wave workgroups on `stream`, each recording the
+ * XCD it ran on and its hardware id word (gfx9 HW_ID: CU id bits 11:8, shader array bit
+ * 12, shader engine bits 15:13) and holding its compute unit for hold_us microseconds, so
+ * the set of (XCD, engine, array, CU) seen covers the CUs the stream may use. out (host)
+ * receives 2 * nblocks values {XCD, HW_ID} in block order. Synchronizes with `stream`.
+ */
+int ccl_cu_probe(void* stream, int nblocks, int hold_us, uint32_t* out);
+
 /* ---- errors --------------------------------------------------------------- */
 const char* ccl_error_string(int status);
 const char* ccl_last_error_detail(void);
