@@ -72,10 +72,15 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also run the plain copy kernel this many times on 256 MiB (counter calibration)")
-    ap.add_argument("--workload", choices=["ring_allreduce_8r", "allgather_24r", "reducescatter_24r"],
+    ap.add_argument("--workload", choices=["ring_allreduce_8r"] + sorted(PROFILE_WORKLOADS),
                     default="ring_allreduce_8r",
-                    help="profiling runs of another collective instead of the headline: the 24-rank ring AllGather "
-                         "or ReduceScatter at 128 MiB (the larger buffer), with --fixed (default 32,512,65536,3)")
+                    help="profiling runs of another collective instead of the headline, in a fixed configuration "
+                         "(--fixed, else the workload's default)")
+    ap.add_argument("--sched", choices=["hpds", "rr", "program"], default="hpds", help="scheduler (--workload runs)")
+    ap.add_argument("--alloc", choices=["state", "connection"], default="state",
+                    help="workgroup allocation (--workload runs)")
+    ap.add_argument("--trace", action="store_true",
+                    help="--workload runs: also one traced launch (workgroup idle and link busy fractions)")
     return ap.parse_args()
 
 
@@ -101,29 +106,58 @@ def progress(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+# Profiling workloads (--workload): (program factory, ranks, dtype, elements per rank input,
+# output elements per rank, bus-bandwidth factor, default --fixed configuration, what it is)
+N_BIG_24 = 24 * ((32 << 20) // 24)  # 33,554,424 fp32: the AllGather output, the ReduceScatter input
+PROFILE_WORKLOADS = {
+    "allgather_24r": ("ring_allgather", (24,), "f32", N_BIG_24 // 24, N_BIG_24, 23 / 24, "32,512,65536,3",
+                      "ring AllGather, 24 virtual ranks, fp32, 128 MiB output per rank"),
+    "reducescatter_24r": ("ring_reducescatter", (24,), "f32", N_BIG_24, N_BIG_24 // 24, 23 / 24, "32,512,65536,3",
+                          "ring ReduceScatter, 24 virtual ranks, fp32, 128 MiB input per rank"),
+    "allgather_2d_24r": ("allgather_2d", (3, 8), "f32", N_BIG_24 // 24, N_BIG_24, 23 / 24, "8,512,65536,3",
+                         "2-D AllGather, 3 x 8 virtual ranks, fp32, 128 MiB output per rank"),
+    "reducescatter_2d_24r": ("reducescatter_2d", (3, 8), "f32", N_BIG_24, N_BIG_24 // 24, 23 / 24, "16,256,65536,3",
+                             "2-D ReduceScatter, 3 x 8 virtual ranks, fp32, 128 MiB input per rank"),
+    "alltoall_32r": ("direct_alltoall", (32,), "i32", 1 << 22, 1 << 22, 31 / 32, "2,256,262144,3",
+                     "direct AllToAll, 32 virtual ranks, int32, 16 MiB per rank"),
+    "alltoall_two_phase_32r": ("two_phase_alltoall", (4, 8), "i32", 1 << 22, 1 << 22, 31 / 32, "1,256,262144,3",
+                               "two-phase AllToAll, 4 x 8 virtual ranks, int32, 16 MiB per rank"),
+    "alltonext_24r": ("alltonext", (3, 8, False), "f32", 1 << 24, 1 << 24, 1.0, "16,256,131072,3",
+                      "AllToNext, 24 virtual ranks, fp32, 64 MiB per rank"),
+    "alltonext_split_24r": ("alltonext", (3, 8, True), "f32", 1 << 24, 1 << 24, 1.0, "16,256,131072,3",
+                            "split AllToNext, 3 x 8 virtual ranks, fp32, 64 MiB per rank"),
+    "hier_ar_16r_bf16": ("hierarchical_allreduce", (2, 8), "bf16", 1 << 25, 1 << 25, 2 * 15 / 16, "32,256,131072,3",
+                         "hierarchical AllReduce, 2 x 8 virtual ranks, bf16, 64 MiB per rank"),
+}
+
+
 def profile_collective(args) -> None:
-    """One JSON line for a 24-rank ring AllGather or ReduceScatter at 128 MiB, timed with
-    HIP events on the launch stream in a fixed configuration (profiling runs)."""
+    """One JSON line for one of PROFILE_WORKLOADS in a fixed configuration, timed with HIP
+    events on the launch stream (profiling runs); with --trace also one traced launch:
+    workgroup idle fractions and per-connection busy fractions from the device trace."""
     import torch
 
+    import workloads as W
     from chunk_schedule_execution_amd import Plan, PlanConfig, capi, programs
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    Pn = 24
-    n_big = Pn * ((32 << 20) // Pn)  # 33,554,424 fp32: the AllGather output, the ReduceScatter input
-    ag = args.workload == "allgather_24r"
-    prog = programs.ring_allgather(Pn) if ag else programs.ring_reducescatter(Pn)
-    count, nout = (n_big // Pn, n_big) if ag else (n_big, n_big // Pn)
-    cfg = tuple(int(v) for v in (args.fixed or "32,512,65536,3").split(","))[:4]
+    factory, fargs, dtype, count, nout, busf, default_cfg, what = PROFILE_WORKLOADS[args.workload]
+    prog = programs.REGISTRY[factory](*fargs)
+    Pn = prog.nranks
+    cfg = tuple(int(v) for v in (args.fixed or default_cfg).split(","))[:4]
     k, nt, sl, proto = cfg
-    g = torch.Generator(device=dev)
-    g.manual_seed(6000 + len(args.workload))
-    ii = [torch.randn(count, generator=g, device=dev) for _ in range(Pn)]
-    oo = [torch.empty(nout, device=dev) for _ in range(Pn)]
-    plan = Plan(prog, k, PlanConfig(dtype="f32", max_count=count, nthreads=nt, slice_bytes=sl,
-                                    protocol=PROTOCOLS[proto][0], transport=PROTOCOLS[proto][1],
-                                    streaming=PROTOCOLS[proto][2], kernel=KERNELS[KERNEL]))
+    kind = {"f32": "normal_f32", "bf16": "normal_bf16", "i32": "uniform_i32"}[dtype]
+    ii = W.device_inputs(kind, count, Pn, 6000 + len(args.workload), device=dev)
+    tt = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}[dtype]
+    oo = [torch.empty(nout, dtype=tt, device=dev) for _ in range(Pn)]
+
+    def make(trace=False):
+        return Plan(prog, k, PlanConfig(dtype=dtype, max_count=count, nthreads=nt, slice_bytes=sl,
+                                        protocol=PROTOCOLS[proto][0], transport=PROTOCOLS[proto][1],
+                                        streaming=PROTOCOLS[proto][2], kernel=KERNELS[KERNEL], scheduler=args.sched,
+                                        wg_alloc=args.alloc, trace=trace))
+    plan = make()
     for _ in range(args.warmup):
         plan.execute(ii, oo, count, stream)
     torch.cuda.synchronize()
@@ -136,7 +170,31 @@ def profile_collective(args) -> None:
     plan.status()
     t = e0.elapsed_time(e1) * 1e-3 / args.steps
     pb = plan.bytes(count)
-    Sb = n_big * 4
+    esz = {"f32": 4, "bf16": 2, "i32": 4}[dtype]
+    Sb = max(count, nout) * esz
+    info = plan.info()
+    out = {"workload": what, "config": list(cfg), "scheduler": args.sched, "wg_alloc": args.alloc,
+           "workgroups": info["num_workgroups"], "steps": args.steps, "us_per_launch": round(t * 1e6, 2),
+           "busbw": round(Sb / t * busf / 1e9, 2), "plan_bytes_per_launch": pb,
+           "hbm_frac": round(pb / t / 1e9 / HBM_PEAK_GBS, 4), "dag_width": info["dag_width"],
+           "dag_depth": info["dag_depth"], "source_digest": source_digest()}
+    plan.destroy()
+    if args.trace:
+        tp = make(trace=True)
+        for _ in range(3):
+            tp.execute(ii, oo, count, stream)
+        torch.cuda.synchronize()
+        recs = [r for r in tp.trace() if r[3] > 0]
+        t0 = min(r[0] for r in recs)
+        span = max(r[1] for r in recs) - t0
+        fr = sorted((r[2] + (r[0] - t0) + (t0 + span - r[1])) / span for r in recs)
+        busy = sorted(b[4] for b in tp.link_busy())
+        out["trace"] = {"span_us": round(span / 100.0, 2), "wg_idle_mean": round(sum(fr) / len(fr), 4),
+                        "wg_idle_max": round(fr[-1], 4), "wg_idle_median": round(fr[len(fr) // 2], 4),
+                        "connections": len(busy), "link_busy_mean": round(sum(busy) / max(1, len(busy)), 4),
+                        "link_busy_min": round(busy[0], 4) if busy else None,
+                        "link_busy_max": round(busy[-1], 4) if busy else None}
+        tp.destroy()
     if args.copy_probe:
         nb = 1 << 28
         a = torch.zeros(nb, dtype=torch.uint8, device=dev)
@@ -144,12 +202,7 @@ def profile_collective(args) -> None:
         for _ in range(args.copy_probe):
             capi.ccl_copy_probe(b.data_ptr(), a.data_ptr(), nb, 256, 256, stream.cuda_stream)
         torch.cuda.synchronize()
-    print(json.dumps({"workload": f"ring {'AllGather' if ag else 'ReduceScatter'}, 24 virtual ranks, fp32, 128 MiB",
-                      "config": list(cfg), "workgroups": plan.info()["num_workgroups"], "steps": args.steps,
-                      "us_per_launch": round(t * 1e6, 2), "busbw": round(Sb / t * (Pn - 1) / Pn / 1e9, 2),
-                      "plan_bytes_per_launch": pb, "hbm_frac": round(pb / t / 1e9 / HBM_PEAK_GBS, 4),
-                      "source_digest": source_digest()}), flush=True)
-    plan.destroy()
+    print(json.dumps(out, separators=(",", ":")), flush=True)
 
 
 def main():

@@ -43,6 +43,7 @@ CCL_FLAG_SPECIALIZE_LOOP = 0x800
 CCL_FLAG_DEBUG_DROP_FLAG = 0x1000
 CCL_FLAG_DEBUG_POISON = 0x2000
 CCL_I_RECV, CCL_I_SRCB, CCL_I_DSTA, CCL_I_SEND, CCL_I_LOCAL_IN = 0x1, 0x2, 0x4, 0x8, 0x10
+CCL_I_SKIP, CCL_I_NOFLAG = 0x20, 0x40
 
 
 class ccl_chunk_op(C.Structure):

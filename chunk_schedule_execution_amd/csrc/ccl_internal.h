@@ -48,6 +48,7 @@ struct Instr {
   int rank = 0, channel = 0, cnt = 1;
   bool recv = false;  // first operand is the staging slot of transfer xin
   bool local_in = false;  // direct transport: the received data is written into `a` by the sender
+  bool skip = false;      // an idle receive (see mark_idle_receives): not executed
   Loc a, b, d;        // local first operand (if !recv), added operand, local destination
   int xin = -1, xout = -1;
   int chunk_id = 0;
@@ -68,6 +69,7 @@ struct Xfer {
   int sender = -1, receiver = -1;  // base instruction ids
   int phase_idx = -1;
   bool direct = false;  // the sender writes the receiver's destination, no staging slot
+  bool noflag = false;  // its receive is skipped: the sender sets no flag
 };
 
 struct BaseWG {

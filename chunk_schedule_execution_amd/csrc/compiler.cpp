@@ -894,6 +894,21 @@ void compute_waits(HostPlan& hp, const std::vector<std::set<int>>& dag) {
     }
 }
 
+// A receive of direct transport whose data the sender writes into its place, that
+// stores nothing itself, forwards nothing, sets no completion flag and precedes no other
+// instruction in the dependency graph only delays its workgroup: nothing observes its
+// wait before the launch ends, and the end of the launch makes the sender's stores
+// visible. It is skipped, and its sender neither waits for its store acknowledgements
+// nor sets the transfer's flag (a bubble per slice on long copies).
+void mark_idle_receives(HostPlan& hp, const std::vector<std::set<int>>& dag) {
+  for (auto& X : hp.xf) X.noflag = false;
+  for (size_t t = 0; t < hp.ins.size(); ++t) {
+    Instr& I = hp.ins[t];
+    I.skip = I.recv && I.local_in && !I.b.valid() && !I.d.valid() && I.xout < 0 && I.done_flag < 0 && dag[t].empty();
+    if (I.skip) hp.xf[I.xin].noflag = true;
+  }
+}
+
 // ---------------------------------------------------------------- lowering
 
 int len_idx_of(const HostPlan& hp, int t, int depth = 0) {
@@ -978,7 +993,7 @@ void lower(HostPlan& hp) {
       for (int t : W.instrs) {
         const Instr& I = hp.ins[t];
         DevInstr D{};
-        D.op = I.opbits();
+        D.op = I.opbits() | (I.skip ? OPB_SKIP : 0u) | (I.xout >= 0 && hp.xf[I.xout].noflag ? OPB_NOFLAG : 0u);
         D.cnt = I.cnt;
         D.a_buf = I.a.buf;
         D.a_idx = I.a.idx;
@@ -1048,7 +1063,8 @@ int64_t plan_bytes(const HostPlan& hp, int64_t count) {
   int64_t total = 0;
   for (size_t j = 0; j < hp.dins.size(); ++j) {
     const DevInstr& D = hp.dins[j];
-    if (D.op == (OPB_RECV | OPB_LOCAL_IN)) continue;  // waits for data the sender already placed
+    // waits for data the sender already placed (or, skipped, not even that)
+    if ((D.op & (OPB_RECV | OPB_LOCAL_IN | OPB_SRCB | OPB_DSTA | OPB_SEND)) == (OPB_RECV | OPB_LOCAL_IN)) continue;
     Range r = op_range(D.pad0, D.cnt, D.instance, hp.k, count, hp.C);
     // slot reads and writes carry one flag byte per data byte under the LL protocol
     const int slot = (hp.cfg.flags & CCL_FLAG_LL) ? 2 : 1;
@@ -1210,6 +1226,7 @@ void compile_plan(HostPlan& hp, const ccl_program_desc* prog, int nranks, int nc
   t0 = Clock::now();
   allocate_workgroups(hp);
   compute_waits(hp, dag);
+  mark_idle_receives(hp, dag);
   hp.ms[4] = ms_since(t0);
   t0 = Clock::now();
   lower(hp);

@@ -14,7 +14,11 @@ constexpr int kNumBufs = 3;  // input, output, scratch
 // OPB_LOCAL_IN a receive's data is already in the local first operand, written there
 // by the sender (direct transport); the receive only waits for the transfer's flag
 // before reading it.
-enum : uint32_t { OPB_RECV = 1u, OPB_SRCB = 2u, OPB_DSTA = 4u, OPB_SEND = 8u, OPB_LOCAL_IN = 16u };
+// OPB_SKIP marks such a receive that nothing depends on (it is not executed) and
+// OPB_NOFLAG a send whose receiver is skipped (no flag, no wait for its stores).
+enum : uint32_t {
+  OPB_RECV = 1u, OPB_SRCB = 2u, OPB_DSTA = 4u, OPB_SEND = 8u, OPB_LOCAL_IN = 16u, OPB_SKIP = 32u, OPB_NOFLAG = 64u
+};
 constexpr uint32_t kStagingBuf = 15u;  // DevExec::op target-buffer field: the staging pool
 
 struct DevWG {  // one workgroup of the launch

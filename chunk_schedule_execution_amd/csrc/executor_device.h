@@ -122,7 +122,7 @@ __device__ __forceinline__ long long wait_slot_flag(unsigned long long* p, unsig
 // wtarget).
 // Returns the ticks waited, or -1 if the wait gave up (the whole workgroup returns
 // -1 together).
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL, bool NT>
+template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL, bool NT, bool NF>
 __device__ __forceinline__ long long run_slice(const unsigned char* pa, const unsigned char* pb,
                                                          unsigned char* pd, unsigned char* pt, int n, int tid,
                                                          int nthr, unsigned long long* wflag,
@@ -135,7 +135,9 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
   constexpr int V = 16 / esz;
   constexpr int CL = NT ? kCpolNt : kCpolNone;      // local-buffer loads and stores
   constexpr int CA = RECV ? kCpolSc1 : CL;          // first operand: slot or local buffer
-  constexpr int CT = XL ? kCpolNone : kCpolSc1;     // outgoing data: plain (XCD-local layout) or coherent
+  // outgoing data: plain (XCD-local layout) or coherent; a flagless send (NF: its receive
+  // is skipped, nothing reads the data before the launch ends) streams like local stores
+  constexpr int CT = NF ? CL : XL ? kCpolNone : kCpolSc1;
   const int bytes = n * esz;
   const __amdgpu_buffer_rsrc_t rA = make_rsrc(pa, bytes);
   const __amdgpu_buffer_rsrc_t rB = make_rsrc(SRCB ? pb : pa, bytes);
@@ -230,29 +232,36 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
 
 // bf16 widening adds need more registers: its slice code stays an out-of-line call so
 // the register allocator sees one variant at a time (no spills); fp32 / int32 inline.
-template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL, bool NT>
+template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL, bool NT, bool NF>
 __device__ __attribute__((noinline)) long long run_slice_call(const unsigned char* pa, const unsigned char* pb,
                                                               unsigned char* pd, unsigned char* pt, int n, int tid,
                                                               int nthr, unsigned long long* wflag,
                                                               unsigned long long wtarget, unsigned int* err,
                                                               unsigned long long* abort_word, unsigned long long epoch,
                                                               long long timeout_ticks, int instr) {
-  return run_slice<DT, RECV, SRCB, DSTA, SEND, XL, NT>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, err, abort_word,
-                                                       epoch, timeout_ticks, instr);
+  return run_slice<DT, RECV, SRCB, DSTA, SEND, XL, NT, NF>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, err,
+                                                           abort_word, epoch, timeout_ticks, instr);
 }
 
+// nf: a flagless send (OPB_NOFLAG); it changes the store policy only in the streaming
+// variant, so only those kernels carry both forms.
 template <int DT, bool XL, bool NT>
-__device__ __forceinline__ long long dispatch_slice(uint32_t op, const unsigned char* pa, const unsigned char* pb,
-                                                    unsigned char* pd, unsigned char* pt, int n, int tid, int nthr,
-                                                    unsigned long long* wflag, unsigned long long wtarget,
-                                                    const ExecArgs& A, int instr) {
+__device__ __forceinline__ long long dispatch_slice(uint32_t op, bool nf, const unsigned char* pa,
+                                                    const unsigned char* pb, unsigned char* pd, unsigned char* pt,
+                                                    int n, int tid, int nthr, unsigned long long* wflag,
+                                                    unsigned long long wtarget, const ExecArgs& A, int instr) {
+#define CCL_CALL(R, B, D, T, F)                                                                                  \
+  ((DT == CCL_BF16) ? run_slice_call<DT, R, B, D, T, XL, NT, F>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget,     \
+                                                              A.err, A.abort_word, A.epoch, A.timeout_ticks,     \
+                                                              instr)                                             \
+                    : run_slice<DT, R, B, D, T, XL, NT, F>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err,   \
+                                                           A.abort_word, A.epoch, A.timeout_ticks, instr))
 #define CCL_CASE(R, B, D, T)                                                                                     \
   case ((R) ? OPB_RECV : 0u) | ((B) ? OPB_SRCB : 0u) | ((D) ? OPB_DSTA : 0u) | ((T) ? OPB_SEND : 0u):            \
-    return (DT == CCL_BF16)                                                                                      \
-               ? run_slice_call<DT, R, B, D, T, XL, NT>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err,      \
-                                                        A.abort_word, A.epoch, A.timeout_ticks, instr)             \
-               : run_slice<DT, R, B, D, T, XL, NT>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err,           \
-                                                   A.abort_word, A.epoch, A.timeout_ticks, instr);
+    if constexpr (NT && (T)) {                                                                                   \
+      if (nf) return CCL_CALL(R, B, D, T, true);                                                                 \
+    }                                                                                                            \
+    return CCL_CALL(R, B, D, T, false);
   switch (op & 15u) {
     CCL_CASE(false, false, true, false)
     CCL_CASE(false, false, false, true)
@@ -270,6 +279,7 @@ __device__ __forceinline__ long long dispatch_slice(uint32_t op, const unsigned 
     default: return 0;  // every other instruction stores somewhere; the compiler never emits these
   }
 #undef CCL_CASE
+#undef CCL_CALL
 }
 
 // ---- low-latency protocol ------------------------------------------------------
@@ -677,8 +687,10 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
   // the transfer's flag. As the workgroup's final instruction, with no completion flag
   // of its own, nothing depends on that wait: the launch ends only once the sending
   // workgroup has, and the end of the launch makes the sender's stores visible. Its
-  // flag round trip would only lengthen the chain, so it is not taken.
-  if (wg_last && done_flag < 0 && !ll && (op & OPB_RECV) && !(op & (OPB_DSTA | OPB_SEND))) {
+  // flag round trip would only lengthen the chain, so it is not taken. The compiler
+  // marks every such receive that nothing depends on (OPB_SKIP), wherever it sits.
+  if ((opw & OPB_SKIP) ||
+      (wg_last && done_flag < 0 && !ll && (op & OPB_RECV) && !(op & (OPB_DSTA | OPB_SEND)))) {
     if (S.itrace && tid == 0 && last) {
       const unsigned long long now = (unsigned long long)wall_clock64();
       S.itrace[4 * size_t(gi) + 1] = now;
@@ -708,9 +720,11 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
     pt = (tb == kStagingBuf ? S.staging : tb == 0u ? A.base[0][tr] : tb == 1u ? A.base[1][tr] : A.base[2][tr]) +
          uni64(R.t_off);
   }
+  // a send whose receive is skipped sets no flag and need not wait for its stores
+  const bool flagged_send = (op & OPB_SEND) && !(opw & OPB_NOFLAG);
   // the receiver's XCD tag: loaded now, first used after this instruction's stores
   unsigned long long peer_tag = 0;
-  if (XL && (op & OPB_SEND) && A.xcd_tags) {
+  if (XL && flagged_send && A.xcd_tags) {
     const int peer = uni(R.peer_wg);
     if (peer >= 0) peer_tag = __hip_atomic_load(&A.xcd_tags[peer], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -740,15 +754,15 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
       const int n = int((len - o < se) ? (len - o) : se);
       const int64_t bo = o * esz;
       const long long waited =
-          dispatch_slice<DT, XL, NT>(op, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr,
+          dispatch_slice<DT, XL, NT>(op, (opw & OPB_NOFLAG) != 0, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr,
                                      pt ? pt + bo : nullptr, n, tid, nthr, (op & OPB_RECV) ? &A.xflags[size_t(xin) * kFlagStride] : nullptr,
                                      S.E + (unsigned long long)(s + 1), A, gi);
       if (waited < 0) return false;  // the wait gave up: uniform across the workgroup
       S.wait_ticks += (unsigned long long)waited;
       if (S.itrace && tid == 0 && s == 0) S.itrace[4 * size_t(gi) + 1] = (unsigned long long)wall_clock64();
-      if (op & OPB_SEND) wait_vm_stores();
+      if (flagged_send) wait_vm_stores();
       __syncthreads();
-      if ((op & OPB_SEND) && tid == 0)
+      if (flagged_send && tid == 0)
         slot_flag_store<XL>(&A.xflags[size_t(xout) * kFlagStride], S.E + (unsigned long long)(s + 1), XL && use_here(peer_tag) == S.my_tag);
     }
   }

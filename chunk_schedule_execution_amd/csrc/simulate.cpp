@@ -132,7 +132,7 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
             if (!dflag[hp.dwaits[D.wait_begin + q]]) ok = false;
           if (!ok) continue;
         }
-        if ((D.op & OPB_RECV) && s_now < geo[j].nsl && xflag[D.xin] < s_now + 1) continue;
+        if ((D.op & OPB_RECV) && !(D.op & OPB_SKIP) && s_now < geo[j].nsl && xflag[D.xin] < s_now + 1) continue;
         runnable.push_back(w);
       }
       if (all_done) break;
@@ -148,6 +148,18 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
       const Geo& g = geo[j];
       started[w] = 1;
       if (lazy) sl[w] = lit[w];
+      if (D.op & OPB_SKIP) {
+        // a skipped receive waits for nothing and touches nothing
+        if (lazy) {
+          ip[w]++;
+          lazy_settle(w);
+        } else {
+          ip[w]++;
+          sl[w] = 0;
+          started[w] = 0;
+        }
+        continue;
+      }
       if (sl[w] < g.nsl) {
         int64_t lo = sl[w] * se, hi = std::min(g.len, lo + se);
         for (int64_t e = lo; e < hi; ++e) {
@@ -171,7 +183,7 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
           else if (D.op & OPB_SEND)
             slot[D.xout][e] = v;
         }
-        if (D.op & OPB_SEND) xflag[D.xout] = sl[w] + 1;
+        if ((D.op & OPB_SEND) && !(D.op & OPB_NOFLAG)) xflag[D.xout] = sl[w] + 1;
         sl[w]++;
       }
       if (lazy) {

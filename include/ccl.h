@@ -313,6 +313,10 @@ int64_t ccl_plan_bytes(const ccl_plan* plan, int64_t count);
                           transport, straight into the receiver's buffer) */
 #define CCL_I_LOCAL_IN 0x10 /* with CCL_I_RECV: the data was written into the local first operand by the
                                sender (direct transport); the receive waits for the flag, then reads it */
+#define CCL_I_SKIP 0x20     /* a CCL_I_LOCAL_IN receive that stores nothing, sets no completion flag and
+                               precedes nothing in the dependency graph: not executed (the end of the
+                               launch makes its sender's stores visible) */
+#define CCL_I_NOFLAG 0x40   /* a send whose receive is CCL_I_SKIP: no flag, no wait for its stores */
 
 typedef struct {
   int32_t rank, wg, subpipe, channel, instance;

@@ -194,3 +194,38 @@ def test_litmus_rejects_bad_arguments_before_touching_the_gpu():
         with pytest.raises(capi.CCLError) as e:
             capi.ccl_litmus_message_passing(*args)
         assert e.value.status == capi.CCL_ERR_INVALID_ARGUMENT
+
+
+def test_tuner_cache_answers_a_known_key_without_timing(tmp_path):
+    """The persistent tuner cache times a key once: a second request (same programs, rank
+    count, dtype, count bucket, device, space and base flags) is answered from the file,
+    also after reloading it; another count bucket or base configuration is a new key."""
+    from chunk_schedule_execution_amd.tuner_cache import TunerCache, count_bucket
+
+    calls = []
+
+    def fake_tune(descs, count, base, space, stream):
+        calls.append(count)
+        best = capi.ccl_tune_point(0, 4, 256, 65536, 2, 0)
+        rep = capi.ccl_tune_report(7, 0, 123.0, 100.0)
+        return best, rep
+
+    arrs = [(C.c_int32 * 3)(1, 4, 16), (C.c_int32 * 2)(256, 512), (C.c_int32 * 2)(32768, 65536)]
+    space = capi.ccl_tune_space(C.cast(arrs[0], C.POINTER(C.c_int32)), 3, C.cast(arrs[1], C.POINTER(C.c_int32)), 2,
+                                C.cast(arrs[2], C.POINTER(C.c_int32)), 2, 1, 2, 5, 5)
+    base = PlanConfig(max_count=1 << 20).to_c()
+    path = str(tmp_path / "tune.json")
+    cache = TunerCache(path, tune=fake_tune)
+    progs = [programs.ring_allreduce(8)]
+    p1 = cache.tune(progs, 300000, base, space, device="MI355X")
+    p2 = cache.tune(progs, 262145, base, space, device="MI355X")  # same bucket (2^19)
+    assert count_bucket(300000) == count_bucket(262145) == 1 << 19
+    assert calls == [300000] and (p2.parallel_factor, p2.protocol) == (p1.parallel_factor, p1.protocol) == (4, 2)
+    cache.tune(progs, 1 << 20, base, space, device="MI355X")  # another bucket
+    cache.tune(progs, 300000, PlanConfig(max_count=1 << 20, num_cus=32).to_c(), space, device="MI355X")
+    assert calls == [300000, 1 << 20, 300000]
+    again = TunerCache(path, tune=fake_tune)
+    again.tune(progs, 300000, base, space, device="MI355X")
+    assert again.hits == 1 and len(calls) == 3
+    again.tune([programs.tree_allreduce(8)], 300000, base, space, device="MI355X")
+    assert len(calls) == 4

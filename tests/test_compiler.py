@@ -144,7 +144,14 @@ def test_direct_transport_bytes_and_opcodes():
         want = collections.Counter({SEND: 2 * P, RRS | LOCAL: 2 * P * (P - 2), RRCS | LOCAL: 2 * P,
                                     capi.CCL_I_RECV | capi.CCL_I_SEND | LOCAL: 2 * P * (P - 2),
                                     capi.CCL_I_RECV | LOCAL: 2 * P})
-        assert hist(plan) == +want
+        marks = capi.CCL_I_SKIP | capi.CCL_I_NOFLAG
+        assert collections.Counter(e.opcode & ~marks for e in plan.export()) == +want
+        # the last hop of every chain only waits and nothing follows it: skipped, and its
+        # sender (the chain's last forwarding instruction) sets no flag
+        ex = plan.export()
+        skipped = [e for e in ex if e.opcode & capi.CCL_I_SKIP]
+        assert len(skipped) == 2 * P and all(e.opcode & ~marks == capi.CCL_I_RECV | LOCAL for e in skipped)
+        assert {e.xout for e in ex if e.opcode & capi.CCL_I_NOFLAG} == {e.xin for e in skipped}
         assert plan.info()["staging_bytes"] == 0
         plan.check(seed=2, nsims=3)
     P, N = 8, 8 * 64
@@ -454,3 +461,29 @@ def test_coordinate_descent_stops_on_infeasible_points():
         return -1.0 if p.parallel_factor > 4 else float(p.parallel_factor)
     best, rep = capi.ccl_tune_coordinate_descent(_space([1, 2, 4, 8, 16], [256], [4096]), f)
     assert best.parallel_factor == 4
+
+
+@pytest.mark.parametrize("name,args,k,knobs,all_skipped", [
+    ("direct_alltoall", (8,), 1, dict(dtype="i32"), True),
+    ("alltonext", (3, 4, False), 2, {}, True),
+    ("alltonext", (3, 4, True), 2, {}, False),
+    ("two_phase_alltoall", (2, 4), 1, dict(dtype="i32"), False),
+    ("ring_allgather", (6,), 2, {}, False),
+])
+def test_idle_receives_are_skipped_and_their_senders_set_no_flag(name, args, k, knobs, all_skipped):
+    """With direct transport a receive whose data the sender places, which stores nothing,
+    sets no completion flag and precedes nothing in the dependency graph is skipped, and
+    its sender sets no flag (and so never waits for its stores): direct AllToAll and
+    unsplit AllToNext consist of such receives only. Random interleavings of the
+    lowered plan still end in the postcondition."""
+    plan = host_plan(programs.REGISTRY[name](*args), k, transport="direct", **knobs)
+    ex = plan.export()
+    recv_only = [e for e in ex if e.opcode & ~(capi.CCL_I_SKIP | capi.CCL_I_NOFLAG) == capi.CCL_I_RECV | capi.CCL_I_LOCAL_IN]
+    skipped = [e for e in ex if e.opcode & capi.CCL_I_SKIP]
+    assert skipped and all(e in recv_only for e in skipped) and all(e.done_flag < 0 for e in skipped)
+    assert (len(skipped) == len(recv_only)) if all_skipped else (len(skipped) <= len(recv_only))
+    assert {e.xout for e in ex if e.opcode & capi.CCL_I_NOFLAG} == {e.xin for e in skipped}
+    plan.check(seed=5, nsims=4)
+    # staged transport keeps every receive (it copies from the slot)
+    staged = host_plan(programs.REGISTRY[name](*args), k, **knobs)
+    assert not any(e.opcode & (capi.CCL_I_SKIP | capi.CCL_I_NOFLAG) for e in staged.export())

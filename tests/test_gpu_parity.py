@@ -849,3 +849,25 @@ def test_cu_budget_bounds_the_grid():
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 71)
     ys, _ = _run(programs.ring_allreduce(P), xs, "f32", k=2, nthreads=256, num_cus=16, kernel="specialized")
     assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
+
+
+def test_chrome_trace_export_of_a_launch(tmp_path):
+    """The device trace of a launch as Chrome / Perfetto trace events: one complete event
+    per instruction of the plan, on the thread of its workgroup, inside the launch's span."""
+    import json
+
+    from chunk_schedule_execution_amd.trace_export import write_chrome_trace
+    P, N = 8, 8 * 8192
+    case("chrome trace export")
+    xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 79)
+    ys, plan = _run(programs.ring_allreduce(P), xs, "f32", k=2, transport="direct", trace=True, kernel="specialized")
+    assert_all_equal(ys, O2.ring_allreduce(xs, P, "f32")[0])
+    path = str(tmp_path / "launch.json")
+    n = write_chrome_trace(plan, path)
+    assert n == plan.info()["num_instructions"]
+    tr = json.load(open(path))
+    xev = [e for e in tr["traceEvents"] if e["ph"] == "X"]
+    assert len(xev) == n and all(e["dur"] >= 0 and e["ts"] >= 0 for e in xev)
+    assert {e["pid"] for e in xev} == set(range(P))
+    assert sum(1 for e in xev if e["name"] == "recv (skipped)") == 2 * P  # the chains' last hops
+    plan.destroy()
