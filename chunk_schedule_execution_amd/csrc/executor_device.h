@@ -244,8 +244,10 @@ __device__ __attribute__((noinline)) long long run_slice_call(const unsigned cha
 }
 
 // nf: a flagless send (OPB_NOFLAG); it changes the store policy only in the streaming
-// variant, so only those kernels carry both forms.
-template <int DT, bool XL, bool NT>
+// variant of generated kernels (SPEC: the operation word is a compile-time constant, so
+// one form is compiled). The interpreting kernel keeps a single form: a second set of
+// slice loops made its streaming variant twice as slow (register pressure).
+template <int DT, bool XL, bool NT, bool SPEC>
 __device__ __forceinline__ long long dispatch_slice(uint32_t op, bool nf, const unsigned char* pa,
                                                     const unsigned char* pb, unsigned char* pd, unsigned char* pt,
                                                     int n, int tid, int nthr, unsigned long long* wflag,
@@ -258,7 +260,7 @@ __device__ __forceinline__ long long dispatch_slice(uint32_t op, bool nf, const 
                                                            A.abort_word, A.epoch, A.timeout_ticks, instr))
 #define CCL_CASE(R, B, D, T)                                                                                     \
   case ((R) ? OPB_RECV : 0u) | ((B) ? OPB_SRCB : 0u) | ((D) ? OPB_DSTA : 0u) | ((T) ? OPB_SEND : 0u):            \
-    if constexpr (NT && (T)) {                                                                                   \
+    if constexpr (SPEC && NT && (T)) {                                                                           \
       if (nf) return CCL_CALL(R, B, D, T, true);                                                                 \
     }                                                                                                            \
     return CCL_CALL(R, B, D, T, false);
@@ -754,7 +756,7 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
       const int n = int((len - o < se) ? (len - o) : se);
       const int64_t bo = o * esz;
       const long long waited =
-          dispatch_slice<DT, XL, NT>(op, (opw & OPB_NOFLAG) != 0, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr,
+          dispatch_slice<DT, XL, NT, (OPW >= 0)>(op, (opw & OPB_NOFLAG) != 0, pa + bo, pb ? pb + bo : nullptr, pd ? pd + bo : nullptr,
                                      pt ? pt + bo : nullptr, n, tid, nthr, (op & OPB_RECV) ? &A.xflags[size_t(xin) * kFlagStride] : nullptr,
                                      S.E + (unsigned long long)(s + 1), A, gi);
       if (waited < 0) return false;  // the wait gave up: uniform across the workgroup
