@@ -689,10 +689,8 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
   // the transfer's flag. As the workgroup's final instruction, with no completion flag
   // of its own, nothing depends on that wait: the launch ends only once the sending
   // workgroup has, and the end of the launch makes the sender's stores visible. Its
-  // flag round trip would only lengthen the chain, so it is not taken. The compiler
-  // marks every such receive that nothing depends on (OPB_SKIP), wherever it sits.
-  if ((opw & OPB_SKIP) ||
-      (wg_last && done_flag < 0 && !ll && (op & OPB_RECV) && !(op & (OPB_DSTA | OPB_SEND)))) {
+  // flag round trip would only lengthen the chain, so it is not taken.
+  if (wg_last && done_flag < 0 && !ll && (op & OPB_RECV) && !(op & (OPB_DSTA | OPB_SEND))) {
     if (S.itrace && tid == 0 && last) {
       const unsigned long long now = (unsigned long long)wall_clock64();
       S.itrace[4 * size_t(gi) + 1] = now;
@@ -710,6 +708,17 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
     }
     __syncthreads();
     if (*S.s_abort) return false;
+  }
+  // The compiler marks every such receive that nothing depends on (OPB_SKIP) wherever
+  // it sits: it runs its completion waits (later instructions of the workgroup may be
+  // ordered through them), then skips the transfer's flag.
+  if (opw & OPB_SKIP) {
+    if (S.itrace && tid == 0 && last) {
+      const unsigned long long now = (unsigned long long)wall_clock64();
+      S.itrace[4 * size_t(gi) + 1] = now;
+      S.itrace[4 * size_t(gi) + 2] = now;
+    }
+    return true;
   }
   // a receive reads its slot, or (direct transport) its own buffer where the sender wrote
   const unsigned char* pa = ((op & OPB_RECV) && !(opw & OPB_LOCAL_IN)) ? S.staging + uni64(R.a_off)

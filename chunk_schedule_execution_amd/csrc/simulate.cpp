@@ -149,7 +149,8 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
       started[w] = 1;
       if (lazy) sl[w] = lit[w];
       if (D.op & OPB_SKIP) {
-        // a skipped receive waits for nothing and touches nothing
+        // a skipped receive has run its completion waits (checked above) and then
+        // waits for no transfer flag and touches nothing
         if (lazy) {
           ip[w]++;
           lazy_settle(w);
