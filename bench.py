@@ -653,6 +653,10 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
                 t, k, nt, streaming, nwg, hf = best
                 row[name] = {"us": round(t * 1e6, 2), "k": k, "nthreads": nt, "streaming": streaming,
                              "workgroups": nwg, "hbm_frac": hf, "busbw": round(S / t * (Pa - 1) / Pa / 1e9, 2)}
+                if name == "two_phase":
+                    # with k > 1 every operation is split per chunk, so the phase-2 transfer of
+                    # a gather region becomes one transfer per block instead of one batch
+                    row[name]["phase2_batched"] = k == 1
         a2a.append(row)
         del ii, oo
         release()
