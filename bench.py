@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--section", choices=["interference", "kernels", "ranks"], default="",
                     help="after the headline run only this part of the long sections")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
+    ap.add_argument("--no-interference", action="store_true",
+                    help="leave out the summary's row of the 3 MiB collective beside GEMMs (shared GPU vs 64 reserved CUs)")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also run the plain copy kernel this many times on 256 MiB (counter calibration)")
     ap.add_argument("--workload", choices=["ring_allreduce_8r"] + sorted(PROFILE_WORKLOADS),
@@ -449,6 +451,14 @@ def main():
             torch.cuda.empty_cache()
         out["large"] = large
         out["target_70pct_cold_at_32mib_and_up"] = all(r["cold_frac"] >= 0.70 for r in large)
+        if not args.no_interference:
+            # the collective beside GEMMs: shared GPU vs reserved compute units
+            try:
+                out["beside_gemms"] = interference_row(torch, dev, stream, prog, cfg, ring_inputs, tune, make_plan,
+                                                       release)
+                progress(f"beside GEMMs: {out['beside_gemms']}")
+            except Exception as e:  # reported, never fatal to the summary line
+                out["beside_gemms"] = {"error": str(e)[:160]}
 
     if args.section == "interference":
         details["interference"] = interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar,
@@ -969,6 +979,57 @@ def interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_a
     del a, b, c
     release()
     return out
+
+
+def interference_row(torch, dev, stream, prog, cfg, ring_inputs, tune, make_plan, release, budget=64):
+    """Compact form of the interference section for the summary line: the 3 MiB ring
+    AllReduce beside 8192^3 bf16 GEMMs on the shared GPU (the headline's configuration)
+    and on `budget` reserved CUs (tuned while the GEMMs run on the other CUs)."""
+    from chunk_schedule_execution_amd import capi
+
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    N, ii, oo = ring_inputs(HEADLINE_BYTES)
+
+    def launches(fn, iters, comm):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(comm)
+        for _ in range(iters):
+            fn()
+        e1.record(comm)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / iters
+
+    row = {"MiB": 3, "reserved_cus": budget}
+    side = torch.cuda.Stream(device=dev)
+    p = make_plan(prog, N, *cfg)
+    with GemmLoad(torch, side, a, b, c) as g:
+        t = launches(lambda: p.execute(ii, oo, N, stream), 50, stream)
+    row["shared_us"], row["shared_gemm_tflops"] = round(t * 1e6, 1), round(g.tflops, 1)
+    release(p)
+    comm_h = capi.ccl_stream_create_cu_masked(capi.cu_mask_words(range(budget)))
+    rest_h = capi.ccl_stream_create_cu_masked(capi.cu_mask_words(range(budget, 256)))
+    try:
+        comm, rest = torch.cuda.ExternalStream(comm_h), torch.cuda.ExternalStream(rest_h)
+        with GemmLoad(torch, rest, a, b, c):
+            cb, _ = tune(prog, N, kernel=0, num_cus=budget, on=comm)
+        p = make_plan(prog, N, *cb[:4], KERNEL, num_cus=budget)
+        with GemmLoad(torch, rest, a, b, c) as g:
+            t = launches(lambda: p.execute(ii, oo, N, comm), 50, comm)
+        row["reserved_us"], row["reserved_gemm_tflops"] = round(t * 1e6, 1), round(g.tflops, 1)
+        row["reserved_k"] = cb[0]
+        release(p)
+    finally:
+        torch.cuda.synchronize()
+        capi.ccl_stream_destroy(comm_h)
+        capi.ccl_stream_destroy(rest_h)
+    del a, b, c, ii, oo
+    release()
+    return row
 
 
 def kernels(prog, ring_inputs, make_plan, time_launches, release, stream):
