@@ -35,7 +35,10 @@ P = 8
 HEADLINE_BYTES = 3 << 20
 SWEEP = [32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20, 2 << 20, 3 << 20]
 HBM_PEAK_GBS = 8000.0
-TUNE_FACTORS = [1, 2, 4, 8, 16, 24, 32]
+# parallelization factors of the 8-rank ring sweep, 32 KiB to 3 MiB per rank (8 x factor chunks);
+# larger sizes and other workloads also try 32, one workgroup per compute unit at 8 ranks
+CONFIG_FACTORS = [1, 2, 4, 8, 16, 24]
+TUNE_FACTORS = CONFIG_FACTORS + [32]
 TUNE_THREADS = [256, 512, 1024]
 TUNE_SLICES = [16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20]
 # tuner protocol ids: (protocol, transport, non-temporal local traffic)
@@ -333,7 +336,7 @@ def main():
         cfg = cfg + (0, 0, KERNEL)[len(cfg) - 2:] if len(cfg) < 5 else cfg
         tune_evals = 0
     else:
-        cfg, tune_evals = tune(prog, N, kernel=KERNEL)
+        cfg, tune_evals = tune(prog, N, kernel=KERNEL, factors=ring_factors(S))
     tune_s = time.perf_counter() - t0
     plan = make_plan(prog, N, *cfg)
     info = plan.info()
@@ -420,6 +423,14 @@ def main():
             fixed[name] = round(busbw_ar(S, time_launches(lambda: pf.execute(ins, outs, N, stream), 30)), 2)
             release(pf)
         out["fixed_busbw"] = fixed
+        if S <= SWEEP[-1]:
+            # the same size at factor 32 (256 workgroups), outside the sweep's factor set
+            c32, _ = tune(prog, N, kernel=KERNEL, factors=[32])
+            p32 = make_plan(prog, N, *c32)
+            t32 = time_launches(lambda: p32.execute(ins, outs, N, stream), args.steps)
+            out["factor_32"] = {"nt": c32[1], "us": round(t32 * 1e6, 2), "busbw": round(busbw_ar(S, t32), 2),
+                                "frac": frac(p32, N, t32)}
+            release(p32)
     release(plan)
     del ins, outs
 
@@ -501,6 +512,11 @@ def main():
     print(json.dumps(out, separators=(",", ":")), flush=True)
 
 
+def ring_factors(S):
+    """Parallelization factors the 8-rank ring AllReduce is tuned over at S bytes per rank."""
+    return CONFIG_FACTORS if S <= SWEEP[-1] else TUNE_FACTORS
+
+
 def reap_children():
     """Leave no process behind: name any child this run started (the runtime compiler
     or a library may), then end it."""
@@ -527,7 +543,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
     sweep = []
     for S in SWEEP + [128 << 20]:
         N, ii, oo = ring_inputs(S)
-        c, _ = tune(prog, N, kernel=KERNEL)
+        c, _ = tune(prog, N, kernel=KERNEL, factors=ring_factors(S))
         p = make_plan(prog, N, *c)
         t = time_launches(lambda: p.execute(ii, oo, N, stream), 20 if S >= DEVICE_INPUT_BYTES else 50)
         row = {"bytes_per_rank": S, "k": c[0], "nthreads": c[1], "slice_bytes": c[2],
@@ -771,7 +787,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         return out
 
     N, ii, oo = ring_inputs(HEADLINE_BYTES)
-    c, _ = tune(prog, N, kernel=KERNEL)
+    c, _ = tune(prog, N, kernel=KERNEL, factors=ring_factors(HEADLINE_BYTES))
     idle_rows = {"ring_ar_8r_3mib_tuned": idle(prog, N, "f32", *c, ii, oo)}
     del ii, oo
     N = (64 << 20) // 4
@@ -948,9 +964,9 @@ def interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_a
             N, ii, oo = ring_inputs(S)
             iters = 50 if S < (32 << 20) else 20
             row = {"bytes_per_rank": S}
-            c_pure, _ = tune(prog, N, kernel=0)
+            c_pure, _ = tune(prog, N, kernel=0, factors=ring_factors(S))
             with GemmLoad(torch, side, a, b, c):
-                c_int, ev = tune(prog, N, kernel=0)
+                c_int, ev = tune(prog, N, kernel=0, factors=ring_factors(S))
             row["shared_tuned_alone"] = measure(c_pure[:4] + (KERNEL,), N, ii, oo, stream, side, iters)
             row["shared_tuned_under_gemms"] = measure(c_int[:4] + (KERNEL,), N, ii, oo, stream, side, iters)
             row["shared_tuner_evaluations_under_gemms"] = ev
@@ -959,9 +975,9 @@ def interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_a
             for B in budgets:
                 comm = torch.cuda.ExternalStream(masked[B][0])
                 gst = torch.cuda.ExternalStream(masked[B][1])
-                c_alone_b, _ = tune(prog, N, kernel=0, num_cus=B, on=comm)
+                c_alone_b, _ = tune(prog, N, kernel=0, num_cus=B, on=comm, factors=ring_factors(S))
                 with GemmLoad(torch, gst, a, b, c):
-                    c_b, ev_b = tune(prog, N, kernel=0, num_cus=B, on=comm)
+                    c_b, ev_b = tune(prog, N, kernel=0, num_cus=B, on=comm, factors=ring_factors(S))
                 entry = {"tuner_evaluations_under_gemms": ev_b,
                          "tuned_alone": measure(c_alone_b[:4] + (KERNEL,), N, ii, oo, comm, gst, iters, num_cus=B),
                          "tuned_under_gemms": measure(c_b[:4] + (KERNEL,), N, ii, oo, comm, gst, iters, num_cus=B)}
@@ -1016,7 +1032,7 @@ def interference_row(torch, dev, stream, prog, cfg, ring_inputs, tune, make_plan
     try:
         comm, rest = torch.cuda.ExternalStream(comm_h), torch.cuda.ExternalStream(rest_h)
         with GemmLoad(torch, rest, a, b, c):
-            cb, _ = tune(prog, N, kernel=0, num_cus=budget, on=comm)
+            cb, _ = tune(prog, N, kernel=0, num_cus=budget, on=comm, factors=CONFIG_FACTORS)
         p = make_plan(prog, N, *cb[:4], KERNEL, num_cus=budget)
         with GemmLoad(torch, rest, a, b, c) as g:
             t = launches(lambda: p.execute(ii, oo, N, comm), 50, comm)

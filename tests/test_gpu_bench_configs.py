@@ -64,19 +64,21 @@ def assert_ranks_equal(ys, want):
 
 # ------------------------------------------------------------------ headline and large ring AllReduce
 
+@pytest.mark.parametrize("k", [24, 32])
 @pytest.mark.parametrize("proto", [0, 1, 2, 3])
-def test_headline_ring_ar_8r_3mib(proto):
+def test_headline_ring_ar_8r_3mib(proto, k):
     """Bench headline (ring AllReduce, 8 ranks, 3 MiB fp32 per rank): the tuner's
-    k = 32 x 256 threads x 32 KiB slices on a generated kernel, under each of the four
-    protocol / transport subspaces it searches. Element-wise against the chain order,
-    two launches on different inputs, and the plain relative error within the bound
-    recursive summation implies."""
+    k = 24 (the largest factor of the sweep's set) and the `factor_32` row's k = 32, at
+    256 threads x 32 KiB slices on a generated kernel, under each of the four
+    protocol / transport subspaces the tuner searches. Element-wise against the chain
+    order, two launches on different inputs, and the plain relative error within the
+    bound recursive summation implies."""
     from gpu_util import run
     P, N = 8, (3 << 20) // 4
-    case(f"headline ring AR 3 MiB k=32 nt=256 slice=32K proto={proto}")
+    case(f"headline ring AR 3 MiB k={k} nt=256 slice=32K proto={proto}")
     xs = W.make_inputs("normal_f32", N, P, W.CFG_RING_AR_8R, size_bytes=3 << 20)
     pr, tr, st = PROTOCOLS[proto]
-    ys, plan = run(programs.ring_allreduce(P), xs, "f32", k=32, nthreads=256, slice_bytes=32 << 10, protocol=pr,
+    ys, plan = run(programs.ring_allreduce(P), xs, "f32", k=k, nthreads=256, slice_bytes=32 << 10, protocol=pr,
                    transport=tr, streaming=st, kernel="specialized", repeat=2,
                    check=lambda y, x, _: assert_ranks_equal(y, O2.ring_allreduce(x, P, "f32")[0]))
     want = O2.ring_allreduce(xs, P, "f32")[0]
@@ -84,7 +86,7 @@ def test_headline_ring_ar_8r_3mib(proto):
     ref = O1.allreduce(xs, "f32")
     assert nm.scaled_error(ys[0], ref.exact, ref.abs_sum, "f32") <= 1e-6 * P
     assert nm.elementwise_rel_error(ys[0], ref.exact, ref.abs_sum, "f32") <= (P - 1) * 2.0**-24 * 1e3 * (1 + 1e-6)
-    assert plan.info()["num_workgroups"] == P * 32
+    assert plan.info()["num_workgroups"] == P * k
     plan.destroy()
 
 
