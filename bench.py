@@ -39,8 +39,8 @@ HBM_PEAK_GBS = 8000.0
 # larger sizes and other workloads also try 32, one workgroup per compute unit at 8 ranks
 CONFIG_FACTORS = [1, 2, 4, 8, 16, 24]
 TUNE_FACTORS = CONFIG_FACTORS + [32]
-TUNE_THREADS = [256, 512, 1024]
-TUNE_SLICES = [16 << 10, 32 << 10, 64 << 10, 128 << 10, 256 << 10, 512 << 10, 1 << 20]
+TUNE_THREADS = [64, 128, 256, 512, 1024]
+TUNE_SLICES = [(4 << 10) << i for i in range(11)]  # 4 KiB ... 4 MiB
 # tuner protocol ids: (protocol, transport, non-temporal local traffic)
 PROTOCOLS = {0: ("simple", "staged", False), 1: ("ll", "staged", False), 2: ("simple", "direct", False),
              3: ("simple", "direct", True)}
