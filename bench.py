@@ -99,12 +99,19 @@ def source_digest() -> str:
 
 def same_launch(a, b, piece_bytes):
     """Two (k, nthreads, slice_bytes, protocol, kernel) configurations run the same
-    kernel work: equal apart from slice sizes that both exceed every instruction's piece
-    (one slice each)."""
+    kernel work: equal apart from slice sizes that both cover the largest instruction
+    piece, piece_bytes (one slice each)."""
     a, b = tuple(a), tuple(b)
     if len(a) != 5 or len(b) != 5 or (a[0], a[1], a[3], a[4]) != (b[0], b[1], b[3], b[4]):
         return False
-    return a[2] == b[2] or (a[2] >= piece_bytes + 64 and b[2] >= piece_bytes + 64)
+    return a[2] == b[2] or (a[2] >= piece_bytes and b[2] >= piece_bytes)
+
+
+def largest_piece(N, P, k):
+    """Elements of the largest instruction piece of a ring AllReduce of N elements per
+    rank over P ranks at factor k: P program chunks, each cut into k instance
+    sub-chunks, both at floor(i N / C) boundaries."""
+    return -(-(-(-N // P)) // k)
 
 
 def progress(msg):
@@ -373,7 +380,7 @@ def main():
     if S % (1 << 20) == 0 and os.path.exists(tpath):
         with open(tpath) as fh:
             tj = json.load(fh)
-        if tj.get("source_digest") == source_digest() and same_launch(tj.get("config", []), cfg, S // P // cfg[0]):
+        if tj.get("source_digest") == source_digest() and same_launch(tj.get("config", []), cfg, largest_piece(N, P, cfg[0]) * 4):
             traffic = tj.get("bytes_per_launch")
     floor_bytes = 2 * P * S  # every rank reads its input once and writes its output once
 
