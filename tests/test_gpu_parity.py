@@ -335,6 +335,27 @@ def test_24r_ring_at_three_workgroups_per_cu(coll):
     plan.destroy()
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "i32"])
+@pytest.mark.parametrize("kernel", ["interpreter", "specialized"])
+@pytest.mark.parametrize("transport", ["staged", "direct"])
+def test_reducescatter_shards_off_the_16_byte_grid_streaming(dtype, kernel, transport):
+    """ReduceScatter whose shards are no multiple of 16 bytes, streaming variant: a
+    reducing slice whose operands sit at different 16-byte phases (staged: every hop's
+    slot against the input chunk; direct: the last hop's input against the output)
+    goes element by element with eight elements per thread in flight, and the last pass
+    of a piece is partial. Chain order, bit for bit, two launches on different inputs."""
+    P, n = 5, 3 * 2048 + 7
+    N = P * n
+    case(f"reducescatter off-grid shards {dtype} {kernel} {transport} streaming")
+    kind = {"f32": "normal_f32", "bf16": "normal_bf16", "i32": "uniform_i32"}[dtype]
+    xs = W.make_inputs(kind, N, P, W.CFG_A2NEXT_AGRS_24R)
+    chk = chk_per_rank(lambda x, _: O2.ring_reducescatter(x, P, dtype))
+    ys, plan = _run(programs.ring_reducescatter(P), xs, dtype, k=2, nthreads=256, slice_bytes=64 << 10,
+                    transport=transport, streaming=True, kernel=kernel, repeat=2, check=chk)
+    chk(ys, xs, None)
+    plan.destroy()
+
+
 def test_int32_reduction_wraps():
     P, N = 4, 1000
     case("ring AR int32 wrap")
