@@ -259,8 +259,13 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
   return waited;
 }
 
-// bf16 widening adds need more registers: its slice code stays an out-of-line call so
-// the register allocator sees one variant at a time (no spills); fp32 / int32 inline.
+// bf16 widening adds need more registers. In the interpreting kernel, which holds every
+// operation's slice code, bf16 slices stay an out-of-line call so the register
+// allocator sees one variant at a time (no spills). Generated kernels inline them like
+// fp32 / int32: each step there is one fixed operation, and a call site makes the
+// caller keep its live values in callee-saved registers (bf16 hierarchical AllReduce:
+// 103 -> 89 VGPRs and no scratch; 1 MiB 40.6 -> 36.8 us; bf16 8-rank ring at 3 MiB
+// 42.9 -> 38.4 us, at 32 MiB 200 -> 189 us).
 template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL, bool NT, bool NF>
 __device__ __attribute__((noinline)) long long run_slice_call(const unsigned char* pa, const unsigned char* pb,
                                                               unsigned char* pd, unsigned char* pt, int n, int tid,
@@ -274,7 +279,7 @@ __device__ __attribute__((noinline)) long long run_slice_call(const unsigned cha
 
 // nf: a flagless send (OPB_NOFLAG); it changes the store policy only in the streaming
 // variant of generated kernels (SPEC: the operation word is a compile-time constant, so
-// one form is compiled). The interpreting kernel keeps a single form: a second set of
+// one form is compiled; SPEC also inlines bf16 slices). The interpreting kernel keeps a single form: a second set of
 // slice loops made its streaming variant twice as slow (register pressure).
 template <int DT, bool XL, bool NT, bool SPEC>
 __device__ __forceinline__ long long dispatch_slice(uint32_t op, bool nf, const unsigned char* pa,
@@ -282,7 +287,7 @@ __device__ __forceinline__ long long dispatch_slice(uint32_t op, bool nf, const 
                                                     int n, int tid, int nthr, unsigned long long* wflag,
                                                     unsigned long long wtarget, const ExecArgs& A, int instr) {
 #define CCL_CALL(R, B, D, T, F)                                                                                  \
-  ((DT == CCL_BF16) ? run_slice_call<DT, R, B, D, T, XL, NT, F>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget,     \
+  ((DT == CCL_BF16 && !SPEC) ? run_slice_call<DT, R, B, D, T, XL, NT, F>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, \
                                                               A.err, A.abort_word, A.epoch, A.timeout_ticks,     \
                                                               instr)                                             \
                     : run_slice<DT, R, B, D, T, XL, NT, F>(pa, pb, pd, pt, n, tid, nthr, wflag, wtarget, A.err,   \
