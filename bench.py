@@ -44,6 +44,9 @@ TUNE_SLICES = [(4 << 10) << i for i in range(11)]  # 4 KiB ... 4 MiB
 # tuner protocol ids: (protocol, transport, non-temporal local traffic)
 PROTOCOLS = {0: ("simple", "staged", False), 1: ("ll", "staged", False), 2: ("simple", "direct", False),
              3: ("simple", "direct", True)}
+# parts of the long measurements, in the order --extras runs them
+EXTRA_SECTIONS = ["sweep", "ranks", "trees", "interference", "kernels", "int4", "hier", "alltoall", "alltonext", "agrs",
+                  "idle", "copy"]
 DEVICE_INPUT_BYTES = 32 << 20  # at or above this many bytes per rank, inputs are drawn on the device
 # executor kernels: the interpreting kernel, a kernel generated for the plan, and the
 # generated kernel in the lazy (slice-outer) loop order
@@ -70,8 +73,8 @@ def parse():
     ap.add_argument("--bytes", type=int, default=0,
                     help="per-rank size of the timed ring AllReduce instead of 3 MiB (profiling runs of other "
                          "sizes; implies --no-extras)")
-    ap.add_argument("--section", choices=["interference", "kernels", "ranks"], default="",
-                    help="after the headline run only this part of the long sections")
+    ap.add_argument("--section", choices=EXTRA_SECTIONS, default="",
+                    help="after the headline run only this part of the long sections (--extras runs them all)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
     ap.add_argument("--no-interference", action="store_true",
                     help="leave out the summary's row of the 3 MiB collective beside GEMMs (shared GPU vs 64 reserved CUs)")
@@ -478,19 +481,10 @@ def main():
             except Exception as e:  # reported, never fatal to the summary line
                 out["beside_gemms"] = {"error": str(e)[:160]}
 
-    if args.section == "interference":
-        details["interference"] = interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar,
-                                               release)
-    elif args.section == "ranks":
-        details["ring_ar_rank_counts"] = rank_counts(np, torch, programs, dev, stream, device_inputs, tune,
-                                                     make_plan, time_launches, busbw_ar, stats, release)
-    elif args.section == "kernels":
-        details["kernels"] = kernels(prog, ring_inputs, make_plan, time_launches, release, stream)
-        details["kernels_other"] = kernels_other(programs, device_inputs, make_plan, time_launches, release, stream,
-                                                 torch, dev)
-    elif args.extras:
+    if args.section or args.extras:
         details.update(extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inputs,
-                              device_inputs, tune, make_plan, time_launches, busbw_ar, stats, release, fitting))
+                              device_inputs, tune, make_plan, time_launches, busbw_ar, stats, release, fitting,
+                              sections={args.section} if args.section else None))
 
     if args.copy_probe:
         nb = 1 << 28
@@ -542,280 +536,307 @@ def reap_children():
 
 
 def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inputs, device_inputs, tune, make_plan,
-           time_launches, busbw_ar, stats, release, fitting):
+           time_launches, busbw_ar, stats, release, fitting, sections=None):
+    """The long measurements, by section (all of them when sections is None)."""
     res = {}
+
+    def want(name):
+        return sections is None or name in sections
+
     prog = programs.ring_allreduce(P)
 
-    # ---- the rest of the 8-rank sweep and the large sizes, each tuned ---------------
-    sweep = []
-    for S in SWEEP + [128 << 20]:
-        N, ii, oo = ring_inputs(S)
-        c, _ = tune(prog, N, kernel=KERNEL, factors=ring_factors(S))
-        p = make_plan(prog, N, *c)
-        t = time_launches(lambda: p.execute(ii, oo, N, stream), 20 if S >= DEVICE_INPUT_BYTES else 50)
-        row = {"bytes_per_rank": S, "k": c[0], "nthreads": c[1], "slice_bytes": c[2],
-               "protocol": PROTOCOLS[c[3]][0], "transport": PROTOCOLS[c[3]][1], "streaming": PROTOCOLS[c[3]][2],
-               "kernel": KERNELS[c[4]], "busbw": round(busbw_ar(S, t), 2), **stats(p, N, t)}
-        if S in (1 << 20, 3 << 20, 32 << 20, 128 << 20):  # tuned versus fixed configurations
-            for name, (k, nt, sl) in (("fixed_k1_nt256_slice128k", (1, 256, min(128 << 10, S // P))),
-                                      ("fixed_k8_nt512_slice256k", (8, 512, 256 << 10))):
-                pf = make_plan(prog, N, k, nt, sl, 0, c[4])  # the tuned point's kernel
-                tf = time_launches(lambda: pf.execute(ii, oo, N, stream), 10 if S >= DEVICE_INPUT_BYTES else 30)
-                row[name + "_busbw"] = round(busbw_ar(S, tf), 2)
-                release(pf)
-        sweep.append(row)
-        progress(f"ring AR 8 ranks {S >> 10} KiB: {row['us']} us")
-        release(p)
-        del ii, oo
-    res["sweep"] = sweep
-
-    res["ring_ar_rank_counts"] = rank_counts(np, torch, programs, dev, stream, device_inputs, tune, make_plan,
-                                             time_launches, busbw_ar, stats, release)
-
-    # ---- tree versus ring AllReduce at small sizes, and the tuner choosing -----------
-    from oracle import schedule_order as O2
-    trees = []
-    for R, S in ((8, 64 << 10), (8, 256 << 10), (8, 1 << 20), (8, 3 << 20), (24, 1 << 20)):
-        N = S // 4
-        ii = device_inputs("f32", N, R, 77000 + R * 64 + S // 65536)
-        oo = [torch.empty(N, device=dev) for _ in range(R)]
-        ring, tree = programs.ring_allreduce(R), programs.tree_allreduce(R)
-        row = {"ranks": R, "bytes_per_rank": S}
-        for name, pr in (("ring", ring), ("tree", tree)):
-            c, _ = tune(pr, N)
-            p = make_plan(pr, N, *c)
-            t = time_launches(lambda: p.execute(ii, oo, N, stream), 50)
-            row[name] = {"k": c[0], "nthreads": c[1], "slice_bytes": c[2], "protocol": PROTOCOLS[c[3]][0],
-                         "transport": PROTOCOLS[c[3]][1], "busbw": round(busbw_ar(S, t, R), 2), **stats(p, N, t)}
-            if name == "tree":  # sampled check of the tree's own association order
-                xs = [x.cpu().numpy() for x in ii]
-                want = O2.tree_allreduce(xs, R, "f32")[0]
-                idx = np.random.default_rng(1).integers(0, N, 256)
-                row[name]["oracle_spot_check"] = bool(np.array_equal(oo[R - 1].cpu().numpy()[idx], want[idx]))
+    if want("sweep"):
+        # ---- the rest of the 8-rank sweep and the large sizes, each tuned ---------------
+        sweep = []
+        for S in SWEEP + [128 << 20]:
+            N, ii, oo = ring_inputs(S)
+            c, _ = tune(prog, N, kernel=KERNEL, factors=ring_factors(S))
+            p = make_plan(prog, N, *c)
+            t = time_launches(lambda: p.execute(ii, oo, N, stream), 20 if S >= DEVICE_INPUT_BYTES else 50)
+            row = {"bytes_per_rank": S, "k": c[0], "nthreads": c[1], "slice_bytes": c[2],
+                   "protocol": PROTOCOLS[c[3]][0], "transport": PROTOCOLS[c[3]][1], "streaming": PROTOCOLS[c[3]][2],
+                   "kernel": KERNELS[c[4]], "busbw": round(busbw_ar(S, t), 2), **stats(p, N, t)}
+            if S in (1 << 20, 3 << 20, 32 << 20, 128 << 20):  # tuned versus fixed configurations
+                for name, (k, nt, sl) in (("fixed_k1_nt256_slice128k", (1, 256, min(128 << 10, S // P))),
+                                          ("fixed_k8_nt512_slice256k", (8, 512, 256 << 10))):
+                    pf = make_plan(prog, N, k, nt, sl, 0, c[4])  # the tuned point's kernel
+                    tf = time_launches(lambda: pf.execute(ii, oo, N, stream), 10 if S >= DEVICE_INPUT_BYTES else 30)
+                    row[name + "_busbw"] = round(busbw_ar(S, tf), 2)
+                    release(pf)
+            sweep.append(row)
+            progress(f"ring AR 8 ranks {S >> 10} KiB: {row['us']} us")
             release(p)
-        c, ev = tune(None, N, variants=[ring, tree])
-        row["tuner_picks"] = ("ring", "tree")[c[5]]
-        row["tuner_evaluations"] = ev
-        trees.append(row)
-        progress(f"tree vs ring {R} ranks {S >> 10} KiB: {row['tree']['us']} vs {row['ring']['us']} us")
+            del ii, oo
+        res["sweep"] = sweep
+
+    if want("ranks"):
+        res["ring_ar_rank_counts"] = rank_counts(np, torch, programs, dev, stream, device_inputs, tune, make_plan,
+                                                 time_launches, busbw_ar, stats, release)
+
+    if want("trees"):
+        # ---- tree versus ring AllReduce at small sizes, and the tuner choosing -----------
+        from oracle import schedule_order as O2
+        trees = []
+        for R, S in ((8, 64 << 10), (8, 256 << 10), (8, 1 << 20), (8, 3 << 20), (24, 1 << 20)):
+            N = S // 4
+            ii = device_inputs("f32", N, R, 77000 + R * 64 + S // 65536)
+            oo = [torch.empty(N, device=dev) for _ in range(R)]
+            ring, tree = programs.ring_allreduce(R), programs.tree_allreduce(R)
+            row = {"ranks": R, "bytes_per_rank": S}
+            for name, pr in (("ring", ring), ("tree", tree)):
+                c, _ = tune(pr, N)
+                p = make_plan(pr, N, *c)
+                t = time_launches(lambda: p.execute(ii, oo, N, stream), 50)
+                row[name] = {"k": c[0], "nthreads": c[1], "slice_bytes": c[2], "protocol": PROTOCOLS[c[3]][0],
+                             "transport": PROTOCOLS[c[3]][1], "busbw": round(busbw_ar(S, t, R), 2), **stats(p, N, t)}
+                if name == "tree":  # sampled check of the tree's own association order
+                    xs = [x.cpu().numpy() for x in ii]
+                    want = O2.tree_allreduce(xs, R, "f32")[0]
+                    idx = np.random.default_rng(1).integers(0, N, 256)
+                    row[name]["oracle_spot_check"] = bool(np.array_equal(oo[R - 1].cpu().numpy()[idx], want[idx]))
+                release(p)
+            c, ev = tune(None, N, variants=[ring, tree])
+            row["tuner_picks"] = ("ring", "tree")[c[5]]
+            row["tuner_evaluations"] = ev
+            trees.append(row)
+            progress(f"tree vs ring {R} ranks {S >> 10} KiB: {row['tree']['us']} vs {row['ring']['us']} us")
+            del ii, oo
+        res["tree_vs_ring"] = trees
+
+    if want("interference"):
+        # ---- tuning under compute interference: bf16 GEMMs on a second stream ----------
+        res["interference"] = interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release)
+        progress("interference done")
+
+    if want("kernels"):
+        # ---- interpreting vs generated kernels, and the lazy loop order ------------------
+        res["kernels"] = kernels(prog, ring_inputs, make_plan, time_launches, release, stream)
+        res["kernels_other"] = kernels_other(programs, device_inputs, make_plan, time_launches, release, stream, torch, dev)
+
+    if want("int4"):
+        # ---- 4 ranks, 1 MiB integer-valued fp32, 4 chunks, one channel, one slice -------
+        N = 262144
+        xs = W.make_inputs("int_f32", N, 4, W.CFG_RING_AR_4R_INT, size_bytes=N * 4)
+        ii = [torch.from_numpy(x).to(dev) for x in xs]
+        oo = [torch.empty(N, device=dev) for _ in range(4)]
+        p4 = make_plan(programs.ring_allreduce(4), N, 1, 512, N * 4)
+        t = time_launches(lambda: p4.execute(ii, oo, N, stream), 100)
+        exact = bool(np.array_equal(oo[0].cpu().numpy(), np.sum(np.stack(xs).astype(np.float64), 0).astype(np.float32)))
+        res["ring_ar_4r_1mib_int"] = {"busbw": round(busbw_ar(N * 4, t, 4), 2), "exact": exact, **stats(p4, N, t)}
+        release(p4)
         del ii, oo
-    res["tree_vs_ring"] = trees
 
-    # ---- tuning under compute interference: bf16 GEMMs on a second stream ----------
-    res["interference"] = interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release)
-    progress("interference done")
+    if want("hier"):
+        # ---- 16 ranks (2 x 8) bf16 hierarchical AllReduce: fused vs three launches -----
+        G, L = 2, 8
+        hier = []
+        fused_prog = programs.hierarchical_allreduce(G, L)
+        stages = (programs.hier_stage_reducescatter_intra(G, L), programs.hier_stage_allreduce_inter(G, L),
+                  programs.hier_stage_allgather_intra(G, L))
+        for S in [(1 << 20) << i for i in range(9)]:  # 1 MiB ... 256 MiB
+            N = S // 2
+            ii = device_inputs("bf16", N, G * L, 3000 + S // (1 << 20))
+            oo = [torch.empty(N, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
+            cf, _ = tune(fused_prog, N, "bf16")
+            pf = make_plan(fused_prog, N, *cf, dtype="bf16")
+            tf = time_launches(lambda: pf.execute(ii, oo, N, stream), 10)
+            sh = N // L
+            mid1 = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
+            mid2 = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
+            c1, _ = tune(stages[0], N, "bf16")
+            c2, _ = tune(stages[1], sh, "bf16")
+            c3, _ = tune(stages[2], sh, "bf16")
+            s1 = make_plan(stages[0], N, *c1, dtype="bf16")
+            s2 = make_plan(stages[1], sh, *c2, dtype="bf16")
+            s3 = make_plan(stages[2], sh, *c3, dtype="bf16")
 
-    # ---- interpreting vs generated kernels, and the lazy loop order ------------------
-    res["kernels"] = kernels(prog, ring_inputs, make_plan, time_launches, release, stream)
-    res["kernels_other"] = kernels_other(programs, device_inputs, make_plan, time_launches, release, stream, torch, dev)
+            def three():
+                s1.execute(ii, mid1, N, stream)
+                s2.execute(mid1, mid2, sh, stream)
+                s3.execute(mid2, oo, sh, stream)
+            t3 = time_launches(three, 10)
+            row = {"bytes_per_rank": S, "fused_config": list(cf), "stage_configs": [list(c1), list(c2), list(c3)],
+                   "fused_us": round(tf * 1e6, 2), "three_launch_us": round(t3 * 1e6, 2),
+                   "fused_busbw": round(busbw_ar(S, tf, G * L), 2), "three_launch_busbw": round(busbw_ar(S, t3, G * L), 2),
+                   "speedup": round(t3 / tf, 3), "fused_hbm_frac": stats(pf, N, tf)["hbm_frac"],
+                   "fused_workgroups": pf.info()["num_workgroups"]}
+            release(pf, s1, s2, s3)
+            hier.append(row)
+            progress(f"hierarchical AllReduce {S >> 20} MiB: fused {row['fused_us']} us, three launches "
+                     f"{row['three_launch_us']} us")
+            del ii, oo, mid1, mid2
+        res["hier_ar_16r_bf16"] = hier
+        progress("hierarchical AllReduce done")
 
-    # ---- 4 ranks, 1 MiB integer-valued fp32, 4 chunks, one channel, one slice -------
-    N = 262144
-    xs = W.make_inputs("int_f32", N, 4, W.CFG_RING_AR_4R_INT, size_bytes=N * 4)
-    ii = [torch.from_numpy(x).to(dev) for x in xs]
-    oo = [torch.empty(N, device=dev) for _ in range(4)]
-    p4 = make_plan(programs.ring_allreduce(4), N, 1, 512, N * 4)
-    t = time_launches(lambda: p4.execute(ii, oo, N, stream), 100)
-    exact = bool(np.array_equal(oo[0].cpu().numpy(), np.sum(np.stack(xs).astype(np.float64), 0).astype(np.float32)))
-    res["ring_ar_4r_1mib_int"] = {"busbw": round(busbw_ar(N * 4, t, 4), 2), "exact": exact, **stats(p4, N, t)}
-    release(p4)
-    del ii, oo
-
-    # ---- 16 ranks (2 x 8) bf16 hierarchical AllReduce: fused vs three launches -----
-    G, L = 2, 8
-    hier = []
-    fused_prog = programs.hierarchical_allreduce(G, L)
-    stages = (programs.hier_stage_reducescatter_intra(G, L), programs.hier_stage_allreduce_inter(G, L),
-              programs.hier_stage_allgather_intra(G, L))
-    for S in (1 << 20, 16 << 20, 64 << 20, 256 << 20):
-        N = S // 2
-        ii = device_inputs("bf16", N, G * L, 3000 + S // (1 << 20))
-        oo = [torch.empty(N, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
-        cf, _ = tune(fused_prog, N, "bf16")
-        pf = make_plan(fused_prog, N, *cf, dtype="bf16")
-        tf = time_launches(lambda: pf.execute(ii, oo, N, stream), 10)
-        sh = N // L
-        mid1 = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
-        mid2 = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
-        c1, _ = tune(stages[0], N, "bf16")
-        c2, _ = tune(stages[1], sh, "bf16")
-        c3, _ = tune(stages[2], sh, "bf16")
-        s1 = make_plan(stages[0], N, *c1, dtype="bf16")
-        s2 = make_plan(stages[1], sh, *c2, dtype="bf16")
-        s3 = make_plan(stages[2], sh, *c3, dtype="bf16")
-
-        def three():
-            s1.execute(ii, mid1, N, stream)
-            s2.execute(mid1, mid2, sh, stream)
-            s3.execute(mid2, oo, sh, stream)
-        t3 = time_launches(three, 10)
-        row = {"bytes_per_rank": S, "fused_config": list(cf), "stage_configs": [list(c1), list(c2), list(c3)],
-               "fused_us": round(tf * 1e6, 2), "three_launch_us": round(t3 * 1e6, 2),
-               "fused_busbw": round(busbw_ar(S, tf, G * L), 2), "three_launch_busbw": round(busbw_ar(S, t3, G * L), 2),
-               "speedup": round(t3 / tf, 3), "fused_hbm_frac": stats(pf, N, tf)["hbm_frac"],
-               "fused_workgroups": pf.info()["num_workgroups"]}
-        release(pf, s1, s2, s3)
-        hier.append(row)
-        del ii, oo, mid1, mid2
-    res["hier_ar_16r_bf16"] = hier
-    progress("hierarchical AllReduce done")
-
-    # ---- 32 ranks (4 x 8) int32 AllToAll: two-phase vs direct ----------------------
-    G, L = 4, 8
-    Pa = G * L
-    a2a = []
-    for S in (1 << 20, 4 << 20, 16 << 20, 64 << 20):
-        N = S // 4
-        ii = device_inputs("i32", N, Pa, 4000 + S // (1 << 20))
-        oo = [torch.empty(N, dtype=torch.int32, device=dev) for _ in range(Pa)]
-        row = {"bytes_per_rank": S}
-        for name, pr in (("two_phase", programs.two_phase_alltoall(G, L)), ("direct", programs.direct_alltoall(Pa))):
-            best = None
-            # direct transport, with and without the streaming variant (whose copies keep
-            # eight vectors per thread in flight)
-            for k, nt, proto in ((1, 256, 2), (2, 256, 2), (2, 128, 2), (4, 128, 2), (1, 256, 3), (2, 256, 3)):
-                try:
-                    pl = make_plan(pr, N, k, nt, 256 << 10, proto, dtype="i32")
-                except capi.CCLError:
-                    continue  # more workgroups than fit at once
-                t = time_launches(lambda: pl.execute(ii, oo, N, stream), 10)
-                if best is None or t < best[0]:
-                    best = (t, k, nt, PROTOCOLS[proto][2], pl.info()["num_workgroups"], stats(pl, N, t)["hbm_frac"])
-                release(pl)
-            if best:
-                t, k, nt, streaming, nwg, hf = best
-                row[name] = {"us": round(t * 1e6, 2), "k": k, "nthreads": nt, "streaming": streaming,
-                             "workgroups": nwg, "hbm_frac": hf, "busbw": round(S / t * (Pa - 1) / Pa / 1e9, 2)}
-                if name == "two_phase":
-                    # with k > 1 every operation is split per chunk, so the phase-2 transfer of
-                    # a gather region becomes one transfer per block instead of one batch
-                    row[name]["phase2_batched"] = k == 1
-        a2a.append(row)
-        del ii, oo
-        release()
-    res["alltoall_32r_int32"] = a2a
-    progress("AllToAll done")
-
-    # ---- 24 ranks (3 x 8): AllToNext split / unsplit, HPDS+state vs RR+connection ---
-    G, L = 3, 8
-    Pn = G * L
-    a2n = []
-    for S in (16 << 20, 64 << 20, 128 << 20):
-        N = S // 4
-        ii = device_inputs("f32", N, Pn, 5000 + S // (1 << 20))
-        oo = [torch.empty(N, device=dev) for _ in range(Pn)]
-        row = {"bytes_per_rank": S}
-        for split in (True, False):
-            modes = (("hpds", "state"), ("rr", "connection"))
-            # one launch configuration for both modes (256 threads, 128 KiB slices, direct
-            # transport with streaming hints: the best of a sweep at 64 MiB, where 256
-            # threads let the split program's 1120-1248 workgroups of k = 16 fit at once)
-            k, pls = fitting([lambda k, sc=sc, al=al: make_plan(programs.alltonext(G, L, split=split), N, k, 256,
-                                                                  128 << 10, 3, scheduler=sc, wg_alloc=al)
-                              for sc, al in modes], ks=(16, 8, 4, 2, 1))
-            for (sched, alloc), pl in zip(modes, pls):
-                t = time_launches(lambda: pl.execute(ii, oo, N, stream), 10)
-                row[f"{'split' if split else 'unsplit'}_{sched}_{alloc}"] = {
-                    "us": round(t * 1e6, 2), "algbw": round(S / t / 1e9, 2), "k": k,
-                    "workgroups": pl.info()["num_workgroups"], "hbm_frac": stats(pl, N, t)["hbm_frac"]}
-            release(*pls)
-        a2n.append(row)
-        del ii, oo
-        release()
-    res["alltonext_24r"] = a2n
-    progress("AllToNext done")
-
-    # AllGather / ReduceScatter on the same 24 ranks, 128 MiB (the larger buffer)
-    n_big = Pn * ((32 << 20) // Pn)  # 33,554,424 fp32
-    agrs = {}
-    for coll in ("allgather", "reducescatter"):
-        for variant in ("ring", "2d"):
-            if coll == "allgather":
-                pr = programs.ring_allgather(Pn) if variant == "ring" else programs.allgather_2d(G, L)
-                count, nout = n_big // Pn, n_big
-            else:
-                pr = programs.ring_reducescatter(Pn) if variant == "ring" else programs.reducescatter_2d(G, L)
-                count, nout = n_big, n_big // Pn
-            ii = device_inputs("f32", count, Pn, 6000 + len(coll))
-            oo = [torch.empty(nout, device=dev) for _ in range(Pn)]
-            modes = (("hpds", "state"), ("rr", "connection"))
-            Sb = n_big * 4
-            if variant == "ring":
-                # one launch configuration for both modes (512 threads, 64 KiB slices, direct
-                # transport with streaming hints: the best of a sweep of the ring at this size)
-                k, pls = fitting([lambda k, sc=sc, al=al: make_plan(pr, count, k, 512, 64 << 10, 3, scheduler=sc,
-                                                                      wg_alloc=al) for sc, al in modes],
-                                 ks=(32, 16, 8, 4, 2, 1))
-                for (sched, alloc), pl in zip(modes, pls):
-                    t = time_launches(lambda: pl.execute(ii, oo, count, stream), 5)
-                    agrs[f"{coll}_{variant}_{sched}_{alloc}"] = {
-                        "us": round(t * 1e6, 2), "busbw": round(Sb / t * (Pn - 1) / Pn / 1e9, 2), "k": k,
-                        "workgroups": pl.info()["num_workgroups"], "hbm_frac": stats(pl, count, t)["hbm_frac"]}
-                release(*pls)
-            else:
-                # each mode at its best point of one small sweep: state-based allocation needs
-                # half the workgroups, so it reaches channel counts whose connection-based
-                # grid would not fit on the device at once
-                for sched, alloc in modes:
-                    best = None
-                    for k, nt in ((4, 512), (8, 512), (8, 256), (16, 256), (16, 128)):
-                        try:
-                            pl = make_plan(pr, count, k, nt, 64 << 10, 3, scheduler=sched, wg_alloc=alloc)
-                        except capi.CCLError:
-                            continue  # more workgroups than fit at once
-                        t = time_launches(lambda: pl.execute(ii, oo, count, stream), 5)
-                        if best is None or t < best[0]:
-                            best = (t, k, nt, pl.info()["num_workgroups"], stats(pl, count, t)["hbm_frac"])
-                        release(pl)
-                    t, k, nt, nwg, hf = best
-                    agrs[f"{coll}_{variant}_{sched}_{alloc}"] = {
-                        "us": round(t * 1e6, 2), "busbw": round(Sb / t * (Pn - 1) / Pn / 1e9, 2), "k": k,
-                        "nthreads": nt, "workgroups": nwg, "hbm_frac": hf}
+    if want("alltoall"):
+        # ---- 32 ranks (4 x 8) int32 AllToAll: two-phase vs direct ----------------------
+        G, L = 4, 8
+        Pa = G * L
+        a2a = []
+        for S in [(1 << 20) << i for i in range(7)]:  # 1 MiB ... 64 MiB
+            N = S // 4
+            ii = device_inputs("i32", N, Pa, 4000 + S // (1 << 20))
+            oo = [torch.empty(N, dtype=torch.int32, device=dev) for _ in range(Pa)]
+            row = {"bytes_per_rank": S}
+            for name, pr in (("two_phase", programs.two_phase_alltoall(G, L)), ("direct", programs.direct_alltoall(Pa))):
+                best = None
+                # direct transport, with and without the streaming variant (whose copies keep
+                # eight vectors per thread in flight)
+                for k, nt, proto in ((1, 256, 2), (2, 256, 2), (2, 128, 2), (4, 128, 2), (1, 256, 3), (2, 256, 3)):
+                    try:
+                        pl = make_plan(pr, N, k, nt, 256 << 10, proto, dtype="i32")
+                    except capi.CCLError:
+                        continue  # more workgroups than fit at once
+                    t = time_launches(lambda: pl.execute(ii, oo, N, stream), 10)
+                    if best is None or t < best[0]:
+                        best = (t, k, nt, PROTOCOLS[proto][2], pl.info()["num_workgroups"], stats(pl, N, t)["hbm_frac"])
+                    release(pl)
+                if best:
+                    t, k, nt, streaming, nwg, hf = best
+                    row[name] = {"us": round(t * 1e6, 2), "k": k, "nthreads": nt, "streaming": streaming,
+                                 "workgroups": nwg, "hbm_frac": hf, "busbw": round(S / t * (Pa - 1) / Pa / 1e9, 2)}
+                    if name == "two_phase":
+                        # with k > 1 every operation is split per chunk, so the phase-2 transfer of
+                        # a gather region becomes one transfer per block instead of one batch
+                        row[name]["phase2_batched"] = k == 1
+            a2a.append(row)
+            progress(f"AllToAll {S >> 20} MiB: " + ", ".join(f"{m} {row[m]['us']} us" for m in ("two_phase", "direct")
+                                                               if m in row))
             del ii, oo
             release()
-    res["allgather_reducescatter_24r_128mib"] = agrs
-    progress("AllGather / ReduceScatter done")
+        res["alltoall_32r_int32"] = a2a
+        progress("AllToAll done")
 
-    # ---- workgroup idle fraction from the device trace (one traced launch) ----------
-    def idle(pr, N, dtype, k, nt, sl, proto, kern, ii, oo, **kw):
-        k, (pl,) = fitting([lambda kk: make_plan(pr, N, kk, nt, sl, proto, kern, dtype=dtype, trace=True, **kw)],
-                           ks=[x for x in (k, 8, 4, 2, 1) if x <= k])
-        for _ in range(3):
-            pl.execute(ii, oo, N, stream)
-        torch.cuda.synchronize()
-        recs = [r for r in pl.trace() if r[3] > 0]
-        t0 = min(r[0] for r in recs)
-        span = max(r[1] for r in recs) - t0
-        # waiting on flags, plus the time a workgroup is not yet started or already done
-        fr = [(r[2] + (r[0] - t0) + (t0 + span - r[1])) / span for r in recs]
-        out = {"workgroups": len(recs), "k": k, "mean": round(float(np.mean(fr)), 4),
-               "max": round(float(np.max(fr)), 4)}
-        release(pl)
-        return out
+    if want("alltonext"):
+        # ---- 24 ranks (3 x 8): AllToNext split / unsplit, HPDS+state vs RR+connection ---
+        G, L = 3, 8
+        Pn = G * L
+        a2n = []
+        for S in (16 << 20, 32 << 20, 64 << 20, 128 << 20):
+            N = S // 4
+            ii = device_inputs("f32", N, Pn, 5000 + S // (1 << 20))
+            oo = [torch.empty(N, device=dev) for _ in range(Pn)]
+            row = {"bytes_per_rank": S}
+            for split in (True, False):
+                modes = (("hpds", "state"), ("rr", "connection"))
+                # one launch configuration for both modes (256 threads, 128 KiB slices, direct
+                # transport with streaming hints: the best of a sweep at 64 MiB, where 256
+                # threads let the split program's 1120-1248 workgroups of k = 16 fit at once)
+                k, pls = fitting([lambda k, sc=sc, al=al: make_plan(programs.alltonext(G, L, split=split), N, k, 256,
+                                                                      128 << 10, 3, scheduler=sc, wg_alloc=al)
+                                  for sc, al in modes], ks=(16, 8, 4, 2, 1))
+                for (sched, alloc), pl in zip(modes, pls):
+                    t = time_launches(lambda: pl.execute(ii, oo, N, stream), 10)
+                    row[f"{'split' if split else 'unsplit'}_{sched}_{alloc}"] = {
+                        "us": round(t * 1e6, 2), "algbw": round(S / t / 1e9, 2), "k": k,
+                        "workgroups": pl.info()["num_workgroups"], "hbm_frac": stats(pl, N, t)["hbm_frac"]}
+                release(*pls)
+            a2n.append(row)
+            progress(f"AllToNext {S >> 20} MiB done")
+            del ii, oo
+            release()
+        res["alltonext_24r"] = a2n
+        progress("AllToNext done")
 
-    N, ii, oo = ring_inputs(HEADLINE_BYTES)
-    c, _ = tune(prog, N, kernel=KERNEL, factors=ring_factors(HEADLINE_BYTES))
-    idle_rows = {"ring_ar_8r_3mib_tuned": idle(prog, N, "f32", *c, ii, oo)}
-    del ii, oo
-    N = (64 << 20) // 4
-    ii = device_inputs("f32", N, Pn, 5064)
-    oo = [torch.empty(N, device=dev) for _ in range(Pn)]
-    for sched, alloc in (("hpds", "state"), ("rr", "connection")):
-        idle_rows[f"alltonext_24r_64mib_split_{sched}_{alloc}"] = idle(
-            programs.alltonext(G, L, split=True), N, "f32", 8, 512, 256 << 10, 2, KERNEL, ii, oo, scheduler=sched,
-            wg_alloc=alloc)
-    del ii, oo
-    release()
-    res["wg_idle_fraction"] = idle_rows
+    if want("agrs"):
+        G, L = 3, 8
+        Pn = G * L
+        # AllGather / ReduceScatter on the same 24 ranks, 128 MiB (the larger buffer)
+        n_big = Pn * ((32 << 20) // Pn)  # 33,554,424 fp32
+        agrs = {}
+        for coll in ("allgather", "reducescatter"):
+            for variant in ("ring", "2d"):
+                if coll == "allgather":
+                    pr = programs.ring_allgather(Pn) if variant == "ring" else programs.allgather_2d(G, L)
+                    count, nout = n_big // Pn, n_big
+                else:
+                    pr = programs.ring_reducescatter(Pn) if variant == "ring" else programs.reducescatter_2d(G, L)
+                    count, nout = n_big, n_big // Pn
+                ii = device_inputs("f32", count, Pn, 6000 + len(coll))
+                oo = [torch.empty(nout, device=dev) for _ in range(Pn)]
+                modes = (("hpds", "state"), ("rr", "connection"))
+                Sb = n_big * 4
+                if variant == "ring":
+                    # one launch configuration for both modes (512 threads, 64 KiB slices, direct
+                    # transport with streaming hints: the best of a sweep of the ring at this size)
+                    k, pls = fitting([lambda k, sc=sc, al=al: make_plan(pr, count, k, 512, 64 << 10, 3, scheduler=sc,
+                                                                          wg_alloc=al) for sc, al in modes],
+                                     ks=(32, 16, 8, 4, 2, 1))
+                    for (sched, alloc), pl in zip(modes, pls):
+                        t = time_launches(lambda: pl.execute(ii, oo, count, stream), 5)
+                        agrs[f"{coll}_{variant}_{sched}_{alloc}"] = {
+                            "us": round(t * 1e6, 2), "busbw": round(Sb / t * (Pn - 1) / Pn / 1e9, 2), "k": k,
+                            "workgroups": pl.info()["num_workgroups"], "hbm_frac": stats(pl, count, t)["hbm_frac"]}
+                    release(*pls)
+                else:
+                    # each mode at its best point of one small sweep: state-based allocation needs
+                    # half the workgroups, so it reaches channel counts whose connection-based
+                    # grid would not fit on the device at once
+                    for sched, alloc in modes:
+                        best = None
+                        for k, nt in ((4, 512), (8, 512), (8, 256), (16, 256), (16, 128)):
+                            try:
+                                pl = make_plan(pr, count, k, nt, 64 << 10, 3, scheduler=sched, wg_alloc=alloc)
+                            except capi.CCLError:
+                                continue  # more workgroups than fit at once
+                            t = time_launches(lambda: pl.execute(ii, oo, count, stream), 5)
+                            if best is None or t < best[0]:
+                                best = (t, k, nt, pl.info()["num_workgroups"], stats(pl, count, t)["hbm_frac"])
+                            release(pl)
+                        t, k, nt, nwg, hf = best
+                        agrs[f"{coll}_{variant}_{sched}_{alloc}"] = {
+                            "us": round(t * 1e6, 2), "busbw": round(Sb / t * (Pn - 1) / Pn / 1e9, 2), "k": k,
+                            "nthreads": nt, "workgroups": nwg, "hbm_frac": hf}
+                del ii, oo
+                release()
+        res["allgather_reducescatter_24r_128mib"] = agrs
+        progress("AllGather / ReduceScatter done")
 
-    # ---- practical streaming ceiling: a plain copy kernel, 1 GiB (beyond every cache) --
-    nb = 1 << 30
-    a = torch.empty(nb, dtype=torch.uint8, device=dev)
-    b = torch.empty(nb, dtype=torch.uint8, device=dev)
-    tc = time_launches(lambda: capi.ccl_copy_probe(b.data_ptr(), a.data_ptr(), nb, 256, 256, stream.cuda_stream), 10)
-    res["copy_probe_GBs"] = round(2 * nb / tc / 1e9, 1)
-    del a, b
-    release()
+    if want("idle"):
+        G, L = 3, 8
+        Pn = G * L
+        # ---- workgroup idle fraction from the device trace (one traced launch) ----------
+        def idle(pr, N, dtype, k, nt, sl, proto, kern, ii, oo, **kw):
+            k, (pl,) = fitting([lambda kk: make_plan(pr, N, kk, nt, sl, proto, kern, dtype=dtype, trace=True, **kw)],
+                               ks=[x for x in (k, 8, 4, 2, 1) if x <= k])
+            for _ in range(3):
+                pl.execute(ii, oo, N, stream)
+            torch.cuda.synchronize()
+            recs = [r for r in pl.trace() if r[3] > 0]
+            t0 = min(r[0] for r in recs)
+            span = max(r[1] for r in recs) - t0
+            # waiting on flags, plus the time a workgroup is not yet started or already done
+            fr = [(r[2] + (r[0] - t0) + (t0 + span - r[1])) / span for r in recs]
+            out = {"workgroups": len(recs), "k": k, "mean": round(float(np.mean(fr)), 4),
+                   "max": round(float(np.max(fr)), 4)}
+            release(pl)
+            return out
+
+        N, ii, oo = ring_inputs(HEADLINE_BYTES)
+        c, _ = tune(prog, N, kernel=KERNEL, factors=ring_factors(HEADLINE_BYTES))
+        idle_rows = {"ring_ar_8r_3mib_tuned": idle(prog, N, "f32", *c, ii, oo)}
+        del ii, oo
+        N = (64 << 20) // 4
+        ii = device_inputs("f32", N, Pn, 5064)
+        oo = [torch.empty(N, device=dev) for _ in range(Pn)]
+        for sched, alloc in (("hpds", "state"), ("rr", "connection")):
+            idle_rows[f"alltonext_24r_64mib_split_{sched}_{alloc}"] = idle(
+                programs.alltonext(G, L, split=True), N, "f32", 8, 512, 256 << 10, 2, KERNEL, ii, oo, scheduler=sched,
+                wg_alloc=alloc)
+        del ii, oo
+        release()
+        res["wg_idle_fraction"] = idle_rows
+
+    if want("copy"):
+        # ---- practical streaming ceiling: a plain copy kernel, 1 GiB (beyond every cache) --
+        nb = 1 << 30
+        a = torch.empty(nb, dtype=torch.uint8, device=dev)
+        b = torch.empty(nb, dtype=torch.uint8, device=dev)
+        tc = time_launches(lambda: capi.ccl_copy_probe(b.data_ptr(), a.data_ptr(), nb, 256, 256, stream.cuda_stream), 10)
+        res["copy_probe_GBs"] = round(2 * nb / tc / 1e9, 1)
+        del a, b
+        release()
+
     return res
 
 
