@@ -45,7 +45,7 @@ TUNE_SLICES = [(4 << 10) << i for i in range(11)]  # 4 KiB ... 4 MiB
 PROTOCOLS = {0: ("simple", "staged", False), 1: ("ll", "staged", False), 2: ("simple", "direct", False),
              3: ("simple", "direct", True)}
 # parts of the long measurements, in the order --extras runs them
-EXTRA_SECTIONS = ["sweep", "ranks", "trees", "interference", "kernels", "int4", "hier", "alltoall", "alltonext", "agrs",
+EXTRA_SECTIONS = ["sweep", "sweep_k", "ranks", "trees", "interference", "kernels", "int4", "hier", "alltoall", "alltonext", "agrs",
                   "idle", "copy"]
 DEVICE_INPUT_BYTES = 32 << 20  # at or above this many bytes per rank, inputs are drawn on the device
 # executor kernels: the interpreting kernel, a kernel generated for the plan, and the
@@ -110,11 +110,26 @@ def same_launch(a, b, piece_bytes):
     return a[2] == b[2] or (a[2] >= piece_bytes and b[2] >= piece_bytes)
 
 
-def largest_piece(N, P, k):
+def instance_bounds(lo, hi, k, align):
+    """Bounds of the k instance pieces of the element range [lo, hi): lo plus floor(i (hi
+    - lo) / k) rounded down to a multiple of align, and hi last (the rule the plan
+    compiler lowers with)."""
+    b = [lo]
+    for i in range(1, k):
+        f = i * (hi - lo) // k
+        b.append(lo + f - f % align)
+    return b + [hi]
+
+
+def largest_piece(N, P, k, align=4):
     """Elements of the largest instruction piece of a ring AllReduce of N elements per
-    rank over P ranks at factor k: P program chunks, each cut into k instance
-    sub-chunks, both at floor(i N / C) boundaries."""
-    return -(-(-(-N // P)) // k)
+    rank over P ranks at factor k: P program chunks at floor(j N / P), each cut into k
+    instance pieces (instance_bounds; align: elements per 16 bytes)."""
+    best = 0
+    for j in range(P):
+        b = instance_bounds(j * N // P, (j + 1) * N // P, k, align)
+        best = max(best, max(b[i + 1] - b[i] for i in range(k)))
+    return best
 
 
 def progress(msg):
@@ -568,6 +583,25 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
             release(p)
             del ii, oo
         res["sweep"] = sweep
+
+    if want("sweep_k"):
+        # every (size, parallelization factor) pair of the 8-rank ring sweep, with threads,
+        # slice size and protocol tuned at that factor
+        grid = []
+        for S in SWEEP:
+            N, ii, oo = ring_inputs(S)
+            for k in CONFIG_FACTORS:
+                c, _ = tune(prog, N, kernel=KERNEL, factors=[k])
+                p = make_plan(prog, N, *c)
+                t = time_launches(lambda: p.execute(ii, oo, N, stream), 50)
+                grid.append({"bytes_per_rank": S, "k": k, "nthreads": c[1], "slice_bytes": c[2],
+                             "protocol": PROTOCOLS[c[3]][0], "transport": PROTOCOLS[c[3]][1],
+                             "busbw": round(busbw_ar(S, t), 2), **stats(p, N, t)})
+                release(p)
+            progress(f"ring AR 8 ranks {S >> 10} KiB by factor: " +
+                     ", ".join(f"k={r['k']} {r['us']} us" for r in grid if r["bytes_per_rank"] == S))
+            del ii, oo
+        res["sweep_by_factor"] = grid
 
     if want("ranks"):
         res["ring_ar_rank_counts"] = rank_counts(np, torch, programs, dev, stream, device_inputs, tune, make_plan,

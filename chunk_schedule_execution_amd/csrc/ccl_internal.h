@@ -26,11 +26,25 @@ inline int64_t chunk_bound(int64_t j, int64_t N, int64_t C) { return (j * N) / C
 struct Range {
   int64_t lo = 0, len = 0;
 };
-inline Range op_range(int idx, int cnt, int instance, int k, int64_t N, int64_t C) {
+// Bound i (0..k) of the k instance pieces of the element range [lo, hi): lo plus
+// floor(i (hi - lo) / k) rounded down to a multiple of `align` elements (16 bytes), and
+// hi for i = k. Which chain an element follows is decided by its program chunk alone, so
+// these bounds change no result. The offsets depend on the range's length only: the
+// two ends of a transfer (equal lengths, possibly different 16-byte phases, as an input
+// shard and the output) get the same pieces, so their slice flags pair up. When the
+// range starts on the 16-byte grid so does every piece (at 8 ranks and 1 MiB, k = 24
+// cuts 32,768-element chunks into pieces of 1365.3 elements). A piece is at most
+// align - 1 elements longer than ceil((hi - lo) / k).
+inline int64_t instance_bound(int i, int k, int64_t lo, int64_t hi, int align) {
+  if (i <= 0) return lo;
+  if (i >= k) return hi;
+  const int64_t f = (int64_t(i) * (hi - lo)) / k;
+  return lo + f - f % align;
+}
+inline Range op_range(int idx, int cnt, int instance, int k, int64_t N, int64_t C, int align) {
   int64_t lo = chunk_bound(idx, N, C), hi = chunk_bound(idx + cnt, N, C);
   if (k > 1) {
-    int64_t len = hi - lo;
-    int64_t a = lo + (instance * len) / k, b = lo + ((instance + 1) * len) / k;
+    const int64_t a = instance_bound(instance, k, lo, hi, align), b = instance_bound(instance + 1, k, lo, hi, align);
     return {a, b - a};
   }
   return {lo, hi - lo};

@@ -946,7 +946,9 @@ void lower(HostPlan& hp) {
   int64_t off = 0;
   for (int x = 0; x < nX; ++x) {
     const Xfer& X = hp.xf[x];
-    int64_t cap = (k == 1) ? (int64_t(X.cnt) * M) / hp.C + 2 : (M / hp.C + 2) / k + 2;
+    // k > 1: a piece is at most ceil(chunk / k) plus 16 bytes' worth of elements (its
+    // bounds are rounded to the 16-byte grid)
+    int64_t cap = (k == 1) ? (int64_t(X.cnt) * M) / hp.C + 2 : (M / hp.C + 2) / k + 2 + 16 / hp.esz;
     int64_t bytes = ((cap + 16) * hp.esz + 255) / 256 * 256;
     if (hp.cfg.flags & CCL_FLAG_LL) bytes *= 2;  // every 4 data bytes travel with a 4-byte flag
     if (X.direct) bytes = 0;                     // written straight into the receiver's buffer
@@ -1065,7 +1067,7 @@ int64_t plan_bytes(const HostPlan& hp, int64_t count) {
     const DevInstr& D = hp.dins[j];
     // waits for data the sender already placed (or, skipped, not even that)
     if ((D.op & (OPB_RECV | OPB_LOCAL_IN | OPB_SRCB | OPB_DSTA | OPB_SEND)) == (OPB_RECV | OPB_LOCAL_IN)) continue;
-    Range r = op_range(D.pad0, D.cnt, D.instance, hp.k, count, hp.C);
+    Range r = op_range(D.pad0, D.cnt, D.instance, hp.k, count, hp.C, 16 / hp.esz);
     // slot reads and writes carry one flag byte per data byte under the LL protocol
     const int slot = (hp.cfg.flags & CCL_FLAG_LL) ? 2 : 1;
     int ops = ((D.op & OPB_RECV) ? slot : 1) + ((D.op & OPB_SRCB) ? 1 : 0) + ((D.op & OPB_DSTA) ? 1 : 0) +
@@ -1087,7 +1089,7 @@ void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec
     const DevXfer& X = hp.dxf[x];
     if (ll) return int64_t(X.slot_off);
     int64_t ph = 0;
-    if (X.phase_idx >= 0) ph = op_range(X.phase_idx, X.cnt, X.instance, hp.k, count, hp.C).lo % V;
+    if (X.phase_idx >= 0) ph = op_range(X.phase_idx, X.cnt, X.instance, hp.k, count, hp.C, 16 / hp.esz).lo % V;
     return int64_t(X.slot_off) + ph * hp.esz;
   };
   for (size_t j = 0; j < hp.dins.size(); ++j) {
@@ -1104,7 +1106,7 @@ void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec
     E.done_flag = D.done_flag;
     E.wait_begin = D.wait_begin;
     E.nwaits = D.nwaits;
-    E.len = op_range(D.pad0, D.cnt, D.instance, hp.k, count, hp.C).len;
+    E.len = op_range(D.pad0, D.cnt, D.instance, hp.k, count, hp.C, 16 / hp.esz).len;
     const int64_t nsl = E.len == 0 ? 0 : (E.len + hp.slice_elems - 1) / hp.slice_elems;
     if (nsl >= (int64_t(1) << kEpochShift)) fail(CCL_ERR_INVALID_ARGUMENT, "too many slices for one transfer");
     E.nsl = int32_t(nsl);
@@ -1113,11 +1115,11 @@ void compute_exec_records(const HostPlan& hp, int64_t count, std::vector<DevExec
     if ((D.op & OPB_RECV) && !(D.op & OPB_LOCAL_IN))
       E.a_off = slot_off(D.xin);
     else
-      E.a_off = op_range(D.a_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
-    if (D.op & OPB_SRCB) E.b_off = op_range(D.b_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
-    if (D.op & OPB_DSTA) E.d_off = op_range(D.d_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz;
+      E.a_off = op_range(D.a_idx, D.cnt, D.instance, hp.k, count, hp.C, 16 / hp.esz).lo * hp.esz;
+    if (D.op & OPB_SRCB) E.b_off = op_range(D.b_idx, D.cnt, D.instance, hp.k, count, hp.C, 16 / hp.esz).lo * hp.esz;
+    if (D.op & OPB_DSTA) E.d_off = op_range(D.d_idx, D.cnt, D.instance, hp.k, count, hp.C, 16 / hp.esz).lo * hp.esz;
     if (D.op & OPB_SEND)
-      E.t_off = D.t_buf >= 0 ? op_range(D.t_idx, D.cnt, D.instance, hp.k, count, hp.C).lo * hp.esz : slot_off(D.xout);
+      E.t_off = D.t_buf >= 0 ? op_range(D.t_idx, D.cnt, D.instance, hp.k, count, hp.C, 16 / hp.esz).lo * hp.esz : slot_off(D.xout);
     out[j] = E;
   }
 }

@@ -84,12 +84,12 @@ void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
     for (size_t j = 0; j < hp.dins.size(); ++j) {
       const DevInstr& D = hp.dins[j];
       Geo g{};
-      g.len = op_range(D.pad0, D.cnt, D.instance, hp.k, N, hp.C).len;
+      g.len = op_range(D.pad0, D.cnt, D.instance, hp.k, N, hp.C, 16 / hp.esz).len;
       const bool local_a = !(D.op & OPB_RECV) || (D.op & OPB_LOCAL_IN);
-      if (local_a) g.alo = op_range(D.a_idx, D.cnt, D.instance, hp.k, N, hp.C).lo;
-      if (D.t_buf >= 0) g.tlo = op_range(D.t_idx, D.cnt, D.instance, hp.k, N, hp.C).lo;
-      if (D.op & OPB_SRCB) g.blo = op_range(D.b_idx, D.cnt, D.instance, hp.k, N, hp.C).lo;
-      if (D.op & OPB_DSTA) g.dlo = op_range(D.d_idx, D.cnt, D.instance, hp.k, N, hp.C).lo;
+      if (local_a) g.alo = op_range(D.a_idx, D.cnt, D.instance, hp.k, N, hp.C, 16 / hp.esz).lo;
+      if (D.t_buf >= 0) g.tlo = op_range(D.t_idx, D.cnt, D.instance, hp.k, N, hp.C, 16 / hp.esz).lo;
+      if (D.op & OPB_SRCB) g.blo = op_range(D.b_idx, D.cnt, D.instance, hp.k, N, hp.C, 16 / hp.esz).lo;
+      if (D.op & OPB_DSTA) g.dlo = op_range(D.d_idx, D.cnt, D.instance, hp.k, N, hp.C, 16 / hp.esz).lo;
       g.nsl = (g.len + se - 1) / se;
       geo[j] = g;
       if ((D.op & OPB_SEND) && D.t_buf < 0) slot[D.xout].assign(g.len, Val{});

@@ -3,23 +3,28 @@
 import bench
 
 
-def _pieces(N, P, k):
-    """Element counts of the instance sub-chunks of a ring AllReduce over P ranks: chunk
-    j of P covers [floor(j N / P), floor((j + 1) N / P)), and instance i of k takes the
-    same floor partition of that chunk."""
-    out = []
-    for j in range(P):
-        a, b = j * N // P, (j + 1) * N // P
-        n = b - a
-        out += [(i + 1) * n // k - i * n // k for i in range(k)]
-    return out
-
-
-def test_largest_piece_bound_is_attained_and_never_exceeded():
-    for N in (786432, 786432 + 5, 262144, 8 * 24 * 7 + 191, 1000003):
-        for P in (4, 8):
+def test_instance_pieces_tile_each_chunk_on_the_16_byte_grid():
+    """Pieces cover each program chunk exactly, in order; every offset from the chunk's
+    start but its length is a multiple of the alignment, so equal-length chunks get equal
+    pieces; no piece exceeds ceil(len / k) + align - 1."""
+    for N in (786432, 786432 + 5, 262144, 8 * 24 * 7 + 191, 1000003, 33554424):
+        for P in (4, 8, 24):
             for k in (1, 2, 4, 8, 16, 24, 32):
-                assert max(_pieces(N, P, k)) == bench.largest_piece(N, P, k), (N, P, k)
+                for align in (4, 8):
+                    for j in range(P):
+                        lo, hi = j * N // P, (j + 1) * N // P
+                        b = bench.instance_bounds(lo, hi, k, align)
+                        assert b[0] == lo and b[-1] == hi and len(b) == k + 1
+                        assert all(b[i] <= b[i + 1] for i in range(k))
+                        assert all((x - lo) % align == 0 for x in b[:-1])
+                        assert [x - lo for x in b] == [x for x in bench.instance_bounds(0, hi - lo, k, align)]
+                        assert max(b[i + 1] - b[i] for i in range(k)) <= -(-(hi - lo) // k) + align - 1
+
+
+def test_largest_piece_of_the_headline():
+    assert bench.largest_piece(786432, 8, 24) == 4096   # 3 MiB per rank: 98,304-element chunks / 24
+    assert bench.largest_piece(262144, 8, 24) == 1368   # 1 MiB: 1365.3 elements, bounds on the 4-element grid
+    assert bench.largest_piece(786432, 8, 32) == 3072
 
 
 def test_same_launch_treats_slices_covering_the_piece_as_one():

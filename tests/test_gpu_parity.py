@@ -339,11 +339,11 @@ def test_24r_ring_at_three_workgroups_per_cu(coll):
 @pytest.mark.parametrize("kernel", ["interpreter", "specialized"])
 @pytest.mark.parametrize("transport", ["staged", "direct"])
 def test_reducescatter_shards_off_the_16_byte_grid_streaming(dtype, kernel, transport):
-    """ReduceScatter whose shards are no multiple of 16 bytes, streaming variant: a
-    reducing slice whose operands sit at different 16-byte phases (staged: every hop's
-    slot against the input chunk; direct: the last hop's input against the output)
-    goes element by element with eight elements per thread in flight, and the last pass
-    of a piece is partial. Chain order, bit for bit, two launches on different inputs."""
+    """ReduceScatter whose shards are no multiple of 16 bytes, streaming variant: the
+    last hop of every chain reads at the shard's phase (slot or landing, and the input)
+    and writes the output at 0, so it goes element by element with eight elements per
+    thread in flight, and the last pass of a piece is partial. Chain order, bit for bit,
+    two launches on different inputs."""
     P, n = 5, 3 * 2048 + 7
     N = P * n
     case(f"reducescatter off-grid shards {dtype} {kernel} {transport} streaming")
