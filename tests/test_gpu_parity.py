@@ -124,6 +124,25 @@ def test_ring_edge_shapes(P, N, k):
         assert_all_equal(ys, (xs[0].astype(np.float64) + xs[1].astype(np.float64)).astype(np.float32))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("knobs", [dict(transport="staged", kernel="interpreter"),
+                                   dict(transport="direct", kernel="specialized"),
+                                   dict(protocol="ll", kernel="specialized")])
+@pytest.mark.parametrize("N", [8 * 10, 8 * 37 + 3])
+def test_ring_instances_shorter_than_the_16_byte_grid(dtype, knobs, N):
+    """Instance bounds sit on the 16-byte grid of their chunk, so with chunks of a few
+    elements and k = 24 most pieces are empty and the rest hold a multiple of 16 bytes'
+    worth (the last one the remainder). Chain order, bit for bit, three launches."""
+    P = 8
+    case(f"ring AR tiny chunks N={N} k=24 {dtype} {knobs}")
+    kind = "normal_f32" if dtype == "f32" else "normal_bf16"
+    xs = W.make_inputs(kind, N, P, W.CFG_RING_AR_8R, size_bytes=N * 4 + 3)
+    chk = chk_ring(P, dtype)
+    ys, _ = _run(programs.ring_allreduce(P), xs, dtype, k=24, nthreads=128, slice_bytes=4096, repeat=3, check=chk,
+                 **knobs)
+    chk(ys, xs, None)
+
+
 def test_ring_subnormals_are_kept():
     P, N = 8, 4096
     case("ring AR subnormal inputs")
