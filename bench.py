@@ -555,12 +555,12 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
     """The long measurements, by section (all of them when sections is None)."""
     res = {}
 
-    def want(name):
+    def section_on(name):
         return sections is None or name in sections
 
     prog = programs.ring_allreduce(P)
 
-    if want("sweep"):
+    if section_on("sweep"):
         # ---- the rest of the 8-rank sweep and the large sizes, each tuned ---------------
         sweep = []
         for S in SWEEP + [128 << 20]:
@@ -584,7 +584,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
             del ii, oo
         res["sweep"] = sweep
 
-    if want("sweep_k"):
+    if section_on("sweep_k"):
         # every (size, parallelization factor) pair of the 8-rank ring sweep, with threads,
         # slice size and protocol tuned at that factor
         grid = []
@@ -603,11 +603,11 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
             del ii, oo
         res["sweep_by_factor"] = grid
 
-    if want("ranks"):
+    if section_on("ranks"):
         res["ring_ar_rank_counts"] = rank_counts(np, torch, programs, dev, stream, device_inputs, tune, make_plan,
                                                  time_launches, busbw_ar, stats, release)
 
-    if want("trees"):
+    if section_on("trees"):
         # ---- tree versus ring AllReduce at small sizes, and the tuner choosing -----------
         from oracle import schedule_order as O2
         trees = []
@@ -637,17 +637,17 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
             del ii, oo
         res["tree_vs_ring"] = trees
 
-    if want("interference"):
+    if section_on("interference"):
         # ---- tuning under compute interference: bf16 GEMMs on a second stream ----------
         res["interference"] = interference(torch, dev, stream, prog, ring_inputs, tune, make_plan, busbw_ar, release)
         progress("interference done")
 
-    if want("kernels"):
+    if section_on("kernels"):
         # ---- interpreting vs generated kernels, and the lazy loop order ------------------
         res["kernels"] = kernels(prog, ring_inputs, make_plan, time_launches, release, stream)
         res["kernels_other"] = kernels_other(programs, device_inputs, make_plan, time_launches, release, stream, torch, dev)
 
-    if want("int4"):
+    if section_on("int4"):
         # ---- 4 ranks, 1 MiB integer-valued fp32, 4 chunks, one channel, one slice -------
         N = 262144
         xs = W.make_inputs("int_f32", N, 4, W.CFG_RING_AR_4R_INT, size_bytes=N * 4)
@@ -660,7 +660,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         release(p4)
         del ii, oo
 
-    if want("hier"):
+    if section_on("hier"):
         # ---- 16 ranks (2 x 8) bf16 hierarchical AllReduce: fused vs three launches -----
         G, L = 2, 8
         hier = []
@@ -702,7 +702,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         res["hier_ar_16r_bf16"] = hier
         progress("hierarchical AllReduce done")
 
-    if want("alltoall"):
+    if section_on("alltoall"):
         # ---- 32 ranks (4 x 8) int32 AllToAll: two-phase vs direct ----------------------
         G, L = 4, 8
         Pa = G * L
@@ -741,7 +741,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         res["alltoall_32r_int32"] = a2a
         progress("AllToAll done")
 
-    if want("alltonext"):
+    if section_on("alltonext"):
         # ---- 24 ranks (3 x 8): AllToNext split / unsplit, HPDS+state vs RR+connection ---
         G, L = 3, 8
         Pn = G * L
@@ -772,7 +772,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         res["alltonext_24r"] = a2n
         progress("AllToNext done")
 
-    if want("agrs"):
+    if section_on("agrs"):
         G, L = 3, 8
         Pn = G * L
         # AllGather / ReduceScatter on the same 24 ranks, 128 MiB (the larger buffer)
@@ -826,7 +826,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         res["allgather_reducescatter_24r_128mib"] = agrs
         progress("AllGather / ReduceScatter done")
 
-    if want("idle"):
+    if section_on("idle"):
         G, L = 3, 8
         Pn = G * L
         # ---- workgroup idle fraction from the device trace (one traced launch) ----------
@@ -861,7 +861,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
         release()
         res["wg_idle_fraction"] = idle_rows
 
-    if want("copy"):
+    if section_on("copy"):
         # ---- practical streaming ceiling: a plain copy kernel, 1 GiB (beyond every cache) --
         nb = 1 << 30
         a = torch.empty(nb, dtype=torch.uint8, device=dev)
