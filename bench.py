@@ -487,6 +487,9 @@ def main():
             torch.cuda.empty_cache()
         out["large"] = large
         out["target_70pct_cold_at_32mib_and_up"] = all(r["cold_frac"] >= 0.70 for r in large)
+        # one point of each of the other configurations
+        out["configs"] = config_rows(torch, W, programs, dev, stream, device_inputs, make_plan, time_launches, release)
+        progress(f"configurations: {out['configs']}")
         if not args.no_interference:
             # the collective beside GEMMs: shared GPU vs reserved compute units
             try:
@@ -526,6 +529,118 @@ def main():
         progress(f"could not write {args.extras_file}: {e}")
     reap_children()
     print(json.dumps(out, separators=(",", ":")), flush=True)
+
+
+# Launch configurations of the one-point rows for the other configurations in the summary
+# line: (parallel factor, threads, slice bytes, protocol id), each the tuned point of the
+# matching --section run (hier, alltoall, alltonext, agrs) and each with a GPU parity test
+# at that configuration.
+CONFIG_POINTS = {
+    "hier_fused": (32, 256, 256 << 10, 3),
+    "hier_stages": ((32, 512, 64 << 10, 3), (16, 512, 1 << 20, 2), (32, 256, 128 << 10, 3)),
+    "a2a_two_phase": (1, 256, 256 << 10, 3),
+    "a2a_direct": (2, 256, 256 << 10, 3),
+    "a2next": (16, 256, 128 << 10, 3),
+    "agrs_ring": (32, 512, 64 << 10, 3),
+}
+
+
+def config_rows(torch, W, programs, dev, stream, device_inputs, make_plan, time_launches, release):
+    """One point of each of the other four configurations, at fixed launch settings
+    (CONFIG_POINTS): the 4-rank exact-sum ring, the 16-rank bf16 hierarchical AllReduce
+    fused and as three launches, the 32-rank int32 AllToAll two-phase and direct, the
+    24-rank AllToNext split (both schedulers) and unsplit, and the 24-rank ring
+    AllGather / ReduceScatter at 128 MiB."""
+    import numpy as np
+    out = {}
+
+    def frac(plan, n, t):
+        return round(plan.bytes(n) / t / 1e9 / HBM_PEAK_GBS, 4)
+
+    # 4 ranks, 1 MiB integer-valued fp32, 4 chunks, one channel, one slice
+    N = 262144
+    xs = W.make_inputs("int_f32", N, 4, W.CFG_RING_AR_4R_INT, size_bytes=N * 4)
+    ii = [torch.from_numpy(x).to(dev) for x in xs]
+    oo = [torch.empty(N, device=dev) for _ in range(4)]
+    p = make_plan(programs.ring_allreduce(4), N, 1, 512, N * 4)
+    t = time_launches(lambda: p.execute(ii, oo, N, stream), 50)
+    exact = bool(np.array_equal(oo[0].cpu().numpy(), np.sum(np.stack(xs).astype(np.float64), 0).astype(np.float32)))
+    out["ring_4r_1mib_int"] = {"us": round(t * 1e6, 1), "exact": exact}
+    release(p)
+    del ii, oo
+    # 16 ranks (2 x 8) bf16, 16 MiB: fused vs three launches
+    G, L = 2, 8
+    N = (16 << 20) // 2
+    sh = N // L
+    ii = device_inputs("bf16", N, G * L, 3016)
+    oo = [torch.empty(N, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
+    mid1 = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
+    mid2 = [torch.empty(sh, dtype=torch.bfloat16, device=dev) for _ in range(G * L)]
+    pf = make_plan(programs.hierarchical_allreduce(G, L), N, *CONFIG_POINTS["hier_fused"], dtype="bf16")
+    c1, c2, c3 = CONFIG_POINTS["hier_stages"]
+    s1 = make_plan(programs.hier_stage_reducescatter_intra(G, L), N, *c1, dtype="bf16")
+    s2 = make_plan(programs.hier_stage_allreduce_inter(G, L), sh, *c2, dtype="bf16")
+    s3 = make_plan(programs.hier_stage_allgather_intra(G, L), sh, *c3, dtype="bf16")
+    tf = time_launches(lambda: pf.execute(ii, oo, N, stream), 20)
+
+    def three():
+        s1.execute(ii, mid1, N, stream)
+        s2.execute(mid1, mid2, sh, stream)
+        s3.execute(mid2, oo, sh, stream)
+    t3 = time_launches(three, 20)
+    out["hier_16r_16mib_bf16"] = {"fused_us": round(tf * 1e6, 1), "three_launch_us": round(t3 * 1e6, 1),
+                                  "fused_frac": frac(pf, N, tf)}
+    release(pf, s1, s2, s3)
+    del ii, oo, mid1, mid2
+    # 32 ranks (4 x 8) int32, 16 MiB: two-phase vs direct
+    G, L = 4, 8
+    N = (16 << 20) // 4
+    ii = device_inputs("i32", N, G * L, 4016)
+    oo = [torch.empty(N, dtype=torch.int32, device=dev) for _ in range(G * L)]
+    row = {}
+    for name, prog in (("two_phase", programs.two_phase_alltoall(G, L)), ("direct", programs.direct_alltoall(G * L))):
+        p = make_plan(prog, N, *CONFIG_POINTS["a2a_" + name], dtype="i32")
+        t = time_launches(lambda: p.execute(ii, oo, N, stream), 20)
+        row[name + "_us"], row[name + "_frac"] = round(t * 1e6, 1), frac(p, N, t)
+        release(p)
+    out["a2a_32r_16mib_i32"] = row
+    del ii, oo
+    release()
+    # 24 ranks (3 x 8): AllToNext at 64 MiB, ring AllGather / ReduceScatter at 128 MiB
+    G, L = 3, 8
+    Pn = G * L
+    N = (64 << 20) // 4
+    ii = device_inputs("f32", N, Pn, 5064)
+    oo = [torch.empty(N, device=dev) for _ in range(Pn)]
+    row = {}
+    for name, split, sched, alloc in (("split_hpds_state", True, "hpds", "state"),
+                                      ("split_rr_connection", True, "rr", "connection"),
+                                      ("unsplit", False, "hpds", "state")):
+        p = make_plan(programs.alltonext(G, L, split=split), N, *CONFIG_POINTS["a2next"], scheduler=sched,
+                      wg_alloc=alloc)
+        t = time_launches(lambda: p.execute(ii, oo, N, stream), 10)
+        row[name + "_us"] = round(t * 1e6, 1)
+        release(p)
+    out["a2next_24r_64mib"] = row
+    del ii, oo
+    release()
+    n_big = Pn * ((32 << 20) // Pn)
+    row = {}
+    for coll in ("allgather", "reducescatter"):
+        if coll == "allgather":
+            prog, count, nout = programs.ring_allgather(Pn), n_big // Pn, n_big
+        else:
+            prog, count, nout = programs.ring_reducescatter(Pn), n_big, n_big // Pn
+        ii = device_inputs("f32", count, Pn, 6000 + len(coll))
+        oo = [torch.empty(nout, device=dev) for _ in range(Pn)]
+        p = make_plan(prog, count, *CONFIG_POINTS["agrs_ring"])
+        t = time_launches(lambda: p.execute(ii, oo, count, stream), 5)
+        row[("ag" if coll == "allgather" else "rs") + "_frac"] = frac(p, count, t)
+        release(p)
+        del ii, oo
+        release()
+    out["agrs_24r_128mib_ring"] = row
+    return out
 
 
 def ring_factors(S):
@@ -1217,10 +1332,9 @@ def cpu_baseline(budget_s: float, S: int = HEADLINE_BYTES):
     except OSError:
         pass
     return {"value": round(S / t2 * 2 * (P - 1) / P / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"chain-order oracle (numpy, one thread) on the ring AllReduce input, 8 ranks x {size_text(S)} "
-                      f"fp32, {r2} runs of {t2 * 1e3:.2f} ms, reported as busbw; the float64 definition oracle: "
-                      f"{r1} runs of {t1 * 1e3:.2f} ms, algbw {S / t1 / 1e9:.3f} GB/s; host: {cores} cores "
-                      f"available ({cpu[:40]})"}
+            "sample": f"chain-order oracle, numpy, one thread, ring AllReduce 8 x {size_text(S)} fp32: {r2} runs of "
+                      f"{t2 * 1e3:.2f} ms as busbw; float64 definition oracle: {r1} runs of {t1 * 1e3:.2f} ms, algbw "
+                      f"{S / t1 / 1e9:.3f} GB/s; {cores} host cores ({cpu[:24]})"}
 
 
 if __name__ == "__main__":

@@ -214,9 +214,10 @@ def test_alltoall_32r_64mib(name):
 
 @pytest.mark.parametrize("split", [True, False])
 def test_alltonext_24r_16mib_bench_config(split):
-    """Bench row `alltonext_24r` at 16 MiB: k = 16 (the largest factor at which both
-    modes' grids fit, as the bench picks it), 256 threads, 128 KiB slices, direct
-    transport with streaming hints, HPDS + state and round robin + connection. Rank r's
+    """Bench row `alltonext_24r` at 16 MiB (and the summary line's `a2next_24r_64mib`
+    launch configuration): k = 16 (the largest factor at which both modes' grids fit, as
+    the bench picks it), 256 threads, 128 KiB slices, direct transport with streaming
+    hints, HPDS + state and round robin + connection. Rank r's
     input lands at r+1; rank 0 keeps its prior contents."""
     G, L = 3, 8
     P, N = G * L, (16 << 20) // 4
@@ -313,6 +314,41 @@ def test_reducescatter_24r_128mib(variant):
 
 
 # ------------------------------------------------------------------ hierarchical AllReduce, 16 ranks bf16
+
+def test_hierarchical_16r_bf16_16mib_summary_points():
+    """Summary-line row `hier_16r_16mib_bf16` (bench.py CONFIG_POINTS): the fused plan at
+    k=32, 256 threads, 256 KiB slices, direct + streaming, and the three launches at
+    their own points, 16 MiB per rank: element-wise against the three-step chain order
+    on every rank."""
+    import bench
+    G, L = 2, 8
+    P, N = G * L, (16 << 20) // 2
+    sh = N // L
+    case("hierarchical bf16 16 MiB, summary-line points")
+    ins = W.device_inputs("normal_bf16", N, P, 3016)
+    xs = [host(t) for t in ins]
+    want = O2.hierarchical_allreduce(xs, G, L, "bf16")[0]
+    outs = filled(N, 0.0, "bf16", P)
+    plan = plan_of(programs.hierarchical_allreduce(G, L), N, *bench.CONFIG_POINTS["hier_fused"], dtype="bf16")
+    launch(plan, ins, outs, N)
+    plan.destroy()
+    assert_ranks_equal([host(t) for t in outs], want)
+    c1, c2, c3 = bench.CONFIG_POINTS["hier_stages"]
+    mid1, mid2 = filled(sh, 0.0, "bf16", P), filled(sh, 0.0, "bf16", P)
+    outs = filled(N, 0.0, "bf16", P)
+    s1 = plan_of(programs.hier_stage_reducescatter_intra(G, L), N, *c1, dtype="bf16")
+    s2 = plan_of(programs.hier_stage_allreduce_inter(G, L), sh, *c2, dtype="bf16")
+    s3 = plan_of(programs.hier_stage_allgather_intra(G, L), sh, *c3, dtype="bf16")
+    import torch
+    s1.execute(ins, mid1, N)
+    s2.execute(mid1, mid2, sh)
+    s3.execute(mid2, outs, sh)
+    torch.cuda.synchronize()
+    for st in (s1, s2, s3):
+        st.status()
+        st.destroy()
+    assert_ranks_equal([host(t) for t in outs], want)
+
 
 def test_hierarchical_16r_bf16_256mib_sampled():
     """Bench row `hier_ar_16r_bf16` at 256 MiB per rank (4 GiB of inputs), sampled: the
