@@ -2,18 +2,19 @@
 
 Headline step: one 8-rank fp32 ring AllReduce of 3 MiB per rank (the top of the
 32 KiB .. 3 MiB sweep), one kernel launch per collective, inputs resident in HBM,
-with the parallelization factor, threads per workgroup, slice size and protocol /
-transport chosen by the on-device coordinate-descent tuner. Plan compilation and
-tuning happen before timing.
+with the parallelization factor (within the sweep's set 1..24), threads per workgroup,
+slice size and protocol / transport chosen by the on-device coordinate-descent tuner.
+Plan compilation and tuning happen before timing.
 
 The last stdout line is one compact JSON object: the headline, its roofline against
-8 TB/s, a cold run over rotating buffer sets, two fixed (untuned) configurations, the
-32 and 256 MiB points (tuned; hot and cold, for the >= 70 % target) and the CPU
-oracle's time. Everything else goes to the extras file (default
-gpurun_out/bench_extras.json); with --extras it also holds the long sections: the
-rest of the sweep, 4/16/32 ranks, tree vs ring, tuning under GEMM interference,
-kernel forms, the other four workloads, workgroup idle fractions and the plain-copy
-ceiling.
+8 TB/s, the same size at factor 32, a cold run over rotating buffer sets, two fixed
+(untuned) configurations, the 32 and 256 MiB points (tuned; hot and cold, for the
+>= 70 % target), one point of each of the other four configurations, the collective
+beside GEMMs, and the CPU oracle's time. Everything else goes to the extras file
+(default gpurun_out/bench_extras.json); --extras (or --section NAME for one part) adds
+the long sections: the sweep and its per-factor grid, 4/16/32 ranks, tree vs ring,
+tuning under GEMM interference, kernel forms, the other four workloads over their
+sizes, workgroup idle fractions and the plain-copy ceiling.
 
 Only one GPU: --gpus above 1 exits with a message.
 """

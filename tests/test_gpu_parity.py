@@ -176,7 +176,8 @@ def test_repeated_launches_and_counts(algo, transport, kernel):
 
 @pytest.mark.parametrize("S,k,nt,sl,knobs", [
     (3 << 20, 8, 512, 256 << 10, dict(kernel="interpreter")),
-    (3 << 20, 32, 256, 64 << 10, dict(transport="direct", kernel="specialized")),  # the benchmark's headline point
+    (3 << 20, 32, 256, 64 << 10, dict(transport="direct", kernel="specialized")),  # the factor_32 point
+    (3 << 20, 24, 256, 16 << 10, dict(transport="direct", kernel="specialized")),  # the benchmark's headline point
     (32 << 20, 32, 512, 64 << 10, dict(transport="direct", streaming=True, kernel="specialized")),
     (256 << 20, 32, 512, 256 << 10, dict(transport="direct", streaming=True, kernel="specialized"))])
 def test_ring_allreduce_8r_full_size_sampled(S, k, nt, sl, knobs):
