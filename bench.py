@@ -489,7 +489,12 @@ def main():
         out["large"] = large
         out["target_70pct_cold_at_32mib_and_up"] = all(r["cold_frac"] >= 0.70 for r in large)
         # one point of each of the other configurations
-        out["configs"] = config_rows(torch, W, programs, dev, stream, device_inputs, make_plan, time_launches, release)
+        try:
+            out["configs"] = config_rows(torch, W, programs, dev, stream, device_inputs, make_plan, time_launches,
+                                         release)
+        except Exception as e:  # reported, never fatal to the summary line
+            out["configs"] = {"error": str(e)[:160]}
+            release()
         progress(f"configurations: {out['configs']}")
         if not args.no_interference:
             # the collective beside GEMMs: shared GPU vs reserved compute units
