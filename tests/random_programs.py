@@ -72,3 +72,16 @@ def case(seed: int):
     if prog.collective == "allreduce":
         n += int(rng.integers(0, prog.in_chunks))  # ragged chunks; AllToAll moves whole blocks
     return prog, k, knobs, n
+
+
+def case_typed(seed: int):
+    """(program, parallel factor, plan knobs, elements per rank, dtype). Seeds below 48
+    are case(seed) in fp32; from 48 on the element type cycles through fp32, bf16 and
+    int32 and the parallel factor is drawn from 1..8, so instance pieces meet the 16-byte
+    grid of both element sizes and empty pieces."""
+    prog, k, knobs, n = case(seed)
+    if seed < 48:
+        return prog, k, knobs, n, "f32"
+    rng = np.random.default_rng([2026, 78, seed])
+    return prog, int(rng.integers(1, 9)), knobs, n, ("f32", "bf16", "i32")[seed % 3]
+

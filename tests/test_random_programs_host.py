@@ -7,14 +7,14 @@ import pytest
 
 from chunk_schedule_execution_amd import Plan, PlanConfig
 from oracle import program as OP
-from random_programs import case
+from random_programs import case_typed
 
-SEEDS = list(range(48))
+SEEDS = list(range(96))
 
 
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_program_case_passes_the_host_checker(seed):
-    prog, k, knobs, n = case(seed)
+    prog, k, knobs, n, dtype = case_typed(seed)
     OP.check_postcondition(prog.as_tuples(), prog.collective, prog.nranks, prog.in_chunks, prog.scratch_chunks)
-    plan = Plan(prog, k, PlanConfig(host_only=True, max_count=n, **knobs))
+    plan = Plan(prog, k, PlanConfig(host_only=True, max_count=n, dtype=dtype, **knobs))
     plan.check(seed=seed, nsims=3)
