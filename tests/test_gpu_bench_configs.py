@@ -137,6 +137,37 @@ def test_ring_ar_8r_large_cold_rotation_sampled(S):
     plan.destroy()
 
 
+@pytest.mark.parametrize("R,S,cfg", [
+    (4, 1 << 20, (64, 128, 4096, 2)), (16, 1 << 20, (32, 128, 65536, 1)), (32, 1 << 20, (32, 64, 32768, 1)),
+    (4, 32 << 20, (64, 1024, 65536, 3)), (16, 32 << 20, (32, 512, 131072, 3)), (32, 32 << 20, (32, 256, 65536, 3))])
+def test_ring_ar_rank_counts_bench_points(R, S, cfg):
+    """Bench section `ranks` (ring AllReduce at 4, 16 and 32 ranks, 1 and 32 MiB per
+    rank) at the points its tuner chose: element-wise at 1 MiB, sampled at 32 MiB (4,000
+    elements plus the chunk bounds, all ranks identical over the whole buffer)."""
+    import torch
+    N = S // 4
+    k, nt, sl, proto = cfg
+    case(f"ring AR {R} ranks {S >> 20} MiB {cfg}")
+    ins = W.device_inputs("normal_f32", N, R, 91000 + R * 64 + S // (1 << 20))
+    outs = filled(N, -7.0, "f32", R)
+    plan = plan_of(programs.ring_allreduce(R), N, k, nt, sl, proto)
+    launch(plan, ins, outs, N)
+    plan.destroy()
+    if S <= (1 << 20):
+        xs = [host(t) for t in ins]
+        assert_ranks_equal([host(t) for t in outs], O2.ring_allreduce(xs, R, "f32")[0])
+        return
+    for r in range(1, R):
+        assert torch.equal(outs[r], outs[0]), r
+    rng = np.random.default_rng(R)
+    bounds = np.concatenate([np.arange(-1, 2) + (N * j) // R for j in range(1, R)])
+    idx = np.unique(np.concatenate([rng.integers(0, N, 4000), [0, N - 1], bounds]))
+    tidx = torch.from_numpy(idx).to("cuda:0")
+    cols = [t[tidx].cpu().numpy() for t in ins]
+    want = O2.ring_allreduce_columns(cols, N, R, idx, "f32")
+    assert np.array_equal(outs[0][tidx].cpu().numpy(), want)
+
+
 def test_ring_ar_4r_1mib_bench_config():
     """Bench row `ring_ar_4r_1mib_int` (4 ranks, 1 MiB integer-valued fp32, one channel,
     one 1 MiB slice, 512 threads, staged, generated kernel): exact sum, bit for bit."""
