@@ -11,7 +11,7 @@ The last stdout line is one compact JSON object: the headline, its roofline agai
 (untuned) configurations, the 32 and 256 MiB points (tuned; hot and cold, for the
 >= 70 % target), one point of each of the other four configurations, the collective
 beside GEMMs, and the CPU oracle's time. Everything else goes to the extras file
-(default gpurun_out/bench_extras.json); --extras (or --section NAME for one part) adds
+(default bench_results/extras.json); --extras (or --section NAME for one part) adds
 the long sections: the sweep and its per-factor grid, 4/16/32 ranks, tree vs ring,
 tuning under GEMM interference, kernel forms, the other four workloads over their
 sizes, workgroup idle fractions and the plain-copy ceiling.
@@ -69,7 +69,7 @@ def parse():
                     help="also run the long sections (the rest of the 8-rank sweep, 4/16/32 ranks, tree vs ring, "
                          "interference, kernel forms, the other four workloads, idle fractions, copy ceiling); "
                          "they go to the extras file only")
-    ap.add_argument("--extras-file", type=str, default=os.path.join("gpurun_out", "bench_extras.json"),
+    ap.add_argument("--extras-file", type=str, default=os.path.join("bench_results", "extras.json"),
                     help="where the full results go (the last stdout line stays a compact summary)")
     ap.add_argument("--bytes", type=int, default=0,
                     help="per-rank size of the timed ring AllReduce instead of 3 MiB (profiling runs of other "

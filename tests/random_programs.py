@@ -1,5 +1,5 @@
 """Seeded random chunk programs for tests (no hypothesis: the same seed gives the same
-program on the host and on the GPU machine).
+program on the host and on the GPU).
 
 AllReduce: every chunk gets its own reduction chain (a random order of the ranks,
 partials through scratch, the sum landing in the last rank's output) and its own
