@@ -159,6 +159,8 @@ PROFILE_WORKLOADS = {
                             "split AllToNext, 3 x 8 virtual ranks, fp32, 64 MiB per rank"),
     "hier_ar_16r_bf16": ("hierarchical_allreduce", (2, 8), "bf16", 1 << 25, 1 << 25, 2 * 15 / 16, "32,256,131072,3",
                          "hierarchical AllReduce, 2 x 8 virtual ranks, bf16, 64 MiB per rank"),
+    "tree_ar_24r": ("tree_allreduce", (24,), "f32", 1 << 18, 1 << 18, 2 * 23 / 24, "8,128,65536,2",
+                    "tree AllReduce, 24 virtual ranks, fp32, 1 MiB per rank"),
 }
 
 
