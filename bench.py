@@ -145,9 +145,9 @@ PROFILE_WORKLOADS = {
                       "ring AllGather, 24 virtual ranks, fp32, 128 MiB output per rank"),
     "reducescatter_24r": ("ring_reducescatter", (24,), "f32", N_BIG_24, N_BIG_24 // 24, 23 / 24, "32,512,65536,3",
                           "ring ReduceScatter, 24 virtual ranks, fp32, 128 MiB input per rank"),
-    "allgather_2d_24r": ("allgather_2d", (3, 8), "f32", N_BIG_24 // 24, N_BIG_24, 23 / 24, "8,512,65536,3",
+    "allgather_2d_24r": ("allgather_2d", (3, 8), "f32", N_BIG_24 // 24, N_BIG_24, 23 / 24, "24,256,65536,3",
                          "2-D AllGather, 3 x 8 virtual ranks, fp32, 128 MiB output per rank"),
-    "reducescatter_2d_24r": ("reducescatter_2d", (3, 8), "f32", N_BIG_24, N_BIG_24 // 24, 23 / 24, "16,256,65536,3",
+    "reducescatter_2d_24r": ("reducescatter_2d", (3, 8), "f32", N_BIG_24, N_BIG_24 // 24, 23 / 24, "24,256,65536,3",
                              "2-D ReduceScatter, 3 x 8 virtual ranks, fp32, 128 MiB input per rank"),
     "alltoall_32r": ("direct_alltoall", (32,), "i32", 1 << 22, 1 << 22, 31 / 32, "2,256,262144,3",
                      "direct AllToAll, 32 virtual ranks, int32, 16 MiB per rank"),
@@ -927,7 +927,7 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
                     # grid would not fit on the device at once
                     for sched, alloc in modes:
                         best = None
-                        for k, nt in ((4, 512), (8, 512), (8, 256), (16, 256), (16, 128)):
+                        for k, nt in ((4, 512), (8, 512), (8, 256), (16, 256), (16, 128), (24, 256), (32, 128)):
                             try:
                                 pl = make_plan(pr, count, k, nt, 64 << 10, 3, scheduler=sched, wg_alloc=alloc)
                             except capi.CCLError:

@@ -280,8 +280,8 @@ N_BIG = 24 * ((32 << 20) // 24)  # 33,554,424 fp32: the AllGather output, the Re
 def _agrs_points(variant):
     if variant == "ring":  # one configuration for both modes: k=32 x 512 threads, 64 KiB slices, streaming
         return [("hpds", "state", 32, 512), ("rr", "connection", 32, 512)]
-    return [("hpds", "state", 8, 512), ("hpds", "state", 4, 512), ("rr", "connection", 16, 128),
-            ("rr", "connection", 8, 256)]
+    return [("hpds", "state", 24, 256), ("hpds", "state", 16, 256), ("hpds", "state", 8, 512),
+            ("rr", "connection", 16, 128), ("rr", "connection", 8, 256)]
 
 
 @pytest.mark.parametrize("variant", ["ring", "2d"])
