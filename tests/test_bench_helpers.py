@@ -43,4 +43,4 @@ def test_same_launch_treats_slices_covering_the_piece_as_one():
 def test_ring_factors_follow_the_sweep():
     assert bench.ring_factors(3 << 20) == [1, 2, 4, 8, 16, 24]
     assert bench.ring_factors(32 << 10) == [1, 2, 4, 8, 16, 24]
-    assert 32 in bench.ring_factors(32 << 20)
+    assert {32, 48, 64} <= set(bench.ring_factors(32 << 20))

@@ -91,6 +91,8 @@ def test_headline_ring_ar_8r_3mib(proto, k):
 
 
 @pytest.mark.parametrize("cfg", [(32, 512, 64 << 10, 3), (32, 1024, 64 << 10, 3), (32, 1024, 128 << 10, 3),
+                                 (64, 512, 128 << 10, 3), (48, 512, 128 << 10, 3), (64, 512, 32 << 10, 3),
+                                 (64, 1024, 128 << 10, 2),
                                  (1, 256, 128 << 10, 0), (8, 512, 256 << 10, 0)])
 def test_ring_ar_8r_32mib(cfg):
     """Bench rows `large` (32 MiB, the tuner's streaming points at 512 / 1024 threads)
@@ -109,15 +111,17 @@ def test_ring_ar_8r_32mib(cfg):
     plan.destroy()
 
 
+@pytest.mark.parametrize("k,nt,proto", [(32, 1024, 3), (64, 512, 3), (64, 1024, 2)])
 @pytest.mark.parametrize("S", [64 << 20, 256 << 20])
-def test_ring_ar_8r_large_cold_rotation_sampled(S):
-    """Bench row `large` cold runs (64 / 256 MiB, streaming, 1024 threads, 128 KiB
-    slices): three buffer sets launched back to back, as the cold timing rotates them;
-    sampled elements of every set against the chain order, all ranks identical."""
+def test_ring_ar_8r_large_cold_rotation_sampled(S, k, nt, proto):
+    """Bench row `large` cold runs (64 / 256 MiB, 128 KiB slices, one or two workgroups per
+    compute unit, streaming or plain direct transport, the tuner's picks at these sizes):
+    three buffer sets launched back to back, as the cold timing rotates them; sampled
+    elements of every set against the chain order, all ranks identical."""
     import torch
     P, N = 8, S // 4
-    case(f"ring AR {S >> 20} MiB rotating sets, sampled")
-    plan = plan_of(programs.ring_allreduce(P), N, 32, 1024, 128 << 10, 3)
+    case(f"ring AR {S >> 20} MiB rotating sets, sampled, k={k} nt={nt} proto={proto}")
+    plan = plan_of(programs.ring_allreduce(P), N, k, nt, 128 << 10, proto)
     sets = []
     for j in range(3):
         sets.append((W.device_inputs("normal_f32", N, P, 70000 + j), filled(N, -7.0, "f32", P)))
