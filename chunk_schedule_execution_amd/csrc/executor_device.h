@@ -10,11 +10,20 @@ namespace {
 
 // ---- element arithmetic --------------------------------------------------
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// fp32 -> bf16, round to nearest, ties to even, in one instruction (v_cvt_pk_bf16_f32,
+// two values at a time); a NaN becomes the quiet NaN 0x7fc0 with its sign. Over all 2^32
+// fp32 inputs the instruction gives the same bits as the rounding written out,
+// (u + 0x7fff + lsb) >> 16, on every non-NaN input; NaNs keep part of their payload
+// there, hence the fix-up. Against the written-out rounding it took a bf16 8-rank ring
+// at 3 MiB from 38.3 to 35.4 us and at 32 MiB from 189 to 180 us.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2_bits(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  uint32_t r = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+  if (__builtin_isnan(lo)) r = (r & 0xffff0000u) | ((__float_as_uint(lo) >> 16) & 0x8000u) | 0x7fc0u;
+  if (__builtin_isnan(hi)) r = (r & 0x0000ffffu) | (__float_as_uint(hi) & 0x80000000u) | 0x7fc00000u;
+  return r;
 }
 
 template <int DT>
@@ -46,12 +55,12 @@ struct Arith<CCL_BF16> {
   typedef uint16_t S;
   static __device__ __forceinline__ S add(S a, S b) {
     float s = __uint_as_float(uint32_t(a) << 16) + __uint_as_float(uint32_t(b) << 16);
-    return S(f32_to_bf16_bits(s));
+    return S(f32x2_to_bf16x2_bits(s, 0.0f) & 0xffffu);
   }
   static __device__ __forceinline__ uint32_t add2(uint32_t a, uint32_t b) {
     float lo = __uint_as_float(a << 16) + __uint_as_float(b << 16);
     float hi = __uint_as_float(a & 0xffff0000u) + __uint_as_float(b & 0xffff0000u);
-    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+    return f32x2_to_bf16x2_bits(lo, hi);
   }
   static __device__ __forceinline__ uint4 add4(uint4 a, uint4 b) {
     return make_uint4(add2(a.x, b.x), add2(a.y, b.y), add2(a.z, b.z), add2(a.w, b.w));

@@ -143,6 +143,34 @@ def test_ring_instances_shorter_than_the_16_byte_grid(dtype, knobs, N):
     chk(ys, xs, None)
 
 
+@pytest.mark.parametrize("knobs", [dict(transport="staged", kernel="interpreter"),
+                                   dict(transport="direct", kernel="specialized"),
+                                   dict(protocol="ll", kernel="specialized")])
+def test_bf16_special_values_round_like_the_oracle(knobs):
+    """bf16 sums whose fp32 results are NaNs with payloads (signalling and quiet inputs),
+    infinities, overflows and subnormals: every stored bf16 is the oracle's, NaNs as the
+    quiet NaN 0x7fc0 (the conversion instruction alone would keep part of the payload).
+    NaNs are positive and +inf never meets -inf, so which operand's NaN an add returns
+    cannot change the bits."""
+    P, N = 8, 8 * 4096 + 37
+    case(f"bf16 ring AR special values {knobs}")
+    xs = [np.asarray(x, np.uint16).copy() for x in W.make_inputs("normal_bf16", N, P, W.CFG_RING_AR_8R)]
+    rng = np.random.default_rng(5)
+    col = np.arange(N)
+    for r in range(P):
+        x = xs[r]
+        nan1 = col % 7 == 1
+        x[nan1 & (rng.integers(0, P, N) == r)] = rng.choice(np.array([0x7F81, 0x7FC1, 0x7FFF, 0x7FA5], np.uint16))
+        x[(col % 7 == 2) & (r < 2)] = np.uint16(0x7F95) if r == 0 else np.uint16(0x7FC3)
+        x[(col % 7 == 3) & (r == 3)] = np.uint16(0x7F80)                       # +inf among finite values
+        x[col % 7 == 4] = np.uint16(0x7F7F)                                      # largest finite: the sum overflows
+        x[col % 7 == 5] = rng.integers(1, 0x80, int(np.count_nonzero(col % 7 == 5))).astype(np.uint16)  # subnormal
+    want = O2.ring_allreduce(xs, P, "bf16")[0]
+    assert np.count_nonzero(want == 0x7FC0) > N // 8 and np.count_nonzero(want == 0x7F80) > N // 8
+    ys, _ = _run(programs.ring_allreduce(P), xs, "bf16", k=3, nthreads=256, slice_bytes=8192, **knobs)
+    assert_all_equal(ys, want)
+
+
 def test_ring_subnormals_are_kept():
     P, N = 8, 4096
     case("ring AR subnormal inputs")
