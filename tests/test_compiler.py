@@ -456,6 +456,18 @@ def test_coordinate_descent_looks_past_one_dip_and_picks_the_subspace():
     assert rep.best_score == 28
 
 
+def test_coordinate_descent_also_starts_from_the_middle():
+    """Every subspace gets a second descent from the middle of each coordinate: here the
+    one from the corner stops behind a dip two candidates wide (past the one-step
+    look-ahead), the one from the middle reaches the peak."""
+    F = [1, 2, 4, 8, 16, 24, 32]
+
+    def f(p):
+        return float({1: 3, 2: 4, 4: 1, 8: 1, 16: 9, 24: 8, 32: 7}[p.parallel_factor])
+    best, rep = capi.ccl_tune_coordinate_descent(_space(F, [256], [65536]), f)
+    assert best.parallel_factor == 16 and rep.best_score == 9
+
+
 def test_coordinate_descent_stops_on_infeasible_points():
     def f(p):
         return -1.0 if p.parallel_factor > 4 else float(p.parallel_factor)
