@@ -9,7 +9,6 @@
 #include <array>
 #include <cmath>
 #include <map>
-#include <string>
 #include <vector>
 
 #include "ccl_internal.h"
@@ -17,8 +16,6 @@
 using namespace ccl;
 
 namespace {
-
-thread_local std::string g_tune_detail;
 
 int index_of(const int32_t* v, int n, int32_t x) {
   for (int i = 0; i < n; ++i)
