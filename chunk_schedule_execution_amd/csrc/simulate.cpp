@@ -42,8 +42,8 @@ struct Rng {
 void check_lowered(const HostPlan& hp, uint64_t seed, int nsims) {
   const int P = hp.P;
   // element count: a multiple of the count granule with about three elements per instance sub-chunk
-  int64_t want = int64_t(3) * hp.C * hp.k;
-  int64_t N = ((want + hp.granule - 1) / hp.granule) * hp.granule;
+  int64_t min_count = int64_t(3) * hp.C * hp.k;
+  int64_t N = ((min_count + hp.granule - 1) / hp.granule) * hp.granule;
   if (N >= (int64_t(1) << 20)) fail(CCL_ERR_INVALID_ARGUMENT, "plan too large for the host check");
   const int64_t se = 2;  // slice length in the simulation: several slices per instruction
   const int64_t nout = output_elems(hp, N);

@@ -64,10 +64,10 @@ int ccl_tune_coordinate_descent(const ccl_tune_space* space, const ccl_tune_poin
         if (it != seen.end()) return it->second;
         ccl_tune_point q = pt;
         for (int c = 0; c < 3; ++c) q.*(coords[c].field) = coords[c].vals[ix[c]];
-        const double v = objective(&q, user);
+        const double score = objective(&q, user);
         ++evals;
-        seen.emplace(key, v);
-        return v;
+        seen.emplace(key, score);
+        return score;
       };
       // One coordinate descent from `from`; returns its score and leaves its point in `at`.
       // Each coordinate moves in direction dir (+1 / -1) while the objective improves,

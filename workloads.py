@@ -122,8 +122,3 @@ def device_inputs(kind: str, n: int, nranks: int, seed: int, device="cuda:0"):
     if kind == "normal_bf16":
         return [torch.randn(n, generator=g, device=device).to(torch.bfloat16) for _ in range(nranks)]
     raise ValueError(f"unknown device input kind {kind!r}")
-
-
-def dtype_of_kind(kind: str) -> str:
-    return {"int_f32": "f32", "normal_f32": "f32", "normal_bf16": "bf16", "uniform_i32": "i32",
-            "prov_i32": "i32", "prov_f32": "f32", "normal_f32_denorm": "f32"}[kind]
