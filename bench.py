@@ -435,6 +435,26 @@ def main():
                           "median_event_bracketed": round(statistics.median(per), 2)},
         }}
     progress(f"headline {t_step * 1e6:.2f} us per launch, config {cfg}")
+    if PROTOCOLS[cfg[3]][0] == "simple" and S <= SWEEP[-1]:
+        # The latency floor of this launch: a ring AllReduce is a chain of 2(P - 1)
+        # dependent hand-offs, P - 1 reducing and P - 1 forwarding, the last of which
+        # sets no flag. The hop probe times one hand-off of this launch's instruction
+        # piece with the executor's own slice code, once over lines still in the L2
+        # and once over lines recent launches did not touch (a 4 MiB window).
+        piece = -(-largest_piece(N, P, cfg[0]) * 4 // 16) * 16
+        hop = {}
+        for name, two, window in (("copy", False, 0), ("reduce", True, 0), ("copy_cold", False, 4 << 20),
+                                  ("reduce_cold", True, 4 << 20)):
+            us, inf = capi.ccl_hop_probe(15, piece, two, cfg[1], 30, window_bytes=window, stream=stream.cuda_stream)
+            if inf[1] or inf[2] or not us:
+                raise RuntimeError(f"hop probe failed: {inf}")
+            hop[name] = round(statistics.median(us), 3)
+        chain = (P - 1) * hop["reduce"] + (P - 2) * hop["copy"]
+        chain_cold = (P - 1) * hop["reduce_cold"] + (P - 2) * hop["copy_cold"]
+        out["latency_floor"] = {"piece_bytes": piece, "hop_us": hop, "chain_us": round(chain, 2),
+                                "chain_cold_us": round(chain_cold, 2), "frac": round(chain / (t_step * 1e6), 4),
+                                "frac_cold": round(chain_cold / (t_step * 1e6), 4)}
+        progress(f"hand-off floor {hop} us: chain {chain:.1f} / {chain_cold:.1f} us of {t_step * 1e6:.1f}")
 
     if not args.no_extras:
         # cold headline: rotate over buffer sets larger than the Infinity Cache

@@ -155,6 +155,8 @@ def _load():
                                P(ccl_tune_space), C.c_void_p, P(ccl_tune_point), P(ccl_tune_report)]),
         "ccl_copy_probe": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_int, C.c_void_p]),
         "ccl_litmus_message_passing": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, P(C.c_int64), C.c_void_p]),
+        "ccl_hop_probe": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64,
+                                    P(C.c_double), P(C.c_int64), C.c_void_p]),
         "ccl_stream_create_cu_masked": (C.c_int, [P(C.c_uint32), C.c_int, P(C.c_void_p)]),
         "ccl_stream_destroy": (C.c_int, [C.c_void_p]),
         "ccl_cu_probe": (C.c_int, [C.c_void_p, C.c_int, C.c_int, P(C.c_uint32)]),
@@ -171,8 +173,8 @@ EXPORTED = ("ccl_version", "ccl_error_string", "ccl_last_error_detail", "ccl_pla
             "ccl_execute_static",
             "ccl_plan_destroy", "ccl_plan_info", "ccl_plan_bytes", "ccl_plan_export", "ccl_plan_check",
             "ccl_plan_status", "ccl_plan_read_trace", "ccl_plan_link_busy", "ccl_tune_coordinate_descent", "ccl_tune",
-            "ccl_copy_probe", "ccl_litmus_message_passing", "ccl_stream_create_cu_masked", "ccl_stream_destroy",
-            "ccl_cu_probe")
+            "ccl_copy_probe", "ccl_litmus_message_passing", "ccl_hop_probe", "ccl_stream_create_cu_masked",
+            "ccl_stream_destroy", "ccl_cu_probe")
 
 
 def lib():
@@ -306,6 +308,17 @@ def ccl_litmus_message_passing(cross_xcd: bool, rounds: int, words: int, timeout
     _check(_lib.ccl_litmus_message_passing(int(bool(cross_xcd)), rounds, words, C.c_int64(timeout_us), res,
                                            C.c_void_p(stream)), "ccl_litmus_message_passing")
     return [tuple(res[8 * p:8 * p + 8]) for p in range(8)]
+
+
+def ccl_hop_probe(hops: int, nbytes: int, two_operands: bool, nthreads: int = 256, launches: int = 20,
+                  window_bytes: int = 0, timeout_us: int = 200000, stream: int = 0):
+    """(microseconds per hand-off of each launch, (chain workgroups off workgroup 0's XCD,
+    launches with an expired wait, launches whose data arrived wrong, launches completed))."""
+    us = (C.c_double * launches)()
+    info = (C.c_int64 * 4)()
+    _check(_lib.ccl_hop_probe(hops, nbytes, int(bool(two_operands)), nthreads, launches, C.c_int64(window_bytes),
+                              C.c_int64(timeout_us), us, info, C.c_void_p(stream)), "ccl_hop_probe")
+    return list(us[:info[3]]), tuple(info)
 
 
 def cu_mask_words(cus, nwords: int = 8):

@@ -747,6 +747,80 @@ int ccl_litmus_message_passing(int cross_xcd, int rounds, int words, int64_t tim
   });
 }
 
+int ccl_hop_probe(int hops, int bytes, int two_operands, int nthreads, int launches, int64_t window_bytes,
+                  int64_t timeout_us, double* us_per_hop, int64_t* info, void* stream) {
+  if (!us_per_hop || !info || hops < 1 || hops > 31 || bytes < 16 || bytes > (4 << 20) || bytes % 16 ||
+      nthreads < 64 || nthreads > 1024 || nthreads % 64 || launches < 1 || launches > 1000 || timeout_us < 1 ||
+      window_bytes < 0 || window_bytes > (int64_t(16) << 20) || (window_bytes > 0 && window_bytes < 2 * int64_t(bytes)))
+    return set_error(CCL_ERR_INVALID_ARGUMENT, "hop probe: bad arguments");
+  return guarded([&] {
+    const size_t rbytes = (size_t(bytes) + 255) / 256 * 256;
+    // region stride: the payload itself, or a window the launches step through
+    const size_t region = window_bytes > 0 ? std::max(rbytes, size_t(window_bytes) / 256 * 256) : rbytes;
+    const int chain = hops + 1;
+    // data (source + one region per chain workgroup), second operands, flags, tags,
+    // ticks, watchdog words, abort word
+    const size_t sizes[7] = {region * (chain + 1), region * chain, size_t(chain) * kFlagStride * 8, size_t(chain) * 8,
+                             16, 16, 8};
+    void* bufs[7] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    struct Free {
+      void** b;
+      ~Free() {
+        for (int i = 0; i < 7; ++i)
+          if (b[i]) (void)hipFree(b[i]);
+      }
+    } guard{bufs};
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (int i = 0; i < 7; ++i) {
+      HIP_TRY(hipMalloc(&bufs[i], sizes[i]));
+      HIP_TRY(hipMemsetAsync(bufs[i], 0, sizes[i], s));
+    }
+    int dev = 0, rate_khz = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev));
+    if (rate_khz <= 0) rate_khz = 100000;
+    const long long timeout_ticks = (long long)(timeout_us * (rate_khz / 1000.0));
+    auto* data = static_cast<unsigned char*>(bufs[0]);
+    std::vector<uint32_t> last(bytes / 4);
+    std::vector<unsigned long long> tags(chain);
+    for (int i = 0; i < 4; ++i) info[i] = 0;
+    for (int l = 0; l < launches; ++l) {
+      const unsigned long long epoch = (unsigned long long)l + 1;
+      // every launch moves one payload further through the window (256-byte aligned)
+      const size_t rot = region > rbytes ? (size_t(l) * rbytes) % (region - rbytes) / 256 * 256 : 0;
+      const uint32_t word = 0x3f800000u + uint32_t(epoch & 0x7fffffu);  // a normal float, new every launch
+      HIP_TRY(hipMemsetD32Async(reinterpret_cast<hipDeviceptr_t>(data + rot), int(word), bytes / 4, s));
+      std::string err;
+      const int rc = launch_hop_probe(data, static_cast<unsigned char*>(bufs[1]),
+                                      static_cast<unsigned long long*>(bufs[2]), static_cast<unsigned long long*>(bufs[3]),
+                                      static_cast<long long*>(bufs[4]), static_cast<unsigned int*>(bufs[5]),
+                                      static_cast<unsigned long long*>(bufs[6]), epoch, timeout_ticks, region, rot,
+                                      hops, bytes, two_operands ? 1 : 0, nthreads, stream, &err);
+      if (rc) fail(rc, err);
+      HIP_TRY(hipStreamSynchronize(s));
+      unsigned int werr[4];
+      long long ticks[2];
+      HIP_TRY(hipMemcpy(werr, bufs[5], sizeof werr, hipMemcpyDeviceToHost));
+      if (werr[0] != 0) {  // a wait expired: the chain stopped, and so does the probe
+        info[1] += 1;
+        break;
+      }
+      HIP_TRY(hipMemcpy(ticks, bufs[4], sizeof ticks, hipMemcpyDeviceToHost));
+      HIP_TRY(hipMemcpy(tags.data(), bufs[3], tags.size() * 8, hipMemcpyDeviceToHost));
+      HIP_TRY(hipMemcpy(last.data(), data + size_t(chain) * region + rot, size_t(bytes), hipMemcpyDeviceToHost));
+      for (int j = 1; j < chain; ++j) info[0] += (tags[j] & 15ull) != (tags[0] & 15ull);
+      for (uint32_t v : last)
+        if (v != word) {
+          info[2] += 1;
+          break;
+        }
+      us_per_hop[l] = double(ticks[1] - ticks[0]) / (rate_khz / 1000.0) / hops;
+      info[3] += 1;
+    }
+    return CCL_OK;
+  });
+}
+
 int ccl_stream_create_cu_masked(const uint32_t* mask, int nwords, void** stream) {
   if (!stream) return set_error(CCL_ERR_INVALID_ARGUMENT, "null stream pointer");
   *stream = nullptr;

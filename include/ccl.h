@@ -468,6 +468,35 @@ int ccl_copy_probe(void* dst, const void* src, size_t bytes, int nblocks, int nt
 int ccl_litmus_message_passing(int cross_xcd, int rounds, int words, int64_t timeout_us, int64_t* results,
                                void* stream);
 
+/*
+ * Hop-latency probe (a diagnostic beside the executor, like the copy probe): the cost
+ * of one hand-off of the executor in isolation, the unit of a latency-bound chain such
+ * as the ring AllReduce's 2(P-1) dependent steps (MSCCLang report, section 3.1: a
+ * receive-reduce-send step waits for the previous rank's send). A chain of hops + 1
+ * workgroups on one XCD (ids 0, 8, 16, ...; the grid's other workgroups exit at once)
+ * passes `bytes` (a multiple of 16, at most 4 MiB) of fp32 data along: workgroup 0
+ * copies a source region into the first hand-off region, and every later workgroup
+ * runs the executor's own slice code on it (flag poll by one thread, agent-coherent
+ * loads, an added second operand of zeros when two_operands is set, XCD-local plain
+ * stores into the next region), waits for its stores and sets its flag as a send does.
+ * hops: 1..31 (the chain fits one XCD's 32 compute units at any workgroup size);
+ * nthreads: a multiple of 64 in 64..1024; launches: 1..1000, each with new data and a
+ * new epoch; every wait is bounded by timeout_us. window_bytes 0: every launch reuses
+ * the same lines, which stay in the L2 between launches; otherwise (2 * bytes .. 16 MiB)
+ * every region owns a window of that size and each launch moves its payload one
+ * payload further through it, so a launch finds lines that recent launches did not
+ * touch, as a collective over buffers larger than the L2 does.
+ * us_per_hop (host, `launches` values): per launch, the wall-clock time from workgroup
+ * 0's flag store to the last workgroup's acknowledged stores, divided by hops.
+ * info (host, 4 values): [0] chain workgroups that ran on another XCD than workgroup 0,
+ * summed over launches; [1] launches in which a wait expired (the probe stops there);
+ * [2] launches whose last region differs from their source; [3] launches completed.
+ * The call allocates its own device buffers, runs on `stream` and synchronizes with it
+ * after every launch.
+ */
+int ccl_hop_probe(int hops, int bytes, int two_operands, int nthreads, int launches, int64_t window_bytes,
+                  int64_t timeout_us, double* us_per_hop, int64_t* info, void* stream);
+
 /* ---- compute-unit reservation (AutoCCL report, method 3 and its interference
  * results: communication tuned while computation runs beside it; ReSCCL report,
  * section 1: thread blocks the collective takes from computation) -------------- */

@@ -196,6 +196,18 @@ def test_litmus_rejects_bad_arguments_before_touching_the_gpu():
         assert e.value.status == capi.CCL_ERR_INVALID_ARGUMENT
 
 
+def test_hop_probe_rejects_bad_arguments_before_touching_the_gpu():
+    """No hops, a chain longer than one XCD's compute units, a payload off the 16-byte
+    grid or above 4 MiB, a workgroup size that is no multiple of 64, no launches, a
+    window smaller than two payloads or above 16 MiB."""
+    for args in ((0, 16, False), (32, 16, False), (15, 24, False), (15, (4 << 20) + 16, True),
+                 (15, 16384, False, 96), (15, 16384, False, 256, 0), (15, 16384, False, 256, 10, 16384),
+                 (15, 16384, False, 256, 10, (16 << 20) + 256)):
+        with pytest.raises(capi.CCLError) as e:
+            capi.ccl_hop_probe(*args)
+        assert e.value.status == capi.CCL_ERR_INVALID_ARGUMENT
+
+
 def test_tuner_cache_answers_a_known_key_without_timing(tmp_path):
     """The persistent tuner cache times a key once: a second request (same programs, rank
     count, dtype, count bucket, device, space and base flags) is answered from the file,
