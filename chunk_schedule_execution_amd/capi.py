@@ -78,7 +78,8 @@ class ccl_plan_info_t(C.Structure):
                 ("staging_bytes", C.c_int64), ("scratch_bytes", C.c_int64), ("flag_bytes", C.c_int64),
                 ("table_bytes", C.c_int64), ("compile_ms", C.c_double * 6), ("opcode_hist", C.c_int32 * 16),
                 ("specialized_instructions", C.c_int32), ("specialized_waves_per_simd", C.c_int32),
-                ("specialized_code_bytes", C.c_int64), ("dag_width", C.c_int32), ("dag_depth", C.c_int32)]
+                ("specialized_code_bytes", C.c_int64), ("dag_width", C.c_int32), ("dag_depth", C.c_int32),
+                ("specialized_scalar_records", C.c_int32)]
 
 
 class ccl_instr_info(C.Structure):

@@ -63,7 +63,7 @@ struct ccl_plan {
   unsigned long long* d_trace = nullptr;
   unsigned long long* d_xcd = nullptr;  // per launch-grid workgroup: XCD tag of the latest launch
   void* spec_fn = nullptr;              // generated kernel (CCL_FLAG_SPECIALIZE / LAZY), or the interpreter
-  int spec_shapes = 0, spec_instructions = 0, spec_waves = 0;
+  int spec_shapes = 0, spec_instructions = 0, spec_waves = 0, spec_scalar_recs = 0;
   int64_t spec_code_bytes = 0;
   hipEvent_t last = nullptr;    // recorded on last_stream when another stream needs ordering
   hipStream_t last_stream = nullptr;
@@ -232,7 +232,7 @@ void setup_device(ccl_plan* p) {
   if (hp.cfg.flags & (CCL_FLAG_SPECIALIZE | CCL_FLAG_LAZY | CCL_FLAG_SPECIALIZE_LOOP)) {
     const std::string src = specialized_source(hp, local, (hp.cfg.flags & CCL_FLAG_LAZY) != 0,
                                                (hp.cfg.flags & CCL_FLAG_SPECIALIZE_LOOP) != 0, cus, &p->spec_shapes,
-                                               &p->spec_instructions, &p->spec_waves);
+                                               &p->spec_instructions, &p->spec_waves, &p->spec_scalar_recs);
     int spec_blocks = 0;
     p->spec_fn = load_specialized(src, p->device_id, hp.cfg.nthreads, &spec_blocks, &p->spec_code_bytes);
     hp.max_resident_wgs = spec_blocks * cus;
@@ -294,7 +294,7 @@ int ccl_plan_create(const ccl_program_desc* prog, int nranks, int nchunks, int p
           bool local = !(p->hp.cfg.flags & CCL_FLAG_COHERENT_ONLY);
           p->spec_code_bytes = compile_specialized(specialized_source(
               p->hp, local, (p->hp.cfg.flags & CCL_FLAG_LAZY) != 0, (p->hp.cfg.flags & CCL_FLAG_SPECIALIZE_LOOP) != 0,
-              p->hp.cfg.num_cus, &p->spec_shapes, &p->spec_instructions, &p->spec_waves));
+              p->hp.cfg.num_cus, &p->spec_shapes, &p->spec_instructions, &p->spec_waves, &p->spec_scalar_recs));
         }
       }
     } catch (...) {
@@ -539,6 +539,7 @@ int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info) {
     for (const auto& D : hp.dins) info->opcode_hist[D.op & 15]++;
     info->dag_width = hp.dag_width;
     info->dag_depth = hp.dag_depth;
+    info->specialized_scalar_records = plan->spec_scalar_recs;
     return CCL_OK;
   });
 }

@@ -176,8 +176,10 @@ int static_scratch_base(int device, unsigned char** base, std::string* err);
 // specialize.cpp: plan-specialized kernels (CCL_FLAG_SPECIALIZE / CCL_FLAG_LAZY).
 // cus: compute units of the target device; the kernel is compiled for the waves per
 // SIMD that the plan's grid needs to be co-resident on them.
+// scalar_records: 1 if each step reads its record through the scalar cache, 0 if the
+// workgroup stages its records in LDS first.
 std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bool force_loop, int cus,
-                               int* num_shapes, int* num_instructions, int* waves_per_simd);
+                               int* num_shapes, int* num_instructions, int* waves_per_simd, int* scalar_records);
 int64_t compile_specialized(const std::string& src);  // compile only (no device needed); code bytes
 void* load_specialized(const std::string& src, int device, int nthreads, int* blocks_per_cu, int64_t* code_bytes);
 int launch_specialized(void* fn, const ExecArgs& args, int nwg, int nthreads, void* stream, std::string* err);

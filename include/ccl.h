@@ -294,6 +294,10 @@ typedef struct {
      instructions on its longest dependency chain. */
   int32_t dag_width;
   int32_t dag_depth;
+  /* generated kernel: 1 if every step reads its instruction record through the scalar
+     cache (straight-line code whose pieces are all at most 8 KiB), 0 if each workgroup
+     first copies its records into LDS */
+  int32_t specialized_scalar_records;
 } ccl_plan_info_t;
 
 int ccl_plan_info(const ccl_plan* plan, ccl_plan_info_t* info);

@@ -21,6 +21,26 @@ def test_ring_allreduce_compiles_to_one_shape(kernel):
     assert host_plan(programs.ring_allreduce(8), 4).info()["specialized_shapes"] == 0
 
 
+def test_small_pieces_read_records_through_the_scalar_cache():
+    """Straight-line code whose instruction pieces are all at most 8 KiB reads each
+    step's record with scalar loads; larger pieces, the loop form, the lazy order and
+    the interpreter keep the records the workgroup copies into LDS."""
+    def rec(S, k, **kw):
+        kw.setdefault("kernel", "specialized")
+        return host_plan(programs.ring_allreduce(8), k, max_count=S // 4, nthreads=256, slice_bytes=131072,
+                         transport="direct", **kw).info()["specialized_scalar_records"]
+    assert rec(1 << 20, 24) == 1 and rec(1 << 20, 16) == 1   # 5.3 and 8 KiB pieces
+    assert rec(32 << 10, 16, protocol="ll") == 1
+    assert rec(3 << 20, 24) == 0 and rec(2 << 20, 24) == 0   # 16 and 10.7 KiB pieces
+    assert rec(1 << 20, 16, kernel="specialized_loop") == 0
+    assert rec(1 << 20, 16, kernel="lazy") == 0
+    assert rec(1 << 20, 16, kernel="interpreter") == 0
+    def bf(S):
+        return host_plan(programs.ring_allreduce(8), 16, max_count=S // 2, dtype="bf16", nthreads=256,
+                         transport="direct", kernel="specialized").info()["specialized_scalar_records"]
+    assert bf(1 << 20) == 1 and bf(2 << 20) == 0              # bf16 pieces of 8 and 16 KiB
+
+
 def test_other_dtypes_and_protocols_compile():
     assert host_plan(programs.hier_stage_reducescatter_intra(2, 8), 2, dtype="bf16", kernel="specialized").info()[
         "specialized_shapes"] == 1
