@@ -46,10 +46,13 @@ constexpr int kMaxStraightInstructions = 24;
 // reads its fields there. Straight-line code whose pieces are all small reads each
 // step's record through the scalar cache instead and skips that start-up copy.
 // Measured on the 8-rank ring AllReduce, same plans, both ways: 1.0-1.3 us faster per
-// launch wherever the largest piece is at most 8 KiB (32 KiB - 1 MiB per rank, LL and
-// direct: 512 KiB direct 21.2 -> 19.9 us, 1 MiB k = 16 21.6 -> 20.3), 0.7-1.0 us slower
-// from 10.9 KiB pieces up (2 MiB k = 24 27.0 -> 28.0, 3 MiB k = 24 30.1 -> 30.8).
+// launch for direct-transport pieces of at most 8 KiB (512 KiB direct 21.2 -> 19.9 us,
+// 1 MiB k = 16 21.6 -> 20.3), 0.7-1.0 us slower from 10.7 KiB pieces up (2 MiB k = 24
+// 27.0 -> 28.0, 3 MiB k = 24 30.1 -> 30.8). Under the LL protocol, whose slots hold twice
+// the data, pieces up to 2.7 KiB gained the same (32 - 512 KiB per rank) and 4 KiB ones
+// lost (1 MiB k = 32: 23.9 -> 25.1 us).
 constexpr int64_t kScalarRecordMaxPiece = 8192;
+constexpr int64_t kScalarRecordMaxPieceLL = 3072;
 
 std::string hex32(uint32_t v) {
   char b[16];
@@ -190,7 +193,7 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bo
   const bool loop_form = force_loop || total > size_t(kMaxStraightInstructions);
   int64_t max_piece = 0;
   for (const auto& R : recs) max_piece = std::max<int64_t>(max_piece, R.len * hp.esz);
-  const bool scalar_recs = !loop_form && !lazy && max_piece <= kScalarRecordMaxPiece;
+  const bool scalar_recs = !loop_form && !lazy && max_piece <= (ll ? kScalarRecordMaxPieceLL : kScalarRecordMaxPiece);
   if (scalar_records) *scalar_records = scalar_recs ? 1 : 0;
   if (lazy) {
     for (const auto& D : hp.dins)

@@ -295,8 +295,8 @@ typedef struct {
   int32_t dag_width;
   int32_t dag_depth;
   /* generated kernel: 1 if every step reads its instruction record through the scalar
-     cache (straight-line code whose pieces are all at most 8 KiB), 0 if each workgroup
-     first copies its records into LDS */
+     cache (straight-line code whose pieces are all at most 8 KiB, 3 KiB under the LL
+     protocol), 0 if each workgroup first copies its records into LDS */
   int32_t specialized_scalar_records;
 } ccl_plan_info_t;
 

@@ -22,15 +22,17 @@ def test_ring_allreduce_compiles_to_one_shape(kernel):
 
 
 def test_small_pieces_read_records_through_the_scalar_cache():
-    """Straight-line code whose instruction pieces are all at most 8 KiB reads each
-    step's record with scalar loads; larger pieces, the loop form, the lazy order and
-    the interpreter keep the records the workgroup copies into LDS."""
+    """Straight-line code whose instruction pieces are all at most 8 KiB (3 KiB under
+    the LL protocol) reads each step's record with scalar loads; larger pieces, the loop
+    form, the lazy order and the interpreter keep the records the workgroup copies into
+    LDS."""
     def rec(S, k, **kw):
         kw.setdefault("kernel", "specialized")
         return host_plan(programs.ring_allreduce(8), k, max_count=S // 4, nthreads=256, slice_bytes=131072,
                          transport="direct", **kw).info()["specialized_scalar_records"]
     assert rec(1 << 20, 24) == 1 and rec(1 << 20, 16) == 1   # 5.3 and 8 KiB pieces
-    assert rec(32 << 10, 16, protocol="ll") == 1
+    assert rec(32 << 10, 16, protocol="ll") == 1 and rec(512 << 10, 24, protocol="ll") == 1  # LL: up to 3 KiB
+    assert rec(1 << 20, 32, protocol="ll") == 0                                             # 4 KiB LL pieces
     assert rec(3 << 20, 24) == 0 and rec(2 << 20, 24) == 0   # 16 and 10.7 KiB pieces
     assert rec(1 << 20, 16, kernel="specialized_loop") == 0
     assert rec(1 << 20, 16, kernel="lazy") == 0
