@@ -316,6 +316,7 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bo
   s += "  wg_begin<" + std::string(xcd_local ? "true" : "false") + ">(A, W, S, &s_abort);\n";
   if (scalar_recs) {
     s += "  const CRec* s_rec = (const CRec*)(A.recs + W.first);\n";
+    s += "  __syncthreads();  // s_abort is cleared before any wave can set it\n";
   } else {
     s += "  stage_records(A, W.first, W.n, s_rec, S.tid, S.nthr);\n";
     s += "  __syncthreads();\n";
