@@ -171,10 +171,12 @@ __device__ __forceinline__ long long run_slice(const unsigned char* pa, const un
     nvec = (n - head) / V;
     base = head * esz;
   }
-  // Vectors per thread per pass: all issued before any is consumed. bf16 needs more
-  // registers per vector for its widening adds and takes two, except in the streaming
-  // variant (long transfers), where two kept half the loads in flight and streamed
-  // 8-12 % slower at 64-256 MiB per rank; at latency-bound sizes four cost 10-17 %.
+  // Vectors per thread per pass: all issued before any is consumed. bf16 takes two,
+  // except in the streaming variant (long transfers), where two kept half the loads in
+  // flight and streamed 8-12 % slower at 64-256 MiB per rank. At latency-bound sizes four
+  // cost 10-17 % when bf16 rounding was emulated; with the hardware conversion they still
+  // cost 1 us at 1 MiB (8-rank ring 21.3 -> 22.4 us, 16-rank hierarchical 35.9 -> 37.4)
+  // and gained only at 3 MiB (35.6 -> 33.9).
   // Streaming copies and forwards of 32-bit data (one operand) take eight: a 24-rank
   // ring AllGather at 128 MiB went from 68 to 77 % of HBM peak, while eight for two
   // operands ran out of registers (ReduceScatter 69 -> 31 %).
