@@ -669,9 +669,12 @@ struct WgState {
 };
 
 template <bool XL>
-__device__ __forceinline__ void wg_begin(const ExecArgs& A, const DevWG& W, WgState& S, int* s_abort) {
+// nthr: the workgroup size. Generated kernels pass it as a constant: reading blockDim.x
+// is a load from the implicit kernel arguments that every workgroup would wait for
+// before its first instruction.
+__device__ __forceinline__ void wg_begin(const ExecArgs& A, const DevWG& W, WgState& S, int* s_abort, int nthr) {
   S.tid = threadIdx.x;
-  S.nthr = blockDim.x;
+  S.nthr = nthr;
   // This workgroup's XCD for this launch, published for the workgroups that send to it.
   S.my_tag = (A.epoch << 8) | 0x10ull | xcd_id();
   if (XL && A.xcd_tags && S.tid == 0)
@@ -851,7 +854,7 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
   const DevWG W = A.wgs[blockIdx.x];
   if (W.n == 0) return;  // padding id
   WgState S;
-  wg_begin<XL>(A, W, S, &s_abort);
+  wg_begin<XL>(A, W, S, &s_abort, blockDim.x);
   int ran = 0;
   for (int c0 = 0; c0 < W.n; c0 += kLdsRecs) {
     const int cnt = (W.n - c0 < kLdsRecs) ? (W.n - c0) : kLdsRecs;

@@ -313,7 +313,8 @@ std::string specialized_source(const HostPlan& hp, bool xcd_local, bool lazy, bo
   s += "  const DevWG W = A.wgs[blockIdx.x];\n";
   s += "  if (W.n == 0) return;  // padding id\n";
   s += "  WgState S;\n";
-  s += "  wg_begin<" + std::string(xcd_local ? "true" : "false") + ">(A, W, S, &s_abort);\n";
+  s += "  wg_begin<" + std::string(xcd_local ? "true" : "false") + ">(A, W, S, &s_abort, " +
+       std::to_string(hp.cfg.nthreads) + ");\n";
   if (scalar_recs) {
     s += "  const CRec* s_rec = (const CRec*)(A.recs + W.first);\n";
     s += "  __syncthreads();  // s_abort is cleared before any wave can set it\n";
