@@ -854,7 +854,7 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
   const DevWG W = A.wgs[blockIdx.x];
   if (W.n == 0) return;  // padding id
   WgState S;
-  wg_begin<XL>(A, W, S, &s_abort, blockDim.x);
+  wg_begin<XL>(A, W, S, &s_abort, A.nthreads);
   int ran = 0;
   for (int c0 = 0; c0 < W.n; c0 += kLdsRecs) {
     const int cnt = (W.n - c0 < kLdsRecs) ? (W.n - c0) : kLdsRecs;
