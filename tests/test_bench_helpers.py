@@ -49,7 +49,7 @@ def test_ring_factors_follow_the_sweep():
 def test_committed_traffic_records_describe_tunable_launches():
     """The headline's traffic record is taken at a launch the headline's tuner can pick
     (a factor of the 3 MiB sweep's set); every record's traffic is its fetch plus write
-    bytes, within 5 % of its plan bytes (no wasted re-reads at these sizes)."""
+    bytes (each rounded to a byte), within 5 % of its plan bytes (no wasted re-reads at these sizes)."""
     import json
     import os
     for mib, factors in ((3, bench.CONFIG_FACTORS), (32, bench.ring_factors(32 << 20)),
@@ -60,6 +60,6 @@ def test_committed_traffic_records_describe_tunable_launches():
         k, nt, sl, proto, kern = t["config"]
         assert k in factors and nt in bench.TUNE_THREADS and sl in bench.TUNE_SLICES
         assert proto in bench.PROTOCOLS and kern == bench.KERNEL
-        assert t["bytes_per_launch"] == t["fetch_bytes_per_launch"] + t["write_bytes_per_launch"]
+        assert abs(t["bytes_per_launch"] - t["fetch_bytes_per_launch"] - t["write_bytes_per_launch"]) <= 1  # rounding
         assert abs(t["bytes_per_launch"] / t["plan_bytes_per_launch"] - 1) < 0.05
         assert len(t["source_digest"]) == 16
