@@ -97,8 +97,6 @@ struct ExecArgs {
   long long timeout_ticks;     // watchdog budget per wait, device wall-clock ticks
   int32_t ll;                  // low-latency protocol: slots hold {4 data bytes, 4-byte flag} units
   uint32_t ll_flag;            // flag value of this launch's units (never 0)
-  int32_t nthreads;            // workgroup size (the interpreting kernel reads it here: blockDim.x is
-                               // a load from the implicit arguments that every workgroup waits for)
   // Per launch-grid workgroup: epoch << 8 | 0x10 | XCD id, published at the start of
   // each launch. A sender whose receiver's entry names the sender's own XCD for this
   // launch sets the transfer's flag with a plain store; otherwise (or when null) with a

@@ -193,12 +193,10 @@ int launch_executor(const ExecArgs& args, int dtype, bool xcd_local, bool stream
                     void* stream, std::string* err) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const dim3 g(nwg), b(nthreads);
-  ExecArgs a = args;
-  a.nthreads = nthreads;
   switch (dtype) {
-    case CCL_F32: launch_dt<CCL_F32>(a, xcd_local, streaming, g, b, s); break;
-    case CCL_BF16: launch_dt<CCL_BF16>(a, xcd_local, streaming, g, b, s); break;
-    case CCL_I32: launch_dt<CCL_I32>(a, xcd_local, streaming, g, b, s); break;
+    case CCL_F32: launch_dt<CCL_F32>(args, xcd_local, streaming, g, b, s); break;
+    case CCL_BF16: launch_dt<CCL_BF16>(args, xcd_local, streaming, g, b, s); break;
+    case CCL_I32: launch_dt<CCL_I32>(args, xcd_local, streaming, g, b, s); break;
     default: *err = "dtype"; return CCL_ERR_UNSUPPORTED;
   }
   hipError_t e = hipGetLastError();

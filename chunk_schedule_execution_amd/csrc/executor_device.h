@@ -669,9 +669,10 @@ struct WgState {
 };
 
 template <bool XL>
-// nthr: the workgroup size. Generated kernels pass it as a constant: reading blockDim.x
-// is a load from the implicit kernel arguments that every workgroup would wait for
-// before its first instruction.
+// nthr: the workgroup size. Straight-line generated kernels pass it as a constant:
+// blockDim.x is a load from the implicit kernel arguments that every workgroup would wait
+// for before its first instruction. Loop-form and interpreting kernels pass blockDim.x
+// (with a constant or argument value the compiler scheduled some of their loops worse).
 __device__ __forceinline__ void wg_begin(const ExecArgs& A, const DevWG& W, WgState& S, int* s_abort, int nthr) {
   S.tid = threadIdx.x;
   S.nthr = nthr;
@@ -854,7 +855,7 @@ __global__ __launch_bounds__(1024) void executor_kernel(ExecArgs A) {
   const DevWG W = A.wgs[blockIdx.x];
   if (W.n == 0) return;  // padding id
   WgState S;
-  wg_begin<XL>(A, W, S, &s_abort, A.nthreads);
+  wg_begin<XL>(A, W, S, &s_abort, blockDim.x);
   int ran = 0;
   for (int c0 = 0; c0 < W.n; c0 += kLdsRecs) {
     const int cnt = (W.n - c0 < kLdsRecs) ? (W.n - c0) : kLdsRecs;
