@@ -111,6 +111,26 @@ def same_launch(a, b, piece_bytes):
     return a[2] == b[2] or (a[2] >= piece_bytes and b[2] >= piece_bytes)
 
 
+def handoff_floor(capi, stream, piece, nthreads, ll, windows=(0,)):
+    """Median microseconds of one forwarding and one reducing hand-off of `piece` bytes
+    (a multiple of 16) by `nthreads`-thread workgroups, per window (0: lines still in
+    the L2; else the hop probe's window, lines recent launches did not touch). Under LL
+    the probe's times include the chain's first send and last plain store, so a hand-off
+    is the difference of a 15-hop and a 1-hop chain."""
+    out = {}
+    for window in windows:
+        for name, two in (("copy", False), ("reduce", True)):
+            def med(hops):
+                us, inf = capi.ccl_hop_probe(hops, piece, two, nthreads, 30, window_bytes=window,
+                                             stream=stream.cuda_stream, ll=ll)
+                if inf[1] or inf[2] or not us:
+                    raise RuntimeError(f"hop probe failed: {inf}")
+                return statistics.median(us)
+            h = (15 * med(15) - med(1)) / 14 if ll else med(15)
+            out[name + ("_cold" if window else "")] = round(h, 3)
+    return out
+
+
 def instance_bounds(lo, hi, k, align):
     """Bounds of the k instance pieces of the element range [lo, hi): lo plus floor(i (hi
     - lo) / k) rounded down to a multiple of align, and hi last (the rule the plan
@@ -316,6 +336,7 @@ def main():
     def frac(plan, N, t):
         return round(plan.bytes(N) / t / 1e9 / HBM_PEAK_GBS, 4)
 
+
     def stats(plan, N, t):
         return {"us": round(t * 1e6, 2), "plan_bytes": plan.bytes(N), "hbm_frac": frac(plan, N, t)}
 
@@ -442,13 +463,7 @@ def main():
         # piece with the executor's own slice code, once over lines still in the L2
         # and once over lines recent launches did not touch (a 4 MiB window).
         piece = -(-largest_piece(N, P, cfg[0]) * 4 // 16) * 16
-        hop = {}
-        for name, two, window in (("copy", False, 0), ("reduce", True, 0), ("copy_cold", False, 4 << 20),
-                                  ("reduce_cold", True, 4 << 20)):
-            us, inf = capi.ccl_hop_probe(15, piece, two, cfg[1], 30, window_bytes=window, stream=stream.cuda_stream)
-            if inf[1] or inf[2] or not us:
-                raise RuntimeError(f"hop probe failed: {inf}")
-            hop[name] = round(statistics.median(us), 3)
+        hop = handoff_floor(capi, stream, piece, cfg[1], False, windows=(0, 4 << 20))
         chain = (P - 1) * hop["reduce"] + (P - 2) * hop["copy"]
         chain_cold = (P - 1) * hop["reduce_cold"] + (P - 2) * hop["copy_cold"]
         out["latency_floor"] = {"piece_bytes": piece, "hop_us": hop, "chain_us": round(chain, 2),
@@ -719,6 +734,15 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
             row = {"bytes_per_rank": S, "k": c[0], "nthreads": c[1], "slice_bytes": c[2],
                    "protocol": PROTOCOLS[c[3]][0], "transport": PROTOCOLS[c[3]][1], "streaming": PROTOCOLS[c[3]][2],
                    "kernel": KERNELS[c[4]], "busbw": round(busbw_ar(S, t), 2), **stats(p, N, t)}
+            if S <= SWEEP[-1]:
+                # the hand-off floor of this pick's chain: P - 1 reducing and P - 2 forwarding
+                # hand-offs of its largest piece, over lines still in the L2
+                hf = handoff_floor(capi, stream, -(-largest_piece(N, P, c[0]) * 4 // 16) * 16, c[1],
+                                   PROTOCOLS[c[3]][0] == "ll")
+                chain = (P - 1) * hf["reduce"] + (P - 2) * hf["copy"]
+                row["handoff_us"] = hf
+                row["chain_floor_us"] = round(chain, 2)
+                row["chain_floor_frac"] = round(chain / row["us"], 4)
             if S in (1 << 20, 3 << 20, 32 << 20, 128 << 20):  # tuned versus fixed configurations
                 for name, (k, nt, sl) in (("fixed_k1_nt256_slice128k", (1, 256, min(128 << 10, S // P))),
                                           ("fixed_k8_nt512_slice256k", (8, 512, 256 << 10))):
@@ -727,7 +751,8 @@ def extras(np, torch, W, Plan, PlanConfig, capi, programs, dev, stream, ring_inp
                     row[name + "_busbw"] = round(busbw_ar(S, tf), 2)
                     release(pf)
             sweep.append(row)
-            progress(f"ring AR 8 ranks {S >> 10} KiB: {row['us']} us")
+            progress(f"ring AR 8 ranks {S >> 10} KiB: {row['us']} us" +
+                     (f", hand-off chain floor {row['chain_floor_us']} us" if "chain_floor_us" in row else ""))
             release(p)
             del ii, oo
         res["sweep"] = sweep

@@ -156,7 +156,7 @@ def _load():
                                P(ccl_tune_space), C.c_void_p, P(ccl_tune_point), P(ccl_tune_report)]),
         "ccl_copy_probe": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t, C.c_int, C.c_int, C.c_void_p]),
         "ccl_litmus_message_passing": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int64, P(C.c_int64), C.c_void_p]),
-        "ccl_hop_probe": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64,
+        "ccl_hop_probe": (C.c_int, [C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int, C.c_int64, C.c_int64,
                                     P(C.c_double), P(C.c_int64), C.c_void_p]),
         "ccl_stream_create_cu_masked": (C.c_int, [P(C.c_uint32), C.c_int, P(C.c_void_p)]),
         "ccl_stream_destroy": (C.c_int, [C.c_void_p]),
@@ -312,12 +312,13 @@ def ccl_litmus_message_passing(cross_xcd: bool, rounds: int, words: int, timeout
 
 
 def ccl_hop_probe(hops: int, nbytes: int, two_operands: bool, nthreads: int = 256, launches: int = 20,
-                  window_bytes: int = 0, timeout_us: int = 200000, stream: int = 0):
+                  window_bytes: int = 0, timeout_us: int = 200000, stream: int = 0, ll: bool = False):
     """(microseconds per hand-off of each launch, (chain workgroups off workgroup 0's XCD,
     launches with an expired wait, launches whose data arrived wrong, launches completed))."""
     us = (C.c_double * launches)()
     info = (C.c_int64 * 4)()
-    _check(_lib.ccl_hop_probe(hops, nbytes, int(bool(two_operands)), nthreads, launches, C.c_int64(window_bytes),
+    _check(_lib.ccl_hop_probe(hops, nbytes, int(bool(two_operands)), int(bool(ll)), nthreads, launches,
+                              C.c_int64(window_bytes),
                               C.c_int64(timeout_us), us, info, C.c_void_p(stream)), "ccl_hop_probe")
     return list(us[:info[3]]), tuple(info)
 

@@ -748,15 +748,17 @@ int ccl_litmus_message_passing(int cross_xcd, int rounds, int words, int64_t tim
   });
 }
 
-int ccl_hop_probe(int hops, int bytes, int two_operands, int nthreads, int launches, int64_t window_bytes,
+int ccl_hop_probe(int hops, int bytes, int two_operands, int ll, int nthreads, int launches, int64_t window_bytes,
                   int64_t timeout_us, double* us_per_hop, int64_t* info, void* stream) {
+  // a hand-off region holds the payload, or under LL its units (twice the payload)
+  const int64_t slot_bytes = (ll ? 2 : 1) * ((int64_t(bytes) + 255) / 256 * 256);
   if (!us_per_hop || !info || hops < 1 || hops > 31 || bytes < 16 || bytes > (4 << 20) || bytes % 16 ||
       nthreads < 64 || nthreads > 1024 || nthreads % 64 || launches < 1 || launches > 1000 || timeout_us < 1 ||
-      window_bytes < 0 || window_bytes > (int64_t(16) << 20) || (window_bytes > 0 && window_bytes < 2 * int64_t(bytes)))
+      window_bytes < 0 || window_bytes > (int64_t(16) << 20) || (window_bytes > 0 && window_bytes < 2 * slot_bytes))
     return set_error(CCL_ERR_INVALID_ARGUMENT, "hop probe: bad arguments");
   return guarded([&] {
-    const size_t rbytes = (size_t(bytes) + 255) / 256 * 256;
-    // region stride: the payload itself, or a window the launches step through
+    const size_t rbytes = size_t(slot_bytes);
+    // region stride: one hand-off region, or a window the launches step through
     const size_t region = window_bytes > 0 ? std::max(rbytes, size_t(window_bytes) / 256 * 256) : rbytes;
     const int chain = hops + 1;
     // data (source + one region per chain workgroup), second operands, flags, tags,
@@ -796,7 +798,7 @@ int ccl_hop_probe(int hops, int bytes, int two_operands, int nthreads, int launc
                                       static_cast<unsigned long long*>(bufs[2]), static_cast<unsigned long long*>(bufs[3]),
                                       static_cast<long long*>(bufs[4]), static_cast<unsigned int*>(bufs[5]),
                                       static_cast<unsigned long long*>(bufs[6]), epoch, timeout_ticks, region, rot,
-                                      hops, bytes, two_operands ? 1 : 0, nthreads, stream, &err);
+                                      hops, bytes, two_operands ? 1 : 0, ll ? 1 : 0, nthreads, stream, &err);
       if (rc) fail(rc, err);
       HIP_TRY(hipStreamSynchronize(s));
       unsigned int werr[4];

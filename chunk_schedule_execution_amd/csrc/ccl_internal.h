@@ -153,7 +153,7 @@ int launch_cu_probe(unsigned* out, int nblocks, long long hold_ticks, void* stre
 int launch_hop_probe(unsigned char* data, unsigned char* second, unsigned long long* flags, unsigned long long* tags,
                      long long* ticks, unsigned int* err_words, unsigned long long* abort_word, unsigned long long epoch,
                      long long timeout_ticks, size_t region, size_t rot, int hops, int bytes, int two_operands,
-                     int nthreads, void* stream, std::string* err);
+                     int ll, int nthreads, void* stream, std::string* err);
 int launch_litmus_mp(unsigned char* data, unsigned long long* flags, unsigned long long* acks,
                      unsigned long long* tags, long long* results, unsigned long long* stop, int npairs, int rounds,
                      int words, int cross, long long timeout_ticks, void* stream, std::string* err);

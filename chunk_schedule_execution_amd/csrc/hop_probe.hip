@@ -28,7 +28,7 @@ namespace {
 // workgroup 0 records it just before its flag store, so the difference is `hops` full
 // hand-offs: flag store, flag seen, loads, stores, acknowledgements.
 struct HopArgs {
-  unsigned char* data;        // hops + 2 regions of `bytes` each (region stride 256-byte aligned)
+  unsigned char* data;        // hops + 2 regions (stride `region`, 256-byte aligned): source, hand-offs, result
   unsigned char* second;      // per chain workgroup a region of zeros: the second operand of a reducing hop
   unsigned long long* flags;  // per chain workgroup, kFlagStride apart
   unsigned long long* tags;   // per chain workgroup: epoch << 8 | 0x10 | XCD id
@@ -40,6 +40,7 @@ struct HopArgs {
   size_t region;  // region stride
   size_t rot;     // this launch's offset inside every region
   int hops, bytes, two_operands;
+  int ll;  // low-latency protocol: regions 1..hops hold {4 data bytes, 4-byte flag} units
 };
 
 __device__ bool hop_wait_tag(unsigned long long* p, const HopArgs& A, unsigned long long& v) {
@@ -58,8 +59,46 @@ __device__ bool hop_wait_tag(unsigned long long* p, const HopArgs& A, unsigned l
   }
 }
 
+// The same chain under the low-latency protocol: workgroup 0 turns the source into
+// flagged units, every later workgroup polls the units it consumes, adds the second
+// operand if asked and writes units for the next one (run_ll, as an LL instruction does;
+// a receiver on another XCD gets the L2 written back first), and the last workgroup
+// writes plain data. Workgroup 0 records the wall clock as it starts, the last one once
+// its stores are acknowledged.
+__device__ void hop_probe_ll(const HopArgs& A, int j, int tid, int nthr, bool colocated, const unsigned char* in,
+                             const unsigned char* second, unsigned char* out, int* s_gave_up) {
+  const int n = A.bytes / 4;
+  const uint32_t flag = uint32_t(A.epoch);
+  bool gave_up = false;
+  if (j == 0) {
+    if (tid == 0) A.ticks[0] = wall_clock64();
+    gave_up = run_ll<CCL_F32, false, false, false, true, true>(in, in, nullptr, out, n, tid, nthr, flag, A.err,
+                                                               A.abort_word, A.epoch, A.timeout_ticks, 0);
+  } else if (j < A.hops) {
+    gave_up = A.two_operands
+                  ? run_ll<CCL_F32, true, true, false, true, true>(in, second, nullptr, out, n, tid, nthr, flag, A.err,
+                                                                   A.abort_word, A.epoch, A.timeout_ticks, j)
+                  : run_ll<CCL_F32, true, false, false, true, true>(in, in, nullptr, out, n, tid, nthr, flag, A.err,
+                                                                    A.abort_word, A.epoch, A.timeout_ticks, j);
+  } else {
+    gave_up = A.two_operands
+                  ? run_ll<CCL_F32, true, true, true, false, true>(in, second, out, nullptr, n, tid, nthr, flag, A.err,
+                                                                   A.abort_word, A.epoch, A.timeout_ticks, j)
+                  : run_ll<CCL_F32, true, false, true, false, true>(in, in, out, nullptr, n, tid, nthr, flag, A.err,
+                                                                    A.abort_word, A.epoch, A.timeout_ticks, j);
+  }
+  if (gave_up) *s_gave_up = 1;
+  if (j == A.hops || !colocated) wait_vm_stores();
+  __syncthreads();
+  if (*s_gave_up) return;  // the whole workgroup leaves together
+  if (tid == 0) {
+    if (j < A.hops && !colocated) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (j == A.hops) A.ticks[1] = wall_clock64();
+  }
+}
+
 __global__ __launch_bounds__(1024) void hop_probe_kernel(HopArgs A) {
-  __shared__ int s_go;
+  __shared__ int s_go, s_gave_up;
   __shared__ unsigned long long s_next;
   if (blockIdx.x % 8 != 0) return;
   const int j = blockIdx.x / 8, tid = threadIdx.x, nthr = blockDim.x;
@@ -67,6 +106,7 @@ __global__ __launch_bounds__(1024) void hop_probe_kernel(HopArgs A) {
   if (tid == 0) {
     __hip_atomic_store(&A.tags[j], my_tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_next = 0;
+    s_gave_up = 0;
     s_go = j == A.hops || hop_wait_tag(&A.tags[j + 1], A, s_next);
   }
   __syncthreads();
@@ -75,6 +115,10 @@ __global__ __launch_bounds__(1024) void hop_probe_kernel(HopArgs A) {
   const unsigned char* in = A.data + size_t(j) * A.region + A.rot;
   const unsigned char* second = A.second + size_t(j) * A.region + A.rot;
   unsigned char* out = A.data + size_t(j + 1) * A.region + A.rot;
+  if (A.ll) {
+    hop_probe_ll(A, j, tid, nthr, colocated, in, second, out, &s_gave_up);
+    return;
+  }
   const int n = A.bytes / 4;
   long long waited = 0;
   if (j == 0)
@@ -104,9 +148,9 @@ __global__ __launch_bounds__(1024) void hop_probe_kernel(HopArgs A) {
 int launch_hop_probe(unsigned char* data, unsigned char* second, unsigned long long* flags, unsigned long long* tags,
                      long long* ticks, unsigned int* err_words, unsigned long long* abort_word, unsigned long long epoch,
                      long long timeout_ticks, size_t region, size_t rot, int hops, int bytes, int two_operands,
-                     int nthreads, void* stream, std::string* err) {
+                     int ll, int nthreads, void* stream, std::string* err) {
   HopArgs A{data, second, flags, tags, ticks, err_words, abort_word, epoch, timeout_ticks, region, rot, hops, bytes,
-            two_operands};
+            two_operands, ll};
   hipLaunchKernelGGL(hop_probe_kernel, dim3(8 * (hops + 1)), dim3(nthreads), 0, reinterpret_cast<hipStream_t>(stream),
                      A);
   hipError_t e = hipGetLastError();

@@ -485,11 +485,17 @@ int ccl_litmus_message_passing(int cross_xcd, int rounds, int words, int64_t tim
  * stores into the next region), waits for its stores and sets its flag as a send does.
  * hops: 1..31 (the chain fits one XCD's 32 compute units at any workgroup size);
  * nthreads: a multiple of 64 in 64..1024; launches: 1..1000, each with new data and a
- * new epoch; every wait is bounded by timeout_us. window_bytes 0: every launch reuses
- * the same lines, which stay in the L2 between launches; otherwise (2 * bytes .. 16 MiB)
- * every region owns a window of that size and each launch moves its payload one
- * payload further through it, so a launch finds lines that recent launches did not
- * touch, as a collective over buffers larger than the L2 does.
+ * new epoch; every wait is bounded by timeout_us. ll: the hand-offs use the low-latency
+ * protocol instead (run_ll: workgroup 0 writes flagged 8-byte units, each later one polls
+ * the units it consumes and writes units for the next, the last writes plain data; no
+ * flag stores or acknowledgement waits; timing from workgroup 0's start, so the per-hop
+ * figure includes that first send and the last plain store: difference two hop counts
+ * for the hand-off alone). window_bytes 0: every launch reuses the same lines, which
+ * stay in the L2 between launches; otherwise (from twice a hand-off region, i.e. twice
+ * the payload, or four times under LL, up to 16 MiB) every region owns a window of that
+ * size and each launch moves its region one region further through it, so a launch
+ * finds lines that recent launches did not touch, as a collective over buffers larger
+ * than the L2 does.
  * us_per_hop (host, `launches` values): per launch, the wall-clock time from workgroup
  * 0's flag store to the last workgroup's acknowledged stores, divided by hops.
  * info (host, 4 values): [0] chain workgroups that ran on another XCD than workgroup 0,
@@ -498,7 +504,7 @@ int ccl_litmus_message_passing(int cross_xcd, int rounds, int words, int64_t tim
  * The call allocates its own device buffers, runs on `stream` and synchronizes with it
  * after every launch.
  */
-int ccl_hop_probe(int hops, int bytes, int two_operands, int nthreads, int launches, int64_t window_bytes,
+int ccl_hop_probe(int hops, int bytes, int two_operands, int ll, int nthreads, int launches, int64_t window_bytes,
                   int64_t timeout_us, double* us_per_hop, int64_t* info, void* stream);
 
 /* ---- compute-unit reservation (AutoCCL report, method 3 and its interference

@@ -206,6 +206,9 @@ def test_hop_probe_rejects_bad_arguments_before_touching_the_gpu():
         with pytest.raises(capi.CCLError) as e:
             capi.ccl_hop_probe(*args)
         assert e.value.status == capi.CCL_ERR_INVALID_ARGUMENT
+    with pytest.raises(capi.CCLError) as e:  # LL regions hold twice the payload: a window of 3 payloads is too small
+        capi.ccl_hop_probe(15, 16384, False, 256, 10, 3 * 16384, ll=True)
+    assert e.value.status == capi.CCL_ERR_INVALID_ARGUMENT
 
 
 def test_tuner_cache_answers_a_known_key_without_timing(tmp_path):

@@ -36,11 +36,13 @@ def test_message_passing_sees_every_round(cross, words):
         assert sum(1 for r in res if r[0] == r[1]) >= 6, res
 
 
+@pytest.mark.parametrize("ll", [False, True])
 @pytest.mark.parametrize("two_operands", [False, True])
 @pytest.mark.parametrize("hops,nbytes,nthreads,window", [(15, 16384, 256, 0), (15, 16384, 256, 4 << 20),
-                                                         (4, 4 << 20, 1024, 0), (31, 16, 64, 0), (3, 48, 128, 4096)])
-def test_hop_probe_chain_delivers_every_launch(two_operands, hops, nbytes, nthreads, window):
-    """The hop-latency probe runs the executor's slice code along a chain of workgroups:
+                                                         (4, 1 << 20, 1024, 0), (31, 16, 64, 0), (3, 48, 128, 4096)])
+def test_hop_probe_chain_delivers_every_launch(ll, two_operands, hops, nbytes, nthreads, window):
+    """The hop-latency probe runs the executor's slice code (or, with ll, its low-latency
+    protocol) along a chain of workgroups:
     every launch's new source arrives unchanged at the end of the chain (adding the zero
     operand keeps the bits), also where launches step through a window (a payload off
     the 256-byte grid of the window's steps included), no wait expires, and each
@@ -49,10 +51,10 @@ def test_hop_probe_chain_delivers_every_launch(two_operands, hops, nbytes, nthre
     another XCD gets a full release, as in the executor.)"""
     import torch
     launches = 10
-    case(f"hop probe hops={hops} bytes={nbytes} two_operands={two_operands} nthreads={nthreads} window={window}")
+    case(f"hop probe hops={hops} bytes={nbytes} two_operands={two_operands} nthreads={nthreads} window={window} ll={ll}")
     us, (off_xcd, expired, wrong, done) = capi.ccl_hop_probe(
         hops, nbytes, two_operands, nthreads, launches, window_bytes=window, timeout_us=200000,
-        stream=torch.cuda.current_stream().cuda_stream)
+        stream=torch.cuda.current_stream().cuda_stream, ll=ll)
     print(f"[hop] {sorted(us)[launches // 2]:.3f} us per hand-off, {off_xcd} chain workgroups off XCD 0", flush=True)
     assert expired == 0 and wrong == 0 and done == launches, (off_xcd, expired, wrong, done)
     assert len(us) == launches and all(0 < u < 1000 for u in us), us
