@@ -437,15 +437,28 @@ __device__ __forceinline__ uint32_t add_word(uint32_t a, uint32_t b) {
   return Arith<DT>::add(a, b);
 }
 
+__device__ __forceinline__ unsigned long long use_here(unsigned long long v);
+
+// Whether outgoing LL units may be plain stores: only in the XCD-local layout, and only
+// when the receiver's tag for this launch names this workgroup's XCD (here_tag). The
+// caller loads the tag before the step's data loads; compared at the first unit store,
+// it has returned with them (a wave's loads return in order), so the decision adds no
+// wait. Otherwise the units are agent-coherent stores, which need no release after them.
+template <bool XL>
+__device__ __forceinline__ bool ll_plain_units(unsigned long long peer_tag, unsigned long long here_tag) {
+  return XL && __builtin_amdgcn_readfirstlane(uint32_t(use_here(peer_tag) == here_tag)) != 0u;
+}
+
 // The wait context travels as separate scalars: a struct argument would go through
-// the stack.
+// the stack. peer_tag / here_tag: see ll_plain_units (both 0: plain units in the
+// XCD-local layout, the caller makes them visible).
 template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL>
 __device__ __forceinline__ bool run_ll(const unsigned char* pa, const unsigned char* pb, unsigned char* pd,
                                                  unsigned char* pt, int n, int tid, int nthr, uint32_t flag,
                                                  unsigned int* err, unsigned long long* abort_word,
-                                                 unsigned long long epoch, long long timeout_ticks, int instr) {
+                                                 unsigned long long epoch, long long timeout_ticks, int instr,
+                                                 unsigned long long peer_tag = 0, unsigned long long here_tag = 0) {
   const WaitCtx w{err, abort_word, epoch, timeout_ticks, instr};
-  constexpr int CT = XL ? kCpolNone : kCpolSc1;  // outgoing units: plain (XCD-local layout) or coherent
   typedef Arith<DT> Ar;
   constexpr int esz = Ar::esz;
   const int bytes = n * esz;
@@ -483,8 +496,13 @@ __device__ __forceinline__ bool run_ll(const unsigned char* pa, const unsigned c
       if (has1) st16<kCpolNone>(rD, 16 * q1, v1);
     }
     if (SEND) {
-      ll_store_quad<CT>(rT, 32 * q, v0, flag);
-      if (has1) ll_store_quad<CT>(rT, 32 * q1, v1, flag);
+      if (ll_plain_units<XL>(peer_tag, here_tag)) {
+        ll_store_quad<kCpolNone>(rT, 32 * q, v0, flag);
+        if (has1) ll_store_quad<kCpolNone>(rT, 32 * q1, v1, flag);
+      } else {
+        ll_store_quad<kCpolSc1>(rT, 32 * q, v0, flag);
+        if (has1) ll_store_quad<kCpolSc1>(rT, 32 * q1, v1, flag);
+      }
     }
   }
   for (int u = 4 * nquads + tid; u < nunits; u += nthr) {
@@ -501,7 +519,10 @@ __device__ __forceinline__ bool run_ll(const unsigned char* pa, const unsigned c
     if (DSTA) st_word<esz>(rD, o, v, second);
     if (SEND) {
       v2u unit = {v, flag};
-      __builtin_amdgcn_raw_buffer_store_b64(unit, rT, 8 * u, 0, CT);
+      if (ll_plain_units<XL>(peer_tag, here_tag))
+        __builtin_amdgcn_raw_buffer_store_b64(unit, rT, 8 * u, 0, kCpolNone);
+      else
+        __builtin_amdgcn_raw_buffer_store_b64(unit, rT, 8 * u, 0, kCpolSc1);
     }
   }
   return false;
@@ -511,21 +532,24 @@ template <int DT, bool RECV, bool SRCB, bool DSTA, bool SEND, bool XL>
 __device__ __attribute__((noinline)) bool run_ll_call(const unsigned char* pa, const unsigned char* pb,
                                                       unsigned char* pd, unsigned char* pt, int n, int tid, int nthr,
                                                       uint32_t flag, unsigned int* err, unsigned long long* abort_word,
-                                                      unsigned long long epoch, long long timeout_ticks, int instr) {
+                                                      unsigned long long epoch, long long timeout_ticks, int instr,
+                                                      unsigned long long peer_tag, unsigned long long here_tag) {
   return run_ll<DT, RECV, SRCB, DSTA, SEND, XL>(pa, pb, pd, pt, n, tid, nthr, flag, err, abort_word, epoch,
-                                                timeout_ticks, instr);
+                                                timeout_ticks, instr, peer_tag, here_tag);
 }
 
 template <int DT, bool XL>
 __device__ __forceinline__ bool dispatch_ll(uint32_t op, const unsigned char* pa, const unsigned char* pb,
                                             unsigned char* pd, unsigned char* pt, int n, int tid, int nthr,
-                                            uint32_t flag, const WaitCtx& w) {
-#define CCL_CASE(R, B, D, T)                                                                                     \
-  case ((R) ? OPB_RECV : 0u) | ((B) ? OPB_SRCB : 0u) | ((D) ? OPB_DSTA : 0u) | ((T) ? OPB_SEND : 0u):            \
-    return (DT == CCL_BF16) ? run_ll_call<DT, R, B, D, T, XL>(pa, pb, pd, pt, n, tid, nthr, flag, w.err,        \
-                                                              w.abort_word, w.epoch, w.timeout_ticks, w.instr)   \
+                                            uint32_t flag, const WaitCtx& w, unsigned long long peer_tag,
+                                            unsigned long long here_tag) {
+#define CCL_CASE(R, B, D, T)                                                                                      \
+  case ((R) ? OPB_RECV : 0u) | ((B) ? OPB_SRCB : 0u) | ((D) ? OPB_DSTA : 0u) | ((T) ? OPB_SEND : 0u):             \
+    return (DT == CCL_BF16) ? run_ll_call<DT, R, B, D, T, XL>(pa, pb, pd, pt, n, tid, nthr, flag, w.err,         \
+                                                              w.abort_word, w.epoch, w.timeout_ticks, w.instr,   \
+                                                              peer_tag, here_tag)                                \
                             : run_ll<DT, R, B, D, T, XL>(pa, pb, pd, pt, n, tid, nthr, flag, w.err, w.abort_word, \
-                                                         w.epoch, w.timeout_ticks, w.instr);
+                                                         w.epoch, w.timeout_ticks, w.instr, peer_tag, here_tag);
   switch (op & 15u) {
     CCL_CASE(false, false, true, false)
     CCL_CASE(false, false, false, true)
@@ -782,7 +806,8 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
   }
   // a send whose receive is skipped sets no flag and need not wait for its stores
   const bool flagged_send = (op & OPB_SEND) && !(opw & OPB_NOFLAG);
-  // the receiver's XCD tag: loaded now, first used after this instruction's stores
+  // the receiver's XCD tag: loaded now, first used after this instruction's stores (LL:
+  // at its first unit store)
   unsigned long long peer_tag = 0;
   if (XL && flagged_send && A.xcd_tags) {
     const int peer = uni(R.peer_wg);
@@ -796,14 +821,19 @@ __device__ __forceinline__ bool run_instr(const ExecArgs& A, WgState& S, const D
     // one pass over the whole range (at s_begin 0); receivers poll the units they consume
     if (s_begin == 0) {
       const WaitCtx wc{A.err, A.abort_word, A.epoch, A.timeout_ticks, gi};
-      const bool gave_up = len > 0 && dispatch_ll<DT, XL>(op, pa, pb, pd, pt, int(len), tid, nthr, A.ll_flag, wc);
-      // plain units for a receiver on another XCD leave this XCD's L2 with a release
-      const bool colocated = !XL || use_here(peer_tag) == S.my_tag;
-      if ((op & OPB_SEND) && !colocated) wait_vm_stores();
+      // Units for a receiver that shares this XCD's L2 are plain stores, any others
+      // agent-coherent ones (ll_plain_units), so nothing waits for the stores and no
+      // release follows them. Deciding after the stores instead (wait, then release for
+      // a receiver elsewhere) made every step wait for its stores, even when no release
+      // ran: 8-rank ring launches 0.1-1.1 us slower (32 KiB at k = 1: 18.4 against
+      // 17.3 us). A send whose receive is skipped (no flag) has no reader before the
+      // launch ends: plain units.
+      const unsigned long long here_tag = (XL && flagged_send) ? S.my_tag : 0ull;
+      const bool gave_up =
+          len > 0 && dispatch_ll<DT, XL>(op, pa, pb, pd, pt, int(len), tid, nthr, A.ll_flag, wc, peer_tag, here_tag);
       if (gave_up) *S.s_abort = 1;
       __syncthreads();
       if (*S.s_abort) return false;
-      if ((op & OPB_SEND) && !colocated && tid == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     }
   } else {
     const int64_t se = A.slice_elems;
