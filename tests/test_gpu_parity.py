@@ -468,7 +468,8 @@ def test_ll_repeated_launches():
 def test_xcd_local_and_coherent_stores_agree(protocol, k, nt, num_cus):
     """An XCD-aligned layout writes transfers with plain stores and sets each flag with a
     plain store when the receiving workgroup published the sender's own XCD, else with a
-    release. With a budget of 10 CUs the layout estimate rejects the aligned grid: the plan keeps
+    release; under LL the units themselves are plain stores for such a receiver and
+    agent-coherent stores for any other. With a budget of 10 CUs the layout estimate rejects the aligned grid: the plan keeps
     coherent stores, or (forced) runs the XCD-local variant with most receivers on other
     XCDs, so both flag kinds occur. Every way the bits are the chain order, launch after
     launch."""
