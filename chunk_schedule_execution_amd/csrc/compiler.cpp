@@ -920,6 +920,51 @@ int len_idx_of(const HostPlan& hp, int t, int depth = 0) {
   fail(CCL_ERR_INTERNAL, "instruction without a chunk range");
 }
 
+// Under LL a workgroup's waves only need a barrier after an instruction when a later
+// instruction of the same workgroup touches a local chunk range it writes, or writes a
+// range it reads: those accesses may use another thread-to-element mapping. The check
+// runs on chunk indices, so it holds for every count; a range whose length is another
+// chunk's is widened by one chunk at its end, since ragged counts give chunks different
+// lengths.
+// Inputs and outputs are separate buffers (out of place), the scratch buffer a third.
+// An instruction that sets a completion flag keeps its barrier: the flag follows the
+// stores of every wave.
+static void mark_unsynced(HostPlan& hp) {
+  struct Acc {
+    int buf, lo, hi;  // chunk indices [lo, hi)
+  };
+  auto accesses = [&](const DevInstr& D, std::vector<Acc>& rd, std::vector<Acc>& wr) {
+    rd.clear();
+    wr.clear();
+    // the element range's length is that of chunk pad0: at another chunk's offset it may
+    // run past that chunk's end by less than a chunk
+    auto acc = [&](int buf, int idx) { return Acc{buf, idx, idx + D.cnt + (idx == D.pad0 ? 0 : 1)}; };
+    if (!(D.op & OPB_RECV) || (D.op & OPB_LOCAL_IN)) rd.push_back(acc(D.a_buf, D.a_idx));
+    if (D.op & OPB_SRCB) rd.push_back(acc(D.b_buf, D.b_idx));
+    if (D.op & OPB_DSTA) wr.push_back(acc(D.d_buf, D.d_idx));
+  };
+  auto meet = [](const std::vector<Acc>& x, const std::vector<Acc>& y) {
+    for (const Acc& a : x)
+      for (const Acc& b : y)
+        if (a.buf == b.buf && a.lo < b.hi && b.lo < a.hi) return true;
+    return false;
+  };
+  std::vector<Acc> ri, wi, rj, wj;
+  for (const DevWG& G : hp.dwg) {
+    for (int i = G.first; i < G.first + G.n; ++i) {
+      DevInstr& D = hp.dins[i];
+      if (D.done_flag >= 0) continue;
+      accesses(D, ri, wi);
+      bool hazard = false;
+      for (int j = i + 1; j < G.first + G.n && !hazard; ++j) {
+        accesses(hp.dins[j], rj, wj);
+        hazard = meet(wi, rj) || meet(wi, wj) || meet(ri, wj);
+      }
+      if (!hazard) D.op |= OPB_NOSYNC;
+    }
+  }
+}
+
 void lower(HostPlan& hp) {
   int k = hp.k;
   int nW = int(hp.wgs.size()), nX = int(hp.xf.size()), nD = hp.num_done_flags;
@@ -1034,6 +1079,7 @@ void lower(HostPlan& hp) {
   int64_t se = hp.cfg.slice_bytes / hp.esz;
   se = se / 64 * 64;
   hp.slice_elems = std::max<int64_t>(se, 64);
+  if (hp.cfg.flags & CCL_FLAG_LL) mark_unsynced(hp);
 }
 
 }  // namespace

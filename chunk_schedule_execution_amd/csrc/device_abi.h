@@ -16,8 +16,12 @@ constexpr int kNumBufs = 3;  // input, output, scratch
 // before reading it.
 // OPB_SKIP marks such a receive that nothing depends on (it is not executed) and
 // OPB_NOFLAG a send whose receiver is skipped (no flag, no wait for its stores).
+// OPB_NOSYNC (LL plans) no later instruction of the workgroup touches a local chunk range
+// this one writes or writes one it reads, and it sets no completion flag: its waves go
+// on to the next instruction without a workgroup barrier.
 enum : uint32_t {
-  OPB_RECV = 1u, OPB_SRCB = 2u, OPB_DSTA = 4u, OPB_SEND = 8u, OPB_LOCAL_IN = 16u, OPB_SKIP = 32u, OPB_NOFLAG = 64u
+  OPB_RECV = 1u, OPB_SRCB = 2u, OPB_DSTA = 4u, OPB_SEND = 8u, OPB_LOCAL_IN = 16u, OPB_SKIP = 32u, OPB_NOFLAG = 64u,
+  OPB_NOSYNC = 128u
 };
 constexpr uint32_t kStagingBuf = 15u;  // DevExec::op target-buffer field: the staging pool
 
